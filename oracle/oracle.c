@@ -1,0 +1,265 @@
+/*
+ * oracle.c -- plain, slow, sequential fp64 reference of the selective scan (S6).
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may call, link or load
+ * this file; only the tests, the smoke check and the benchmark's CPU-baseline leg
+ * use it.  It shares no code, header, table or constant with the HIP library.
+ *
+ * Every routine takes its inputs as fp64 arrays (the caller converts the exact
+ * bf16 / fp32 bits the GPU receives) and computes in fp64, one independent
+ * single-input single-output channel (b, d) at a time, stepping t = 0 .. L-1.
+ *
+ * Sources (pages, sections):
+ *  - "Mamba explained" translation (hackbyte.io), section on the state: Eq 1a
+ *    h'(t) = A h(t) + B x(t) and Eq 1b y(t) = C h(t) + D x(t); section on
+ *    discretization: the first-order (Euler) step h_{t+1} ~ (I + dA) h_t + (dB) x_t.
+ *  - "Mamba: S4 epic upgrade" (hk.pswp.cn), sections "TL;DR" (shapes u, delta:
+ *    (B,L,D); B, C: (B,L,N); A: (D,N)), "S4 intro" (zero-order hold, one SISO
+ *    system per input channel) and "parameter-efficient data dependence"
+ *    (A_bar = exp(delta A), A diagonal and real).
+ *  - Gu & Dao wiki note (git.lyz.one), section "From S4 to S6": B_t = s_B(x_t),
+ *    C_t = s_C(x_t), delta_t = tau(Delta + s_Delta(x_t)); section "Mamba
+ *    architecture": SiLU gating branch.
+ *  - "A Visual Guide to Mamba" summary (wenxiaobai), section "The Scan Operation":
+ *    each state is the previous state times A plus the current input times B;
+ *    section "Hardware-aware Algorithm": states are recomputed for the backward.
+ *  - "A Survey of Mamba" summary (csdn), sections "SSM" (ZOH discretised form,
+ *    D x(t) is the skip connection) and "Selection" (Broadcast_D of delta terms).
+ *
+ * Readings taken where the pages are silent or garbled:
+ *  - tau_Delta is softplus; the per-channel parameter Delta enters as a bias added
+ *    to the raw per-token delta before softplus.
+ *  - exact ZOH input matrix: B_bar = (exp(dA) - 1) / A * B, with the limit d*B at
+ *    A = 0.  "Euler" switches only B_bar to d*B; A_bar stays exp(dA).
+ *  - h_t = A_bar_t h_{t-1} + B_bar_t u_t, y_t uses h_t (current input included).
+ *  - initial state 0 unless h0 is given; out = y * silu(z) with the D skip inside
+ *    the gate.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORACLE_ZOH 0
+#define ORACLE_EULER 1
+
+/* softplus(x) = log(1 + e^x), evaluated without overflow. */
+double oracle_softplus(double x) {
+  if (x > 0.0) return x + log1p(exp(-x));
+  return log1p(exp(x));
+}
+
+/* logistic sigma(x) = 1 / (1 + e^-x) */
+static double sigmoid(double x) {
+  if (x >= 0.0) return 1.0 / (1.0 + exp(-x));
+  double e = exp(x);
+  return e / (1.0 + e);
+}
+
+/* Discretise one (step dt, diagonal entry a) pair.
+ * abar = exp(dt * a) (ZOH state matrix; also used in Euler mode).
+ * bcoef = (exp(dt*a) - 1) / a  (exact ZOH), limit dt at a == 0;  dt for Euler.
+ * The input coefficient multiplies B and u: B_bar u = bcoef * B * u. */
+void oracle_discretize(double dt, double a, int disc, double* abar, double* bcoef) {
+  *abar = exp(dt * a);
+  if (disc == ORACLE_EULER || a == 0.0) {
+    *bcoef = dt;
+  } else {
+    *bcoef = expm1(dt * a) / a;
+  }
+}
+
+/* d(bcoef)/d(a) for the exact ZOH coefficient.  f(a) = expm1(dt a)/a, so
+ * f'(a) = (dt a e^{dt a} - expm1(dt a)) / a^2.  Near dt*a = 0 the closed form
+ * cancels, so the Taylor series of f'(a) = dt^2 sum_j (j+1) (dt a)^j / (j+2)!
+ * is summed instead (terms to j = 6; the first dropped term is < 1e-17 relative
+ * for |dt a| < 1e-2). */
+static double zoh_dbcoef_da(double dt, double a) {
+  double x = dt * a;
+  if (fabs(x) < 1e-2) {
+    double s = 0.0, p = 1.0, fact = 2.0; /* (j+2)! for j = 0 */
+    for (int j = 0; j <= 6; ++j) {
+      s += (double)(j + 1) * p / fact;
+      p *= x;
+      fact *= (double)(j + 3);
+    }
+    return dt * dt * s;
+  }
+  return (x * exp(x) - expm1(x)) / (a * a);
+}
+
+static double step_size(double delta, double bias, int softplus) {
+  double x = delta + bias;
+  return softplus ? oracle_softplus(x) : x;
+}
+
+/*
+ * Forward scan.  Shapes (row-major, contiguous):
+ *   u, delta, z, out : (Bt, L, D)      A : (D, N)        Bm, Cm : (Bt, L, N)
+ *   Dskip, bias : (D) or NULL           h0, h_last : (Bt, D, N) or NULL
+ * out receives y * silu(z) when z != NULL, else y.
+ * nthreads > 1 splits the independent channels over OpenMP threads.
+ */
+int oracle_fwd(int64_t Bt, int64_t L, int64_t D, int64_t N, int disc, int softplus,
+               const double* u, const double* delta, const double* A,
+               const double* Bm, const double* Cm, const double* Dskip,
+               const double* bias, const double* z, const double* h0,
+               double* out, double* h_last, int nthreads) {
+  if (Bt < 0 || L < 0 || D < 0 || N < 1 || N > 64) return -1;
+  int64_t nch = Bt * D;
+#ifdef _OPENMP
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads > 0 ? nthreads : 1)
+#endif
+  for (int64_t ch = 0; ch < nch; ++ch) {
+    int64_t b = ch / D, d = ch % D;
+    double h[64];
+    for (int64_t n = 0; n < N; ++n) h[n] = h0 ? h0[(b * D + d) * N + n] : 0.0;
+    double dsk = Dskip ? Dskip[d] : 0.0;
+    double bi = bias ? bias[d] : 0.0;
+    for (int64_t t = 0; t < L; ++t) {
+      int64_t i = (b * L + t) * D + d;
+      double dt = step_size(delta[i], bi, softplus);
+      double ut = u[i];
+      double y = 0.0;
+      for (int64_t n = 0; n < N; ++n) {
+        double abar, bcoef;
+        oracle_discretize(dt, A[d * N + n], disc, &abar, &bcoef);
+        int64_t j = (b * L + t) * N + n;
+        h[n] = abar * h[n] + bcoef * Bm[j] * ut;   /* recurrence */
+        y += Cm[j] * h[n];                          /* output contraction */
+      }
+      y += dsk * ut;                                /* skip connection D u */
+      if (z) y *= z[i] * sigmoid(z[i]);             /* silu(z) gate */
+      out[i] = y;
+    }
+    if (h_last)
+      for (int64_t n = 0; n < N; ++n) h_last[(b * D + d) * N + n] = h[n];
+  }
+  (void)nthreads;
+  return 0;
+}
+
+/*
+ * Backward of oracle_fwd by the chain rule, with every intermediate state of a
+ * channel kept (the GPU recomputes them instead).  g = d(loss)/d(out), (Bt,L,D).
+ * Outputs (all overwritten, never accumulated into):
+ *   du, ddelta (w.r.t. the raw delta, through softplus), dz : (Bt,L,D)
+ *   dA : (D,N)   dB, dC : (Bt,L,N)   dDskip, dbias : (D)   dh0 : (Bt,D,N)
+ * Any output pointer may be NULL (dz is ignored when z is NULL).
+ */
+int oracle_bwd(int64_t Bt, int64_t L, int64_t D, int64_t N, int disc, int softplus,
+               const double* u, const double* delta, const double* A,
+               const double* Bm, const double* Cm, const double* Dskip,
+               const double* bias, const double* z, const double* h0,
+               const double* g,
+               double* du, double* ddelta, double* dA, double* dB, double* dC,
+               double* dDskip, double* dbias, double* dz, double* dh0) {
+  if (Bt < 0 || L < 0 || D < 0 || N < 1 || N > 64) return -1;
+  double* hs = (double*)malloc(sizeof(double) * (size_t)(L + 1) * (size_t)N);
+  double* dts = (double*)malloc(sizeof(double) * (size_t)(L > 0 ? L : 1));
+  double* gys = (double*)malloc(sizeof(double) * (size_t)(L > 0 ? L : 1));
+  if (!hs || !dts || !gys) { free(hs); free(dts); free(gys); return -2; }
+  if (dA) memset(dA, 0, sizeof(double) * (size_t)(D * N));
+  if (dB) memset(dB, 0, sizeof(double) * (size_t)(Bt * L * N));
+  if (dC) memset(dC, 0, sizeof(double) * (size_t)(Bt * L * N));
+  if (dDskip) memset(dDskip, 0, sizeof(double) * (size_t)D);
+  if (dbias) memset(dbias, 0, sizeof(double) * (size_t)D);
+
+  for (int64_t b = 0; b < Bt; ++b) {
+    for (int64_t d = 0; d < D; ++d) {
+      double dsk = Dskip ? Dskip[d] : 0.0;
+      double bi = bias ? bias[d] : 0.0;
+      /* forward, keeping h_{-1} .. h_{L-1} in hs[0 .. L] */
+      for (int64_t n = 0; n < N; ++n) hs[n] = h0 ? h0[(b * D + d) * N + n] : 0.0;
+      for (int64_t t = 0; t < L; ++t) {
+        int64_t i = (b * L + t) * D + d;
+        double dt = step_size(delta[i], bi, softplus);
+        dts[t] = dt;
+        double y = 0.0;
+        for (int64_t n = 0; n < N; ++n) {
+          double abar, bcoef;
+          oracle_discretize(dt, A[d * N + n], disc, &abar, &bcoef);
+          int64_t j = (b * L + t) * N + n;
+          double hn = abar * hs[t * N + n] + bcoef * Bm[j] * u[i];
+          hs[(t + 1) * N + n] = hn;
+          y += Cm[j] * hn;
+        }
+        y += dsk * u[i];
+        double gy = g[i];
+        if (z) {
+          double s = sigmoid(z[i]);
+          if (dz) dz[i] = g[i] * y * s * (1.0 + z[i] * (1.0 - s));
+          gy = g[i] * z[i] * s;
+        }
+        gys[t] = gy;   /* d(loss)/dy_t */
+        if (dDskip) dDskip[d] += gy * u[i];
+      }
+      /* reverse sweep; mu[n] = A_bar_{t+1} * lambda_{t+1} carried backwards */
+      double mu[64];
+      for (int64_t n = 0; n < N; ++n) mu[n] = 0.0;
+      for (int64_t t = L - 1; t >= 0; --t) {
+        int64_t i = (b * L + t) * D + d;
+        double dt = dts[t], gy = gys[t], ut = u[i];
+        double ddt = 0.0, dut = gy * dsk;
+        for (int64_t n = 0; n < N; ++n) {
+          double a = A[d * N + n];
+          double abar, bcoef;
+          oracle_discretize(dt, a, disc, &abar, &bcoef);
+          int64_t j = (b * L + t) * N + n;
+          double lam = gy * Cm[j] + mu[n];          /* d(loss)/dh_t */
+          double hprev = hs[t * N + n];
+          if (dC) dC[j] += gy * hs[(t + 1) * N + n];
+          double dabar = lam * hprev;
+          double dbb = lam * ut;                    /* d(loss)/d(B_bar) */
+          dut += lam * bcoef * Bm[j];
+          if (dB) dB[j] += dbb * bcoef;
+          /* d(bcoef)/d(dt) and d(bcoef)/d(a) */
+          double dc_ddt, dc_da;
+          if (disc == ORACLE_EULER) { dc_ddt = 1.0; dc_da = 0.0; }
+          else if (a == 0.0) { dc_ddt = 1.0; dc_da = 0.5 * dt * dt; }
+          else { dc_ddt = abar; dc_da = zoh_dbcoef_da(dt, a); }
+          ddt += dabar * abar * a + dbb * Bm[j] * dc_ddt;
+          if (dA) dA[d * N + n] += dabar * abar * dt + dbb * Bm[j] * dc_da;
+          mu[n] = abar * lam;
+        }
+        if (du) du[i] = dut;
+        double dx = softplus ? ddt * sigmoid(delta[i] + bi) : ddt;
+        if (ddelta) ddelta[i] = dx;
+        if (dbias) dbias[d] += dx;
+      }
+      if (dh0)
+        for (int64_t n = 0; n < N; ++n) dh0[(b * D + d) * N + n] = mu[n];
+    }
+  }
+  free(hs); free(dts); free(gys);
+  return 0;
+}
+
+/*
+ * One recurrent step (inference mode): h (Bt,D,N) is read and overwritten;
+ * u, delta, z, out are (Bt,D); Bm, Cm are (Bt,N).
+ */
+int oracle_step(int64_t Bt, int64_t D, int64_t N, int disc, int softplus,
+                double* h, const double* u, const double* delta, const double* A,
+                const double* Bm, const double* Cm, const double* Dskip,
+                const double* bias, const double* z, double* out) {
+  if (Bt < 0 || D < 0 || N < 1 || N > 64) return -1;
+  for (int64_t b = 0; b < Bt; ++b) {
+    for (int64_t d = 0; d < D; ++d) {
+      int64_t i = b * D + d;
+      double dt = step_size(delta[i], bias ? bias[d] : 0.0, softplus);
+      double y = 0.0;
+      for (int64_t n = 0; n < N; ++n) {
+        double abar, bcoef;
+        oracle_discretize(dt, A[d * N + n], disc, &abar, &bcoef);
+        double* hn = &h[i * N + n];
+        *hn = abar * *hn + bcoef * Bm[b * N + n] * u[i];
+        y += Cm[b * N + n] * *hn;
+      }
+      y += (Dskip ? Dskip[d] : 0.0) * u[i];
+      if (z) y *= z[i] * sigmoid(z[i]);
+      out[i] = y;
+    }
+  }
+  return 0;
+}

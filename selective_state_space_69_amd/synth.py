@@ -1,0 +1,159 @@
+"""Seeded synthetic inputs for the selective scan.
+
+This module only draws random numbers and lays them out; it contains none of the
+scan's arithmetic, so both the HIP path and the fp64 oracle can be fed from it.
+
+The value recipe follows the shapes and parameterisation of the pages
+("Mamba: S4 epic upgrade", section "TL;DR": u, delta: (B,L,D); B, C: (B,L,N);
+A: (D,N)) with the standard selective-scan initialisation:
+  * u, z, B, C ~ N(0, 1); raw delta ~ N(0, 0.1) (standard deviation 0.1);
+  * a per-channel step bias chosen so that softplus(bias) is log-uniform in a
+    range (the bias is the inverse softplus of dt = exp(U(ln lo, ln hi)));
+  * D_skip ~ U(0.5, 1.5);
+  * A[d, n] = -(n + 1) (the real diagonal "S4D-Real" initialisation), or, for
+    tests that must not rely on that structure, other real diagonals.
+bf16 workloads are rounded once from the fp32 draws with round-to-nearest-even,
+and the same bits are given to both sides.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import numpy as np
+
+
+def round_to_bf16(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to the nearest bfloat16 (ties to even); returns float32
+    arrays whose low 16 bits are zero (exact bf16 values)."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    bits = x.view(np.uint32)
+    lsb = (bits >> np.uint32(16)) & np.uint32(1)
+    r = (bits + np.uint32(0x7FFF) + lsb) & np.uint32(0xFFFF0000)
+    return r.view(np.float32)
+
+
+def bf16_bits(x: np.ndarray) -> np.ndarray:
+    """uint16 bit patterns of float32 values that are exact bf16 numbers."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    return (x.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+
+
+@dataclass(frozen=True)
+class Workload:
+    """One named workload: shapes, number type and discretisation."""
+    name: str
+    B: int
+    L: int
+    D: int
+    N: int
+    dtype: str              # "f32" or "bf16" (u, delta, z, B, C)
+    disc: str               # "zoh" or "euler"
+    dt_range: tuple = (1e-3, 1e-1)
+    seed: int = 0
+    op: str = "fwd"         # "fwd" or "bwd"
+    desc: str = ""
+
+    @property
+    def elements(self) -> int:
+        return self.B * self.L * self.D * self.N
+
+
+# The workloads the scan is measured and checked on.  Widths follow Mamba-130M
+# (d_model 768 x expand 2 = 1536) and Mamba-2.8B (2560 x 2 = 5120); N = 16.
+WORKLOADS = {
+    w.name: w for w in [
+        Workload("fwd_tiny_f32_b1_l256_d64", 1, 256, 64, 16, "f32", "zoh", seed=1000,
+                 desc="tiny fp32 forward, exact ZOH, silu gate"),
+        Workload("fwd_130m_bf16_b8_l2048_d1536", 8, 2048, 1536, 16, "bf16", "euler", seed=1001,
+                 desc="Mamba-130M-shaped layer forward, Euler B_bar"),
+        Workload("fwd_2p8b_bf16_b8_l2048_d5120", 8, 2048, 5120, 16, "bf16", "zoh", seed=1002,
+                 desc="Mamba-2.8B-shaped layer forward, exact ZOH"),
+        Workload("fwd_2p8b_bf16_b2_l8192_d5120", 2, 8192, 5120, 16, "bf16", "zoh", seed=1012,
+                 desc="Mamba-2.8B-shaped layer forward, 8192-long variant"),
+        Workload("fwd_long_bf16_b1_l1048576_d256", 1, 1048576, 256, 16, "bf16", "zoh",
+                 dt_range=(1e-4, 1e-2), seed=1003,
+                 desc="million-step forward through the chunked carry"),
+        Workload("bwd_130m_bf16_b8_l2048_d1536", 8, 2048, 1536, 16, "bf16", "euler", seed=1004,
+                 op="bwd", desc="backward with recompute at the Mamba-130M shape"),
+    ]
+}
+
+
+@dataclass
+class Inputs:
+    """Host arrays (float32 holding the exact values both sides receive)."""
+    u: np.ndarray
+    delta: np.ndarray
+    A: np.ndarray
+    B: np.ndarray
+    C: np.ndarray
+    D: np.ndarray | None
+    delta_bias: np.ndarray | None
+    z: np.ndarray | None
+    h0: np.ndarray | None = None
+    dy: np.ndarray | None = None
+    dtype: str = "f32"
+    meta: dict = field(default_factory=dict)
+
+
+def make_A(D: int, N: int, mode: str = "s4d_real", rng: np.random.Generator | None = None):
+    """Diagonal A (D, N), float32.
+    s4d_real : A[d, n] = -(n + 1)
+    random   : A = -exp(N(0, 1))      (no integer structure)
+    mixed    : random, with a few exact zeros and small positive entries
+    """
+    if mode == "s4d_real":
+        return np.tile(-np.arange(1, N + 1, dtype=np.float32), (D, 1))
+    rng = rng or np.random.default_rng(7)
+    A = -np.exp(rng.standard_normal((D, N))).astype(np.float32)
+    if mode == "mixed":
+        A[0, 0] = 0.0
+        if D > 1:
+            A[1, N - 1] = 0.0
+        if D > 2:
+            A[2, 0] = np.float32(0.05)   # mildly unstable entry, still finite over short L
+    return A
+
+
+def make_inputs(B: int, L: int, D: int, N: int, seed: int, dtype: str = "f32",
+                dt_range=(1e-3, 1e-1), a_mode: str = "s4d_real", with_z: bool = True,
+                with_bias: bool = True, with_D: bool = True, with_h0: bool = False,
+                with_dy: bool = False, delta_std: float = 0.1) -> Inputs:
+    """Draw one seeded problem.  Order of draws (float32): u, z, B, C, raw delta,
+    U for the log step, D_skip, dy; then h0 (if asked) and A (non-default modes)."""
+    rng = np.random.default_rng(seed)
+    f32 = np.float32
+    u = rng.standard_normal((B, L, D), dtype=f32)
+    z = rng.standard_normal((B, L, D), dtype=f32)
+    Bm = rng.standard_normal((B, L, N), dtype=f32)
+    Cm = rng.standard_normal((B, L, N), dtype=f32)
+    delta = rng.standard_normal((B, L, D), dtype=f32)
+    delta *= f32(delta_std)
+    lo, hi = dt_range
+    U = rng.random(D)
+    dskip = (0.5 + rng.random(D)).astype(f32)
+    dy = rng.standard_normal((B, L, D), dtype=f32) if with_dy else None
+    h0 = rng.standard_normal((B, D, N)).astype(f32) if with_h0 else None
+    A = make_A(D, N, a_mode, rng)
+    # step bias: inverse softplus of a log-uniform step (input recipe, fp64)
+    dt = np.exp(math.log(lo) + U * (math.log(hi) - math.log(lo)))
+    bias = (dt + np.log(-np.expm1(-dt))).astype(f32)
+    if dtype == "bf16":
+        u, z, Bm, Cm, delta = (round_to_bf16(x) for x in (u, z, Bm, Cm, delta))
+        if dy is not None:
+            dy = round_to_bf16(dy)
+    elif dtype != "f32":
+        raise ValueError(dtype)
+    return Inputs(u=u, delta=delta, A=A, B=Bm, C=Cm, D=dskip if with_D else None,
+                  delta_bias=bias if with_bias else None, z=z if with_z else None,
+                  h0=h0, dy=dy, dtype=dtype,
+                  meta=dict(B=B, L=L, D=D, N=N, seed=seed, dt_range=tuple(dt_range),
+                            a_mode=a_mode))
+
+
+def make_workload(name: str, with_dy: bool | None = None) -> Inputs:
+    w = WORKLOADS[name]
+    if with_dy is None:
+        with_dy = w.op == "bwd"
+    return make_inputs(w.B, w.L, w.D, w.N, w.seed, w.dtype, w.dt_range, with_dy=with_dy)
