@@ -1,0 +1,260 @@
+"""Selective-scan benchmark on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu] [--no-extra]
+
+A step is one forward selective scan (steps a1-a8 of the hot path: loads,
+softplus, on-the-fly discretisation, recurrence, C contraction, D skip, gate)
+over one batch of seeded synthetic inputs already resident in HBM.  The default
+workload is the Mamba-2.8B-shaped layer (B=8, L=2048, D=5120, N=16, bf16 inputs,
+fp32 state and output, exact ZOH).  The backward and decode-step rows are timed
+on their own workloads and reported under "extra".
+
+Prints ONE JSON line.  value = scanned elements (B*L*D*N) per second.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+SIMD_LANES = 256 * 4 * 16      # CUs x SIMDs x lanes
+CLOCK_HZ = 2.4e9
+VALU_PEAK_TSLOT = SIMD_LANES * CLOCK_HZ / 1e12   # 39.32 T lane-slots/s (non-packed fp32)
+# minimal VALU issue slots per scanned element (b, t, d, n): one v_exp_f32 (2 slots,
+# half rate on gfx950) + 4 (Euler) or 6 (exact ZOH) single-slot vector ops
+SLOTS_PER_ELEM = {"euler": 6.0, "zoh": 8.0}
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "selective_state_space_69_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".hpp", ".h", ".cpp")):
+            h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic_bytes(w, in_bytes=2, out_bytes=4):
+    """Each input read once, y written once: u, delta, z (B,L,D), B and C (B,L,N),
+    A (D,N), D_skip and bias (D)."""
+    bld = w.B * w.L * w.D
+    bln = w.B * w.L * w.N
+    return bld * (3 * in_bytes + out_bytes) + 2 * bln * in_bytes + w.D * (w.N + 2) * 4
+
+
+def load_traffic(name):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was
+    taken on the current kernel sources; else None."""
+    p = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(p):
+        return None
+    try:
+        d = json.load(open(p))
+    except ValueError:
+        return None
+    e = d.get(name)
+    if not e or e.get("kernel_hash") != kernel_source_hash():
+        return None
+    return e.get("bytes_per_launch")
+
+
+def upload(inp, torch):
+    it = torch.bfloat16 if inp.dtype == "bf16" else torch.float32
+    cv = lambda x, dt: None if x is None else torch.from_numpy(x).to("cuda").to(dt).contiguous()  # noqa
+    return dict(u=cv(inp.u, it), delta=cv(inp.delta, it), A=cv(inp.A, torch.float32),
+                B=cv(inp.B, it), C=cv(inp.C, it), D=cv(inp.D, torch.float32),
+                delta_bias=cv(inp.delta_bias, torch.float32), z=cv(inp.z, it),
+                dy=cv(inp.dy, it))
+
+
+def time_calls(fn, steps, warmup, torch):
+    """Warm up, then time `steps` calls: total wall (events around the whole region)
+    and the mean per-call duration from events around each call (same stream)."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    t0 = time.perf_counter()
+    ev[0].record()
+    for i in range(steps):
+        fn()
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
+    total_ms = ev[0].elapsed_time(ev[steps])
+    return total_ms, sum(per) / len(per), min(per), wall
+
+
+def cpu_baseline(inp, w, budget_s=12.0):
+    """The fp64 oracle on a bounded sample of channels of the same workload."""
+    import numpy as np
+    from oracle import oracle
+    try:
+        threads = len(os.sched_getaffinity(0))
+    except AttributeError:
+        threads = os.cpu_count() or 1
+    threads = max(1, min(16, threads))
+    b = 0
+
+    def run(nch):
+        sl = (slice(b, b + 1), slice(None), slice(0, nch))
+        t0 = time.perf_counter()
+        oracle.fwd(inp.u[sl], inp.delta[sl], inp.A[:nch], inp.B[b:b + 1], inp.C[b:b + 1],
+                   D=inp.D[:nch], delta_bias=inp.delta_bias[:nch], z=inp.z[sl],
+                   disc=w.disc, nthreads=threads)
+        return time.perf_counter() - t0
+
+    nch = min(w.D, 4 * threads)
+    dt = run(nch)
+    if dt < budget_s / 4 and nch < w.D:
+        nch = int(min(w.D, max(nch, nch * budget_s / max(dt, 1e-3))))
+        dt = run(nch)
+    elems = w.L * nch * w.N
+    return {"value": elems / dt, "unit": "elements/s", "cores": threads, "kind": "oracle",
+            "sample": "batch row 0, channels 0..%d (%d of %d), full L=%d, N=%d; %.1f s fp64 C, "
+                      "OpenMP over channels" % (nch - 1, nch, w.D, w.L, w.N, dt)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="fwd_2p8b_bf16_b8_l2048_d5120")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-extra", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: the selective scan needs no communication "
+              "(every (b, d) channel is independent) and this build has no multi-GPU path; "
+              "run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from selective_state_space_69_amd import binding as Bnd
+    from selective_state_space_69_amd import synth
+
+    Bnd.load_library()
+    w = synth.WORKLOADS[args.workload]
+    inp = synth.make_workload(w.name, with_dy=False)
+    d = upload(inp, torch)
+    out_dt = torch.float32
+    y = torch.empty(d["u"].shape, dtype=out_dt, device="cuda")
+    desc = Bnd.make_desc(w.B, w.L, w.D, w.N, Bnd.SS_BF16 if w.dtype == "bf16" else Bnd.SS_F32,
+                         Bnd.SS_F32, Bnd.SS_ZOH if w.disc == "zoh" else Bnd.SS_EULER, True)
+    nb = Bnd.ss_scan_workspace_bytes(desc, Bnd.SS_OP_FWD)
+    ws = Bnd.workspace(nb, "cuda")
+
+    def step():
+        rc = Bnd.ss_scan_fwd(desc, d["u"], d["delta"], d["A"], d["B"], d["C"], d["D"],
+                             d["delta_bias"], d["z"], None, y, None, ws, nb)
+        if rc != 0:
+            raise RuntimeError(Bnd.ss_scan_strerror(rc))
+
+    torch.cuda.synchronize()
+    total_ms, per_ms, min_ms, wall = time_calls(step, args.steps, args.warmup, torch)
+    torch.cuda.synchronize()
+    elems = w.elements
+    value = elems * args.steps / (total_ms * 1e-3)
+    alg = algorithmic_bytes(w, 2 if w.dtype == "bf16" else 4, 4)
+    hbm_gbs = alg / (per_ms * 1e-3) / 1e9
+    slots = SLOTS_PER_ELEM[w.disc] * elems / (per_ms * 1e-3) / 1e12
+    roof = {"bound": "alu", "achieved": round(slots, 3), "peak": round(VALU_PEAK_TSLOT, 3),
+            "unit": "Tslot/s", "frac": round(slots / VALU_PEAK_TSLOT, 4),
+            "traffic": load_traffic(w.name),
+            "kernel_ms": round(per_ms, 4), "kernel_ms_min": round(min_ms, 4),
+            "work_per_element": "%s: %d VALU lane-slots (1 v_exp_f32 = 2 slots)" % (
+                w.disc, SLOTS_PER_ELEM[w.disc]),
+            "hbm": {"achieved": round(hbm_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(hbm_gbs / HBM_PEAK_GBS, 4), "algorithmic_bytes": alg}}
+    res = {"metric": "selective-scan elements (B*L*D*N)/s, 1 GPU", "value": value,
+           "unit": "elements/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "ms_per_step": total_ms / args.steps, "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+           "config": {"workload": w.name, "B": w.B, "L": w.L, "D": w.D, "N": w.N,
+                      "in_dtype": w.dtype, "out_dtype": "f32", "disc": w.disc,
+                      "plan_workspace_bytes": nb},
+           "roofline": roof}
+    del d, y, ws
+    torch.cuda.empty_cache()
+
+    if not args.no_extra:
+        res["extra"] = extras(torch, Bnd, synth, args)
+    if not args.no_cpu:
+        res["cpu_baseline"] = cpu_baseline(inp, w)
+    print(json.dumps(res), flush=True)
+
+
+def extras(torch, Bnd, synth, args):
+    """Other rows of the hot path, each on its own workload (not part of value)."""
+    out = {}
+    steps, warm = max(5, args.steps // 2), 2
+    # forward on the other forward workloads
+    for name in ("fwd_2p8b_bf16_b8_l2048_d5120:euler", "fwd_130m_bf16_b8_l2048_d1536",
+                 "fwd_2p8b_bf16_b2_l8192_d5120", "fwd_long_bf16_b1_l1048576_d256"):
+        wname, _, disc = name.partition(":")
+        w = synth.WORKLOADS[wname]
+        disc = disc or w.disc
+        inp = synth.make_workload(wname, with_dy=False)
+        d = upload(inp, torch)
+        y = torch.empty(d["u"].shape, dtype=torch.float32, device="cuda")
+        desc = Bnd.make_desc(w.B, w.L, w.D, w.N, Bnd.SS_BF16, Bnd.SS_F32,
+                             Bnd.SS_ZOH if disc == "zoh" else Bnd.SS_EULER, True)
+        nb = Bnd.ss_scan_workspace_bytes(desc, Bnd.SS_OP_FWD)
+        ws = Bnd.workspace(nb, "cuda")
+        f = lambda: Bnd.ss_scan_fwd(desc, d["u"], d["delta"], d["A"], d["B"], d["C"], d["D"],  # noqa
+                                    d["delta_bias"], d["z"], None, y, None, ws, nb)
+        total, per, mn, _ = time_calls(f, steps, warm, torch)
+        alg = algorithmic_bytes(w)
+        out[name] = {"ms": round(per, 4), "elements_per_s": w.elements / (per * 1e-3),
+                     "hbm_gbs": round(alg / (per * 1e-3) / 1e9, 1),
+                     "alu_frac": round(SLOTS_PER_ELEM[disc] * w.elements / (per * 1e-3) / 1e12
+                                       / VALU_PEAK_TSLOT, 4),
+                     "chunks": "workspace %d B" % nb}
+        del d, y, ws, inp
+        torch.cuda.empty_cache()
+    # backward
+    w = synth.WORKLOADS["bwd_130m_bf16_b8_l2048_d1536"]
+    inp = synth.make_workload(w.name, with_dy=True)
+    d = upload(inp, torch)
+    for disc in ("euler", "zoh"):
+        try:
+            g = Bnd.scan_bwd(d["u"], d["delta"], d["A"], d["B"], d["C"], d["dy"], D=d["D"],
+                             delta_bias=d["delta_bias"], z=d["z"], disc=disc)
+            f = lambda: Bnd.scan_bwd(d["u"], d["delta"], d["A"], d["B"], d["C"], d["dy"],  # noqa
+                                     D=d["D"], delta_bias=d["delta_bias"], z=d["z"], disc=disc)
+            total, per, mn, _ = time_calls(f, steps, warm, torch)
+            bld, bln = w.B * w.L * w.D, w.B * w.L * w.N
+            alg = bld * (4 * 2 + 3 * 4) + bln * (2 * 2 + 2 * 4) + w.D * (2 * w.N + 4) * 4
+            out["bwd_130m:" + disc] = {"ms": round(per, 4),
+                                       "elements_per_s": w.elements / (per * 1e-3),
+                                       "hbm_gbs": round(alg / (per * 1e-3) / 1e9, 1)}
+            del g
+        except Exception as e:  # backward not available in this build
+            out["bwd_130m:" + disc] = {"error": str(e)}
+    del d, inp
+    torch.cuda.empty_cache()
+    # decode step at the Mamba-2.8B width
+    Bt, D, N = 8, 5120, 16
+    inp = synth.make_inputs(Bt, 1, D, N, seed=77, dtype="bf16", with_h0=True)
+    d = upload(inp, torch)
+    h = torch.from_numpy(inp.h0).cuda()
+    args1 = [d[k][:, 0].contiguous() for k in ("u", "delta")]
+    Bc, Cc, zc = (d[k][:, 0].contiguous() for k in ("B", "C", "z"))
+    f = lambda: Bnd.scan_step(h, args1[0], args1[1], d["A"], Bc, Cc, D=d["D"],  # noqa
+                              delta_bias=d["delta_bias"], z=zc)
+    total, per, mn, _ = time_calls(f, 50, 5, torch)
+    out["step_b8_d5120"] = {"us": round(per * 1e3, 2), "state_bytes": Bt * D * N * 4 * 2}
+    return out
+
+
+if __name__ == "__main__":
+    main()

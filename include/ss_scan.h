@@ -1,0 +1,157 @@
+/*
+ * ss_scan.h -- C ABI of the MI355X (gfx950) selective-scan (S6) library.
+ *
+ * The operation (pages and sections it follows):
+ *   For every batch row b and channel d an independent single-input
+ *   single-output state-space system with N real diagonal states ("Mamba: S4
+ *   epic upgrade", hk.pswp.cn, sections "S4 intro" and "parameter-efficient data
+ *   dependence": one SISO system per input channel, A diagonal with N entries
+ *   per channel, A_bar = exp(delta A)).  Per time step t, with the selective,
+ *   input-dependent delta_t, B_t, C_t (Gu & Dao wiki note, git.lyz.one, section
+ *   "From S4 to S6": delta_t = tau(Delta + s_Delta(x_t)), here tau = softplus and
+ *   Delta = delta_bias):
+ *     step   dt     = softplus(delta[b,t,d] + delta_bias[d])   (or without softplus)
+ *     decay  abar_n = exp(dt * A[d,n])
+ *     input  bbar_n = (exp(dt*A[d,n]) - 1) / A[d,n] * B[b,t,n]   exact zero-order hold,
+ *                     dt * B[b,t,n] when A[d,n] == 0 or in Euler mode
+ *            (ZOH and its first-order form: "Mamba explained", hackbyte.io,
+ *             discretization section; "A Survey of Mamba" summary, csdn, SSM section)
+ *     state  h_n    = abar_n * h_n + bbar_n * u[b,t,d]
+ *            ("A Visual Guide to Mamba" summary, wenxiaobai, The Scan Operation)
+ *     output y      = sum_n C[b,t,n] h_n + D_skip[d] * u[b,t,d]     (Eq 1b, hackbyte.io)
+ *     gate   out    = y * silu(z[b,t,d])            (Gu & Dao note, Mamba architecture)
+ *   The discretised abar, bbar are never stored; the states are kept on chip
+ *   (wenxiaobai summary, Hardware-aware Algorithm; hk.pswp.cn, IO-aware Parallel Scan).
+ *
+ * Conventions shared by every entry point
+ *   - Tensors are dense, row-major, with the last index fastest:
+ *       u, delta, z, y, dy, du, ddelta, dz : (B, L, D)
+ *       Bm, Cm, dB, dC                     : (B, L, N)
+ *       A, dA : (D, N)   D_skip, delta_bias, dD_skip, ddelta_bias : (D)
+ *       h0, h_last, dh0, step state h      : (B, D, N)
+ *   - Pointers are DEVICE pointers owned by the caller, 16-byte aligned, and valid until
+ *     the stream reaches the queued work.  Element types: in_dtype for u, delta,
+ *     z, Bm, Cm and dy; out_dtype for y, du, ddelta and dz; float32 for everything
+ *     else.  bf16 values are raw IEEE bfloat16 bit patterns (uint16).
+ *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = the null
+ *     stream).  Kernel faults surface at the next synchronisation.
+ *   - All validation happens before any HIP call, so every error code can be
+ *     produced without a GPU.  No exception crosses the ABI.  The library never
+ *     allocates device memory: scratch comes from the caller's workspace.
+ *   - NaN / Inf inputs propagate unchecked.
+ *   - The forward and step are deterministic (bitwise repeatable).
+ */
+#ifndef SS_SCAN_H
+#define SS_SCAN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define SS_OK 0
+#define SS_ERR_INVALID_ARG (-1)  /* NULL required pointer, size out of range, aliasing */
+#define SS_ERR_UNSUPPORTED (-2)  /* dtype / discretisation / flag combination not provided */
+#define SS_ERR_WORKSPACE (-3)    /* workspace NULL or smaller than ss_scan_workspace_bytes */
+#define SS_ERR_HIP (-4)          /* a HIP launch reported an error */
+
+typedef enum { SS_F32 = 0, SS_BF16 = 1 } ss_dtype_t;
+typedef enum { SS_ZOH = 0, SS_EULER = 1 } ss_disc_t;
+
+/* Problem description.  1 <= dstate <= 16; batch, seqlen, dim >= 1. */
+typedef struct ss_desc {
+  int64_t batch;          /* B */
+  int64_t seqlen;         /* L (ignored by ss_scan_step) */
+  int64_t dim;            /* D, channels */
+  int64_t dstate;         /* N, states per channel */
+  int32_t in_dtype;       /* ss_dtype_t of u, delta, z, Bm, Cm, dy */
+  int32_t out_dtype;      /* ss_dtype_t of y (fwd, step) and of du, ddelta, dz (bwd; must be SS_F32) */
+  int32_t disc;           /* ss_disc_t: exact zero-order hold or Euler input coefficient */
+  int32_t delta_softplus; /* nonzero: dt = softplus(delta + delta_bias); zero: dt = delta + delta_bias */
+} ss_desc_t;
+
+/* Operations for ss_scan_workspace_bytes. */
+#define SS_OP_FWD 0
+#define SS_OP_BWD 1
+
+/*
+ * Bytes of device workspace that ss_scan_fwd (op = SS_OP_FWD) or ss_scan_bwd
+ * (op = SS_OP_BWD) needs for this description (0 when none).  The size depends
+ * only on the description (and the SS_SCAN_CHUNK tuning variable, if set).
+ * Returns 0 for an invalid description.  Workspace contents are scratch: they
+ * need not be initialised and are clobbered.
+ */
+size_t ss_scan_workspace_bytes(const ss_desc_t* desc, int op);
+
+/*
+ * Forward selective scan.
+ *   u, delta, Bm, Cm, A, y     required.
+ *   D_skip, delta_bias, z, h0  optional (NULL = zero skip, zero bias, no gate,
+ *                              zero initial state).
+ *   h_last                     optional output: the state after the last step;
+ *                              must not alias h0.
+ *   workspace, ws_bytes        at least ss_scan_workspace_bytes(desc, SS_OP_FWD).
+ * Long or narrow problems are split into time chunks whose start states are
+ * found by a scan over per-chunk (decay, end state) summaries under
+ * (a1, b1) o (a2, b2) = (a1 a2, a2 b1 + b2) ("A Visual Guide to Mamba" summary,
+ * The Scan Operation: compute in segments and combine them associatively).
+ */
+int ss_scan_fwd(const ss_desc_t* desc,
+                const void* u, const void* delta, const float* A,
+                const void* Bm, const void* Cm,
+                const float* D_skip, const float* delta_bias, const void* z,
+                const float* h0,
+                void* y, float* h_last,
+                void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * Backward of ss_scan_fwd with recomputation: the states are rebuilt from the
+ * inputs (chunk start states in the workspace, the rest on chip), never read
+ * from a stored (B,L,D,N) tensor ("A Visual Guide to Mamba" summary,
+ * Hardware-aware Algorithm: recomputation; "A Survey of Mamba" summary,
+ * hardware-aware computation).
+ *   Inputs: as ss_scan_fwd (h0 optional) plus dy = d(loss)/d(out), in_dtype.
+ *   Outputs, all overwritten (never accumulated into):
+ *     du, ddelta (w.r.t. the raw delta input, through softplus)   required
+ *     dA, dB, dC                                                    required
+ *     dD_skip (required iff D_skip given), ddelta_bias (required iff
+ *     delta_bias given), dz (required iff z given), dh0 (optional).
+ *   out_dtype must be SS_F32.  dA, dB, dC, dD_skip, ddelta_bias are reduced in
+ *   fp32 in a fixed order (deterministic).
+ */
+int ss_scan_bwd(const ss_desc_t* desc,
+                const void* u, const void* delta, const float* A,
+                const void* Bm, const void* Cm,
+                const float* D_skip, const float* delta_bias, const void* z,
+                const float* h0, const void* dy,
+                void* du, void* ddelta, float* dA, float* dB, float* dC,
+                float* dD_skip, float* ddelta_bias, void* dz, float* dh0,
+                void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * One recurrent (inference) step for every (b, d): the state h (B,D,N) fp32 is
+ * read and overwritten in place; u, delta, z, y are (B,D); Bm, Cm are (B,N).
+ * desc->seqlen is ignored.  Optional pointers as in ss_scan_fwd.  The state is
+ * O(1) per token, unlike a growing attention cache ("Mamba explained",
+ * hackbyte.io, quadratic-bottleneck section).
+ */
+int ss_scan_step(const ss_desc_t* desc, float* h,
+                 const void* u, const void* delta, const float* A,
+                 const void* Bm, const void* Cm,
+                 const float* D_skip, const float* delta_bias, const void* z,
+                 void* y, void* stream);
+
+/* Static, human-readable text for a status code. */
+const char* ss_scan_strerror(int status);
+
+/* Library ABI version (major * 10000 + minor * 100 + patch). */
+int ss_scan_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SS_SCAN_H */

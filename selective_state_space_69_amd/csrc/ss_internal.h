@@ -1,0 +1,108 @@
+// Internal interface between the C-ABI layer (ss_api.cpp: validation and
+// planning, pure host logic) and the HIP launchers (ss_fwd.hip, ss_bwd.hip,
+// ss_step.hip).  Not installed; the public contract is include/ss_scan.h.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+
+#include "ss_scan.h"
+
+namespace ss {
+
+constexpr int kWave = 64;      // lanes per wavefront on CDNA
+constexpr int kMaxState = 16;  // states held per lane
+
+// How a forward (or the forward recompute inside the backward) is split in time.
+// nchunks == 1: one sequential pass per (b, 64-channel block).
+// nchunks  > 1: (1) chunk summaries, (2) carry scan over chunks, (3) output pass.
+struct TimePlan {
+  int64_t chunk_len = 0;
+  int64_t nchunks = 1;
+};
+
+// Workspace layout of the forward: fp32 arrays, each 256-byte aligned.
+//   hend : (B, nchunks, N, D)  chunk-local end state, then (after the carry scan)
+//                              the start state of the chunk
+//   dsum : (B, nchunks, D)     sum over the chunk of the step, in log2 units
+struct FwdPlan {
+  TimePlan tp;
+  size_t off_hend = 0, off_dsum = 0, bytes = 0;
+};
+
+// Backward workspace:
+//   the forward's carry arrays (chunk start states), plus per 64-channel block
+//   partial sums that are reduced in a fixed order by a second kernel:
+//   pB, pC : (B, L, nblk, N)     partial dB, dC over the block's channels
+//   pA     : (B, nchunks, N, D)  partial dA over the chunk's time steps
+//   pD, pbias : (B, nchunks, D)  partial dD_skip, ddelta_bias
+//   lam    : (B, nchunks, N, D)  adjoint carries for the chunked backward
+struct BwdPlan {
+  TimePlan tp;
+  int64_t nblk = 0;
+  size_t off_hend = 0, off_dsum = 0, off_pB = 0, off_pC = 0, off_pA = 0, off_pD = 0,
+         off_pbias = 0, off_lam = 0, off_lsum = 0, bytes = 0;
+};
+
+TimePlan plan_time(const ss_desc_t& d);
+FwdPlan plan_fwd(const ss_desc_t& d);
+BwdPlan plan_bwd(const ss_desc_t& d);
+
+struct FwdArgs {
+  const void* u;
+  const void* delta;
+  const float* A;
+  const void* Bm;
+  const void* Cm;
+  const float* Dskip;
+  const float* bias;
+  const void* z;
+  const float* h0;
+  void* y;
+  float* h_last;
+  float* hend;
+  float* dsum;
+};
+
+struct BwdArgs {
+  const void* u;
+  const void* delta;
+  const float* A;
+  const void* Bm;
+  const void* Cm;
+  const float* Dskip;
+  const float* bias;
+  const void* z;
+  const float* h0;
+  const void* dy;
+  float* du;
+  float* ddelta;
+  float* dA;
+  float* dB;
+  float* dC;
+  float* dDskip;
+  float* dbias;
+  float* dz;
+  float* dh0;
+  char* ws;
+};
+
+struct StepArgs {
+  float* h;
+  const void* u;
+  const void* delta;
+  const float* A;
+  const void* Bm;
+  const void* Cm;
+  const float* Dskip;
+  const float* bias;
+  const void* z;
+  void* y;
+};
+
+// Launchers: return 0 or a HIP error code (converted to SS_ERR_HIP by the caller).
+int launch_fwd(const ss_desc_t& d, const FwdPlan& p, const FwdArgs& a, void* stream);
+int launch_bwd(const ss_desc_t& d, const BwdPlan& p, const BwdArgs& a, void* stream);
+int launch_step(const ss_desc_t& d, const StepArgs& a, void* stream);
+
+}  // namespace ss

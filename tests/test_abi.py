@@ -1,0 +1,120 @@
+"""CPU-side checks of the C ABI: the library loads, exports every function the
+header declares, and rejects invalid arguments before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from selective_state_space_69_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ss_scan.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(B.LIB_PATH):
+        from selective_state_space_69_amd import build
+        build.build(verbose=False)
+    return B.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ss_scan_\w+)\s*\(", text)))
+
+
+def test_header_declares_entry_points():
+    names = declared_functions()
+    for n in ("ss_scan_fwd", "ss_scan_bwd", "ss_scan_step", "ss_scan_workspace_bytes",
+              "ss_scan_strerror", "ss_scan_version"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_strerror_and_version(lib):
+    for code in (0, -1, -2, -3, -4, 99):
+        assert isinstance(B.ss_scan_strerror(code), str) and B.ss_scan_strerror(code)
+    assert B.ss_scan_version() >= 10000
+
+
+FAKE = 1 << 20   # a 16-byte aligned non-null "device pointer"; never dereferenced
+
+
+def fwd(desc, **kw):
+    args = dict(u=FAKE, delta=FAKE, A=FAKE, Bm=FAKE, Cm=FAKE, D_skip=None, delta_bias=None,
+                z=None, h0=None, y=FAKE, h_last=None, workspace=None, ws_bytes=0)
+    args.update(kw)
+    return B.ss_scan_fwd(desc, args["u"], args["delta"], args["A"], args["Bm"], args["Cm"],
+                         args["D_skip"], args["delta_bias"], args["z"], args["h0"], args["y"],
+                         args["h_last"], args["workspace"], args["ws_bytes"], stream=0)
+
+
+def desc(**kw):
+    base = dict(batch=2, seqlen=64, dim=128, dstate=16, in_dtype=B.SS_BF16, out_dtype=B.SS_F32,
+                disc=B.SS_ZOH, delta_softplus=True)
+    base.update(kw)
+    return B.make_desc(**base)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(batch=0), B.SS_ERR_INVALID_ARG), (dict(seqlen=0), B.SS_ERR_INVALID_ARG),
+    (dict(dim=0), B.SS_ERR_INVALID_ARG), (dict(dstate=0), B.SS_ERR_INVALID_ARG),
+    (dict(dstate=17), B.SS_ERR_INVALID_ARG), (dict(seqlen=-5), B.SS_ERR_INVALID_ARG),
+    (dict(seqlen=1 << 31), B.SS_ERR_INVALID_ARG), (dict(in_dtype=7), B.SS_ERR_UNSUPPORTED),
+    (dict(out_dtype=3), B.SS_ERR_UNSUPPORTED), (dict(disc=2), B.SS_ERR_UNSUPPORTED),
+])
+def test_fwd_rejects_bad_descriptor(lib, kw, code):
+    assert fwd(desc(**kw)) == code
+
+
+@pytest.mark.parametrize("field", ["u", "delta", "A", "Bm", "Cm", "y"])
+def test_fwd_rejects_null_required(lib, field):
+    assert fwd(desc(), **{field: None}) == B.SS_ERR_INVALID_ARG
+
+
+def test_fwd_rejects_misaligned_and_aliasing(lib):
+    assert fwd(desc(), u=FAKE + 2) == B.SS_ERR_INVALID_ARG
+    assert fwd(desc(), h0=FAKE + 64, h_last=FAKE + 64) == B.SS_ERR_INVALID_ARG
+
+
+def test_fwd_workspace_checks(lib):
+    d = desc(batch=1, seqlen=1 << 20, dim=256)       # narrow and long: chunked plan
+    need = B.ss_scan_workspace_bytes(d, B.SS_OP_FWD)
+    assert need > 0
+    assert fwd(d, workspace=None, ws_bytes=0) == B.SS_ERR_WORKSPACE
+    assert fwd(d, workspace=FAKE, ws_bytes=need - 1) == B.SS_ERR_WORKSPACE
+    assert fwd(d, workspace=FAKE + 16, ws_bytes=need) == B.SS_ERR_WORKSPACE   # not 256-aligned
+
+
+def test_plan_sizes(lib):
+    # wide problems run as one pass per (b, 64-channel block): no workspace
+    assert B.ss_scan_workspace_bytes(desc(batch=8, seqlen=2048, dim=5120), B.SS_OP_FWD) == 0
+    # narrow ones are chunked: start states (B, chunks, N, D) + step sums (B, chunks, D)
+    n = B.ss_scan_workspace_bytes(desc(batch=8, seqlen=2048, dim=1536), B.SS_OP_FWD)
+    assert n > 0 and n % 256 == 0
+    assert B.ss_scan_workspace_bytes(desc(batch=0), B.SS_OP_FWD) == 0
+    assert B.ss_scan_workspace_bytes(desc(), 5) == 0
+
+
+def test_bwd_and_step_validation(lib):
+    d = desc()
+    P = FAKE
+    args = [P, P, P, P, P, None, None, None, None, P, P, P, P, P, P, None, None, None, None, None, 0]
+    assert B.ss_scan_bwd(desc(out_dtype=B.SS_BF16), *args, stream=0) == B.SS_ERR_UNSUPPORTED
+    bad = list(args)
+    bad[9] = None   # dy
+    assert B.ss_scan_bwd(d, *bad, stream=0) == B.SS_ERR_INVALID_ARG
+    bad = list(args)
+    bad[5] = P      # D_skip given without dD_skip
+    assert B.ss_scan_bwd(d, *bad, stream=0) == B.SS_ERR_INVALID_ARG
+    assert B.ss_scan_step(desc(dstate=0), P, P, P, P, P, P, None, None, None, P, stream=0) == \
+        B.SS_ERR_INVALID_ARG
+    assert B.ss_scan_step(d, None, P, P, P, P, P, None, None, None, P, stream=0) == \
+        B.SS_ERR_INVALID_ARG

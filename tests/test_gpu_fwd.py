@@ -1,0 +1,201 @@
+"""GPU parity of the forward scan and the decode step against the fp64 oracle,
+through the C ABI (libssscan.so).  Marked gpu: run on an MI355X."""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from selective_state_space_69_amd import binding as B
+from selective_state_space_69_amd import synth
+from gpu_util import (TOL_BF16, check_f32, check_rel_max, gpu_fwd, log, oracle_channels,
+                      sample_channels, upload)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible")
+    B.load_library()
+    yield
+    torch.cuda.synchronize()
+
+
+def _full_oracle(oracle, inp, disc, softplus=True):
+    return oracle.fwd(inp.u, inp.delta, inp.A, inp.B, inp.C, D=inp.D, delta_bias=inp.delta_bias,
+                      z=inp.z, h0=inp.h0, disc=disc, softplus=softplus)
+
+
+# ------------------------------------------------------------------ small fp32 cases
+CASES = [
+    # (B, L, D, N, disc, z, bias, Dskip, h0, softplus, a_mode)
+    (1, 256, 64, 16, "zoh", True, True, True, False, True, "s4d_real"),
+    (2, 77, 150, 16, "zoh", True, True, True, True, True, "random"),
+    (2, 77, 150, 16, "euler", True, True, True, True, True, "random"),
+    (3, 45, 64, 16, "zoh", False, True, False, False, True, "s4d_real"),
+    (2, 64, 70, 16, "euler", False, False, True, True, True, "s4d_real"),
+    (2, 33, 100, 16, "zoh", True, True, True, True, True, "mixed"),
+    (2, 33, 100, 16, "euler", True, True, True, True, True, "mixed"),
+    (1, 19, 5, 16, "zoh", True, True, True, True, False, "s4d_real"),
+    (2, 40, 66, 1, "zoh", True, True, True, True, True, "random"),
+    (2, 40, 66, 5, "euler", True, True, True, True, True, "random"),
+    (1, 50, 130, 8, "zoh", True, False, True, True, True, "mixed"),
+    (1, 1, 64, 16, "zoh", True, True, True, True, True, "random"),
+    (2, 1000, 150, 16, "zoh", True, True, True, True, True, "random"),     # chunked plan
+    (2, 1000, 150, 16, "euler", True, True, True, True, True, "mixed"),    # chunked, A = 0
+    (1, 3001, 64, 16, "zoh", True, True, True, True, True, "s4d_real"),    # chunked, ragged
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "b%d_l%d_d%d_n%d_%s_z%d_bias%d_D%d_h0%d_sp%d_%s" % c)
+def test_fwd_fp32_parity(oracle, case):
+    Bt, L, D, N, disc, z, bias, dsk, h0, sp, amode = case
+    log("fwd fp32 case", case)
+    inp = synth.make_inputs(Bt, L, D, N, seed=1000 + CASES.index(case), dtype="f32", with_z=z,
+                            with_bias=bias, with_D=dsk, with_h0=h0, a_mode=amode,
+                            delta_std=0.1 if sp else 0.02)
+    if not sp:   # keep the raw step positive without the activation
+        inp.delta_bias = np.abs(inp.delta_bias) * 0 + np.float32(0.05)
+    d = upload(inp)
+    y, hl = gpu_fwd(d, disc, softplus=sp, return_last_state=True)
+    torch.cuda.synchronize()
+    ref, href = _full_oracle(oracle, inp, disc, softplus=sp)
+    w = check_f32(y.cpu().numpy(), ref, "y")
+    check_f32(hl.cpu().numpy(), href, "h_last")
+    log("  worst err/bound", w)
+
+
+def test_fwd_tiny_workload(oracle):
+    """The tiny fp32 workload (B=1, L=256, D=64, N=16, exact ZOH, gate)."""
+    inp = synth.make_workload("fwd_tiny_f32_b1_l256_d64")
+    d = upload(inp)
+    y = gpu_fwd(d, "zoh")
+    torch.cuda.synchronize()
+    ref, _ = _full_oracle(oracle, inp, "zoh")
+    check_f32(y.cpu().numpy(), ref, "y")
+
+
+def test_chunked_equals_sequential(monkeypatch):
+    """The chunked two-level carry reproduces the one-pass result (fp32 reassociation)."""
+    inp = synth.make_inputs(2, 1500, 96, 16, seed=5, dtype="f32", with_h0=True, a_mode="random")
+    d = upload(inp)
+    monkeypatch.setenv("SS_SCAN_CHUNK", "100000")
+    y1, h1 = gpu_fwd(d, "zoh", return_last_state=True)
+    for chunk in ("64", "256", "333"):
+        monkeypatch.setenv("SS_SCAN_CHUNK", chunk)
+        y2, h2 = gpu_fwd(d, "zoh", return_last_state=True)
+        torch.cuda.synchronize()
+        # chunk decays are exp(A * sum dt) instead of a product of per-step exps
+        scale = float(y1.abs().max())
+        assert float((y1 - y2).abs().max()) <= 1e-4 * scale, chunk
+        assert float((h1 - h2).abs().max()) <= 1e-4 * float(h1.abs().max()), chunk
+
+
+def test_fwd_deterministic():
+    inp = synth.make_inputs(4, 512, 320, 16, seed=6, dtype="bf16")
+    d = upload(inp)
+    y1 = gpu_fwd(d, "zoh")
+    y2 = gpu_fwd(d, "zoh")
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2)
+
+
+def test_fwd_split_resume():
+    """fwd(L1) -> h_last -> fwd(L2, h0 = h_last) equals fwd(L1 + L2)."""
+    inp = synth.make_inputs(2, 300, 128, 16, seed=7, dtype="f32", with_h0=True, a_mode="random")
+    d = upload(inp)
+    y, h = gpu_fwd(d, "zoh", return_last_state=True)
+    cut = 123
+    part = lambda k, s: d[k][:, s].contiguous()  # noqa: E731
+    y1, h1 = gpu_fwd(d, "zoh", return_last_state=True,
+                     **{k: part(k, slice(0, cut)) for k in ("u", "delta", "z", "B", "C")})
+    y2, h2 = gpu_fwd(d, "zoh", return_last_state=True, h0=h1,
+                     **{k: part(k, slice(cut, None)) for k in ("u", "delta", "z", "B", "C")})
+    torch.cuda.synchronize()
+    yy = torch.cat([y1, y2], dim=1)
+    assert float((yy - y).abs().max()) <= 1e-5 * (1 + float(y.abs().max()))
+    assert float((h2 - h).abs().max()) <= 1e-5 * (1 + float(h.abs().max()))
+
+
+def test_fwd_bf16_output(oracle):
+    inp = synth.make_inputs(2, 200, 192, 16, seed=8, dtype="bf16")
+    d = upload(inp)
+    y = gpu_fwd(d, "zoh", out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    ref, _ = _full_oracle(oracle, inp, "zoh")
+    # bf16 storage adds at most 2^-9 relative rounding on top of the fp32 result
+    check_rel_max(y.float().cpu().numpy(), ref, TOL_BF16 + 2.0 ** -8, "y bf16")
+
+
+# ------------------------------------------------------------------ full-size workloads
+FULL = ["fwd_130m_bf16_b8_l2048_d1536", "fwd_2p8b_bf16_b8_l2048_d5120",
+        "fwd_2p8b_bf16_b2_l8192_d5120", "fwd_long_bf16_b1_l1048576_d256"]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_fwd_full_size_sampled(oracle, name):
+    """Full-size bf16 workloads in the benchmark's launch configuration; sampled
+    channels checked against the oracle (<= 2e-3 max|y_ref|), the rest checked
+    for finiteness."""
+    w = synth.WORKLOADS[name]
+    log("full-size fwd", name, "generating inputs")
+    inp = synth.make_workload(name)
+    d = upload(inp)
+    log("  running GPU")
+    y = gpu_fwd(d, w.disc)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(y).all())
+    chans = sample_channels(w.B, w.D, 10 if w.L > 100000 else 24, seed=1)
+    log("  oracle on", len(chans), "channels")
+    ref, _ = oracle_channels(oracle, inp, chans, w.disc)
+    got = np.stack([y[b, :, dd].cpu().numpy() for b, dd in chans])
+    r = check_rel_max(got, ref, TOL_BF16, name)
+    log("  max err / max|ref| =", r)
+
+
+# ------------------------------------------------------------------ decode step
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("disc", ["zoh", "euler"])
+def test_step_parity(oracle, dtype, disc):
+    inp = synth.make_inputs(3, 1, 200, 16, seed=9, dtype=dtype, with_h0=True, a_mode="mixed")
+    d = upload(inp)
+    h = d["h0"].clone()
+    y = B.scan_step(h, d["u"][:, 0].contiguous(), d["delta"][:, 0].contiguous(), d["A"],
+                    d["B"][:, 0].contiguous(), d["C"][:, 0].contiguous(), D=d["D"],
+                    delta_bias=d["delta_bias"], z=d["z"][:, 0].contiguous(), disc=disc)
+    torch.cuda.synchronize()
+    ref_y, ref_h = oracle.step(inp.h0, inp.u[:, 0], inp.delta[:, 0], inp.A, inp.B[:, 0],
+                               inp.C[:, 0], D=inp.D, delta_bias=inp.delta_bias, z=inp.z[:, 0],
+                               disc=disc)
+    check_f32(y.cpu().numpy(), ref_y, "step y")
+    check_f32(h.cpu().numpy(), ref_h, "step h")
+
+
+def test_step_continues_forward():
+    """fwd over L steps, then one decode step, equals the last row of fwd over L+1."""
+    inp = synth.make_inputs(2, 65, 128, 16, seed=10, dtype="f32", with_h0=True, a_mode="random")
+    d = upload(inp)
+    yfull = gpu_fwd(d, "zoh")
+    L = 64
+    y, h = gpu_fwd(d, "zoh", return_last_state=True,
+                   **{k: d[k][:, :L].contiguous() for k in ("u", "delta", "z", "B", "C")})
+    ys = B.scan_step(h, d["u"][:, L].contiguous(), d["delta"][:, L].contiguous(), d["A"],
+                     d["B"][:, L].contiguous(), d["C"][:, L].contiguous(), D=d["D"],
+                     delta_bias=d["delta_bias"], z=d["z"][:, L].contiguous())
+    torch.cuda.synchronize()
+    assert float((ys - yfull[:, L]).abs().max()) <= 1e-5 * (1 + float(yfull.abs().max()))
+
+
+def test_errors_do_not_launch():
+    """Invalid calls return a status and leave outputs untouched."""
+    inp = synth.make_inputs(1, 8, 64, 16, seed=11, dtype="f32")
+    d = upload(inp)
+    y = torch.full(d["u"].shape, 7.0, device="cuda")
+    desc = B.make_desc(1, 8, 64, 17, B.SS_F32, B.SS_F32, B.SS_ZOH)
+    rc = B.ss_scan_fwd(desc, d["u"], d["delta"], d["A"], d["B"], d["C"], None, None, None, None,
+                       y, None, None, 0)
+    assert rc == B.SS_ERR_INVALID_ARG
+    torch.cuda.synchronize()
+    assert bool((y == 7.0).all())
