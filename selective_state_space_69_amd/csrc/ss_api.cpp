@@ -13,6 +13,7 @@ namespace {
 
 constexpr size_t kAlign = 256;     // workspace alignment
 constexpr size_t kPtrAlign = 16;   // every tensor pointer (rows are read with 16-byte loads)
+constexpr int64_t kBwdChunk = 64;   // backward time chunk (8 blocks of 8 steps)
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
@@ -37,8 +38,8 @@ int check_desc(const ss_desc_t* d, bool need_len) {
   return SS_OK;
 }
 
-int64_t env_chunk() {
-  const char* s = std::getenv("SS_SCAN_CHUNK");
+int64_t env_int(const char* name) {
+  const char* s = std::getenv(name);
   if (!s || !*s) return 0;
   long long v = std::atoll(s);
   return v > 0 ? int64_t(v) : 0;
@@ -46,21 +47,33 @@ int64_t env_chunk() {
 
 }  // namespace
 
-// Split the sequence into chunks when one pass per (b, 64-channel block) would
-// leave most of the GPU idle.  A chunked forward costs about 1.8x the arithmetic
-// (summary pass + output pass), so chunking is only chosen when the sequential
-// plan would fill less than half of the 1024 SIMDs of a 256-CU MI355X.
+// Work decomposition.  The scan is bound by the vector ALU (one v_exp_f32 and
+// 4-6 FMA-class ops per element), and a SIMD running a single wave stalls on
+// transcendental and LDS latency, so the plan aims for several waves per SIMD
+// (the MI355X has 1024 SIMDs in 256 CUs) with the least redundant work:
+//  - >= 2048 channel blocks (B * ceil(D/64)): one wave per block, one pass;
+//  - >= 512 blocks: split the 16 states of a block over 4 waves (each wave
+//    repeats only cheap per-step work), one pass over time;
+//  - fewer: split the states over 2 waves and cut time into chunks of >= 128
+//    steps, targeting 8192 waves; a chunked forward costs about 1.8x the
+//    arithmetic (summary pass + output pass) but keeps every SIMD busy.
+// Measured on MI355X for the Mamba-130M/2.8B shapes and the 1M-step case.
+// SS_SCAN_NSPLIT / SS_SCAN_CHUNK override the choice.
 TimePlan plan_time(const ss_desc_t& d) {
   TimePlan tp;
   const int64_t L = d.seqlen;
   const int64_t cols = d.batch * ((d.dim + kWave - 1) / kWave);
-  int64_t chunk = env_chunk();
+  constexpr int64_t kWide = 2048, kMid = 512, kChunkWaves = 8192, kMinChunk = 128;
+  int nsplit = int(env_int("SS_SCAN_NSPLIT"));
+  const bool forced_split = nsplit == 1 || nsplit == 2 || nsplit == 4;
+  if (!forced_split) nsplit = cols >= kWide ? 1 : (cols >= kMid ? 4 : 2);
+  int64_t chunk = env_int("SS_SCAN_CHUNK");
   if (chunk <= 0) {
-    constexpr int64_t kSimds = 1024, kTargetWaves = 2048, kMinChunk = 64;
-    if (cols >= kSimds / 2 || L <= 2 * kMinChunk) {
+    if (cols >= kMid || L < 2 * kMinChunk) {
       chunk = L;
     } else {
-      int64_t want = (kTargetWaves + cols - 1) / cols;
+      const int64_t waves = cols * nsplit;
+      const int64_t want = (kChunkWaves + waves - 1) / waves;
       chunk = (L + want - 1) / want;
       if (chunk < kMinChunk) chunk = kMinChunk;
       chunk = (chunk + 15) / 16 * 16;
@@ -69,33 +82,49 @@ TimePlan plan_time(const ss_desc_t& d) {
   if (chunk > L) chunk = L;
   tp.chunk_len = chunk;
   tp.nchunks = (L + chunk - 1) / chunk;
+  tp.nsplit = nsplit;
   return tp;
 }
 
 FwdPlan plan_fwd(const ss_desc_t& d) {
   FwdPlan p;
   p.tp = plan_time(d);
-  if (p.tp.nchunks > 1) {
-    const size_t B = size_t(d.batch), C = size_t(p.tp.nchunks), D = size_t(d.dim), N = size_t(d.dstate);
-    p.off_hend = 0;
-    p.off_dsum = align_up(B * C * N * D * sizeof(float));
-    p.bytes = p.off_dsum + align_up(B * C * D * sizeof(float));
+  const size_t B = size_t(d.batch), L = size_t(d.seqlen), C = size_t(p.tp.nchunks),
+               D = size_t(d.dim), N = size_t(d.dstate);
+  size_t off = 0;
+  p.packed_rows = d.in_dtype != SS_F32 || d.dstate != kMaxState;
+  if (p.packed_rows) {
+    p.off_brow = off; off += align_up(B * L * kMaxState * sizeof(float));
+    p.off_crow = off; off += align_up(B * L * kMaxState * sizeof(float));
   }
+  if (p.tp.nchunks > 1) {
+    p.off_hend = off; off += align_up(B * C * N * D * sizeof(float));
+    p.off_dsum = off; off += align_up(B * C * D * sizeof(float));
+  }
+  p.bytes = off;
   return p;
 }
 
+// The backward always splits the states over 4 waves and cuts time into chunks
+// of 64 steps: a chunk's 8 block checkpoints then fit in registers.
 BwdPlan plan_bwd(const ss_desc_t& d) {
   BwdPlan p;
-  p.tp = plan_time(d);
+  p.tp.nsplit = 4;
+  p.tp.chunk_len = d.seqlen < kBwdChunk ? d.seqlen : kBwdChunk;
+  p.tp.nchunks = (d.seqlen + p.tp.chunk_len - 1) / p.tp.chunk_len;
   const size_t B = size_t(d.batch), L = size_t(d.seqlen), C = size_t(p.tp.nchunks),
                D = size_t(d.dim), N = size_t(d.dstate);
   p.nblk = (d.dim + kWave - 1) / kWave;
   const size_t nb = size_t(p.nblk);
+  p.packed_rows = d.in_dtype != SS_F32 || d.dstate != kMaxState;
   size_t off = 0;
+  if (p.packed_rows) {
+    p.off_brow = off; off += align_up(B * L * kMaxState * sizeof(float));
+    p.off_crow = off; off += align_up(B * L * kMaxState * sizeof(float));
+  }
   p.off_hend = off; off += align_up(B * C * N * D * sizeof(float));
   p.off_dsum = off; off += align_up(B * C * D * sizeof(float));
   p.off_lam = off;  off += align_up(B * C * N * D * sizeof(float));
-  p.off_lsum = off; off += align_up(B * C * D * sizeof(float));
   p.off_pB = off;   off += align_up(B * L * nb * N * sizeof(float));
   p.off_pC = off;   off += align_up(B * L * nb * N * sizeof(float));
   p.off_pA = off;   off += align_up(B * C * N * D * sizeof(float));
@@ -146,9 +175,14 @@ int ss_scan_fwd(const ss_desc_t* desc, const void* u, const void* delta, const f
   const FwdPlan plan = plan_fwd(*desc);
   if (plan.bytes > 0 && (!workspace || ws_bytes < plan.bytes || !aligned(workspace, kAlign)))
     return SS_ERR_WORKSPACE;
-  FwdArgs a{u, delta, A, Bm, Cm, D_skip, delta_bias, z, h0, y, h_last, nullptr, nullptr};
-  if (plan.bytes > 0) {
-    char* ws = static_cast<char*>(workspace);
+  FwdArgs a{u, delta, A, Bm, Cm, D_skip, delta_bias, z, h0, y, h_last,
+            nullptr, nullptr, nullptr, nullptr};
+  char* ws = static_cast<char*>(workspace);
+  if (plan.packed_rows) {
+    a.Brow = reinterpret_cast<float*>(ws + plan.off_brow);
+    a.Crow = reinterpret_cast<float*>(ws + plan.off_crow);
+  }
+  if (plan.tp.nchunks > 1) {
     a.hend = reinterpret_cast<float*>(ws + plan.off_hend);
     a.dsum = reinterpret_cast<float*>(ws + plan.off_dsum);
   }

@@ -1,8 +1,628 @@
-// Backward selective scan (placeholder until the recompute kernels land).
+// Backward selective scan for gfx950, with recomputation.
+//
+// The states are never stored in memory: they are rebuilt from the inputs
+// ("A Visual Guide to Mamba" summary, Hardware-aware Algorithm: recomputation;
+// "A Survey of Mamba" summary, hardware-aware computation).  Time is cut into
+// chunks of 64 steps.  Per chunk:
+//   - its start state comes from the forward's summary pass + carry scan;
+//   - the adjoint carry entering it from its end comes from a reverse summary
+//     pass + reverse carry scan (the adjoint recurrence
+//     lambda_t = gy_t C_t + A_bar_{t+1} lambda_{t+1} is the same linear scan run
+//     backwards in time);
+//   - a workgroup of 4 waves (lane = channel d, 4 states per wave) runs the
+//     chunk forward keeping one state checkpoint per 8-step block in registers,
+//     then walks the blocks backwards: recompute the block (A_bar and h kept in
+//     registers), reverse sweep, gradients.
+// Reductions: dB, dC over the 64 channels of a block by a cross-lane
+// reduce-scatter (permlane swaps and DPP), then over channel blocks; dA, dD_skip
+// and ddelta_bias per channel over the chunk, then over chunks and batch rows.
+// All partial sums are added in a fixed order: the backward is deterministic.
 #include "ss_device.hpp"
 
 namespace ss {
-int launch_bwd(const ss_desc_t&, const BwdPlan&, const BwdArgs&, void*) {
-  return int(hipErrorNotSupported);
+namespace {
+
+constexpr int kZoh = SS_ZOH;
+constexpr int kEuler = SS_EULER;
+constexpr int kNW = 4;                 // waves per workgroup
+constexpr int kNS = kMaxState / kNW;   // states per wave
+constexpr int kKB = 8;                 // steps per block
+constexpr int kNB = 8;                 // blocks per chunk
+constexpr int kChunk = kKB * kNB;      // steps per chunk (matches the backward plan)
+
+struct BwdParams {
+  const void* u;
+  const void* delta;
+  const void* z;
+  const void* dy;
+  const float* A;
+  const float* Brow;     // (B, L, 16) fp32
+  const float* Crow;
+  const float* Dskip;
+  const float* bias;
+  const float* h0;
+  const float* hstart;   // (B, nc, N, D): start state of chunk c (c >= 1)
+  const float* dsum;     // (B, nc, D): sum of dt * log2 e over chunk c (c <= nc - 2)
+  float* lam;            // (B, nc, N, D): adjoint carry entering chunk c from its end
+  float* du;
+  float* ddelta;
+  float* dz;
+  float* dh0;
+  float* pB;             // (B, L, nblk, N)
+  float* pC;
+  float* pA;             // (B, nc, N, D)
+  float* pD;             // (B, nc, D)
+  float* pbias;
+  int64_t L, D;
+  int32_t N, ndblk, nchunks;
+};
+
+using ConstF32 = __attribute__((address_space(4))) const float;
+
+// This wave's 4 values of a B or C row: a scalar load (same address in every lane).
+__device__ __forceinline__ void row4(const float* rows, int64_t row, int n0, float (&v)[kNS]) {
+  ConstF32* q = (ConstF32*)(rows + row * kMaxState + n0);
+#pragma unroll
+  for (int j = 0; j < kNS; ++j) v[j] = q[j];
 }
+
+template <typename In>
+__device__ __forceinline__ float ld(const void* base, int64_t i) {
+  return to_f32(static_cast<const In*>(base)[i]);
+}
+
+// (delta + bias) log2 e -> dt log2 e
+template <bool SOFTPLUS>
+__device__ __forceinline__ float step_log2(float x2) {
+  return SOFTPLUS ? softplus_log2(x2) : x2;
+}
+
+__device__ __forceinline__ float sigmoid_log2(float x2) {   // 1 / (1 + e^-x), x2 = x log2 e
+  return hw_rcp(1.0f + hw_exp2(-x2));
+}
+
+// ---------------------------------------------------------------- reduce-scatter
+// 64 values per lane -> lane l holds the sum over the 64 lanes of value l.
+// Stages pair lanes at distance 32 and 16 (permlane swaps: the pair's two sums
+// come out of one swap + add), then 8 (row rotate), the mirror pairs inside
+// each 8-lane group, 2 and 1 (quad permutes).  After each stage a lane keeps
+// the half of its values selected by one bit of its lane id, so lane l ends
+// with value l.
+__device__ __forceinline__ float swap_add32(float lo, float hi) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(lo), __float_as_uint(hi), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float swap_add16(float lo, float hi) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(lo), __float_as_uint(hi), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_pair(float lo, float hi, bool upper) {
+  const float send = upper ? lo : hi;
+  const float keep = upper ? hi : lo;
+  return keep + __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(send), CTRL, 0xf, 0xf, false));
+}
+constexpr int kDppRowRor8 = 0x128;
+constexpr int kDppRowHalfMirror = 0x141;
+constexpr int kDppQuadXor2 = 0x4e;   // quad_perm [2, 3, 0, 1]
+constexpr int kDppQuadXor1 = 0xb1;   // quad_perm [1, 0, 3, 2]
+
+__device__ __forceinline__ float reduce_scatter64(const float (&v)[64], uint32_t lane) {
+  float a[32];
+#pragma unroll
+  for (int i = 0; i < 32; ++i) a[i] = swap_add32(v[i], v[i + 32]);
+  float b[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) b[i] = swap_add16(a[i], a[i + 16]);
+  float c[8];
+  const bool u3 = (lane >> 3) & 1u, u2 = (lane >> 2) & 1u, u1 = (lane >> 1) & 1u, u0 = lane & 1u;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) c[i] = dpp_pair<kDppRowRor8>(b[i], b[i + 8], u3);
+  float d[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) d[i] = dpp_pair<kDppRowHalfMirror>(c[i], c[i + 4], u2);
+  float e[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) e[i] = dpp_pair<kDppQuadXor2>(d[i], d[i + 2], u1);
+  return dpp_pair<kDppQuadXor1>(e[0], e[1], u0);
+}
+
+// ---------------------------------------------------------------- main kernel
+template <typename In, int DISC, bool HAS_Z, bool SOFTPLUS, bool SAFE>
+__device__ __forceinline__ void bwd_chunk(const BwdParams& p, float* lds, int64_t b, int dblk,
+                                          int chunk, int wave, uint32_t lane) {
+  const int n0 = wave * kNS;
+  const int N = p.N;
+  const int64_t D = p.D;
+  const int64_t d = int64_t(dblk) * kWave + lane;
+  const bool active = d < D;
+  const int64_t dc = active ? d : D - 1;
+  const float amask = active ? 1.0f : 0.0f;
+  const int32_t t0 = chunk * kChunk;
+  const int32_t t1 = int32_t(t0 + kChunk < p.L ? t0 + kChunk : p.L);
+  const int64_t row0 = b * p.L;
+  const int64_t ibase = row0 * D + dc;          // element (b, t = 0, d)
+
+  float A[kNS], iA[kNS], zm[kNS];
+#pragma unroll
+  for (int j = 0; j < kNS; ++j) {
+    const int n = n0 + j;
+    const float a = n < N ? p.A[dc * N + n] : -1.0f;
+    A[j] = a;
+    iA[j] = a == 0.0f ? 0.0f : 1.0f / a;
+    zm[j] = a == 0.0f ? 1.0f : 0.0f;
+  }
+  const float Dd = p.Dskip ? p.Dskip[dc] : 0.0f;
+  const float bias2 = (p.bias ? p.bias[dc] : 0.0f) * kLog2e;
+
+  float* actDl = lds;                            // [64 steps][64 lanes]
+  float* actGy = lds + kChunk * kWave;           // [64 steps][64 lanes]
+  float* xch = lds + 2 * kChunk * kWave;         // [4 waves][3][8 steps][64 lanes]
+
+  // ---- phase A1: step sizes and gated upstream gradients of the chunk, each
+  //      wave computing the steps k with k % 4 == wave, shared through LDS
+#pragma unroll
+  for (int s = 0; s < kChunk / kNW; ++s) {
+    const int k = s * kNW + wave;
+    const int32_t t = t0 + k;
+    float dl = 0.0f, gy = 0.0f;
+    if (t < t1) {
+      const int64_t i = ibase + int64_t(t) * D;
+      dl = step_log2<SOFTPLUS>(__builtin_fmaf(ld<In>(p.delta, i), kLog2e, bias2));
+      gy = ld<In>(p.dy, i);
+      if (HAS_Z) gy *= silu(ld<In>(p.z, i));
+    }
+    actDl[k * kWave + lane] = dl;
+    actGy[k * kWave + lane] = gy * amask;
+  }
+  __syncthreads();
+
+  // ---- phase A2: forward over the chunk, one checkpoint per block
+  float h[kNS];
+  if (chunk == 0) {
+#pragma unroll
+    for (int j = 0; j < kNS; ++j) h[j] = (p.h0 && n0 + j < N) ? p.h0[(b * D + dc) * N + n0 + j] : 0.0f;
+  } else {
+    const float* hs = p.hstart + (b * p.nchunks + chunk) * int64_t(N) * D + dc;
+#pragma unroll
+    for (int j = 0; j < kNS; ++j) h[j] = n0 + j < N ? hs[int64_t(n0 + j) * D] : 0.0f;
+  }
+  float ck[kNB][kNS];
+#pragma unroll
+  for (int jb = 0; jb < kNB; ++jb) {
+#pragma unroll
+    for (int j = 0; j < kNS; ++j) ck[jb][j] = h[j];
+#pragma unroll
+    for (int k = 0; k < kKB; ++k) {
+      const int kk = jb * kKB + k;
+      const int32_t t = t0 + kk;
+      const int32_t tr = t < t1 ? t : t1 - 1;
+      const float dl = actDl[kk * kWave + lane];
+      const float uf = ld<In>(p.u, ibase + int64_t(tr) * D);
+      float Bv[kNS];
+      row4(p.Brow, row0 + tr, n0, Bv);
+#pragma unroll
+      for (int j = 0; j < kNS; ++j) {
+        const float a = hw_exp2(dl * A[j]);
+        float coef;
+        if (DISC == kEuler) {
+          coef = dl * kLn2;
+        } else {
+          coef = __builtin_fmaf(a, iA[j], -iA[j]);
+          if (SAFE) coef = __builtin_fmaf(dl * kLn2, zm[j], coef);
+        }
+        h[j] = __builtin_fmaf(a, h[j], coef * (Bv[j] * uf));
+      }
+    }
+  }
+
+  // ---- phase B: blocks in reverse
+  float nu[kNS];   // adjoint carried from later steps: A_bar_{t+1} lambda_{t+1}
+  if (chunk == p.nchunks - 1) {
+#pragma unroll
+    for (int j = 0; j < kNS; ++j) nu[j] = 0.0f;
+  } else {
+    const float* ls = p.lam + (b * p.nchunks + chunk) * int64_t(N) * D + dc;
+#pragma unroll
+    for (int j = 0; j < kNS; ++j) nu[j] = n0 + j < N ? ls[int64_t(n0 + j) * D] : 0.0f;
+  }
+  float dA[kNS];
+#pragma unroll
+  for (int j = 0; j < kNS; ++j) dA[j] = 0.0f;
+  float dDacc = 0.0f, dbacc = 0.0f;
+
+#pragma unroll
+  for (int jb = kNB - 1; jb >= 0; --jb) {
+    if (t0 + jb * kKB >= t1) continue;          // wave-uniform: block past the end
+    float uf[kKB], dl[kKB], gy[kKB];
+    float as[kKB][kNS], hs[kKB][kNS], yp[kKB];
+    float Bs[kKB][kNS], Cs[kKB][kNS];
+    // recompute the block
+#pragma unroll
+    for (int j = 0; j < kNS; ++j) h[j] = ck[jb][j];
+#pragma unroll
+    for (int k = 0; k < kKB; ++k) {
+      const int kk = jb * kKB + k;
+      const int32_t t = t0 + kk;
+      const int32_t tr = t < t1 ? t : t1 - 1;
+      dl[k] = actDl[kk * kWave + lane];
+      gy[k] = actGy[kk * kWave + lane];
+      uf[k] = ld<In>(p.u, ibase + int64_t(tr) * D) * amask;
+      row4(p.Brow, row0 + tr, n0, Bs[k]);
+      row4(p.Crow, row0 + tr, n0, Cs[k]);
+      float y0 = 0.0f;
+#pragma unroll
+      for (int j = 0; j < kNS; ++j) {
+        const float a = hw_exp2(dl[k] * A[j]);
+        float coef;
+        if (DISC == kEuler) {
+          coef = dl[k] * kLn2;
+        } else {
+          coef = __builtin_fmaf(a, iA[j], -iA[j]);
+          if (SAFE) coef = __builtin_fmaf(dl[k] * kLn2, zm[j], coef);
+        }
+        h[j] = __builtin_fmaf(a, h[j], coef * (Bs[k][j] * uf[k]));
+        as[k][j] = a;
+        hs[k][j] = h[j];
+        y0 = __builtin_fmaf(Cs[k][j], h[j], y0);
+      }
+      yp[k] = y0;
+    }
+    // reverse sweep
+    float dup[kKB], ddp[kKB];
+    float red[64];   // [which: dB, dC][8 steps][4 states]
+#pragma unroll
+    for (int k = kKB - 1; k >= 0; --k) {
+      const float dtn = dl[k] * kLn2;           // dt
+      float du0 = 0.0f, dd0 = 0.0f;
+#pragma unroll
+      for (int j = 0; j < kNS; ++j) {
+        const float a = as[k][j];
+        const float hp = k > 0 ? hs[k - 1][j] : ck[jb][j];
+        const float lam = __builtin_fmaf(gy[k], Cs[k][j], nu[j]);   // d loss / d h_t
+        float coef;
+        if (DISC == kEuler) {
+          coef = dtn;
+        } else {
+          coef = __builtin_fmaf(a, iA[j], -iA[j]);
+          if (SAFE) coef = __builtin_fmaf(dtn, zm[j], coef);
+        }
+        const float pu = lam * uf[k];                 // d loss / d (coef B)
+        const float q = pu * Bs[k][j];                // d loss / d coef
+        red[k * kNS + j] = pu * coef;                 // dB
+        red[32 + k * kNS + j] = gy[k] * hs[k][j];     // dC
+        du0 = __builtin_fmaf(lam, coef * Bs[k][j], du0);
+        const float da = lam * hp;                    // d loss / d A_bar
+        if (DISC == kEuler) {
+          dd0 = __builtin_fmaf(da * a, A[j], dd0 + q);
+          dA[j] = __builtin_fmaf(da, a * dtn, dA[j]);
+        } else {
+          dd0 = __builtin_fmaf(a, __builtin_fmaf(da, A[j], q), dd0);
+          dA[j] = __builtin_fmaf(a * dtn, __builtin_fmaf(q, iA[j], da), dA[j]);
+          dA[j] = __builtin_fmaf(-(q * coef), iA[j], dA[j]);
+          if (SAFE) dA[j] = __builtin_fmaf(q * zm[j], 0.5f * dtn * dtn, dA[j]);
+        }
+        nu[j] = a * lam;
+      }
+      dup[k] = du0;
+      ddp[k] = dd0;
+    }
+    // per-step partials of this wave -> LDS; dB, dC over the 64 channels
+#pragma unroll
+    for (int k = 0; k < kKB; ++k) {
+      xch[((wave * 3 + 0) * kKB + k) * kWave + lane] = dup[k];
+      xch[((wave * 3 + 1) * kKB + k) * kWave + lane] = ddp[k];
+      xch[((wave * 3 + 2) * kKB + k) * kWave + lane] = yp[k];
+    }
+    {
+      const float r = reduce_scatter64(red, lane);
+      const int which = int(lane >> 5), k = int((lane >> 2) & 7u), j = int(lane & 3u);
+      const int32_t t = t0 + jb * kKB + k;
+      if (t < t1 && n0 + j < N) {
+        float* dst = which ? p.pC : p.pB;
+        dst[((row0 + t) * p.ndblk + dblk) * N + n0 + j] = r;
+      }
+    }
+    __syncthreads();
+    // outputs of the steps this wave owns: k % 4 == wave
+#pragma unroll
+    for (int s = 0; s < kKB / kNW; ++s) {
+      const int k = s * kNW + wave;
+      const int32_t t = t0 + jb * kKB + k;
+      float sdu = 0.0f, sdd = 0.0f, sy = 0.0f;
+#pragma unroll
+      for (int w = 0; w < kNW; ++w) {
+        sdu += xch[((w * 3 + 0) * kKB + k) * kWave + lane];
+        sdd += xch[((w * 3 + 1) * kKB + k) * kWave + lane];
+        sy += xch[((w * 3 + 2) * kKB + k) * kWave + lane];
+      }
+      if (t < t1 && active) {
+        const int64_t i = ibase + int64_t(t) * D;
+        const float ui = ld<In>(p.u, i), g = ld<In>(p.dy, i);
+        float gyk = g, dzv = 0.0f;
+        if (HAS_Z) {
+          const float zf = ld<In>(p.z, i);
+          const float sz = sigmoid_log2(zf * kLog2e);
+          gyk = g * zf * sz;
+          const float y = __builtin_fmaf(Dd, ui, sy);   // pre-gate output
+          dzv = g * y * sz * __builtin_fmaf(zf, 1.0f - sz, 1.0f);
+          p.dz[i] = dzv;
+        }
+        p.du[i] = __builtin_fmaf(gyk, Dd, sdu);
+        float ddv = sdd;                                 // d loss / d dt
+        if (SOFTPLUS) {
+          const float x2 = __builtin_fmaf(ld<In>(p.delta, i), kLog2e, bias2);
+          ddv *= sigmoid_log2(x2);                       // through softplus
+        }
+        p.ddelta[i] = ddv;
+        dDacc = __builtin_fmaf(gyk, ui, dDacc);
+        dbacc += ddv;
+      }
+    }
+    __syncthreads();
+  }
+
+  if (chunk == 0 && p.dh0 && active) {
+#pragma unroll
+    for (int j = 0; j < kNS; ++j)
+      if (n0 + j < N) p.dh0[(b * D + d) * N + n0 + j] = nu[j];
+  }
+  if (active) {
+    float* pa = p.pA + (b * p.nchunks + chunk) * int64_t(N) * D + d;
+#pragma unroll
+    for (int j = 0; j < kNS; ++j)
+      if (n0 + j < N) pa[int64_t(n0 + j) * D] = dA[j];
+  }
+  // dD_skip and ddelta_bias: the four waves' per-channel sums, added by wave 0
+  xch[(wave * 2 + 0) * kWave + lane] = dDacc;
+  xch[(wave * 2 + 1) * kWave + lane] = dbacc;
+  __syncthreads();
+  if (wave == 0 && active) {
+    float sD = 0.0f, sb = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kNW; ++w) {
+      sD += xch[(w * 2 + 0) * kWave + lane];
+      sb += xch[(w * 2 + 1) * kWave + lane];
+    }
+    p.pD[(b * p.nchunks + chunk) * D + d] = sD;
+    p.pbias[(b * p.nchunks + chunk) * D + d] = sb;
+  }
+}
+
+constexpr int kLdsFloats = 2 * kChunk * kWave + kNW * 3 * kKB * kWave;
+
+template <typename In, int DISC, bool HAS_Z, bool SOFTPLUS>
+__global__ __launch_bounds__(kWave * kNW) void bwd_kernel(BwdParams p) {
+  __shared__ float lds[kLdsFloats];
+  const int wave = __builtin_amdgcn_readfirstlane(int(threadIdx.x) / kWave);
+  const uint32_t lane = threadIdx.x % kWave;
+  int64_t bid = blockIdx.x;
+  const int dblk = int(bid % p.ndblk);
+  bid /= p.ndblk;
+  const int chunk = int(bid % p.nchunks);
+  const int64_t b = bid / p.nchunks;
+  // exact ZOH with some A == 0 in the block takes the guarded path (all waves agree)
+  bool zero = false;
+  if (DISC == kZoh) {
+    const int64_t d = int64_t(dblk) * kWave + lane;
+    const int64_t dc = d < p.D ? d : p.D - 1;
+    for (int n = 0; n < p.N; ++n) zero |= p.A[dc * p.N + n] == 0.0f;
+  }
+  if (DISC == kZoh && __syncthreads_or(zero))
+    bwd_chunk<In, DISC, HAS_Z, SOFTPLUS, true>(p, lds, b, dblk, chunk, wave, lane);
+  else
+    bwd_chunk<In, DISC, HAS_Z, SOFTPLUS, false>(p, lds, b, dblk, chunk, wave, lane);
+}
+
+// ---------------------------------------------------------------- reverse summaries
+// Local adjoint of chunk c (c >= 1) with nothing entering from its end:
+// R_c = A_bar-weighted sum of gy C over the chunk, one lane per (b, d), all N
+// states.  Stored in lam[b][c].
+template <typename In, bool HAS_Z, bool SOFTPLUS>
+__global__ __launch_bounds__(kWave) void rev_summary_kernel(BwdParams p) {
+  const uint32_t lane = threadIdx.x;
+  int64_t bid = blockIdx.x;
+  const int dblk = int(bid % p.ndblk);
+  bid /= p.ndblk;
+  const int chunk = 1 + int(bid % (p.nchunks - 1));
+  const int64_t b = bid / (p.nchunks - 1);
+  const int64_t D = p.D;
+  const int N = p.N;
+  const int64_t d = int64_t(dblk) * kWave + lane;
+  const bool active = d < D;
+  const int64_t dc = active ? d : D - 1;
+  const int32_t t0 = chunk * kChunk;
+  const int32_t t1 = int32_t(t0 + kChunk < p.L ? t0 + kChunk : p.L);
+  const int64_t row0 = b * p.L;
+  const int64_t ibase = row0 * D + dc;
+  const float bias2 = (p.bias ? p.bias[dc] : 0.0f) * kLog2e;
+  float A[kMaxState], nu[kMaxState];
+#pragma unroll
+  for (int n = 0; n < kMaxState; ++n) {
+    A[n] = n < N ? p.A[dc * N + n] : -1.0f;
+    nu[n] = 0.0f;
+  }
+  for (int32_t t = t1 - 1; t >= t0; --t) {
+    const int64_t i = ibase + int64_t(t) * D;
+    const float dl = step_log2<SOFTPLUS>(__builtin_fmaf(ld<In>(p.delta, i), kLog2e, bias2));
+    float gy = ld<In>(p.dy, i);
+    if (HAS_Z) gy *= silu(ld<In>(p.z, i));
+    ConstF32* c = (ConstF32*)(p.Crow + (row0 + t) * kMaxState);
+#pragma unroll
+    for (int n = 0; n < kMaxState; ++n)
+      nu[n] = hw_exp2(dl * A[n]) * __builtin_fmaf(gy, c[n], nu[n]);
+  }
+  if (!active) return;
+  float* ls = p.lam + (b * p.nchunks + chunk) * int64_t(N) * D + d;
+#pragma unroll
+  for (int n = 0; n < kMaxState; ++n)
+    if (n < N) ls[int64_t(n) * D] = nu[n];
+}
+
+// Adjoint carries, last chunk to first, one lane per (b, n, d): slot c of lam
+// becomes the adjoint entering chunk c from its end:
+//   nu_end(nc-1) = 0,  nu_end(c-1) = P_c nu_end(c) + R_c,  P_c = exp2(A sum_c dt log2 e).
+__global__ __launch_bounds__(256) void rev_carry_kernel(float* __restrict__ lam,
+                                                        const float* __restrict__ dsum,
+                                                        const float* __restrict__ A, int64_t B,
+                                                        int64_t D, int N, int nchunks) {
+  const int64_t gid = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (gid >= B * N * D) return;
+  const int64_t d = gid % D;
+  const int n = int((gid / D) % N);
+  const int64_t b = gid / (D * N);
+  const float a = A[d * N + n];
+  const int64_t sstride = int64_t(N) * D;
+  float* ls = lam + (b * nchunks) * sstride + int64_t(n) * D + d;
+  const float* ds = dsum + (b * nchunks) * D + d;
+  float carry = ls[(nchunks - 1) * sstride];     // R of the last chunk
+  ls[(nchunks - 1) * sstride] = 0.0f;
+  for (int c = nchunks - 2; c >= 1; --c) {
+    const float R = ls[c * sstride];
+    ls[c * sstride] = carry;
+    carry = __builtin_fmaf(hw_exp2(a * ds[c * D]), carry, R);
+  }
+  ls[0] = carry;
+}
+
+// ---------------------------------------------------------------- reductions
+__global__ __launch_bounds__(256) void reduce_rows_kernel(const float* __restrict__ pB,
+                                                          const float* __restrict__ pC,
+                                                          float* __restrict__ dB,
+                                                          float* __restrict__ dC, int64_t rows,
+                                                          int nblk, int N) {
+  const int64_t gid = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (gid >= rows * N) return;
+  const int64_t r = gid / N;
+  const int n = int(gid % N);
+  const float* qb = pB + r * nblk * N + n;
+  const float* qc = pC + r * nblk * N + n;
+  float sb = 0.0f, sc = 0.0f;
+  for (int k = 0; k < nblk; ++k) {
+    sb += qb[k * N];
+    sc += qc[k * N];
+  }
+  dB[gid] = sb;
+  dC[gid] = sc;
+}
+
+__global__ __launch_bounds__(256) void reduce_chan_kernel(const float* __restrict__ pA,
+                                                          const float* __restrict__ pD,
+                                                          const float* __restrict__ pbias,
+                                                          float* __restrict__ dA,
+                                                          float* __restrict__ dD,
+                                                          float* __restrict__ dbias, int64_t B,
+                                                          int64_t D, int N, int nchunks) {
+  const int64_t gid = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (gid >= D * (N + 1)) return;
+  const int64_t d = gid % D;
+  const int n = int(gid / D);       // n == N: the per-channel vectors
+  const int64_t terms = B * nchunks;
+  if (n < N) {
+    float s = 0.0f;
+    for (int64_t k = 0; k < terms; ++k) s += pA[(k * N + n) * D + d];
+    dA[d * N + n] = s;
+  } else {
+    float sD = 0.0f, sb = 0.0f;
+    for (int64_t k = 0; k < terms; ++k) {
+      sD += pD[k * D + d];
+      sb += pbias[k * D + d];
+    }
+    if (dD) dD[d] = sD;
+    if (dbias) dbias[d] = sb;
+  }
+}
+
+template <typename In, bool HAS_Z, bool SOFTPLUS>
+hipError_t launch_main(const ss_desc_t& d, const BwdParams& p, int64_t blocks, hipStream_t st) {
+  if (d.disc == SS_ZOH)
+    hipLaunchKernelGGL((bwd_kernel<In, kZoh, HAS_Z, SOFTPLUS>), dim3(unsigned(blocks)),
+                       dim3(kWave * kNW), 0, st, p);
+  else
+    hipLaunchKernelGGL((bwd_kernel<In, kEuler, HAS_Z, SOFTPLUS>), dim3(unsigned(blocks)),
+                       dim3(kWave * kNW), 0, st, p);
+  return hipGetLastError();
+}
+
+template <typename In, bool HAS_Z, bool SOFTPLUS>
+hipError_t launch_rev(const BwdParams& p, int64_t blocks, hipStream_t st) {
+  hipLaunchKernelGGL((rev_summary_kernel<In, HAS_Z, SOFTPLUS>), dim3(unsigned(blocks)),
+                     dim3(kWave), 0, st, p);
+  return hipGetLastError();
+}
+
+template <typename In>
+hipError_t dispatch_bwd(const ss_desc_t& d, const BwdParams& p, bool rev, int64_t blocks,
+                        hipStream_t st) {
+  const bool z = p.z != nullptr, sp = d.delta_softplus != 0;
+  if (rev) {
+    if (z) return sp ? launch_rev<In, true, true>(p, blocks, st) : launch_rev<In, true, false>(p, blocks, st);
+    return sp ? launch_rev<In, false, true>(p, blocks, st) : launch_rev<In, false, false>(p, blocks, st);
+  }
+  if (z) return sp ? launch_main<In, true, true>(d, p, blocks, st) : launch_main<In, true, false>(d, p, blocks, st);
+  return sp ? launch_main<In, false, true>(d, p, blocks, st) : launch_main<In, false, false>(d, p, blocks, st);
+}
+
+}  // namespace
+
+int launch_bwd(const ss_desc_t& d, const BwdPlan& plan, const BwdArgs& a, void* stream) {
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (plan.tp.chunk_len != kChunk && plan.tp.nchunks > 1) return int(hipErrorInvalidValue);
+  char* ws = a.ws;
+  float* Brow = plan.packed_rows ? reinterpret_cast<float*>(ws + plan.off_brow)
+                                 : const_cast<float*>(static_cast<const float*>(a.Bm));
+  float* Crow = plan.packed_rows ? reinterpret_cast<float*>(ws + plan.off_crow)
+                                 : const_cast<float*>(static_cast<const float*>(a.Cm));
+  float* hend = reinterpret_cast<float*>(ws + plan.off_hend);
+  float* dsum = reinterpret_cast<float*>(ws + plan.off_dsum);
+  float* lam = reinterpret_cast<float*>(ws + plan.off_lam);
+  if (plan.packed_rows) {
+    const int e = launch_pack_rows(d, a.Bm, a.Cm, Brow, Crow, stream);
+    if (e != 0) return e;
+  }
+  const int nc = int(plan.tp.nchunks);
+  const int ndblk = int(plan.nblk);
+  if (nc > 1) {
+    FwdArgs fa{a.u, a.delta, a.A, a.Bm, a.Cm, a.Dskip, a.bias, a.z, a.h0, nullptr, nullptr,
+               Brow, Crow, hend, dsum};
+    const int e = launch_fwd_carries(d, plan.tp, fa, stream);
+    if (e != 0) return e;
+  }
+  BwdParams p{};
+  p.u = a.u; p.delta = a.delta; p.z = a.z; p.dy = a.dy; p.A = a.A;
+  p.Brow = Brow; p.Crow = Crow; p.Dskip = a.Dskip; p.bias = a.bias; p.h0 = a.h0;
+  p.hstart = hend; p.dsum = dsum; p.lam = lam;
+  p.du = a.du; p.ddelta = a.ddelta; p.dz = a.dz; p.dh0 = a.dh0;
+  p.pB = reinterpret_cast<float*>(ws + plan.off_pB);
+  p.pC = reinterpret_cast<float*>(ws + plan.off_pC);
+  p.pA = reinterpret_cast<float*>(ws + plan.off_pA);
+  p.pD = reinterpret_cast<float*>(ws + plan.off_pD);
+  p.pbias = reinterpret_cast<float*>(ws + plan.off_pbias);
+  p.L = d.seqlen; p.D = d.dim; p.N = int32_t(d.dstate); p.ndblk = ndblk; p.nchunks = nc;
+  const int64_t cols = d.batch * ndblk;
+  hipError_t e;
+  if (nc > 1) {
+    e = d.in_dtype == SS_BF16 ? dispatch_bwd<uint16_t>(d, p, true, cols * (nc - 1), st)
+                              : dispatch_bwd<float>(d, p, true, cols * (nc - 1), st);
+    if (e != hipSuccess) return int(e);
+    const int64_t total = d.batch * d.dstate * d.dim;
+    hipLaunchKernelGGL(rev_carry_kernel, dim3(unsigned((total + 255) / 256)), dim3(256), 0, st,
+                       lam, dsum, a.A, d.batch, d.dim, int(d.dstate), nc);
+    e = hipGetLastError();
+    if (e != hipSuccess) return int(e);
+  }
+  e = d.in_dtype == SS_BF16 ? dispatch_bwd<uint16_t>(d, p, false, cols * nc, st)
+                            : dispatch_bwd<float>(d, p, false, cols * nc, st);
+  if (e != hipSuccess) return int(e);
+  const int64_t rows = d.batch * d.seqlen;
+  hipLaunchKernelGGL(reduce_rows_kernel, dim3(unsigned((rows * d.dstate + 255) / 256)), dim3(256),
+                     0, st, p.pB, p.pC, a.dB, a.dC, rows, ndblk, int(d.dstate));
+  e = hipGetLastError();
+  if (e != hipSuccess) return int(e);
+  hipLaunchKernelGGL(reduce_chan_kernel, dim3(unsigned((d.dim * (d.dstate + 1) + 255) / 256)),
+                     dim3(256), 0, st, p.pA, p.pD, p.pbias, a.dA, a.dDskip, a.dbias, d.batch,
+                     d.dim, int(d.dstate), nc);
+  return int(hipGetLastError());
+}
+
 }  // namespace ss

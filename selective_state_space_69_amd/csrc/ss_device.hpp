@@ -20,11 +20,14 @@ __device__ __forceinline__ float hw_rcp(float x) { return __builtin_amdgcn_rcpf(
 
 // Raw buffer access: a wave-uniform 64-bit base in a buffer resource (SGPRs),
 // a 32-bit per-lane byte offset (VGPR) and a 32-bit uniform byte offset (SGPR),
-// so address arithmetic stays on the scalar unit.  Range checking is disabled
-// (num_records = max); callers keep every access inside its tensor.
+// so address arithmetic stays on the scalar unit.  Callers keep every real
+// access inside its tensor.
+// An access whose total offset is >= 2^31 - 1 (num_records) is dropped (loads
+// return 0): idle lanes store with kOutOfRange instead of branching.
 using Rsrc = __amdgpu_buffer_rsrc_t;
+constexpr uint32_t kOutOfRange = 0x80000000u;
 __device__ __forceinline__ Rsrc make_rsrc(const void* p) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), short(0), -1, 0x00020000);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), short(0), 0x7fffffff, 0x00020000);
 }
 template <typename T> __device__ __forceinline__ T buf_load(Rsrc r, uint32_t voff, uint32_t soff);
 template <> __device__ __forceinline__ uint16_t buf_load<uint16_t>(Rsrc r, uint32_t voff, uint32_t soff) {
@@ -76,57 +79,6 @@ __device__ __forceinline__ float softplus_log2(float x2) {
 // silu(z) = z * sigmoid(z) = z / (1 + 2^(-z log2 e)); saturates cleanly at +-inf.
 __device__ __forceinline__ float silu(float z) {
   return z * hw_rcp(1.0f + hw_exp2(-z * kLog2e));
-}
-
-// One row of B or C (N values, N <= 16) for a time step.  The row is the same
-// for every lane of the wave, so it is read through the constant address space:
-// scalar loads into SGPRs (bf16 unpacked by scalar shifts), which the vector
-// FMAs then take as free operands.  Raw dwords are kept so the load for the next
-// step can be issued one step ahead.  Unused states read 0.
-using ConstU32 = __attribute__((address_space(4))) const uint32_t;
-
-template <typename In>
-struct RowRaw {
-  uint32_t w[sizeof(In) == 2 ? kMaxState / 2 : kMaxState];
-};
-
-template <typename In, bool FULLN>
-__device__ __forceinline__ void load_row_raw(const In* base, int64_t row, int N, RowRaw<In>& r) {
-  constexpr int kW = sizeof(In) == 2 ? kMaxState / 2 : kMaxState;
-  if constexpr (FULLN) {
-    ConstU32* q = (ConstU32*)(base + row * kMaxState);  // generic -> constant address space
-#pragma unroll
-    for (int k = 0; k < kW; ++k) r.w[k] = q[k];
-  } else {
-    // generic N: element loads, packed into the same raw layout
-#pragma unroll
-    for (int k = 0; k < kW; ++k) r.w[k] = 0;
-#pragma unroll
-    for (int n = 0; n < kMaxState; ++n) {
-      if (n < N) {
-        if constexpr (sizeof(In) == 2) {
-          const uint32_t v = reinterpret_cast<const uint16_t*>(base)[row * N + n];
-          r.w[n >> 1] |= (n & 1) ? (v << 16) : v;
-        } else {
-          r.w[n] = reinterpret_cast<const uint32_t*>(base)[row * N + n];
-        }
-      }
-    }
-  }
-}
-
-template <typename In>
-__device__ __forceinline__ void unpack_row(const RowRaw<In>& r, float (&v)[kMaxState]) {
-  if constexpr (sizeof(In) == 2) {
-#pragma unroll
-    for (int k = 0; k < kMaxState / 2; ++k) {
-      v[2 * k] = __uint_as_float(r.w[k] << 16);
-      v[2 * k + 1] = __uint_as_float(r.w[k] & 0xffff0000u);
-    }
-  } else {
-#pragma unroll
-    for (int k = 0; k < kMaxState; ++k) v[k] = __uint_as_float(r.w[k]);
-  }
 }
 
 }  // namespace ss

@@ -1,21 +1,28 @@
 // Forward selective scan for gfx950.
 //
-// Mapping: one wavefront per (batch row b, block of 64 channels, time chunk).
-// Lane = channel d.  Each lane keeps its channel's N <= 16 fp32 states in VGPRs
-// and walks its time range sequentially; every (b, t) row of B and C is shared
-// by all channels (Broadcast over D: "A Survey of Mamba" summary, Selection), so
-// the row is the same for the whole wave and sits in SGPRs.  Per element
-// (b, t, d, n) the work is one v_exp_f32 and 4 (Euler) or 6 (exact ZOH) vector
-// ops; the discretised A_bar, B_bar and the states never touch memory
+// Mapping: one workgroup per (batch row b, block of 64 channels, time chunk),
+// made of NSPLIT wavefronts (1, 2 or 4).  Lane = channel d; wave w of the group
+// keeps states n in [w*NS, (w+1)*NS), NS = 16 / NSPLIT, as fp32 in VGPRs and
+// walks the chunk's time steps sequentially.  Every (b, t) row of B and C is
+// shared by all channels (Broadcast over D: "A Survey of Mamba" summary,
+// Selection), so it is the same for the whole wave: the rows are staged through
+// LDS a block of 8 steps at a time and read back with broadcast loads.  Per
+// element (b, t, d, n) the work is one v_exp_f32 and 4 (Euler) or 6 (exact ZOH)
+// vector ops; the discretised A_bar, B_bar and the states never touch memory
 // ("A Visual Guide to Mamba" summary, Hardware-aware Algorithm: discretisation,
-// scan and the C contraction fused in one kernel).
+// scan and the C contraction fused in one kernel).  With NSPLIT > 1 the waves'
+// partial sums over n of C h are added through LDS once per 8-step block; wave 0
+// applies the D skip and the gate and stores y.  Splitting the states gives more
+// waves per SIMD on wide problems, which hides the latency of the
+// transcendental units; each wave repeats the cheap per-step softplus.
 //
 // Long or narrow problems are cut into time chunks (two-level carry):
 //   1. summary pass: per chunk, the zero-start end state S and the summed step
 //      sum(dt) (the chunk decay is exp(A * sum(dt)));
 //   2. carry scan: start state of chunk c+1 = exp(A sum_c) * start_c + S_c, the
-//      associative combine (a1, b1) o (a2, b2) = (a1 a2, a2 b1 + b2) applied
-//      left to right ("A Visual Guide to Mamba" summary, The Scan Operation);
+//      associative combine (a1, b1) o (a2, b2) = (a1 a2, a2 b1 + b2) ("A Visual
+//      Guide to Mamba" summary, The Scan Operation: segments combined
+//      associatively), done as a wave64 scan over chunks;
 //   3. output pass: each chunk re-runs from its true start state and writes y.
 #include "ss_device.hpp"
 
@@ -24,14 +31,14 @@ namespace {
 
 constexpr int kZoh = SS_ZOH;
 constexpr int kEuler = SS_EULER;
-constexpr int kPrefetch = 8;  // time steps of u, delta, z in flight per lane
+constexpr int kPrefetch = 8;  // time steps per block (u, delta, z ring; B, C staging)
 
 struct FwdParams {
   const void* u;
   const void* delta;
   const float* A;
-  const void* Bm;
-  const void* Cm;
+  const float* Brow;   // (B, L, 16) fp32 rows of B (padded with zeros past N)
+  const float* Crow;   // (B, L, 16) fp32 rows of C
   const float* Dskip;
   const float* bias;
   const void* z;
@@ -45,131 +52,245 @@ struct FwdParams {
   int32_t N, ndblk, nchunks, grid_chunks;
 };
 
-// Per-lane constants of a channel.
+template <int NS>
 struct Chan {
-  float A[kMaxState];    // diagonal A[d, n]; unused states get -1 (inert: B = C = 0)
-  float iA[kMaxState];   // 1 / A (0 where A == 0)
-  float zm[kMaxState];   // 1 where A == 0 (exact ZOH falls back to dt * B there)
+  float A[NS];    // diagonal A[d, n]; unused states get -1 (inert: B = C = 0)
+  float iA[NS];   // 1 / A (0 where A == 0)
+  float zm[NS];   // 1 where A == 0 (exact ZOH falls back to dt * B there)
 };
 
-template <typename In, typename Out, int DISC, bool HAS_Z, bool SOFTPLUS, bool SUMMARY, bool SAFE,
-          bool FULLN>
-__device__ __forceinline__ void scan_range(const FwdParams& p, const Chan& ch, float (&h)[kMaxState],
-                                           int64_t b, int64_t dblk, uint32_t lane_c, bool active,
-                                           int32_t t0, int32_t t1, float Dd, float bias2,
-                                           float& dsum) {
-  const int64_t D = p.D;
-  const int N = FULLN ? kMaxState : p.N;
-  constexpr uint32_t kIn = sizeof(In), kOut = sizeof(Out);
-  const uint32_t rowb_in = uint32_t(D) * kIn;      // bytes between time steps
-  const uint32_t rowb_out = uint32_t(D) * kOut;
-  const uint32_t vin = lane_c * kIn, vout = lane_c * kOut;
-  // wave-uniform pointers of (b, t = 0, d = 64 * dblk)
-  const int64_t base = b * p.L * D + dblk * kWave;
-  const In* ub = static_cast<const In*>(p.u) + base;
-  const In* db = static_cast<const In*>(p.delta) + base;
-  const In* zb = HAS_Z ? static_cast<const In*>(p.z) + base : nullptr;
-  Out* yb = SUMMARY ? nullptr : static_cast<Out*>(p.y) + base;
-  const In* Bp = static_cast<const In*>(p.Bm);
-  const In* Cp = static_cast<const In*>(p.Cm);
-  const int64_t row0 = b * p.L;
-  const int32_t tlast = t1 - 1;
+// LDS per workgroup: B/C row staging, per wave 2 buffers x 8 steps x 2*NS floats
+// (= 512 floats for the whole group); with NSPLIT > 1 also the shared step
+// sizes, 2 buffers x 64 lanes x 8 steps, and the partial outputs, 2 buffers x
+// NSPLIT waves x 64 lanes x 8 steps.
+template <int NSPLIT>
+struct Lds {
+  static constexpr int kNS = kMaxState / NSPLIT;
+  static constexpr int kStage = 2 * kPrefetch * 2 * kNS;                 // floats per wave
+  static constexpr int kAct = NSPLIT > 1 ? 2 * kWave * kPrefetch : 0;
+  static constexpr int kPart = NSPLIT > 1 ? 2 * NSPLIT * kWave * kPrefetch : 0;
+  static constexpr int kFloats = NSPLIT * kStage + kAct + kPart;
+};
 
-  // prefetch ring of u, delta, z, kPrefetch steps deep (indices clamped to the
-  // last step of the range, so every load is in bounds)
-  In ur[kPrefetch], dr[kPrefetch], zr[kPrefetch];
-  {
-    const Rsrc ru = make_rsrc(ub + int64_t(t0) * D), rd = make_rsrc(db + int64_t(t0) * D);
-    const Rsrc rz = make_rsrc(HAS_Z ? zb + int64_t(t0) * D : ub);
+// Step ownership inside a block of 8 steps: step k belongs to wave k % NSPLIT,
+// which alone computes its softplus step size (shared with the other waves
+// through LDS), its gate, and its final output.
+template <typename In, typename Out, int DISC, bool HAS_Z, bool SOFTPLUS, bool SUMMARY, bool SAFE,
+          int NSPLIT>
+struct Scan {
+  static constexpr int NS = kMaxState / NSPLIT;
+  static constexpr int OWN = kPrefetch / NSPLIT;   // steps owned per block
+  const FwdParams& p;
+  const Chan<NS>& ch;
+  float (&h)[NS];
+  float Dd, bias2;
+  float dsum;
+  int64_t row0;          // b * L
+  const In* ub;          // wave-uniform base pointers of (b, t = 0, d = 64 * dblk)
+  const In* db;
+  const In* zb;
+  Out* yb;
+  uint32_t vin, vout;    // per-lane byte offsets (vout is out of range for idle lanes)
+  uint32_t rowb_in, rowb_out;
+  int32_t t1, tlast;
+  float* stage;          // this wave's row staging buffer (2 x 8 x 2*NS floats)
+  float* act;            // shared step sizes (NSPLIT > 1)
+  float* part;           // partial outputs (NSPLIT > 1)
+  uint32_t lane;
+  int wave, n0;          // wave index in the group, first state of this wave
+  In ur[kPrefetch];      // prefetch ring: u of every step of the next block
+  In dr[OWN], zr[OWN];   // delta, z of the owned steps of the next block
+  float dl_own[OWN], g_own[OWN];   // step size and gate of the owned steps
+  float4 rowq;           // this lane's 16 bytes of the next block's rows
+
+  __device__ __forceinline__ int owned(int i) const { return i * NSPLIT + wave; }
+
+  __device__ __forceinline__ void load_ring(int32_t tbase, int32_t t, bool clamp) {
+    const Rsrc ru = make_rsrc(ub + int64_t(tbase) * p.D), rd = make_rsrc(db + int64_t(tbase) * p.D);
+    const Rsrc rz = make_rsrc(HAS_Z ? zb + int64_t(tbase) * p.D : ub);
 #pragma unroll
     for (int k = 0; k < kPrefetch; ++k) {
-      const int32_t tt = t0 + k < tlast ? t0 + k : tlast;
-      const uint32_t so = uint32_t(tt - t0) * rowb_in;
-      ur[k] = buf_load<In>(ru, vin, so);
-      dr[k] = buf_load<In>(rd, vin, so);
-      if (HAS_Z && !SUMMARY) zr[k] = buf_load<In>(rz, vin, so);
+      int32_t tt = t + k;
+      if (clamp) tt = tt < tlast ? tt : tlast;
+      ur[k] = buf_load<In>(ru, vin, uint32_t(tt - tbase) * rowb_in);
+    }
+#pragma unroll
+    for (int i = 0; i < OWN; ++i) {
+      int32_t tt = t + owned(i);
+      if (clamp) tt = tt < tlast ? tt : tlast;
+      const uint32_t so = uint32_t(tt - tbase) * rowb_in;
+      dr[i] = buf_load<In>(rd, vin, so);
+      if (HAS_Z && !SUMMARY) zr[i] = buf_load<In>(rz, vin, so);
     }
   }
-  RowRaw<In> bn, cn;
-  load_row_raw<In, FULLN>(Bp, row0 + t0, N, bn);
-  if (!SUMMARY) load_row_raw<In, FULLN>(Cp, row0 + t0, N, cn);
 
-  // Time steps run in blocks of kPrefetch; steps past t1 (only in a ragged
-  // last block) get dt = 0, which leaves the state unchanged, and store nothing.
-  for (int32_t t = t0; t < t1; t += kPrefetch) {
-    const Rsrc ru = make_rsrc(ub + int64_t(t) * D), rd = make_rsrc(db + int64_t(t) * D);
-    const Rsrc rz = make_rsrc(HAS_Z ? zb + int64_t(t) * D : ub);
-    const Rsrc ry = make_rsrc(SUMMARY ? static_cast<const void*>(ub) : static_cast<const void*>(yb + int64_t(t) * D));
+  // step size (log2 units) and gate of the owned steps of the block at t, from
+  // the ring; steps at or past t1 get dt = 0
+  __device__ __forceinline__ void activations(int32_t t) {
+#pragma unroll
+    for (int i = 0; i < OWN; ++i) {
+      float x2 = __builtin_fmaf(to_f32(dr[i]), kLog2e, bias2);    // (delta + bias) log2 e
+      if (t + owned(i) >= t1) x2 = SOFTPLUS ? -__builtin_inff() : 0.0f;
+      dl_own[i] = SOFTPLUS ? softplus_log2(x2) : x2;               // dt * log2 e
+      if (HAS_Z && !SUMMARY) g_own[i] = silu(to_f32(zr[i]));
+    }
+  }
+  __device__ __forceinline__ void publish(int buf) {
+    if (NSPLIT == 1) return;
+#pragma unroll
+    for (int i = 0; i < OWN; ++i) act[(buf * kWave + lane) * kPrefetch + owned(i)] = dl_own[i];
+  }
+
+  // Rows of block [t, t + 8): per step, NS values of B then NS of C (this wave's
+  // states), i.e. NS/2 float4 per step; lane l fetches float4 g = l % (NS/2) of
+  // step k = (l / (NS/2)) % 8 (lanes beyond 4*NS repeat lower lanes' work).
+  __device__ __forceinline__ void fetch_rows(int32_t t) {
+    constexpr int G = NS / 2;
+    const uint32_t l = lane % uint32_t(4 * NS);
+    const int k = int(l / G), g = int(l % G);
+    int32_t tr = t + k;
+    tr = tr < tlast ? tr : tlast;
+    const float* src = (g < G / 2 ? p.Brow : p.Crow) + (row0 + tr) * kMaxState + n0 +
+                       4 * (g % (G / 2));
+    rowq = *reinterpret_cast<const float4*>(src);
+  }
+  __device__ __forceinline__ void stage_rows(int buf) {
+    constexpr int G = NS / 2;
+    const uint32_t l = lane % uint32_t(4 * NS);
+    const uint32_t off = buf * (kPrefetch * 2 * NS) + (l / G) * (2 * NS) + 4 * (l % G);
+    *reinterpret_cast<float4*>(stage + off) = rowq;
+  }
+  __device__ __forceinline__ void read_rows(int buf, int k, float (&Bv)[NS], float (&Cv)[NS]) {
+    const float4* q = reinterpret_cast<const float4*>(stage + buf * (kPrefetch * 2 * NS) + k * 2 * NS);
+#pragma unroll
+    for (int m = 0; m < NS / 4; ++m) {
+      const float4 v = q[m];
+      Bv[4 * m] = v.x; Bv[4 * m + 1] = v.y; Bv[4 * m + 2] = v.z; Bv[4 * m + 3] = v.w;
+    }
+    if (!SUMMARY) {
+#pragma unroll
+      for (int m = 0; m < NS / 4; ++m) {
+        const float4 v = q[NS / 4 + m];
+        Cv[4 * m] = v.x; Cv[4 * m + 1] = v.y; Cv[4 * m + 2] = v.z; Cv[4 * m + 3] = v.w;
+      }
+    }
+  }
+
+  // One block of 8 steps starting at t.  On entry the ring holds this block's
+  // inputs (owned-step activations already computed and, for NSPLIT > 1,
+  // published to act[buf] behind a barrier).  GUARD: the block may run past t1
+  // and the prefetch of the next block is clamped to the range.
+  template <bool GUARD>
+  __device__ __forceinline__ void block(int32_t t, int buf) {
+    // 1. inputs of this block: u of every step, dt of every step
+    float uf[kPrefetch], dl[kPrefetch], acc[kPrefetch], g[OWN];
+#pragma unroll
+    for (int k = 0; k < kPrefetch; ++k) uf[k] = to_f32(ur[k]);
+    if (NSPLIT == 1) {
+#pragma unroll
+      for (int k = 0; k < kPrefetch; ++k) dl[k] = dl_own[k];
+    } else {
+      const float4* q = reinterpret_cast<const float4*>(act + (buf * kWave + lane) * kPrefetch);
+      const float4 x = q[0], y = q[1];
+      dl[0] = x.x; dl[1] = x.y; dl[2] = x.z; dl[3] = x.w;
+      dl[4] = y.x; dl[5] = y.y; dl[6] = y.z; dl[7] = y.w;
+    }
+#pragma unroll
+    for (int i = 0; i < OWN; ++i) g[i] = g_own[i];
+    // 2. prefetch the next block (u, owned delta and z, B and C rows)
+    load_ring(t, t + kPrefetch, GUARD);
+    fetch_rows(t + kPrefetch < t1 ? t + kPrefetch : tlast);
+    // 3. the recurrence, one step at a time (rows read from LDS one step ahead)
+    float Bn[NS], Cn[NS];
+    read_rows(buf, 0, Bn, Cn);
 #pragma unroll
     for (int k = 0; k < kPrefetch; ++k) {
-      const int32_t tt = t + k;
-      const bool valid = tt < t1;                       // wave-uniform
-      const float uf = to_f32(ur[k]);
-      const float df = to_f32(dr[k]);
-      const float zf = (HAS_Z && !SUMMARY) ? to_f32(zr[k]) : 0.0f;
-      {
-        const int32_t tn = tt + kPrefetch < tlast ? tt + kPrefetch : tlast;
-        const uint32_t so = uint32_t(tn - t) * rowb_in;
-        ur[k] = buf_load<In>(ru, vin, so);
-        dr[k] = buf_load<In>(rd, vin, so);
-        if (HAS_Z && !SUMMARY) zr[k] = buf_load<In>(rz, vin, so);
-      }
-      float Bv[kMaxState], Cv[kMaxState];
-      unpack_row(bn, Bv);
-      if (!SUMMARY) unpack_row(cn, Cv);
-      {
-        const int32_t tn = tt + 1 < tlast ? tt + 1 : tlast;
-        load_row_raw<In, FULLN>(Bp, row0 + tn, N, bn);
-        if (!SUMMARY) load_row_raw<In, FULLN>(Cp, row0 + tn, N, cn);
-      }
-
-      float dl;                                          // dt * log2(e)
-      if (SOFTPLUS) {
-        const float x2 = valid ? __builtin_fmaf(df, kLog2e, bias2) : -__builtin_inff();
-        dl = softplus_log2(x2);
-      } else {
-        dl = valid ? __builtin_fmaf(df, kLog2e, bias2) : 0.0f;
-      }
+      float Bv[NS], Cv[NS];
+#pragma unroll
+      for (int n = 0; n < NS; ++n) { Bv[n] = Bn[n]; Cv[n] = Cn[n]; }
+      if (k + 1 < kPrefetch) read_rows(buf, k + 1, Bn, Cn);
+      const float d2 = dl[k];
       float acc0 = 0.0f, acc1 = 0.0f;
       if (DISC == kEuler) {
-        const float dtu = dl * (kLn2 * uf);              // dt * u
+        const float dtu = d2 * (kLn2 * uf[k]);                    // dt * u
 #pragma unroll
-        for (int n = 0; n < kMaxState; ++n) {
-          const float a = hw_exp2(dl * ch.A[n]);         // A_bar = exp(dt A)
-          h[n] = __builtin_fmaf(a, h[n], dtu * Bv[n]);   // + dt B u
+        for (int n = 0; n < NS; ++n) {
+          const float a = hw_exp2(d2 * ch.A[n]);                  // A_bar = exp(dt A)
+          h[n] = __builtin_fmaf(a, h[n], dtu * Bv[n]);            // + dt B u
           if (!SUMMARY) {
             if (n & 1) acc1 = __builtin_fmaf(Cv[n], h[n], acc1);
             else acc0 = __builtin_fmaf(Cv[n], h[n], acc0);
           }
         }
       } else {
-        const float dt = SAFE ? dl * kLn2 : 0.0f;
+        const float dt = SAFE ? d2 * kLn2 : 0.0f;
 #pragma unroll
-        for (int n = 0; n < kMaxState; ++n) {
-          const float a = hw_exp2(dl * ch.A[n]);              // A_bar = exp(dt A)
-          float coef = __builtin_fmaf(a, ch.iA[n], -ch.iA[n]);  // (A_bar - 1) / A
-          if (SAFE) coef = __builtin_fmaf(dt, ch.zm[n], coef);  // dt where A == 0
-          h[n] = __builtin_fmaf(a, h[n], coef * (Bv[n] * uf));
+        for (int n = 0; n < NS; ++n) {
+          const float a = hw_exp2(d2 * ch.A[n]);                  // A_bar = exp(dt A)
+          float coef = __builtin_fmaf(a, ch.iA[n], -ch.iA[n]);    // (A_bar - 1) / A
+          if (SAFE) coef = __builtin_fmaf(dt, ch.zm[n], coef);    // dt where A == 0
+          h[n] = __builtin_fmaf(a, h[n], coef * (Bv[n] * uf[k]));
           if (!SUMMARY) {
             if (n & 1) acc1 = __builtin_fmaf(Cv[n], h[n], acc1);
             else acc0 = __builtin_fmaf(Cv[n], h[n], acc0);
           }
         }
       }
-      if (SUMMARY) {
-        dsum += dl;
+      if (SUMMARY) dsum += d2;
+      // wave 0 adds the D skip into its partial sum
+      else acc[k] = wave == 0 ? __builtin_fmaf(Dd, uf[k], acc0 + acc1) : acc0 + acc1;
+    }
+    // 4. activations of the next block's owned steps, rows of the next block
+    activations(t + kPrefetch);
+    publish(buf ^ 1);
+    stage_rows(buf ^ 1);
+    if (NSPLIT > 1 && !SUMMARY) {
+      float4* q = reinterpret_cast<float4*>(part + ((buf * NSPLIT + wave) * kWave + lane) * kPrefetch);
+      q[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+      q[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+    }
+    if (NSPLIT > 1) __syncthreads();
+    if (SUMMARY) return;
+    // 5. outputs of the owned steps: sum of the waves' partials, gate, store
+    const Rsrc ry = make_rsrc(yb + int64_t(t) * p.D);
+#pragma unroll
+    for (int i = 0; i < OWN; ++i) {
+      const int k = owned(i);
+      float yv;
+      if (NSPLIT == 1) {
+        yv = acc[k];
       } else {
-        float yv = __builtin_fmaf(Dd, uf, acc0 + acc1);      // C h + D u
-        if (HAS_Z) yv *= silu(zf);                            // gate
-        if (active && valid) buf_store<Out>(ry, vout, uint32_t(k) * rowb_out, yv);
+        yv = 0.0f;
+#pragma unroll
+        for (int w = 0; w < NSPLIT; ++w) yv += part[((buf * NSPLIT + w) * kWave + lane) * kPrefetch + k];
       }
+      if (HAS_Z) yv *= g[i];                                       // silu(z) gate
+      if (!GUARD || t + k < t1) buf_store<Out>(ry, vout, uint32_t(k) * rowb_out, yv);
     }
   }
-}
 
-template <typename In, typename Out, int DISC, bool HAS_Z, bool SOFTPLUS, bool SUMMARY>
-__global__ __launch_bounds__(kWave) void fwd_kernel(FwdParams p) {
-  const int lane = threadIdx.x;
+  __device__ __forceinline__ void run(int32_t t0) {
+    load_ring(t0, t0, true);
+    fetch_rows(t0);
+    stage_rows(0);
+    activations(t0);
+    publish(0);
+    if (NSPLIT > 1) __syncthreads();
+    int32_t t = t0;
+    int buf = 0;
+    // full blocks whose next-block prefetch stays inside the range: no guards
+    for (; t + 2 * kPrefetch <= t1; t += kPrefetch, buf ^= 1) block<false>(t, buf);
+    for (; t < t1; t += kPrefetch, buf ^= 1) block<true>(t, buf);
+  }
+};
+
+template <typename In, typename Out, int DISC, bool HAS_Z, bool SOFTPLUS, bool SUMMARY, int NSPLIT>
+__global__ __launch_bounds__(kWave * NSPLIT) void fwd_kernel(FwdParams p) {
+  constexpr int NS = kMaxState / NSPLIT;
+  // wave-uniform by construction; readfirstlane lets the compiler keep it in an SGPR
+  const int wave = __builtin_amdgcn_readfirstlane(int(threadIdx.x) / kWave);
+  const int lane = int(threadIdx.x) % kWave;
+  const int n0 = wave * NS;
   int64_t bid = blockIdx.x;
   const int dblk = int(bid % p.ndblk);
   bid /= p.ndblk;
@@ -183,58 +304,98 @@ __global__ __launch_bounds__(kWave) void fwd_kernel(FwdParams p) {
   const int32_t t1 = int32_t(t0 + p.chunk_len < p.L ? t0 + p.chunk_len : p.L);
   const int N = p.N;
 
-  Chan ch;
+  Chan<NS> ch;
   bool zero = false;
 #pragma unroll
-  for (int n = 0; n < kMaxState; ++n) {
+  for (int j = 0; j < NS; ++j) {
+    const int n = n0 + j;
     const float a = n < N ? p.A[dc * N + n] : -1.0f;
-    ch.A[n] = a;
-    ch.iA[n] = a == 0.0f ? 0.0f : 1.0f / a;
-    ch.zm[n] = a == 0.0f ? 1.0f : 0.0f;
+    ch.A[j] = a;
+    ch.iA[j] = a == 0.0f ? 0.0f : 1.0f / a;
+    ch.zm[j] = a == 0.0f ? 1.0f : 0.0f;
     zero |= (a == 0.0f);
   }
-  const float Dd = p.Dskip ? p.Dskip[dc] : 0.0f;
-  const float bias2 = (p.bias ? p.bias[dc] : 0.0f) * kLog2e;
 
-  float h[kMaxState];
+  float h[NS];
   if (SUMMARY) {
 #pragma unroll
-    for (int n = 0; n < kMaxState; ++n) h[n] = 0.0f;
+    for (int j = 0; j < NS; ++j) h[j] = 0.0f;
   } else if (chunk == 0) {
 #pragma unroll
-    for (int n = 0; n < kMaxState; ++n)
-      h[n] = (p.h0 && n < N) ? p.h0[(b * p.D + dc) * N + n] : 0.0f;
+    for (int j = 0; j < NS; ++j)
+      h[j] = (p.h0 && n0 + j < N) ? p.h0[(b * p.D + dc) * N + n0 + j] : 0.0f;
   } else {
     const float* hs = p.hend + (b * p.nchunks + chunk) * int64_t(N) * p.D + dc;
 #pragma unroll
-    for (int n = 0; n < kMaxState; ++n) h[n] = n < N ? hs[int64_t(n) * p.D] : 0.0f;
+    for (int j = 0; j < NS; ++j) h[j] = n0 + j < N ? hs[int64_t(n0 + j) * p.D] : 0.0f;
   }
 
-  float dsum = 0.0f;
+  __shared__ float4 lds4[(Lds<NSPLIT>::kFloats + 3) / 4];
+  float* lds = reinterpret_cast<float*>(lds4);
+  const int64_t base = b * p.L * p.D + int64_t(dblk) * kWave;
+  auto setup = [&](auto& sc) {
+    sc.stage = lds + wave * Lds<NSPLIT>::kStage;
+    sc.act = lds + NSPLIT * Lds<NSPLIT>::kStage;
+    sc.part = sc.act + Lds<NSPLIT>::kAct;
+    sc.lane = uint32_t(lane);
+    sc.wave = wave;
+    sc.n0 = n0;
+    sc.Dd = p.Dskip ? p.Dskip[dc] : 0.0f;
+    sc.bias2 = (p.bias ? p.bias[dc] : 0.0f) * kLog2e;
+    sc.dsum = 0.0f;
+    sc.row0 = b * p.L;
+    sc.ub = static_cast<const In*>(p.u) + base;
+    sc.db = static_cast<const In*>(p.delta) + base;
+    sc.zb = p.z ? static_cast<const In*>(p.z) + base : nullptr;
+    sc.yb = SUMMARY ? nullptr : static_cast<Out*>(p.y) + base;
+    sc.vin = lane_c * uint32_t(sizeof(In));
+    sc.vout = active ? lane_c * uint32_t(sizeof(Out)) : kOutOfRange;
+    sc.rowb_in = uint32_t(p.D) * uint32_t(sizeof(In));
+    sc.rowb_out = uint32_t(p.D) * uint32_t(sizeof(Out));
+    sc.t1 = t1;
+    sc.tlast = t1 - 1;
+    sc.run(t0);
+    return sc.dsum;
+  };
+  float dsum;
   // exact ZOH needs the dt * B fallback only where some A entry is exactly 0
-  const bool safe = DISC == kZoh && __any(zero);
-  if (N == kMaxState) {
-    if (safe)
-      scan_range<In, Out, DISC, HAS_Z, SOFTPLUS, SUMMARY, true, true>(p, ch, h, b, dblk, lane_c, active, t0, t1, Dd, bias2, dsum);
-    else
-      scan_range<In, Out, DISC, HAS_Z, SOFTPLUS, SUMMARY, false, true>(p, ch, h, b, dblk, lane_c, active, t0, t1, Dd, bias2, dsum);
+  // (decided per wave; every wave still passes the same barriers)
+  if (DISC == kZoh && __any(zero)) {
+    Scan<In, Out, DISC, HAS_Z, SOFTPLUS, SUMMARY, true, NSPLIT> sc{p, ch, h};
+    dsum = setup(sc);
   } else {
-    // N < 16: unused states carry A = -1 and B = C = 0; always the guarded ZOH form
-    scan_range<In, Out, DISC, HAS_Z, SOFTPLUS, SUMMARY, DISC == kZoh, false>(p, ch, h, b, dblk, lane_c, active, t0, t1, Dd, bias2, dsum);
+    Scan<In, Out, DISC, HAS_Z, SOFTPLUS, SUMMARY, false, NSPLIT> sc{p, ch, h};
+    dsum = setup(sc);
   }
 
   if (!active) return;
   if (SUMMARY) {
     float* hs = p.hend + (b * p.nchunks + chunk) * int64_t(N) * p.D + d;
 #pragma unroll
-    for (int n = 0; n < kMaxState; ++n)
-      if (n < N) hs[int64_t(n) * p.D] = h[n];
-    p.dsum[(b * p.nchunks + chunk) * p.D + d] = dsum;
+    for (int j = 0; j < NS; ++j)
+      if (n0 + j < N) hs[int64_t(n0 + j) * p.D] = h[j];
+    if (wave == 0) p.dsum[(b * p.nchunks + chunk) * p.D + d] = dsum;
   } else if (p.h_last && t1 == p.L) {
 #pragma unroll
-    for (int n = 0; n < kMaxState; ++n)
-      if (n < N) p.h_last[(b * p.D + d) * N + n] = h[n];
+    for (int j = 0; j < NS; ++j)
+      if (n0 + j < N) p.h_last[(b * p.D + d) * N + n0 + j] = h[j];
   }
+}
+
+// B and C rows as fp32 with 16 entries per (b, t), zero past N: the layout the
+// scan kernels stage through LDS.
+template <typename In>
+__global__ __launch_bounds__(256) void pack_rows_kernel(const In* __restrict__ Bm,
+                                                        const In* __restrict__ Cm,
+                                                        float* __restrict__ Bf,
+                                                        float* __restrict__ Cf, int64_t rows,
+                                                        int N) {
+  const int64_t gid = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (gid >= rows * kMaxState) return;
+  const int64_t r = gid / kMaxState;
+  const int n = int(gid % kMaxState);
+  Bf[gid] = n < N ? to_f32(Bm[r * N + n]) : 0.0f;
+  Cf[gid] = n < N ? to_f32(Cm[r * N + n]) : 0.0f;
 }
 
 // Carry scan over chunks, one lane per (b, n, d).  In place on hend: slot c of
@@ -279,72 +440,123 @@ __global__ __launch_bounds__(256) void carry_scan_kernel(float* __restrict__ hen
   hs[(nchunks - 1) * sstride] = carry;
 }
 
-template <typename In, typename Out, int DISC, bool HAS_Z, bool SOFTPLUS, bool SUMMARY>
+template <typename In, typename Out, int DISC, bool HAS_Z, bool SOFTPLUS, bool SUMMARY, int NSPLIT>
 hipError_t launch_one(const FwdParams& p, int64_t nblocks, hipStream_t st) {
-  hipLaunchKernelGGL((fwd_kernel<In, Out, DISC, HAS_Z, SOFTPLUS, SUMMARY>), dim3(unsigned(nblocks)),
-                     dim3(kWave), 0, st, p);
+  hipLaunchKernelGGL((fwd_kernel<In, Out, DISC, HAS_Z, SOFTPLUS, SUMMARY, NSPLIT>),
+                     dim3(unsigned(nblocks)), dim3(kWave * NSPLIT), 0, st, p);
   return hipGetLastError();
 }
 
+template <typename In, typename Out, int DISC, bool HAS_Z, bool SOFTPLUS, bool SUMMARY>
+hipError_t dispatch_split(const FwdParams& p, int nsplit, int64_t nblocks, hipStream_t st) {
+  switch (nsplit) {
+    case 4: return launch_one<In, Out, DISC, HAS_Z, SOFTPLUS, SUMMARY, 4>(p, nblocks, st);
+    case 2: return launch_one<In, Out, DISC, HAS_Z, SOFTPLUS, SUMMARY, 2>(p, nblocks, st);
+    default: return launch_one<In, Out, DISC, HAS_Z, SOFTPLUS, SUMMARY, 1>(p, nblocks, st);
+  }
+}
+
 template <typename In, typename Out, int DISC>
-hipError_t dispatch_flags(const FwdParams& p, bool has_z, bool softplus, bool summary,
+hipError_t dispatch_flags(const FwdParams& p, int nsplit, bool has_z, bool softplus, bool summary,
                           int64_t nblocks, hipStream_t st) {
   if (summary) {
-    return softplus ? launch_one<In, Out, DISC, false, true, true>(p, nblocks, st)
-                    : launch_one<In, Out, DISC, false, false, true>(p, nblocks, st);
+    return softplus ? dispatch_split<In, Out, DISC, false, true, true>(p, nsplit, nblocks, st)
+                    : dispatch_split<In, Out, DISC, false, false, true>(p, nsplit, nblocks, st);
   }
   if (has_z)
-    return softplus ? launch_one<In, Out, DISC, true, true, false>(p, nblocks, st)
-                    : launch_one<In, Out, DISC, true, false, false>(p, nblocks, st);
-  return softplus ? launch_one<In, Out, DISC, false, true, false>(p, nblocks, st)
-                  : launch_one<In, Out, DISC, false, false, false>(p, nblocks, st);
+    return softplus ? dispatch_split<In, Out, DISC, true, true, false>(p, nsplit, nblocks, st)
+                    : dispatch_split<In, Out, DISC, true, false, false>(p, nsplit, nblocks, st);
+  return softplus ? dispatch_split<In, Out, DISC, false, true, false>(p, nsplit, nblocks, st)
+                  : dispatch_split<In, Out, DISC, false, false, false>(p, nsplit, nblocks, st);
 }
 
 template <typename In, typename Out>
-hipError_t dispatch_disc(const FwdParams& p, int disc, bool has_z, bool softplus, bool summary,
-                         int64_t nblocks, hipStream_t st) {
-  return disc == kZoh ? dispatch_flags<In, Out, kZoh>(p, has_z, softplus, summary, nblocks, st)
-                      : dispatch_flags<In, Out, kEuler>(p, has_z, softplus, summary, nblocks, st);
+hipError_t dispatch_disc(const FwdParams& p, int disc, int nsplit, bool has_z, bool softplus,
+                         bool summary, int64_t nblocks, hipStream_t st) {
+  return disc == kZoh
+             ? dispatch_flags<In, Out, kZoh>(p, nsplit, has_z, softplus, summary, nblocks, st)
+             : dispatch_flags<In, Out, kEuler>(p, nsplit, has_z, softplus, summary, nblocks, st);
 }
 
-hipError_t dispatch(const ss_desc_t& d, const FwdParams& p, bool summary, int64_t nblocks,
-                    hipStream_t st) {
+hipError_t dispatch(const ss_desc_t& d, const FwdParams& p, int nsplit, bool summary,
+                    int64_t nblocks, hipStream_t st) {
   const bool has_z = p.z != nullptr, sp = d.delta_softplus != 0;
   if (d.in_dtype == SS_BF16) {
     if (summary || d.out_dtype == SS_F32)
-      return dispatch_disc<uint16_t, float>(p, d.disc, has_z, sp, summary, nblocks, st);
-    return dispatch_disc<uint16_t, uint16_t>(p, d.disc, has_z, sp, summary, nblocks, st);
+      return dispatch_disc<uint16_t, float>(p, d.disc, nsplit, has_z, sp, summary, nblocks, st);
+    return dispatch_disc<uint16_t, uint16_t>(p, d.disc, nsplit, has_z, sp, false, nblocks, st);
   }
   if (summary || d.out_dtype == SS_F32)
-    return dispatch_disc<float, float>(p, d.disc, has_z, sp, summary, nblocks, st);
-  return dispatch_disc<float, uint16_t>(p, d.disc, has_z, sp, summary, nblocks, st);
+    return dispatch_disc<float, float>(p, d.disc, nsplit, has_z, sp, summary, nblocks, st);
+  return dispatch_disc<float, uint16_t>(p, d.disc, nsplit, has_z, sp, false, nblocks, st);
 }
 
 }  // namespace
 
-int launch_fwd(const ss_desc_t& d, const FwdPlan& plan, const FwdArgs& a, void* stream) {
-  hipStream_t st = static_cast<hipStream_t>(stream);
+namespace {
+
+FwdParams make_params(const ss_desc_t& d, const TimePlan& tp, const FwdArgs& a) {
   FwdParams p{};
-  p.u = a.u; p.delta = a.delta; p.A = a.A; p.Bm = a.Bm; p.Cm = a.Cm;
+  p.u = a.u; p.delta = a.delta; p.A = a.A;
   p.Dskip = a.Dskip; p.bias = a.bias; p.z = a.z; p.h0 = a.h0;
   p.y = a.y; p.h_last = a.h_last; p.hend = a.hend; p.dsum = a.dsum;
+  p.Brow = a.Brow; p.Crow = a.Crow;
   p.L = d.seqlen; p.D = d.dim; p.N = int32_t(d.dstate);
-  p.chunk_len = plan.tp.chunk_len;
-  p.nchunks = int32_t(plan.tp.nchunks);
+  p.chunk_len = tp.chunk_len;
+  p.nchunks = int32_t(tp.nchunks);
   p.ndblk = int32_t((d.dim + kWave - 1) / kWave);
+  return p;
+}
+
+}  // namespace
+
+int launch_pack_rows(const ss_desc_t& d, const void* Bm, const void* Cm, float* Brow, float* Crow,
+                     void* stream) {
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int64_t rows = d.batch * d.seqlen;
+  const unsigned nb = unsigned((rows * kMaxState + 255) / 256);
+  if (d.in_dtype == SS_BF16)
+    hipLaunchKernelGGL(pack_rows_kernel<uint16_t>, dim3(nb), dim3(256), 0, st,
+                       static_cast<const uint16_t*>(Bm), static_cast<const uint16_t*>(Cm), Brow,
+                       Crow, rows, int(d.dstate));
+  else
+    hipLaunchKernelGGL(pack_rows_kernel<float>, dim3(nb), dim3(256), 0, st,
+                       static_cast<const float*>(Bm), static_cast<const float*>(Cm), Brow, Crow,
+                       rows, int(d.dstate));
+  return int(hipGetLastError());
+}
+
+int launch_fwd_carries(const ss_desc_t& d, const TimePlan& tp, const FwdArgs& a, void* stream) {
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  FwdParams p = make_params(d, tp, a);
   const int64_t cols = d.batch * p.ndblk;
-  if (p.nchunks > 1) {
-    p.grid_chunks = p.nchunks - 1;   // the last chunk's summary is never needed
-    hipError_t e = dispatch(d, p, true, cols * p.grid_chunks, st);
-    if (e != hipSuccess) return int(e);
-    const int64_t total = d.batch * d.dstate * d.dim;
-    hipLaunchKernelGGL(carry_scan_kernel, dim3(unsigned((total + 255) / 256)), dim3(256), 0, st,
-                       a.hend, a.dsum, a.A, a.h0, d.batch, d.dim, int(d.dstate), p.nchunks);
-    e = hipGetLastError();
-    if (e != hipSuccess) return int(e);
+  p.grid_chunks = p.nchunks - 1;   // the last chunk's summary is never needed
+  hipError_t e = dispatch(d, p, tp.nsplit, true, cols * p.grid_chunks, st);
+  if (e != hipSuccess) return int(e);
+  const int64_t total = d.batch * d.dstate * d.dim;
+  hipLaunchKernelGGL(carry_scan_kernel, dim3(unsigned((total + 255) / 256)), dim3(256), 0, st,
+                     a.hend, a.dsum, a.A, a.h0, d.batch, d.dim, int(d.dstate), p.nchunks);
+  return int(hipGetLastError());
+}
+
+int launch_fwd(const ss_desc_t& d, const FwdPlan& plan, const FwdArgs& args, void* stream) {
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  FwdArgs a = args;
+  if (plan.packed_rows) {
+    const int e = launch_pack_rows(d, a.Bm, a.Cm, a.Brow, a.Crow, stream);
+    if (e != 0) return e;
+  } else {
+    a.Brow = const_cast<float*>(static_cast<const float*>(a.Bm));
+    a.Crow = const_cast<float*>(static_cast<const float*>(a.Cm));
   }
+  if (plan.tp.nchunks > 1) {
+    const int e = launch_fwd_carries(d, plan.tp, a, stream);
+    if (e != 0) return e;
+  }
+  FwdParams p = make_params(d, plan.tp, a);
   p.grid_chunks = p.nchunks;
-  return int(dispatch(d, p, false, cols * p.grid_chunks, st));
+  const int64_t cols = d.batch * p.ndblk;
+  return int(dispatch(d, p, plan.tp.nsplit, false, cols * p.grid_chunks, st));
 }
 
 }  // namespace ss

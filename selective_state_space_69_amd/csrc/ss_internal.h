@@ -13,35 +13,43 @@ namespace ss {
 constexpr int kWave = 64;      // lanes per wavefront on CDNA
 constexpr int kMaxState = 16;  // states held per lane
 
-// How a forward (or the forward recompute inside the backward) is split in time.
-// nchunks == 1: one sequential pass per (b, 64-channel block).
+// How a forward (or the forward recompute inside the backward) is split.
+// nsplit : waves per (b, 64-channel block), each holding 16 / nsplit states.
+// nchunks == 1: one sequential pass over time per workgroup.
 // nchunks  > 1: (1) chunk summaries, (2) carry scan over chunks, (3) output pass.
 struct TimePlan {
   int64_t chunk_len = 0;
   int64_t nchunks = 1;
+  int nsplit = 1;
 };
 
 // Workspace layout of the forward: fp32 arrays, each 256-byte aligned.
+//   brow, crow : (B, L, 16)    B and C rows as fp32, zero past N (only when the
+//                              inputs are bf16 or N < 16; else the inputs are read)
 //   hend : (B, nchunks, N, D)  chunk-local end state, then (after the carry scan)
 //                              the start state of the chunk
 //   dsum : (B, nchunks, D)     sum over the chunk of the step, in log2 units
 struct FwdPlan {
   TimePlan tp;
-  size_t off_hend = 0, off_dsum = 0, bytes = 0;
+  bool packed_rows = false;
+  size_t off_brow = 0, off_crow = 0, off_hend = 0, off_dsum = 0, bytes = 0;
 };
 
-// Backward workspace:
-//   the forward's carry arrays (chunk start states), plus per 64-channel block
-//   partial sums that are reduced in a fixed order by a second kernel:
-//   pB, pC : (B, L, nblk, N)     partial dB, dC over the block's channels
-//   pA     : (B, nchunks, N, D)  partial dA over the chunk's time steps
-//   pD, pbias : (B, nchunks, D)  partial dD_skip, ddelta_bias
-//   lam    : (B, nchunks, N, D)  adjoint carries for the chunked backward
+// Backward workspace (fp32 arrays, 256-byte aligned):
+//   brow, crow : (B, L, 16)   fp32 B and C rows (bf16 inputs or N < 16)
+//   hend, dsum : (B, nchunks, N, D), (B, nchunks, D)  forward chunk carries
+//   lam        : (B, nchunks, N, D)  adjoint carry entering each chunk from its end
+//   pB, pC     : (B, L, nblk, N)     dB, dC summed over one 64-channel block
+//   pA         : (B, nchunks, N, D)  dA summed over one chunk
+//   pD, pbias  : (B, nchunks, D)     dD_skip, ddelta_bias summed over one chunk
+// The partial sums are added in a fixed order by reduction kernels, so the
+// backward is deterministic.
 struct BwdPlan {
   TimePlan tp;
   int64_t nblk = 0;
-  size_t off_hend = 0, off_dsum = 0, off_pB = 0, off_pC = 0, off_pA = 0, off_pD = 0,
-         off_pbias = 0, off_lam = 0, off_lsum = 0, bytes = 0;
+  bool packed_rows = false;
+  size_t off_brow = 0, off_crow = 0, off_hend = 0, off_dsum = 0, off_lam = 0, off_pB = 0,
+         off_pC = 0, off_pA = 0, off_pD = 0, off_pbias = 0, bytes = 0;
 };
 
 TimePlan plan_time(const ss_desc_t& d);
@@ -60,6 +68,8 @@ struct FwdArgs {
   const float* h0;
   void* y;
   float* h_last;
+  float* Brow;
+  float* Crow;
   float* hend;
   float* dsum;
 };
@@ -102,6 +112,12 @@ struct StepArgs {
 
 // Launchers: return 0 or a HIP error code (converted to SS_ERR_HIP by the caller).
 int launch_fwd(const ss_desc_t& d, const FwdPlan& p, const FwdArgs& a, void* stream);
+// B and C rows as (B, L, 16) fp32, zero past N.
+int launch_pack_rows(const ss_desc_t& d, const void* Bm, const void* Cm, float* Brow, float* Crow,
+                     void* stream);
+// Chunk start states of a chunked forward (summary pass + carry scan) into
+// a.hend / a.dsum; a.Brow / a.Crow must hold the fp32 rows.
+int launch_fwd_carries(const ss_desc_t& d, const TimePlan& tp, const FwdArgs& a, void* stream);
 int launch_bwd(const ss_desc_t& d, const BwdPlan& p, const BwdArgs& a, void* stream);
 int launch_step(const ss_desc_t& d, const StepArgs& a, void* stream);
 

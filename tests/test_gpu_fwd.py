@@ -67,6 +67,31 @@ def test_fwd_fp32_parity(oracle, case):
     log("  worst err/bound", w)
 
 
+SPLIT_CASES = [
+    (2, 150, 150, 16, "zoh", "mixed"), (2, 150, 150, 16, "euler", "random"),
+    (1, 300, 64, 5, "zoh", "random"), (3, 61, 130, 16, "zoh", "s4d_real"),
+]
+
+
+@pytest.mark.parametrize("nsplit", ["1", "2", "4"])
+@pytest.mark.parametrize("chunk", ["0", "48"])
+@pytest.mark.parametrize("case", SPLIT_CASES, ids=lambda c: "b%d_l%d_d%d_n%d_%s_%s" % c)
+def test_fwd_split_variants(oracle, monkeypatch, nsplit, chunk, case):
+    """Every state split (1, 2, 4 waves per channel block), with and without time
+    chunks, against the oracle."""
+    Bt, L, D, N, disc, amode = case
+    monkeypatch.setenv("SS_SCAN_NSPLIT", nsplit)
+    monkeypatch.setenv("SS_SCAN_CHUNK", chunk)
+    inp = synth.make_inputs(Bt, L, D, N, seed=2000 + SPLIT_CASES.index(case), dtype="f32",
+                            with_h0=True, a_mode=amode)
+    d = upload(inp)
+    y, hl = gpu_fwd(d, disc, return_last_state=True)
+    torch.cuda.synchronize()
+    ref, href = _full_oracle(oracle, inp, disc)
+    check_f32(y.cpu().numpy(), ref, "y")
+    check_f32(hl.cpu().numpy(), href, "h_last")
+
+
 def test_fwd_tiny_workload(oracle):
     """The tiny fp32 workload (B=1, L=256, D=64, N=16, exact ZOH, gate)."""
     inp = synth.make_workload("fwd_tiny_f32_b1_l256_d64")
