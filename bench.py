@@ -93,34 +93,51 @@ def time_calls(fn, steps, warmup, torch):
     return total_ms, sum(per) / len(per), min(per), wall
 
 
-def cpu_baseline(inp, w, budget_s=12.0):
-    """The fp64 oracle on a bounded sample of channels of the same workload."""
-    import numpy as np
+def cpu_baseline(inp, w, budget_s=20.0):
+    """The fp64 oracle on the same workload: whole batch rows, as many as fit in
+    about budget_s seconds (all of them when the estimate allows)."""
     from oracle import oracle
     try:
         threads = len(os.sched_getaffinity(0))
     except AttributeError:
         threads = os.cpu_count() or 1
     threads = max(1, min(16, threads))
-    b = 0
 
-    def run(nch):
-        sl = (slice(b, b + 1), slice(None), slice(0, nch))
+    def run(rows):
+        sl = slice(0, rows)
         t0 = time.perf_counter()
-        oracle.fwd(inp.u[sl], inp.delta[sl], inp.A[:nch], inp.B[b:b + 1], inp.C[b:b + 1],
-                   D=inp.D[:nch], delta_bias=inp.delta_bias[:nch], z=inp.z[sl],
+        oracle.fwd(inp.u[sl], inp.delta[sl], inp.A, inp.B[sl], inp.C[sl], D=inp.D,
+                   delta_bias=inp.delta_bias, z=None if inp.z is None else inp.z[sl],
                    disc=w.disc, nthreads=threads)
         return time.perf_counter() - t0
 
-    nch = min(w.D, 4 * threads)
-    dt = run(nch)
-    if dt < budget_s / 4 and nch < w.D:
-        nch = int(min(w.D, max(nch, nch * budget_s / max(dt, 1e-3))))
-        dt = run(nch)
-    elems = w.L * nch * w.N
+    if w.L * w.D > 64 * 1024 * 1024:          # one row alone is large: sample channels
+        nch = max(1, min(w.D, int(w.D * budget_s / 60.0)))
+        sl = (slice(0, 1), slice(None), slice(0, nch))
+        t0 = time.perf_counter()
+        oracle.fwd(inp.u[sl], inp.delta[sl], inp.A[:nch], inp.B[:1], inp.C[:1], D=inp.D[:nch],
+                   delta_bias=inp.delta_bias[:nch], z=inp.z[sl], disc=w.disc, nthreads=threads)
+        dt = time.perf_counter() - t0
+        elems, what = w.L * nch * w.N, "batch row 0, channels 0..%d of %d" % (nch - 1, w.D)
+    else:
+        dt1 = run(1)
+        rows = int(max(1, min(w.B, budget_s / max(dt1, 1e-3))))
+        dt = run(rows) if rows > 1 else dt1
+        elems, what = rows * w.L * w.D * w.N, "batch rows 0..%d of %d (all channels)" % (rows - 1, w.B)
     return {"value": elems / dt, "unit": "elements/s", "cores": threads, "kind": "oracle",
-            "sample": "batch row 0, channels 0..%d (%d of %d), full L=%d, N=%d; %.1f s fp64 C, "
-                      "OpenMP over channels" % (nch - 1, nch, w.D, w.L, w.N, dt)}
+            "sample": "%s, full L=%d, N=%d, %s: %.2f s of fp64 C (OpenMP over channels)" % (
+                what, w.L, w.N, w.disc, dt)}
+
+
+def copy_calibration(torch, nbytes=1 << 30, reps=3):
+    """A plain device copy of known size, to calibrate the FETCH_SIZE / WRITE_SIZE
+    counters (run under rocprofv3 --pmc)."""
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": nbytes, "copy_bytes_written": nbytes, "reps": reps}))
 
 
 def main():
@@ -131,6 +148,8 @@ def main():
     ap.add_argument("--workload", default="fwd_2p8b_bf16_b8_l2048_d5120")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: the selective scan needs no communication "
@@ -139,6 +158,9 @@ def main():
         sys.exit(2)
 
     import torch
+    if args.copy_calibration:
+        copy_calibration(torch)
+        return
     from selective_state_space_69_amd import binding as Bnd
     from selective_state_space_69_amd import synth
 

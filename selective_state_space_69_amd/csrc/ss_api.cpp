@@ -92,10 +92,11 @@ FwdPlan plan_fwd(const ss_desc_t& d) {
   const size_t B = size_t(d.batch), L = size_t(d.seqlen), C = size_t(p.tp.nchunks),
                D = size_t(d.dim), N = size_t(d.dstate);
   size_t off = 0;
-  p.packed_rows = d.in_dtype != SS_F32 || d.dstate != kMaxState;
+  p.packed_rows = d.dstate != kMaxState;
+  const size_t es = d.in_dtype == SS_BF16 ? 2 : 4;
   if (p.packed_rows) {
-    p.off_brow = off; off += align_up(B * L * kMaxState * sizeof(float));
-    p.off_crow = off; off += align_up(B * L * kMaxState * sizeof(float));
+    p.off_brow = off; off += align_up(B * L * kMaxState * es);
+    p.off_crow = off; off += align_up(B * L * kMaxState * es);
   }
   if (p.tp.nchunks > 1) {
     p.off_hend = off; off += align_up(B * C * N * D * sizeof(float));
@@ -116,11 +117,12 @@ BwdPlan plan_bwd(const ss_desc_t& d) {
                D = size_t(d.dim), N = size_t(d.dstate);
   p.nblk = (d.dim + kWave - 1) / kWave;
   const size_t nb = size_t(p.nblk);
-  p.packed_rows = d.in_dtype != SS_F32 || d.dstate != kMaxState;
+  p.packed_rows = d.dstate != kMaxState;
+  const size_t es = d.in_dtype == SS_BF16 ? 2 : 4;
   size_t off = 0;
   if (p.packed_rows) {
-    p.off_brow = off; off += align_up(B * L * kMaxState * sizeof(float));
-    p.off_crow = off; off += align_up(B * L * kMaxState * sizeof(float));
+    p.off_brow = off; off += align_up(B * L * kMaxState * es);
+    p.off_crow = off; off += align_up(B * L * kMaxState * es);
   }
   p.off_hend = off; off += align_up(B * C * N * D * sizeof(float));
   p.off_dsum = off; off += align_up(B * C * D * sizeof(float));
@@ -179,8 +181,8 @@ int ss_scan_fwd(const ss_desc_t* desc, const void* u, const void* delta, const f
             nullptr, nullptr, nullptr, nullptr};
   char* ws = static_cast<char*>(workspace);
   if (plan.packed_rows) {
-    a.Brow = reinterpret_cast<float*>(ws + plan.off_brow);
-    a.Crow = reinterpret_cast<float*>(ws + plan.off_crow);
+    a.Brow = ws + plan.off_brow;
+    a.Crow = ws + plan.off_crow;
   }
   if (plan.tp.nchunks > 1) {
     a.hend = reinterpret_cast<float*>(ws + plan.off_hend);

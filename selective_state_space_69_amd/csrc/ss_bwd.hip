@@ -36,8 +36,8 @@ struct BwdParams {
   const void* z;
   const void* dy;
   const float* A;
-  const float* Brow;     // (B, L, 16) fp32
-  const float* Crow;
+  const void* Brow;      // (B, L, 16) rows in the input type
+  const void* Crow;
   const float* Dskip;
   const float* bias;
   const float* h0;
@@ -57,13 +57,20 @@ struct BwdParams {
   int32_t N, ndblk, nchunks;
 };
 
-using ConstF32 = __attribute__((address_space(4))) const float;
+using ConstU32 = __attribute__((address_space(4))) const uint32_t;
 
 // This wave's 4 values of a B or C row: a scalar load (same address in every lane).
-__device__ __forceinline__ void row4(const float* rows, int64_t row, int n0, float (&v)[kNS]) {
-  ConstF32* q = (ConstF32*)(rows + row * kMaxState + n0);
+template <typename In>
+__device__ __forceinline__ void row4(const void* rows, int64_t row, int n0, float (&v)[kNS]) {
+  ConstU32* q = (ConstU32*)(static_cast<const In*>(rows) + row * kMaxState + n0);
+  if constexpr (sizeof(In) == 2) {
+    const uint32_t w0 = q[0], w1 = q[1];
+    v[0] = __uint_as_float(w0 << 16); v[1] = __uint_as_float(w0 & 0xffff0000u);
+    v[2] = __uint_as_float(w1 << 16); v[3] = __uint_as_float(w1 & 0xffff0000u);
+  } else {
 #pragma unroll
-  for (int j = 0; j < kNS; ++j) v[j] = q[j];
+    for (int j = 0; j < kNS; ++j) v[j] = __uint_as_float(q[j]);
+  }
 }
 
 template <typename In>
@@ -200,7 +207,7 @@ __device__ __forceinline__ void bwd_chunk(const BwdParams& p, float* lds, int64_
       const float dl = actDl[kk * kWave + lane];
       const float uf = ld<In>(p.u, ibase + int64_t(tr) * D);
       float Bv[kNS];
-      row4(p.Brow, row0 + tr, n0, Bv);
+      row4<In>(p.Brow, row0 + tr, n0, Bv);
 #pragma unroll
       for (int j = 0; j < kNS; ++j) {
         const float a = hw_exp2(dl * A[j]);
@@ -248,8 +255,8 @@ __device__ __forceinline__ void bwd_chunk(const BwdParams& p, float* lds, int64_
       dl[k] = actDl[kk * kWave + lane];
       gy[k] = actGy[kk * kWave + lane];
       uf[k] = ld<In>(p.u, ibase + int64_t(tr) * D) * amask;
-      row4(p.Brow, row0 + tr, n0, Bs[k]);
-      row4(p.Crow, row0 + tr, n0, Cs[k]);
+      row4<In>(p.Brow, row0 + tr, n0, Bs[k]);
+      row4<In>(p.Crow, row0 + tr, n0, Cs[k]);
       float y0 = 0.0f;
 #pragma unroll
       for (int j = 0; j < kNS; ++j) {
@@ -447,7 +454,14 @@ __global__ __launch_bounds__(kWave) void rev_summary_kernel(BwdParams p) {
     const float dl = step_log2<SOFTPLUS>(__builtin_fmaf(ld<In>(p.delta, i), kLog2e, bias2));
     float gy = ld<In>(p.dy, i);
     if (HAS_Z) gy *= silu(ld<In>(p.z, i));
-    ConstF32* c = (ConstF32*)(p.Crow + (row0 + t) * kMaxState);
+    float c[kMaxState];
+#pragma unroll
+    for (int q = 0; q < kNW; ++q) {
+      float v[kNS];
+      row4<In>(p.Crow, row0 + t, q * kNS, v);
+#pragma unroll
+      for (int j = 0; j < kNS; ++j) c[q * kNS + j] = v[j];
+    }
 #pragma unroll
     for (int n = 0; n < kMaxState; ++n)
       nu[n] = hw_exp2(dl * A[n]) * __builtin_fmaf(gy, c[n], nu[n]);
@@ -569,10 +583,8 @@ int launch_bwd(const ss_desc_t& d, const BwdPlan& plan, const BwdArgs& a, void* 
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (plan.tp.chunk_len != kChunk && plan.tp.nchunks > 1) return int(hipErrorInvalidValue);
   char* ws = a.ws;
-  float* Brow = plan.packed_rows ? reinterpret_cast<float*>(ws + plan.off_brow)
-                                 : const_cast<float*>(static_cast<const float*>(a.Bm));
-  float* Crow = plan.packed_rows ? reinterpret_cast<float*>(ws + plan.off_crow)
-                                 : const_cast<float*>(static_cast<const float*>(a.Cm));
+  void* Brow = plan.packed_rows ? static_cast<void*>(ws + plan.off_brow) : const_cast<void*>(a.Bm);
+  void* Crow = plan.packed_rows ? static_cast<void*>(ws + plan.off_crow) : const_cast<void*>(a.Cm);
   float* hend = reinterpret_cast<float*>(ws + plan.off_hend);
   float* dsum = reinterpret_cast<float*>(ws + plan.off_dsum);
   float* lam = reinterpret_cast<float*>(ws + plan.off_lam);

@@ -48,6 +48,17 @@ template <> __device__ __forceinline__ float to_f32<uint16_t>(uint16_t x) {
   return __uint_as_float(uint32_t(x) << 16);
 }
 
+// Four consecutive elements (8 bytes of bf16 or 16 bytes of fp32) as fp32.
+template <typename T> __device__ __forceinline__ float4 load4(const T* p);
+template <> __device__ __forceinline__ float4 load4<float>(const float* p) {
+  return *reinterpret_cast<const float4*>(p);
+}
+template <> __device__ __forceinline__ float4 load4<uint16_t>(const uint16_t* p) {
+  const uint2 w = *reinterpret_cast<const uint2*>(p);
+  return make_float4(__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xffff0000u),
+                     __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xffff0000u));
+}
+
 // fp32 -> bf16 with round-to-nearest-even; NaN stays NaN.
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   uint32_t x = __float_as_uint(f);

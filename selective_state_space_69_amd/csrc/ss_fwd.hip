@@ -37,8 +37,8 @@ struct FwdParams {
   const void* u;
   const void* delta;
   const float* A;
-  const float* Brow;   // (B, L, 16) fp32 rows of B (padded with zeros past N)
-  const float* Crow;   // (B, L, 16) fp32 rows of C
+  const void* Brow;    // (B, L, 16) rows of B in the input type (zero past N)
+  const void* Crow;    // (B, L, 16) rows of C
   const float* Dskip;
   const float* bias;
   const void* z;
@@ -150,9 +150,9 @@ struct Scan {
     const int k = int(l / G), g = int(l % G);
     int32_t tr = t + k;
     tr = tr < tlast ? tr : tlast;
-    const float* src = (g < G / 2 ? p.Brow : p.Crow) + (row0 + tr) * kMaxState + n0 +
-                       4 * (g % (G / 2));
-    rowq = *reinterpret_cast<const float4*>(src);
+    const In* src = static_cast<const In*>(g < G / 2 ? p.Brow : p.Crow) +
+                    (row0 + tr) * kMaxState + n0 + 4 * (g % (G / 2));
+    rowq = load4<In>(src);
   }
   __device__ __forceinline__ void stage_rows(int buf) {
     constexpr int G = NS / 2;
@@ -382,20 +382,19 @@ __global__ __launch_bounds__(kWave * NSPLIT) void fwd_kernel(FwdParams p) {
   }
 }
 
-// B and C rows as fp32 with 16 entries per (b, t), zero past N: the layout the
-// scan kernels stage through LDS.
+// B and C rows padded to 16 entries per (b, t) (zero past N), in the input type:
+// the layout the scan kernels read.  Only needed when N < 16.
 template <typename In>
 __global__ __launch_bounds__(256) void pack_rows_kernel(const In* __restrict__ Bm,
                                                         const In* __restrict__ Cm,
-                                                        float* __restrict__ Bf,
-                                                        float* __restrict__ Cf, int64_t rows,
-                                                        int N) {
+                                                        In* __restrict__ Bp, In* __restrict__ Cp,
+                                                        int64_t rows, int N) {
   const int64_t gid = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
   if (gid >= rows * kMaxState) return;
   const int64_t r = gid / kMaxState;
   const int n = int(gid % kMaxState);
-  Bf[gid] = n < N ? to_f32(Bm[r * N + n]) : 0.0f;
-  Cf[gid] = n < N ? to_f32(Cm[r * N + n]) : 0.0f;
+  Bp[gid] = n < N ? Bm[r * N + n] : In(0);
+  Cp[gid] = n < N ? Cm[r * N + n] : In(0);
 }
 
 // Carry scan over chunks, one lane per (b, n, d).  In place on hend: slot c of
@@ -510,19 +509,20 @@ FwdParams make_params(const ss_desc_t& d, const TimePlan& tp, const FwdArgs& a) 
 
 }  // namespace
 
-int launch_pack_rows(const ss_desc_t& d, const void* Bm, const void* Cm, float* Brow, float* Crow,
+int launch_pack_rows(const ss_desc_t& d, const void* Bm, const void* Cm, void* Brow, void* Crow,
                      void* stream) {
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int64_t rows = d.batch * d.seqlen;
   const unsigned nb = unsigned((rows * kMaxState + 255) / 256);
   if (d.in_dtype == SS_BF16)
     hipLaunchKernelGGL(pack_rows_kernel<uint16_t>, dim3(nb), dim3(256), 0, st,
-                       static_cast<const uint16_t*>(Bm), static_cast<const uint16_t*>(Cm), Brow,
-                       Crow, rows, int(d.dstate));
+                       static_cast<const uint16_t*>(Bm), static_cast<const uint16_t*>(Cm),
+                       static_cast<uint16_t*>(Brow), static_cast<uint16_t*>(Crow), rows,
+                       int(d.dstate));
   else
     hipLaunchKernelGGL(pack_rows_kernel<float>, dim3(nb), dim3(256), 0, st,
-                       static_cast<const float*>(Bm), static_cast<const float*>(Cm), Brow, Crow,
-                       rows, int(d.dstate));
+                       static_cast<const float*>(Bm), static_cast<const float*>(Cm),
+                       static_cast<float*>(Brow), static_cast<float*>(Crow), rows, int(d.dstate));
   return int(hipGetLastError());
 }
 
@@ -546,8 +546,8 @@ int launch_fwd(const ss_desc_t& d, const FwdPlan& plan, const FwdArgs& args, voi
     const int e = launch_pack_rows(d, a.Bm, a.Cm, a.Brow, a.Crow, stream);
     if (e != 0) return e;
   } else {
-    a.Brow = const_cast<float*>(static_cast<const float*>(a.Bm));
-    a.Crow = const_cast<float*>(static_cast<const float*>(a.Cm));
+    a.Brow = const_cast<void*>(a.Bm);
+    a.Crow = const_cast<void*>(a.Cm);
   }
   if (plan.tp.nchunks > 1) {
     const int e = launch_fwd_carries(d, plan.tp, a, stream);

@@ -24,8 +24,8 @@ struct TimePlan {
 };
 
 // Workspace layout of the forward: fp32 arrays, each 256-byte aligned.
-//   brow, crow : (B, L, 16)    B and C rows as fp32, zero past N (only when the
-//                              inputs are bf16 or N < 16; else the inputs are read)
+//   brow, crow : (B, L, 16)    B and C rows padded with zeros to 16 states, in
+//                              the input type (only when N < 16; else the inputs are read)
 //   hend : (B, nchunks, N, D)  chunk-local end state, then (after the carry scan)
 //                              the start state of the chunk
 //   dsum : (B, nchunks, D)     sum over the chunk of the step, in log2 units
@@ -36,7 +36,7 @@ struct FwdPlan {
 };
 
 // Backward workspace (fp32 arrays, 256-byte aligned):
-//   brow, crow : (B, L, 16)   fp32 B and C rows (bf16 inputs or N < 16)
+//   brow, crow : (B, L, 16)   B and C rows padded to 16 states (only when N < 16)
 //   hend, dsum : (B, nchunks, N, D), (B, nchunks, D)  forward chunk carries
 //   lam        : (B, nchunks, N, D)  adjoint carry entering each chunk from its end
 //   pB, pC     : (B, L, nblk, N)     dB, dC summed over one 64-channel block
@@ -68,8 +68,8 @@ struct FwdArgs {
   const float* h0;
   void* y;
   float* h_last;
-  float* Brow;
-  float* Crow;
+  void* Brow;    // B, C rows padded to 16 per (b, t), input type
+  void* Crow;
   float* hend;
   float* dsum;
 };
@@ -112,11 +112,11 @@ struct StepArgs {
 
 // Launchers: return 0 or a HIP error code (converted to SS_ERR_HIP by the caller).
 int launch_fwd(const ss_desc_t& d, const FwdPlan& p, const FwdArgs& a, void* stream);
-// B and C rows as (B, L, 16) fp32, zero past N.
-int launch_pack_rows(const ss_desc_t& d, const void* Bm, const void* Cm, float* Brow, float* Crow,
+// B and C rows as (B, L, 16) in the input type, zero past N.
+int launch_pack_rows(const ss_desc_t& d, const void* Bm, const void* Cm, void* Brow, void* Crow,
                      void* stream);
 // Chunk start states of a chunked forward (summary pass + carry scan) into
-// a.hend / a.dsum; a.Brow / a.Crow must hold the fp32 rows.
+// a.hend / a.dsum; a.Brow / a.Crow must hold the 16-wide rows.
 int launch_fwd_carries(const ss_desc_t& d, const TimePlan& tp, const FwdArgs& a, void* stream);
 int launch_bwd(const ss_desc_t& d, const BwdPlan& p, const BwdArgs& a, void* stream);
 int launch_step(const ss_desc_t& d, const StepArgs& a, void* stream);

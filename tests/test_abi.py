@@ -94,12 +94,12 @@ def test_fwd_workspace_checks(lib):
 
 
 def test_plan_sizes(lib):
-    # wide problems run as one pass per (b, 64-channel block): the workspace only
-    # holds the fp32 B and C rows (B, L, 16) made from bf16 inputs
-    rows = 2 * 8 * 2048 * 16 * 4
-    assert B.ss_scan_workspace_bytes(desc(batch=8, seqlen=2048, dim=5120), B.SS_OP_FWD) == rows
-    assert B.ss_scan_workspace_bytes(desc(batch=8, seqlen=2048, dim=5120, in_dtype=B.SS_F32),
-                                     B.SS_OP_FWD) == 0
+    # wide problems run as one pass over time: no workspace
+    assert B.ss_scan_workspace_bytes(desc(batch=8, seqlen=2048, dim=5120), B.SS_OP_FWD) == 0
+    # N < 16: B and C rows padded to 16 states (B, L, 16) in the input type
+    rows = 2 * 8 * 2048 * 16 * 2
+    assert B.ss_scan_workspace_bytes(desc(batch=8, seqlen=2048, dim=5120, dstate=8),
+                                     B.SS_OP_FWD) == rows
     # narrow ones are chunked: start states (B, chunks, N, D) + step sums (B, chunks, D)
     n = B.ss_scan_workspace_bytes(desc(batch=8, seqlen=2048, dim=1536), B.SS_OP_FWD)
     assert n > 0 and n % 256 == 0
