@@ -11,8 +11,8 @@
 // vector ops; the discretised A_bar, B_bar and the states never touch memory
 // ("A Visual Guide to Mamba" summary, Hardware-aware Algorithm: discretisation,
 // scan and the C contraction fused in one kernel).  With NSPLIT > 1 the waves'
-// partial sums over n of C h are added through LDS once per 8-step block; wave 0
-// applies the D skip and the gate and stores y.  Splitting the states gives more
+// partial sums over n of C h are added through LDS once per 8-step block; the
+// wave that owns a step adds the D skip, applies the gate and stores y.  Splitting the states gives more
 // waves per SIMD on wide problems, which hides the latency of the
 // transcendental units; each wave repeats the cheap per-step softplus.
 //
@@ -61,8 +61,9 @@ struct Chan {
 
 // LDS per workgroup: B/C row staging, per wave 2 buffers x 8 steps x 2*NS floats
 // (= 512 floats for the whole group); with NSPLIT > 1 also the shared step
-// sizes, 2 buffers x 64 lanes x 8 steps, and the partial outputs, 2 buffers x
-// NSPLIT waves x 64 lanes x 8 steps.
+// sizes, [2 buffers][8 steps][64 lanes], and the partial outputs, [2 buffers]
+// [NSPLIT waves][8 steps][64 lanes].  Lane is the fastest index, so the 32-bit
+// accesses of a wave hit consecutive banks.
 template <int NSPLIT>
 struct Lds {
   static constexpr int kNS = kMaxState / NSPLIT;
@@ -99,8 +100,8 @@ struct Scan {
   uint32_t lane;
   int wave, n0;          // wave index in the group, first state of this wave
   In ur[kPrefetch];      // prefetch ring: u of every step of the next block
-  In dr[OWN], zr[OWN];   // delta, z of the owned steps of the next block
-  float dl_own[OWN], g_own[OWN];   // step size and gate of the owned steps
+  In dr[OWN], zr[OWN], uo[OWN];   // delta, z, u of the owned steps of the next block
+  float dl_own[OWN], g_own[OWN], u_own[OWN];   // step size, gate and u of the owned steps
   float4 rowq;           // this lane's 16 bytes of the next block's rows
 
   __device__ __forceinline__ int owned(int i) const { return i * NSPLIT + wave; }
@@ -121,6 +122,9 @@ struct Scan {
       const uint32_t so = uint32_t(tt - tbase) * rowb_in;
       dr[i] = buf_load<In>(rd, vin, so);
       if (HAS_Z && !SUMMARY) zr[i] = buf_load<In>(rz, vin, so);
+      // a second read of u for the owned steps: the ring cannot be indexed by
+      // the (runtime) wave number without leaving registers
+      if (!SUMMARY && NSPLIT > 1) uo[i] = buf_load<In>(ru, vin, so);
     }
   }
 
@@ -133,12 +137,13 @@ struct Scan {
       if (t + owned(i) >= t1) x2 = SOFTPLUS ? -__builtin_inff() : 0.0f;
       dl_own[i] = SOFTPLUS ? softplus_log2(x2) : x2;               // dt * log2 e
       if (HAS_Z && !SUMMARY) g_own[i] = silu(to_f32(zr[i]));
+      if (!SUMMARY) u_own[i] = to_f32(NSPLIT > 1 ? uo[i] : ur[i]);
     }
   }
   __device__ __forceinline__ void publish(int buf) {
     if (NSPLIT == 1) return;
 #pragma unroll
-    for (int i = 0; i < OWN; ++i) act[(buf * kWave + lane) * kPrefetch + owned(i)] = dl_own[i];
+    for (int i = 0; i < OWN; ++i) act[(buf * kPrefetch + owned(i)) * kWave + lane] = dl_own[i];
   }
 
   // Rows of block [t, t + 8): per step, NS values of B then NS of C (this wave's
@@ -183,20 +188,21 @@ struct Scan {
   template <bool GUARD>
   __device__ __forceinline__ void block(int32_t t, int buf) {
     // 1. inputs of this block: u of every step, dt of every step
-    float uf[kPrefetch], dl[kPrefetch], acc[kPrefetch], g[OWN];
+    float uf[kPrefetch], dl[kPrefetch], acc[kPrefetch], g[OWN], us[OWN];
 #pragma unroll
     for (int k = 0; k < kPrefetch; ++k) uf[k] = to_f32(ur[k]);
     if (NSPLIT == 1) {
 #pragma unroll
       for (int k = 0; k < kPrefetch; ++k) dl[k] = dl_own[k];
     } else {
-      const float4* q = reinterpret_cast<const float4*>(act + (buf * kWave + lane) * kPrefetch);
-      const float4 x = q[0], y = q[1];
-      dl[0] = x.x; dl[1] = x.y; dl[2] = x.z; dl[3] = x.w;
-      dl[4] = y.x; dl[5] = y.y; dl[6] = y.z; dl[7] = y.w;
+#pragma unroll
+      for (int k = 0; k < kPrefetch; ++k) dl[k] = act[(buf * kPrefetch + k) * kWave + lane];
     }
 #pragma unroll
-    for (int i = 0; i < OWN; ++i) g[i] = g_own[i];
+    for (int i = 0; i < OWN; ++i) {
+      g[i] = g_own[i];
+      us[i] = u_own[i];
+    }
     // 2. prefetch the next block (u, owned delta and z, B and C rows)
     load_ring(t, t + kPrefetch, GUARD);
     fetch_rows(t + kPrefetch < t1 ? t + kPrefetch : tlast);
@@ -210,7 +216,8 @@ struct Scan {
       for (int n = 0; n < NS; ++n) { Bv[n] = Bn[n]; Cv[n] = Cn[n]; }
       if (k + 1 < kPrefetch) read_rows(buf, k + 1, Bn, Cn);
       const float d2 = dl[k];
-      float acc0 = 0.0f, acc1 = 0.0f;
+      float acc0 = 0.0f, acc1 = 0.0f;   // two chains when a wave holds many states
+      constexpr bool kTwo = NS > 4;
       if (DISC == kEuler) {
         const float dtu = d2 * (kLn2 * uf[k]);                    // dt * u
 #pragma unroll
@@ -218,7 +225,7 @@ struct Scan {
           const float a = hw_exp2(d2 * ch.A[n]);                  // A_bar = exp(dt A)
           h[n] = __builtin_fmaf(a, h[n], dtu * Bv[n]);            // + dt B u
           if (!SUMMARY) {
-            if (n & 1) acc1 = __builtin_fmaf(Cv[n], h[n], acc1);
+            if (kTwo && (n & 1)) acc1 = __builtin_fmaf(Cv[n], h[n], acc1);
             else acc0 = __builtin_fmaf(Cv[n], h[n], acc0);
           }
         }
@@ -231,23 +238,21 @@ struct Scan {
           if (SAFE) coef = __builtin_fmaf(dt, ch.zm[n], coef);    // dt where A == 0
           h[n] = __builtin_fmaf(a, h[n], coef * (Bv[n] * uf[k]));
           if (!SUMMARY) {
-            if (n & 1) acc1 = __builtin_fmaf(Cv[n], h[n], acc1);
+            if (kTwo && (n & 1)) acc1 = __builtin_fmaf(Cv[n], h[n], acc1);
             else acc0 = __builtin_fmaf(Cv[n], h[n], acc0);
           }
         }
       }
       if (SUMMARY) dsum += d2;
-      // wave 0 adds the D skip into its partial sum
-      else acc[k] = wave == 0 ? __builtin_fmaf(Dd, uf[k], acc0 + acc1) : acc0 + acc1;
+      else acc[k] = kTwo ? acc0 + acc1 : acc0;
     }
     // 4. activations of the next block's owned steps, rows of the next block
     activations(t + kPrefetch);
     publish(buf ^ 1);
     stage_rows(buf ^ 1);
     if (NSPLIT > 1 && !SUMMARY) {
-      float4* q = reinterpret_cast<float4*>(part + ((buf * NSPLIT + wave) * kWave + lane) * kPrefetch);
-      q[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
-      q[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+#pragma unroll
+      for (int k = 0; k < kPrefetch; ++k) part[((buf * NSPLIT + wave) * kPrefetch + k) * kWave + lane] = acc[k];
     }
     if (NSPLIT > 1) __syncthreads();
     if (SUMMARY) return;
@@ -262,8 +267,9 @@ struct Scan {
       } else {
         yv = 0.0f;
 #pragma unroll
-        for (int w = 0; w < NSPLIT; ++w) yv += part[((buf * NSPLIT + w) * kWave + lane) * kPrefetch + k];
+        for (int w = 0; w < NSPLIT; ++w) yv += part[((buf * NSPLIT + w) * kPrefetch + k) * kWave + lane];
       }
+      yv = __builtin_fmaf(Dd, us[i], yv);                          // + D skip
       if (HAS_Z) yv *= g[i];                                       // silu(z) gate
       if (!GUARD || t + k < t1) buf_store<Out>(ry, vout, uint32_t(k) * rowb_out, yv);
     }
