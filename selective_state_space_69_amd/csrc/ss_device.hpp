@@ -48,13 +48,17 @@ template <> __device__ __forceinline__ float to_f32<uint16_t>(uint16_t x) {
   return __uint_as_float(uint32_t(x) << 16);
 }
 
-// Four consecutive elements (8 bytes of bf16 or 16 bytes of fp32) as fp32.
-template <typename T> __device__ __forceinline__ float4 load4(const T* p);
-template <> __device__ __forceinline__ float4 load4<float>(const float* p) {
-  return *reinterpret_cast<const float4*>(p);
+// Four consecutive elements (8 bytes of bf16 or 16 bytes of fp32): loaded in
+// their storage form (Raw4), widened to fp32 where they are used, so that a
+// prefetch does not make the wave wait for the load.
+template <typename T> struct Raw4;
+template <> struct Raw4<float> { using type = float4; };
+template <> struct Raw4<uint16_t> { using type = uint2; };
+template <typename T> __device__ __forceinline__ typename Raw4<T>::type load_raw4(const T* p) {
+  return *reinterpret_cast<const typename Raw4<T>::type*>(p);
 }
-template <> __device__ __forceinline__ float4 load4<uint16_t>(const uint16_t* p) {
-  const uint2 w = *reinterpret_cast<const uint2*>(p);
+__device__ __forceinline__ float4 unpack4(float4 v) { return v; }
+__device__ __forceinline__ float4 unpack4(uint2 w) {
   return make_float4(__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xffff0000u),
                      __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xffff0000u));
 }

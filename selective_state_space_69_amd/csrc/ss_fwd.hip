@@ -99,56 +99,64 @@ struct Scan {
   float* part;           // partial outputs (NSPLIT > 1)
   uint32_t lane;
   int wave, n0;          // wave index in the group, first state of this wave
-  In ur[kPrefetch];      // prefetch ring: u of every step of the next block
-  In dr[OWN], zr[OWN], uo[OWN];   // delta, z, u of the owned steps of the next block
+  // Two-deep prefetch ring, slot = block parity: while block t runs, slot
+  // (t / 8) & 1 receives block t + 16 and the other slot holds block t + 8.  A
+  // load thus has a whole block of compute before its value is needed.
+  In ur[2][kPrefetch];                  // u of every step
+  In dr[2][OWN], zr[2][OWN], uo[2][OWN];   // delta, z, u of the owned steps
+  typename Raw4<In>::type rowq[2];      // this lane's 16 (fp32) or 8 (bf16) bytes of rows
   float dl_own[OWN], g_own[OWN], u_own[OWN];   // step size, gate and u of the owned steps
-  float4 rowq;           // this lane's 16 bytes of the next block's rows
 
   __device__ __forceinline__ int owned(int i) const { return i * NSPLIT + wave; }
 
-  __device__ __forceinline__ void load_ring(int32_t tbase, int32_t t, bool clamp) {
-    const Rsrc ru = make_rsrc(ub + int64_t(tbase) * p.D), rd = make_rsrc(db + int64_t(tbase) * p.D);
-    const Rsrc rz = make_rsrc(HAS_Z ? zb + int64_t(tbase) * p.D : ub);
+  template <int S>
+  __device__ __forceinline__ void load_ring(int32_t t, bool clamp) {
+    const Rsrc ru = make_rsrc(ub + int64_t(t) * p.D), rd = make_rsrc(db + int64_t(t) * p.D);
+    const Rsrc rz = make_rsrc(HAS_Z ? zb + int64_t(t) * p.D : ub);
+    const int32_t lim = tlast - t;    // last valid step, relative to t
 #pragma unroll
     for (int k = 0; k < kPrefetch; ++k) {
-      int32_t tt = t + k;
-      if (clamp) tt = tt < tlast ? tt : tlast;
-      ur[k] = buf_load<In>(ru, vin, uint32_t(tt - tbase) * rowb_in);
+      int32_t tt = k;
+      if (clamp) tt = tt < lim ? tt : lim;
+      ur[S][k] = buf_load<In>(ru, vin, uint32_t(tt) * rowb_in);
     }
 #pragma unroll
     for (int i = 0; i < OWN; ++i) {
-      int32_t tt = t + owned(i);
-      if (clamp) tt = tt < tlast ? tt : tlast;
-      const uint32_t so = uint32_t(tt - tbase) * rowb_in;
-      dr[i] = buf_load<In>(rd, vin, so);
-      if (HAS_Z && !SUMMARY) zr[i] = buf_load<In>(rz, vin, so);
+      int32_t tt = owned(i);
+      if (clamp) tt = tt < lim ? tt : lim;
+      const uint32_t so = uint32_t(tt) * rowb_in;
+      dr[S][i] = buf_load<In>(rd, vin, so);
+      if (HAS_Z && !SUMMARY) zr[S][i] = buf_load<In>(rz, vin, so);
       // a second read of u for the owned steps: the ring cannot be indexed by
       // the (runtime) wave number without leaving registers
-      if (!SUMMARY && NSPLIT > 1) uo[i] = buf_load<In>(ru, vin, so);
+      if (!SUMMARY && NSPLIT > 1) uo[S][i] = buf_load<In>(ru, vin, so);
     }
   }
 
   // step size (log2 units) and gate of the owned steps of the block at t, from
-  // the ring; steps at or past t1 get dt = 0
+  // ring slot S; steps at or past t1 get dt = 0
+  template <int S>
   __device__ __forceinline__ void activations(int32_t t) {
 #pragma unroll
     for (int i = 0; i < OWN; ++i) {
-      float x2 = __builtin_fmaf(to_f32(dr[i]), kLog2e, bias2);    // (delta + bias) log2 e
+      float x2 = __builtin_fmaf(to_f32(dr[S][i]), kLog2e, bias2);  // (delta + bias) log2 e
       if (t + owned(i) >= t1) x2 = SOFTPLUS ? -__builtin_inff() : 0.0f;
       dl_own[i] = SOFTPLUS ? softplus_log2(x2) : x2;               // dt * log2 e
-      if (HAS_Z && !SUMMARY) g_own[i] = silu(to_f32(zr[i]));
-      if (!SUMMARY) u_own[i] = to_f32(NSPLIT > 1 ? uo[i] : ur[i]);
+      if (HAS_Z && !SUMMARY) g_own[i] = silu(to_f32(zr[S][i]));
+      if (!SUMMARY) u_own[i] = to_f32(NSPLIT > 1 ? uo[S][i] : ur[S][i]);
     }
   }
-  __device__ __forceinline__ void publish(int buf) {
+  template <int S>
+  __device__ __forceinline__ void publish() {
     if (NSPLIT == 1) return;
 #pragma unroll
-    for (int i = 0; i < OWN; ++i) act[(buf * kPrefetch + owned(i)) * kWave + lane] = dl_own[i];
+    for (int i = 0; i < OWN; ++i) act[(S * kPrefetch + owned(i)) * kWave + lane] = dl_own[i];
   }
 
   // Rows of block [t, t + 8): per step, NS values of B then NS of C (this wave's
-  // states), i.e. NS/2 float4 per step; lane l fetches float4 g = l % (NS/2) of
-  // step k = (l / (NS/2)) % 8 (lanes beyond 4*NS repeat lower lanes' work).
+  // states), i.e. NS/2 groups of 4; lane l fetches group g = l % (NS/2) of step
+  // k = (l / (NS/2)) % 8 (lanes beyond 4*NS repeat lower lanes' work).
+  template <int S>
   __device__ __forceinline__ void fetch_rows(int32_t t) {
     constexpr int G = NS / 2;
     const uint32_t l = lane % uint32_t(4 * NS);
@@ -157,16 +165,18 @@ struct Scan {
     tr = tr < tlast ? tr : tlast;
     const In* src = static_cast<const In*>(g < G / 2 ? p.Brow : p.Crow) +
                     (row0 + tr) * kMaxState + n0 + 4 * (g % (G / 2));
-    rowq = load4<In>(src);
+    rowq[S] = load_raw4(src);
   }
-  __device__ __forceinline__ void stage_rows(int buf) {
+  template <int S>
+  __device__ __forceinline__ void stage_rows() {
     constexpr int G = NS / 2;
     const uint32_t l = lane % uint32_t(4 * NS);
-    const uint32_t off = buf * (kPrefetch * 2 * NS) + (l / G) * (2 * NS) + 4 * (l % G);
-    *reinterpret_cast<float4*>(stage + off) = rowq;
+    const uint32_t off = S * (kPrefetch * 2 * NS) + (l / G) * (2 * NS) + 4 * (l % G);
+    *reinterpret_cast<float4*>(stage + off) = unpack4(rowq[S]);
   }
-  __device__ __forceinline__ void read_rows(int buf, int k, float (&Bv)[NS], float (&Cv)[NS]) {
-    const float4* q = reinterpret_cast<const float4*>(stage + buf * (kPrefetch * 2 * NS) + k * 2 * NS);
+  template <int S>
+  __device__ __forceinline__ void read_rows(int k, float (&Bv)[NS], float (&Cv)[NS]) {
+    const float4* q = reinterpret_cast<const float4*>(stage + S * (kPrefetch * 2 * NS) + k * 2 * NS);
 #pragma unroll
     for (int m = 0; m < NS / 4; ++m) {
       const float4 v = q[m];
@@ -181,40 +191,43 @@ struct Scan {
     }
   }
 
-  // One block of 8 steps starting at t.  On entry the ring holds this block's
-  // inputs (owned-step activations already computed and, for NSPLIT > 1,
-  // published to act[buf] behind a barrier).  GUARD: the block may run past t1
-  // and the prefetch of the next block is clamped to the range.
-  template <bool GUARD>
-  __device__ __forceinline__ void block(int32_t t, int buf) {
+  // One block of 8 steps starting at t, ring slot / LDS buffer S = (t / 8) & 1.
+  // On entry slot S holds this block's u, the LDS buffer S its rows and step
+  // sizes (behind a barrier), and the owned-step activations are computed;
+  // slot S^1 holds block t + 8.  GUARD: the prefetch of block t + 16 is clamped
+  // to the range and stores past t1 are skipped.
+  template <bool GUARD, int S>
+  __device__ __forceinline__ void block(int32_t t) {
     // 1. inputs of this block: u of every step, dt of every step
     float uf[kPrefetch], dl[kPrefetch], acc[kPrefetch], g[OWN], us[OWN];
 #pragma unroll
-    for (int k = 0; k < kPrefetch; ++k) uf[k] = to_f32(ur[k]);
+    for (int k = 0; k < kPrefetch; ++k) uf[k] = to_f32(ur[S][k]);
     if (NSPLIT == 1) {
 #pragma unroll
       for (int k = 0; k < kPrefetch; ++k) dl[k] = dl_own[k];
     } else {
 #pragma unroll
-      for (int k = 0; k < kPrefetch; ++k) dl[k] = act[(buf * kPrefetch + k) * kWave + lane];
+      for (int k = 0; k < kPrefetch; ++k) dl[k] = act[(S * kPrefetch + k) * kWave + lane];
     }
 #pragma unroll
     for (int i = 0; i < OWN; ++i) {
       g[i] = g_own[i];
       us[i] = u_own[i];
     }
-    // 2. prefetch the next block (u, owned delta and z, B and C rows)
-    load_ring(t, t + kPrefetch, GUARD);
-    fetch_rows(t + kPrefetch < t1 ? t + kPrefetch : tlast);
+    // 2. prefetch block t + 16 into slot S (u, owned delta and z, B and C rows)
+    const int32_t tn = t + 2 * kPrefetch;
+    const int32_t tnc = tn < tlast ? tn : tlast;
+    load_ring<S>(tnc, GUARD);
+    fetch_rows<S>(tnc);
     // 3. the recurrence, one step at a time (rows read from LDS one step ahead)
     float Bn[NS], Cn[NS];
-    read_rows(buf, 0, Bn, Cn);
+    read_rows<S>(0, Bn, Cn);
 #pragma unroll
     for (int k = 0; k < kPrefetch; ++k) {
       float Bv[NS], Cv[NS];
 #pragma unroll
       for (int n = 0; n < NS; ++n) { Bv[n] = Bn[n]; Cv[n] = Cn[n]; }
-      if (k + 1 < kPrefetch) read_rows(buf, k + 1, Bn, Cn);
+      if (k + 1 < kPrefetch) read_rows<S>(k + 1, Bn, Cn);
       const float d2 = dl[k];
       float acc0 = 0.0f, acc1 = 0.0f;   // two chains when a wave holds many states
       constexpr bool kTwo = NS > 4;
@@ -246,17 +259,17 @@ struct Scan {
       if (SUMMARY) dsum += d2;
       else acc[k] = kTwo ? acc0 + acc1 : acc0;
     }
-    // 4. activations of the next block's owned steps, rows of the next block
-    activations(t + kPrefetch);
-    publish(buf ^ 1);
-    stage_rows(buf ^ 1);
+    // 4. activations of block t + 8 (slot S^1, loaded one block ago), its rows
+    activations<S ^ 1>(t + kPrefetch);
+    publish<S ^ 1>();
+    stage_rows<S ^ 1>();
     if (NSPLIT > 1 && !SUMMARY) {
 #pragma unroll
-      for (int k = 0; k < kPrefetch; ++k) part[((buf * NSPLIT + wave) * kPrefetch + k) * kWave + lane] = acc[k];
+      for (int k = 0; k < kPrefetch; ++k) part[((S * NSPLIT + wave) * kPrefetch + k) * kWave + lane] = acc[k];
     }
     if (NSPLIT > 1) __syncthreads();
     if (SUMMARY) return;
-    // 5. outputs of the owned steps: sum of the waves' partials, gate, store
+    // 5. outputs of the owned steps: sum of the waves' partials, skip, gate, store
     const Rsrc ry = make_rsrc(yb + int64_t(t) * p.D);
 #pragma unroll
     for (int i = 0; i < OWN; ++i) {
@@ -267,7 +280,7 @@ struct Scan {
       } else {
         yv = 0.0f;
 #pragma unroll
-        for (int w = 0; w < NSPLIT; ++w) yv += part[((buf * NSPLIT + w) * kPrefetch + k) * kWave + lane];
+        for (int w = 0; w < NSPLIT; ++w) yv += part[((S * NSPLIT + w) * kPrefetch + k) * kWave + lane];
       }
       yv = __builtin_fmaf(Dd, us[i], yv);                          // + D skip
       if (HAS_Z) yv *= g[i];                                       // silu(z) gate
@@ -276,17 +289,25 @@ struct Scan {
   }
 
   __device__ __forceinline__ void run(int32_t t0) {
-    load_ring(t0, t0, true);
-    fetch_rows(t0);
-    stage_rows(0);
-    activations(t0);
-    publish(0);
+    const int32_t t8 = t0 + kPrefetch < tlast ? t0 + kPrefetch : tlast;
+    load_ring<0>(t0, true);
+    fetch_rows<0>(t0);
+    load_ring<1>(t8, true);
+    fetch_rows<1>(t8);
+    stage_rows<0>();
+    activations<0>(t0);
+    publish<0>();
     if (NSPLIT > 1) __syncthreads();
     int32_t t = t0;
-    int buf = 0;
-    // full blocks whose next-block prefetch stays inside the range: no guards
-    for (; t + 2 * kPrefetch <= t1; t += kPrefetch, buf ^= 1) block<false>(t, buf);
-    for (; t < t1; t += kPrefetch, buf ^= 1) block<true>(t, buf);
+    // pairs of full blocks whose prefetch (up to t + 31) stays inside the range
+    for (; t + 4 * kPrefetch <= t1; t += 2 * kPrefetch) {
+      block<false, 0>(t);
+      block<false, 1>(t + kPrefetch);
+    }
+    for (; t < t1; t += 2 * kPrefetch) {
+      block<true, 0>(t);
+      if (t + kPrefetch < t1) block<true, 1>(t + kPrefetch);
+    }
   }
 };
 
