@@ -50,29 +50,47 @@ int64_t env_int(const char* name) {
 // Work decomposition.  The scan is bound by the vector ALU (one v_exp_f32 and
 // 4-6 FMA-class ops per element), and a SIMD running a single wave stalls on
 // transcendental and LDS latency, so the plan aims for several waves per SIMD
-// (the MI355X has 1024 SIMDs in 256 CUs) with the least redundant work:
-//  - >= 2048 channel blocks (B * ceil(D/64)): one wave per block, one pass;
-//  - >= 512 blocks: split the 16 states of a block over 4 waves (each wave
-//    repeats only cheap per-step work), one pass over time;
-//  - fewer: split the states over 2 waves and cut time into chunks of >= 128
-//    steps, targeting 8192 waves; a chunked forward costs about 1.8x the
+// (the MI355X has 1024 SIMDs in 256 CUs) with the least redundant work.  With
+// cols = B * ceil(D / 64) channel blocks:
+//  - cols >= 2048: one wave per block (16 states per lane), one pass;
+//  - cols >= 512: one pass, either 64-channel groups with the states split
+//    over 4 waves, or 32-channel groups with two states per lane (twice the
+//    groups, 5% more instructions per element).  The second is taken when it
+//    spreads the groups over the 256 CUs clearly more evenly: a CU holds at
+//    most 4 of the first kind at a time and 5 of the second, and the time is
+//    set by the most loaded CU (B = 8, D = 5120: 3 vs 2.5 groups' worth);
+//  - fewer: 4 waves per 64-channel group and time cut into chunks of >= 128
+//    steps, about 8192 waves in all; a chunked forward costs about 1.8x the
 //    arithmetic (summary pass + output pass) but keeps every SIMD busy.
 // Measured on MI355X for the Mamba-130M/2.8B shapes and the 1M-step case.
-// SS_SCAN_NSPLIT / SS_SCAN_CHUNK override the choice.
+// SS_SCAN_NSPLIT (1, 2, 4, or 8 for the 32-channel kernel) and SS_SCAN_CHUNK
+// override the choice.
 TimePlan plan_time(const ss_desc_t& d) {
   TimePlan tp;
   const int64_t L = d.seqlen;
   const int64_t cols = d.batch * ((d.dim + kWave - 1) / kWave);
-  constexpr int64_t kWide = 2048, kMid = 512, kChunkWaves = 8192, kMinChunk = 128;
+  const int64_t cols32 = d.batch * ((d.dim + 31) / 32);
+  constexpr int64_t kWide = 2048, kMid = 512, kChunkWaves = 8192, kMinChunk = 128, kCUs = 256;
   int nsplit = int(env_int("SS_SCAN_NSPLIT"));
-  const bool forced_split = nsplit == 1 || nsplit == 2 || nsplit == 4;
-  if (!forced_split) nsplit = cols >= kWide ? 1 : (cols >= kMid ? 4 : 2);
+  const bool forced_split = nsplit == 1 || nsplit == 2 || nsplit == 4 || nsplit == kHalfWaveSplit;
+  if (!forced_split) {
+    if (cols >= kWide) {
+      nsplit = 1;
+    } else if (cols >= kMid) {
+      // most loaded CU, in units of one 64-channel group's work
+      const double t4 = double((cols + kCUs - 1) / kCUs);
+      const double t8 = 0.5 * 1.05 * double((cols32 + kCUs - 1) / kCUs);
+      nsplit = t8 < 0.9 * t4 ? kHalfWaveSplit : 4;
+    } else {
+      nsplit = 4;
+    }
+  }
   int64_t chunk = env_int("SS_SCAN_CHUNK");
   if (chunk <= 0) {
     if (cols >= kMid || L < 2 * kMinChunk) {
       chunk = L;
     } else {
-      const int64_t waves = cols * nsplit;
+      const int64_t waves = nsplit == kHalfWaveSplit ? cols32 * 4 : cols * nsplit;
       const int64_t want = (kChunkWaves + waves - 1) / waves;
       chunk = (L + want - 1) / want;
       if (chunk < kMinChunk) chunk = kMinChunk;

@@ -24,33 +24,12 @@
 //      Guide to Mamba" summary, The Scan Operation: segments combined
 //      associatively), done as a wave64 scan over chunks;
 //   3. output pass: each chunk re-runs from its true start state and writes y.
-#include "ss_device.hpp"
+#include "ss_fwd_common.hpp"
 
 namespace ss {
 namespace {
 
-constexpr int kZoh = SS_ZOH;
-constexpr int kEuler = SS_EULER;
-constexpr int kPrefetch = 8;  // time steps per block (u, delta, z ring; B, C staging)
-
-struct FwdParams {
-  const void* u;
-  const void* delta;
-  const float* A;
-  const void* Brow;    // (B, L, 16) rows of B in the input type (zero past N)
-  const void* Crow;    // (B, L, 16) rows of C
-  const float* Dskip;
-  const float* bias;
-  const void* z;
-  const float* h0;
-  void* y;
-  float* h_last;
-  float* hend;   // (B, nchunks, N, D)
-  float* dsum;   // (B, nchunks, D)
-  int64_t L, D;
-  int64_t chunk_len;
-  int32_t N, ndblk, nchunks, grid_chunks;
-};
+constexpr int kPrefetch = kBlk;  // time steps per block (u, delta, z ring; B, C staging)
 
 template <int NS>
 struct Chan {
@@ -109,17 +88,22 @@ struct Scan {
 
   __device__ __forceinline__ int owned(int i) const { return i * NSPLIT + wave; }
 
+  // Prefetch of block t into ring slot S: u of every step, delta, z and u of
+  // the owned steps, B/C rows.  load_u issues one step's u, so that inside a
+  // block each load can reuse the register its predecessor in the slot has
+  // just released.
+  __device__ __forceinline__ Rsrc u_rsrc(int32_t t) const { return make_rsrc(ub + int64_t(t) * p.D); }
   template <int S>
-  __device__ __forceinline__ void load_ring(int32_t t, bool clamp) {
-    const Rsrc ru = make_rsrc(ub + int64_t(t) * p.D), rd = make_rsrc(db + int64_t(t) * p.D);
+  __device__ __forceinline__ void load_u(const Rsrc& ru, int k, int32_t lim, bool clamp) {
+    int32_t tt = k;
+    if (clamp) tt = tt < lim ? tt : lim;
+    ur[S][k] = buf_load<In>(ru, vin, uint32_t(tt) * rowb_in);
+  }
+  template <int S>
+  __device__ __forceinline__ void load_owned(int32_t t, bool clamp) {
+    const Rsrc ru = u_rsrc(t), rd = make_rsrc(db + int64_t(t) * p.D);
     const Rsrc rz = make_rsrc(HAS_Z ? zb + int64_t(t) * p.D : ub);
     const int32_t lim = tlast - t;    // last valid step, relative to t
-#pragma unroll
-    for (int k = 0; k < kPrefetch; ++k) {
-      int32_t tt = k;
-      if (clamp) tt = tt < lim ? tt : lim;
-      ur[S][k] = buf_load<In>(ru, vin, uint32_t(tt) * rowb_in);
-    }
 #pragma unroll
     for (int i = 0; i < OWN; ++i) {
       int32_t tt = owned(i);
@@ -131,6 +115,13 @@ struct Scan {
       // the (runtime) wave number without leaving registers
       if (!SUMMARY && NSPLIT > 1) uo[S][i] = buf_load<In>(ru, vin, so);
     }
+  }
+  template <int S>
+  __device__ __forceinline__ void load_ring(int32_t t, bool clamp) {
+    const Rsrc ru = u_rsrc(t);
+#pragma unroll
+    for (int k = 0; k < kPrefetch; ++k) load_u<S>(ru, k, tlast - t, clamp);
+    load_owned<S>(t, clamp);
   }
 
   // step size (log2 units) and gate of the owned steps of the block at t, from
@@ -198,41 +189,45 @@ struct Scan {
   // to the range and stores past t1 are skipped.
   template <bool GUARD, int S>
   __device__ __forceinline__ void block(int32_t t) {
-    // 1. inputs of this block: u of every step, dt of every step
-    float uf[kPrefetch], dl[kPrefetch], acc[kPrefetch], g[OWN], us[OWN];
-#pragma unroll
-    for (int k = 0; k < kPrefetch; ++k) uf[k] = to_f32(ur[S][k]);
-    if (NSPLIT == 1) {
-#pragma unroll
-      for (int k = 0; k < kPrefetch; ++k) dl[k] = dl_own[k];
-    } else {
-#pragma unroll
-      for (int k = 0; k < kPrefetch; ++k) dl[k] = act[(S * kPrefetch + k) * kWave + lane];
-    }
+    float g[OWN], us[OWN];
 #pragma unroll
     for (int i = 0; i < OWN; ++i) {
       g[i] = g_own[i];
       us[i] = u_own[i];
     }
-    // 2. prefetch block t + 16 into slot S (u, owned delta and z, B and C rows)
-    const int32_t tn = t + 2 * kPrefetch;
-    const int32_t tnc = tn < tlast ? tn : tlast;
-    load_ring<S>(tnc, GUARD);
-    fetch_rows<S>(tnc);
-    // 3. the recurrence, one step at a time (rows read from LDS one step ahead)
+    // prefetch block t + 16 into slot S: owned-step inputs and rows now, the u
+    // of step k right after step k has read its slot entry
+    const int32_t tn0 = t + 2 * kPrefetch;
+    const int32_t tn = tn0 < tlast ? tn0 : tlast;
+    load_owned<S>(tn, GUARD);
+    fetch_rows<S>(tn);
+    const Rsrc ru = u_rsrc(tn);
+    const Rsrc ry = make_rsrc(yb + int64_t(t) * p.D);
+    const float* dls = act + S * kPrefetch * kWave + lane;
+    float* parts = part + (S * NSPLIT + wave) * kPrefetch * kWave + lane;
+    // the recurrence, one step at a time (rows and step sizes read one step ahead)
     float Bn[NS], Cn[NS];
     read_rows<S>(0, Bn, Cn);
+    float dn;
+    if constexpr (NSPLIT == 1) dn = dl_own[0];
+    else dn = dls[0];
 #pragma unroll
     for (int k = 0; k < kPrefetch; ++k) {
       float Bv[NS], Cv[NS];
 #pragma unroll
       for (int n = 0; n < NS; ++n) { Bv[n] = Bn[n]; Cv[n] = Cn[n]; }
-      if (k + 1 < kPrefetch) read_rows<S>(k + 1, Bn, Cn);
-      const float d2 = dl[k];
+      const float d2 = dn;
+      if (k + 1 < kPrefetch) {
+        read_rows<S>(k + 1, Bn, Cn);
+        if constexpr (NSPLIT == 1) dn = dl_own[k + 1];
+        else dn = dls[(k + 1) * kWave];
+      }
+      const float uk = to_f32(ur[S][k]);
+      load_u<S>(ru, k, tlast - tn, GUARD);
       float acc0 = 0.0f, acc1 = 0.0f;   // two chains when a wave holds many states
       constexpr bool kTwo = NS > 4;
       if (DISC == kEuler) {
-        const float dtu = d2 * (kLn2 * uf[k]);                    // dt * u
+        const float dtu = d2 * (kLn2 * uk);                       // dt * u
 #pragma unroll
         for (int n = 0; n < NS; ++n) {
           const float a = hw_exp2(d2 * ch.A[n]);                  // A_bar = exp(dt A)
@@ -249,39 +244,40 @@ struct Scan {
           const float a = hw_exp2(d2 * ch.A[n]);                  // A_bar = exp(dt A)
           float coef = __builtin_fmaf(a, ch.iA[n], -ch.iA[n]);    // (A_bar - 1) / A
           if (SAFE) coef = __builtin_fmaf(dt, ch.zm[n], coef);    // dt where A == 0
-          h[n] = __builtin_fmaf(a, h[n], coef * (Bv[n] * uf[k]));
+          h[n] = __builtin_fmaf(a, h[n], coef * (Bv[n] * uk));
           if (!SUMMARY) {
             if (kTwo && (n & 1)) acc1 = __builtin_fmaf(Cv[n], h[n], acc1);
             else acc0 = __builtin_fmaf(Cv[n], h[n], acc0);
           }
         }
       }
-      if (SUMMARY) dsum += d2;
-      else acc[k] = kTwo ? acc0 + acc1 : acc0;
+      if (SUMMARY) {
+        dsum += d2;
+      } else {
+        const float acc = kTwo ? acc0 + acc1 : acc0;
+        if constexpr (NSPLIT > 1) {
+          parts[k * kWave] = acc;                                  // partial C h
+        } else {
+          // one wave holds every state: y of step k is complete
+          float yv = __builtin_fmaf(Dd, uk, acc);                  // + D skip
+          if (HAS_Z) yv *= g[k];                                   // silu(z) gate
+          if (!GUARD || t + k < t1) buf_store<Out>(ry, vout, uint32_t(k) * rowb_out, yv);
+        }
+      }
     }
     // 4. activations of block t + 8 (slot S^1, loaded one block ago), its rows
     activations<S ^ 1>(t + kPrefetch);
     publish<S ^ 1>();
     stage_rows<S ^ 1>();
-    if (NSPLIT > 1 && !SUMMARY) {
-#pragma unroll
-      for (int k = 0; k < kPrefetch; ++k) part[((S * NSPLIT + wave) * kPrefetch + k) * kWave + lane] = acc[k];
-    }
     if (NSPLIT > 1) __syncthreads();
-    if (SUMMARY) return;
+    if (SUMMARY || NSPLIT == 1) return;
     // 5. outputs of the owned steps: sum of the waves' partials, skip, gate, store
-    const Rsrc ry = make_rsrc(yb + int64_t(t) * p.D);
 #pragma unroll
     for (int i = 0; i < OWN; ++i) {
       const int k = owned(i);
-      float yv;
-      if (NSPLIT == 1) {
-        yv = acc[k];
-      } else {
-        yv = 0.0f;
+      float yv = 0.0f;
 #pragma unroll
-        for (int w = 0; w < NSPLIT; ++w) yv += part[((S * NSPLIT + w) * kPrefetch + k) * kWave + lane];
-      }
+      for (int w = 0; w < NSPLIT; ++w) yv += part[((S * NSPLIT + w) * kPrefetch + k) * kWave + lane];
       yv = __builtin_fmaf(Dd, us[i], yv);                          // + D skip
       if (HAS_Z) yv *= g[i];                                       // silu(z) gate
       if (!GUARD || t + k < t1) buf_store<Out>(ry, vout, uint32_t(k) * rowb_out, yv);
@@ -311,8 +307,14 @@ struct Scan {
   }
 };
 
+// Minimum waves per SIMD the register allocation must allow: the one-wave
+// layout keeps 16 states per lane and runs on very wide problems; the split
+// layouts need several resident waves per SIMD to hide latency.
+template <int NSPLIT>
+constexpr int kMinWaves = NSPLIT == 1 ? 2 : 3;
+
 template <typename In, typename Out, int DISC, bool HAS_Z, bool SOFTPLUS, bool SUMMARY, int NSPLIT>
-__global__ __launch_bounds__(kWave * NSPLIT) void fwd_kernel(FwdParams p) {
+__global__ __launch_bounds__(kWave * NSPLIT, kMinWaves<NSPLIT>) void fwd_kernel(FwdParams p) {
   constexpr int NS = kMaxState / NSPLIT;
   // wave-uniform by construction; readfirstlane lets the compiler keep it in an SGPR
   const int wave = __builtin_amdgcn_readfirstlane(int(threadIdx.x) / kWave);
@@ -530,7 +532,8 @@ FwdParams make_params(const ss_desc_t& d, const TimePlan& tp, const FwdArgs& a) 
   p.L = d.seqlen; p.D = d.dim; p.N = int32_t(d.dstate);
   p.chunk_len = tp.chunk_len;
   p.nchunks = int32_t(tp.nchunks);
-  p.ndblk = int32_t((d.dim + kWave - 1) / kWave);
+  const int64_t width = tp.nsplit == kHalfWaveSplit ? 32 : kWave;   // channels per workgroup
+  p.ndblk = int32_t((d.dim + width - 1) / width);
   return p;
 }
 
@@ -558,7 +561,9 @@ int launch_fwd_carries(const ss_desc_t& d, const TimePlan& tp, const FwdArgs& a,
   FwdParams p = make_params(d, tp, a);
   const int64_t cols = d.batch * p.ndblk;
   p.grid_chunks = p.nchunks - 1;   // the last chunk's summary is never needed
-  hipError_t e = dispatch(d, p, tp.nsplit, true, cols * p.grid_chunks, st);
+  hipError_t e = tp.nsplit == kHalfWaveSplit
+                     ? launch_fwd_hw(d, p, true, cols * p.grid_chunks, st)
+                     : dispatch(d, p, tp.nsplit, true, cols * p.grid_chunks, st);
   if (e != hipSuccess) return int(e);
   const int64_t total = d.batch * d.dstate * d.dim;
   hipLaunchKernelGGL(carry_scan_kernel, dim3(unsigned((total + 255) / 256)), dim3(256), 0, st,
@@ -583,6 +588,7 @@ int launch_fwd(const ss_desc_t& d, const FwdPlan& plan, const FwdArgs& args, voi
   FwdParams p = make_params(d, plan.tp, a);
   p.grid_chunks = p.nchunks;
   const int64_t cols = d.batch * p.ndblk;
+  if (plan.tp.nsplit == kHalfWaveSplit) return int(launch_fwd_hw(d, p, false, cols * p.grid_chunks, st));
   return int(dispatch(d, p, plan.tp.nsplit, false, cols * p.grid_chunks, st));
 }
 

@@ -12,9 +12,12 @@ namespace ss {
 
 constexpr int kWave = 64;      // lanes per wavefront on CDNA
 constexpr int kMaxState = 16;  // states held per lane
+constexpr int kHalfWaveSplit = 8;
 
 // How a forward (or the forward recompute inside the backward) is split.
-// nsplit : waves per (b, 64-channel block), each holding 16 / nsplit states.
+// nsplit : waves per (b, 64-channel block), each holding 16 / nsplit states;
+//          kHalfWaveSplit selects the 32-channel kernel (4 waves per
+//          (b, 32-channel block), two states per lane).
 // nchunks == 1: one sequential pass over time per workgroup.
 // nchunks  > 1: (1) chunk summaries, (2) carry scan over chunks, (3) output pass.
 struct TimePlan {

@@ -68,26 +68,30 @@ def test_fwd_fp32_parity(oracle, case):
 
 
 SPLIT_CASES = [
-    (2, 150, 150, 16, "zoh", "mixed"), (2, 150, 150, 16, "euler", "random"),
-    (1, 300, 64, 5, "zoh", "random"), (3, 61, 130, 16, "zoh", "s4d_real"),
+    (2, 150, 150, 16, "zoh", "mixed", "f32"), (2, 150, 150, 16, "euler", "random", "f32"),
+    (1, 300, 64, 5, "zoh", "random", "f32"), (3, 61, 130, 16, "zoh", "s4d_real", "f32"),
+    (2, 203, 100, 16, "zoh", "random", "bf16"), (1, 77, 40, 7, "euler", "mixed", "bf16"),
 ]
 
 
-@pytest.mark.parametrize("nsplit", ["1", "2", "4"])
+@pytest.mark.parametrize("nsplit", ["1", "2", "4", "8"])
 @pytest.mark.parametrize("chunk", ["0", "48"])
-@pytest.mark.parametrize("case", SPLIT_CASES, ids=lambda c: "b%d_l%d_d%d_n%d_%s_%s" % c)
+@pytest.mark.parametrize("case", SPLIT_CASES, ids=lambda c: "b%d_l%d_d%d_n%d_%s_%s_%s" % c)
 def test_fwd_split_variants(oracle, monkeypatch, nsplit, chunk, case):
-    """Every state split (1, 2, 4 waves per channel block), with and without time
-    chunks, against the oracle."""
-    Bt, L, D, N, disc, amode = case
+    """Every kernel layout (64-channel groups with 1, 2 or 4 waves over the
+    states; "8" = 32-channel groups, two states per lane), with and without
+    time chunks, against the oracle."""
+    Bt, L, D, N, disc, amode, dt = case
+    log("split case", nsplit, chunk, case)
     monkeypatch.setenv("SS_SCAN_NSPLIT", nsplit)
     monkeypatch.setenv("SS_SCAN_CHUNK", chunk)
-    inp = synth.make_inputs(Bt, L, D, N, seed=2000 + SPLIT_CASES.index(case), dtype="f32",
+    inp = synth.make_inputs(Bt, L, D, N, seed=2000 + SPLIT_CASES.index(case), dtype=dt,
                             with_h0=True, a_mode=amode)
     d = upload(inp)
     y, hl = gpu_fwd(d, disc, return_last_state=True)
     torch.cuda.synchronize()
     ref, href = _full_oracle(oracle, inp, disc)
+    # bf16 inputs reach both sides as the same bits, so the fp32 bound applies
     check_f32(y.cpu().numpy(), ref, "y")
     check_f32(hl.cpu().numpy(), href, "h_last")
 
