@@ -13,7 +13,7 @@ namespace {
 
 constexpr size_t kAlign = 256;     // workspace alignment
 constexpr size_t kPtrAlign = 16;   // every tensor pointer (rows are read with 16-byte loads)
-constexpr int64_t kBwdChunk = 64;   // backward time chunk (8 blocks of 8 steps)
+constexpr int64_t kBwdChunk = 32;   // backward time chunk (8 blocks of 4 steps)
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
@@ -125,7 +125,7 @@ FwdPlan plan_fwd(const ss_desc_t& d) {
 }
 
 // The backward always splits the states over 4 waves and cuts time into chunks
-// of 64 steps: a chunk's 8 block checkpoints then fit in registers.
+// of 32 steps: a chunk's 8 block checkpoints then fit in registers.
 BwdPlan plan_bwd(const ss_desc_t& d) {
   BwdPlan p;
   p.tp.nsplit = 4;

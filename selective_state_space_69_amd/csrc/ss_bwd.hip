@@ -3,20 +3,23 @@
 // The states are never stored in memory: they are rebuilt from the inputs
 // ("A Visual Guide to Mamba" summary, Hardware-aware Algorithm: recomputation;
 // "A Survey of Mamba" summary, hardware-aware computation).  Time is cut into
-// chunks of 64 steps.  Per chunk:
+// chunks of 32 steps.  Per chunk:
 //   - its start state comes from the forward's summary pass + carry scan;
 //   - the adjoint carry entering it from its end comes from a reverse summary
 //     pass + reverse carry scan (the adjoint recurrence
 //     lambda_t = gy_t C_t + A_bar_{t+1} lambda_{t+1} is the same linear scan run
 //     backwards in time);
-//   - a workgroup of 4 waves (lane = channel d, 4 states per wave) runs the
-//     chunk forward keeping one state checkpoint per 8-step block in registers,
-//     then walks the blocks backwards: recompute the block (A_bar and h kept in
-//     registers), reverse sweep, gradients.
+//   - a workgroup of 4 waves (lane = channel d, 4 states per wave) stages the
+//     chunk's step sizes, gated output gradients and B/C rows in LDS, runs the
+//     chunk forward keeping one state checkpoint per 4-step block in
+//     registers, then walks the blocks backwards: recompute the block (A_bar
+//     and h kept in registers), reverse sweep, gradients.
 // Reductions: dB, dC over the 64 channels of a block by a cross-lane
 // reduce-scatter (permlane swaps and DPP), then over channel blocks; dA, dD_skip
 // and ddelta_bias per channel over the chunk, then over chunks and batch rows.
 // All partial sums are added in a fixed order: the backward is deterministic.
+// The register footprint (about 150 VGPRs) leaves room for three waves per
+// SIMD, which hides the latency of the transcendental unit and of LDS.
 #include "ss_device.hpp"
 
 namespace ss {
@@ -26,7 +29,7 @@ constexpr int kZoh = SS_ZOH;
 constexpr int kEuler = SS_EULER;
 constexpr int kNW = 4;                 // waves per workgroup
 constexpr int kNS = kMaxState / kNW;   // states per wave
-constexpr int kKB = 8;                 // steps per block
+constexpr int kKB = 4;                 // steps per block (one owned step per wave)
 constexpr int kNB = 8;                 // blocks per chunk
 constexpr int kChunk = kKB * kNB;      // steps per chunk (matches the backward plan)
 
@@ -134,7 +137,35 @@ __device__ __forceinline__ float reduce_scatter64(const float (&v)[64], uint32_t
   return dpp_pair<kDppQuadXor1>(e[0], e[1], u0);
 }
 
+// 16 values per lane -> lanes 4i .. 4i+3 hold the sum over the 64 lanes of
+// value i: the same pairing stages down to one value per lane, then two
+// butterflies inside each quad.
+__device__ __forceinline__ float reduce_scatter16(const float (&v)[16], uint32_t lane) {
+  float a[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) a[i] = swap_add32(v[i], v[i + 8]);
+  float b[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) b[i] = swap_add16(a[i], a[i + 4]);
+  const bool u3 = (lane >> 3) & 1u, u2 = (lane >> 2) & 1u;
+  float c[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) c[i] = dpp_pair<kDppRowRor8>(b[i], b[i + 2], u3);
+  float d = dpp_pair<kDppRowHalfMirror>(c[0], c[1], u2);
+  d += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(d), kDppQuadXor2, 0xf, 0xf, false));
+  d += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(d), kDppQuadXor1, 0xf, 0xf, false));
+  return d;
+}
+
 // ---------------------------------------------------------------- main kernel
+// LDS (floats): step sizes and gated output gradients [32 steps][64 lanes],
+// B/C rows [32 steps][B 16, C 16], per-step partials of du, d(dt) and y
+// [4 waves][3][4 steps][64 lanes].
+constexpr int kActF = kChunk * kWave;
+constexpr int kRowF = kChunk * 2 * kMaxState;
+constexpr int kXchF = kNW * 3 * kKB * kWave;
+constexpr int kLdsFloats = 2 * kActF + kRowF + kXchF;
+
 template <typename In, int DISC, bool HAS_Z, bool SOFTPLUS, bool SAFE>
 __device__ __forceinline__ void bwd_chunk(const BwdParams& p, float* lds, int64_t b, int dblk,
                                           int chunk, int wave, uint32_t lane) {
@@ -162,12 +193,13 @@ __device__ __forceinline__ void bwd_chunk(const BwdParams& p, float* lds, int64_
   const float Dd = p.Dskip ? p.Dskip[dc] : 0.0f;
   const float bias2 = (p.bias ? p.bias[dc] : 0.0f) * kLog2e;
 
-  float* actDl = lds;                            // [64 steps][64 lanes]
-  float* actGy = lds + kChunk * kWave;           // [64 steps][64 lanes]
-  float* xch = lds + 2 * kChunk * kWave;         // [4 waves][3][8 steps][64 lanes]
+  float* actDl = lds;                            // [32 steps][64 lanes]
+  float* actGy = lds + kActF;                    // [32 steps][64 lanes]
+  float* rows = lds + 2 * kActF;                 // [32 steps][B 16, C 16]
+  float* xch = rows + kRowF;                     // [4 waves][3][4 steps][64 lanes]
 
   // ---- phase A1: step sizes and gated upstream gradients of the chunk, each
-  //      wave computing the steps k with k % 4 == wave, shared through LDS
+  //      wave computing the steps k with k % 4 == wave; the chunk's B/C rows
 #pragma unroll
   for (int s = 0; s < kChunk / kNW; ++s) {
     const int k = s * kNW + wave;
@@ -182,7 +214,22 @@ __device__ __forceinline__ void bwd_chunk(const BwdParams& p, float* lds, int64_
     actDl[k * kWave + lane] = dl;
     actGy[k * kWave + lane] = gy * amask;
   }
+  {
+    // 256 threads, 4 values each: step tid / 8, B (parts 0-3) or C (4-7)
+    const int tid = wave * kWave + int(lane);
+    const int k = tid / 8, part = tid % 8;
+    int32_t tr = t0 + k;
+    tr = tr < t1 ? tr : t1 - 1;
+    const In* src = static_cast<const In*>(part < 4 ? p.Brow : p.Crow) + (row0 + tr) * kMaxState +
+                    4 * (part % 4);
+    *reinterpret_cast<float4*>(rows + k * 2 * kMaxState + 4 * part) = unpack4(load_raw4(src));
+  }
   __syncthreads();
+  // this wave's 4 states of the B (m = 0) or C (m = 1) row of step kk
+  auto row_of = [&](int kk, int m) -> float4 {
+    return *reinterpret_cast<const float4*>(rows + kk * 2 * kMaxState + m * kMaxState + n0);
+  };
+
 
   // ---- phase A2: forward over the chunk, one checkpoint per block
   float h[kNS];
@@ -206,8 +253,8 @@ __device__ __forceinline__ void bwd_chunk(const BwdParams& p, float* lds, int64_
       const int32_t tr = t < t1 ? t : t1 - 1;
       const float dl = actDl[kk * kWave + lane];
       const float uf = ld<In>(p.u, ibase + int64_t(tr) * D);
-      float Bv[kNS];
-      row4<In>(p.Brow, row0 + tr, n0, Bv);
+      const float4 B4 = row_of(kk, 0);
+      const float Bv[kNS] = {B4.x, B4.y, B4.z, B4.w};
 #pragma unroll
       for (int j = 0; j < kNS; ++j) {
         const float a = hw_exp2(dl * A[j]);
@@ -237,14 +284,17 @@ __device__ __forceinline__ void bwd_chunk(const BwdParams& p, float* lds, int64_
 #pragma unroll
   for (int j = 0; j < kNS; ++j) dA[j] = 0.0f;
   float dDacc = 0.0f, dbacc = 0.0f;
+  // the value a lane holds after a reduce-scatter of [4 steps][4 states]
+  const int rk = int(lane >> 4), rj = int((lane >> 2) & 3u);
+  const bool rwrite = (lane & 3u) == 0 && n0 + rj < N;
 
 #pragma unroll
   for (int jb = kNB - 1; jb >= 0; --jb) {
     if (t0 + jb * kKB >= t1) continue;          // wave-uniform: block past the end
-    float uf[kKB], dl[kKB], gy[kKB];
-    float as[kKB][kNS], hs[kKB][kNS], yp[kKB];
-    float Bs[kKB][kNS], Cs[kKB][kNS];
-    // recompute the block
+    float uf[kKB], dl[kKB], gy[kKB], yp[kKB];
+    float hs[kKB][kNS];
+    float red[kKB * kNS];
+    // recompute the block; dC = gy h
 #pragma unroll
     for (int j = 0; j < kNS; ++j) h[j] = ck[jb][j];
 #pragma unroll
@@ -255,8 +305,8 @@ __device__ __forceinline__ void bwd_chunk(const BwdParams& p, float* lds, int64_
       dl[k] = actDl[kk * kWave + lane];
       gy[k] = actGy[kk * kWave + lane];
       uf[k] = ld<In>(p.u, ibase + int64_t(tr) * D) * amask;
-      row4<In>(p.Brow, row0 + tr, n0, Bs[k]);
-      row4<In>(p.Crow, row0 + tr, n0, Cs[k]);
+      const float4 B4 = row_of(kk, 0), C4 = row_of(kk, 1);
+      const float Bv[kNS] = {B4.x, B4.y, B4.z, B4.w}, Cv[kNS] = {C4.x, C4.y, C4.z, C4.w};
       float y0 = 0.0f;
 #pragma unroll
       for (int j = 0; j < kNS; ++j) {
@@ -268,25 +318,32 @@ __device__ __forceinline__ void bwd_chunk(const BwdParams& p, float* lds, int64_
           coef = __builtin_fmaf(a, iA[j], -iA[j]);
           if (SAFE) coef = __builtin_fmaf(dl[k] * kLn2, zm[j], coef);
         }
-        h[j] = __builtin_fmaf(a, h[j], coef * (Bs[k][j] * uf[k]));
-        as[k][j] = a;
+        h[j] = __builtin_fmaf(a, h[j], coef * (Bv[j] * uf[k]));
         hs[k][j] = h[j];
-        y0 = __builtin_fmaf(Cs[k][j], h[j], y0);
+        y0 = __builtin_fmaf(Cv[j], h[j], y0);
+        red[k * kNS + j] = gy[k] * h[j];                       // dC
       }
       yp[k] = y0;
     }
+    {
+      const float r = reduce_scatter16(red, lane);
+      const int32_t t = t0 + jb * kKB + rk;
+      if (rwrite && t < t1) p.pC[((row0 + t) * p.ndblk + dblk) * N + n0 + rj] = r;
+    }
     // reverse sweep
     float dup[kKB], ddp[kKB];
-    float red[64];   // [which: dB, dC][8 steps][4 states]
 #pragma unroll
     for (int k = kKB - 1; k >= 0; --k) {
+      const int kk = jb * kKB + k;
+      const float4 B4 = row_of(kk, 0), C4 = row_of(kk, 1);
+      const float Bv[kNS] = {B4.x, B4.y, B4.z, B4.w}, Cv[kNS] = {C4.x, C4.y, C4.z, C4.w};
       const float dtn = dl[k] * kLn2;           // dt
       float du0 = 0.0f, dd0 = 0.0f;
 #pragma unroll
       for (int j = 0; j < kNS; ++j) {
-        const float a = as[k][j];
+        const float a = hw_exp2(dl[k] * A[j]);     // same value as in the recompute
         const float hp = k > 0 ? hs[k - 1][j] : ck[jb][j];
-        const float lam = __builtin_fmaf(gy[k], Cs[k][j], nu[j]);   // d loss / d h_t
+        const float lam = __builtin_fmaf(gy[k], Cv[j], nu[j]);   // d loss / d h_t
         float coef;
         if (DISC == kEuler) {
           coef = dtn;
@@ -295,10 +352,9 @@ __device__ __forceinline__ void bwd_chunk(const BwdParams& p, float* lds, int64_
           if (SAFE) coef = __builtin_fmaf(dtn, zm[j], coef);
         }
         const float pu = lam * uf[k];                 // d loss / d (coef B)
-        const float q = pu * Bs[k][j];                // d loss / d coef
+        const float q = pu * Bv[j];                   // d loss / d coef
         red[k * kNS + j] = pu * coef;                 // dB
-        red[32 + k * kNS + j] = gy[k] * hs[k][j];     // dC
-        du0 = __builtin_fmaf(lam, coef * Bs[k][j], du0);
+        du0 = __builtin_fmaf(lam, coef * Bv[j], du0);
         const float da = lam * hp;                    // d loss / d A_bar
         if (DISC == kEuler) {
           dd0 = __builtin_fmaf(da * a, A[j], dd0 + q);
@@ -314,27 +370,22 @@ __device__ __forceinline__ void bwd_chunk(const BwdParams& p, float* lds, int64_
       dup[k] = du0;
       ddp[k] = dd0;
     }
-    // per-step partials of this wave -> LDS; dB, dC over the 64 channels
+    {
+      const float r = reduce_scatter16(red, lane);
+      const int32_t t = t0 + jb * kKB + rk;
+      if (rwrite && t < t1) p.pB[((row0 + t) * p.ndblk + dblk) * N + n0 + rj] = r;
+    }
+    // per-step partials of this wave -> LDS
 #pragma unroll
     for (int k = 0; k < kKB; ++k) {
       xch[((wave * 3 + 0) * kKB + k) * kWave + lane] = dup[k];
       xch[((wave * 3 + 1) * kKB + k) * kWave + lane] = ddp[k];
       xch[((wave * 3 + 2) * kKB + k) * kWave + lane] = yp[k];
     }
-    {
-      const float r = reduce_scatter64(red, lane);
-      const int which = int(lane >> 5), k = int((lane >> 2) & 7u), j = int(lane & 3u);
-      const int32_t t = t0 + jb * kKB + k;
-      if (t < t1 && n0 + j < N) {
-        float* dst = which ? p.pC : p.pB;
-        dst[((row0 + t) * p.ndblk + dblk) * N + n0 + j] = r;
-      }
-    }
     __syncthreads();
-    // outputs of the steps this wave owns: k % 4 == wave
-#pragma unroll
-    for (int s = 0; s < kKB / kNW; ++s) {
-      const int k = s * kNW + wave;
+    // output of the step this wave owns (k = wave)
+    {
+      const int k = wave;
       const int32_t t = t0 + jb * kKB + k;
       float sdu = 0.0f, sdd = 0.0f, sy = 0.0f;
 #pragma unroll
@@ -396,11 +447,11 @@ __device__ __forceinline__ void bwd_chunk(const BwdParams& p, float* lds, int64_
   }
 }
 
-constexpr int kLdsFloats = 2 * kChunk * kWave + kNW * 3 * kKB * kWave;
-
+// two waves per SIMD: at most 256 VGPRs
 template <typename In, int DISC, bool HAS_Z, bool SOFTPLUS>
-__global__ __launch_bounds__(kWave * kNW) void bwd_kernel(BwdParams p) {
-  __shared__ float lds[kLdsFloats];
+__global__ __launch_bounds__(kWave * kNW, 2) void bwd_kernel(BwdParams p) {
+  __shared__ float4 lds4[kLdsFloats / 4];
+  float* lds = reinterpret_cast<float*>(lds4);
   const int wave = __builtin_amdgcn_readfirstlane(int(threadIdx.x) / kWave);
   const uint32_t lane = threadIdx.x % kWave;
   int64_t bid = blockIdx.x;
@@ -520,30 +571,52 @@ __global__ __launch_bounds__(256) void reduce_rows_kernel(const float* __restric
   dC[gid] = sc;
 }
 
-__global__ __launch_bounds__(256) void reduce_chan_kernel(const float* __restrict__ pA,
-                                                          const float* __restrict__ pD,
-                                                          const float* __restrict__ pbias,
-                                                          float* __restrict__ dA,
-                                                          float* __restrict__ dD,
-                                                          float* __restrict__ dbias, int64_t B,
-                                                          int64_t D, int N, int nchunks) {
-  const int64_t gid = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (gid >= D * (N + 1)) return;
-  const int64_t d = gid % D;
-  const int n = int(gid / D);       // n == N: the per-channel vectors
+// dA (D, N), dD_skip and ddelta_bias (D): sums over (batch row, chunk) of the
+// per-chunk partials.  A workgroup takes 64 columns (column = n * D + d; n == N
+// holds the two per-channel vectors) and splits the terms over 4 thread
+// groups, each with 4 interleaved running sums, so 16 loads per column are in
+// flight.  Every addition happens in a fixed order: the result is deterministic.
+constexpr int kRedCols = 64, kRedGroups = 4;
+__global__ __launch_bounds__(kRedCols * kRedGroups) void reduce_chan_kernel(
+    const float* __restrict__ pA, const float* __restrict__ pD, const float* __restrict__ pbias,
+    float* __restrict__ dA, float* __restrict__ dD, float* __restrict__ dbias, int64_t B,
+    int64_t D, int N, int nchunks) {
+  __shared__ float part[2][kRedGroups][kRedCols];
+  const int c = int(threadIdx.x) % kRedCols, g = int(threadIdx.x) / kRedCols;
+  const int64_t col = int64_t(blockIdx.x) * kRedCols + c;
+  const bool valid = col < D * (N + 1);
+  const int64_t d = valid ? col % D : 0;
+  const int n = valid ? int(col / D) : 0;
   const int64_t terms = B * nchunks;
-  if (n < N) {
-    float s = 0.0f;
-    for (int64_t k = 0; k < terms; ++k) s += pA[(k * N + n) * D + d];
-    dA[d * N + n] = s;
-  } else {
-    float sD = 0.0f, sb = 0.0f;
-    for (int64_t k = 0; k < terms; ++k) {
-      sD += pD[k * D + d];
-      sb += pbias[k * D + d];
+  auto sum = [&](const float* x, int64_t stride) {
+    float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    int64_t k = g;
+    for (; k + 3 * kRedGroups < terms; k += 4 * kRedGroups) {
+#pragma unroll
+      for (int m = 0; m < 4; ++m) acc[m] += x[(k + m * kRedGroups) * stride];
     }
-    if (dD) dD[d] = sD;
-    if (dbias) dbias[d] = sb;
+    for (int m = 0; k < terms; k += kRedGroups, ++m) acc[m] += x[k * stride];
+    return (acc[0] + acc[1]) + (acc[2] + acc[3]);
+  };
+  float s0 = 0.0f, s1 = 0.0f;
+  if (valid) {
+    if (n < N) {
+      s0 = sum(pA + int64_t(n) * D + d, int64_t(N) * D);
+    } else {
+      s0 = sum(pD + d, D);
+      s1 = sum(pbias + d, D);
+    }
+  }
+  part[0][g][c] = s0;
+  part[1][g][c] = s1;
+  __syncthreads();
+  if (g != 0 || !valid) return;
+  const float t0 = (part[0][0][c] + part[0][1][c]) + (part[0][2][c] + part[0][3][c]);
+  if (n < N) {
+    dA[d * N + n] = t0;
+  } else {
+    if (dD) dD[d] = t0;
+    if (dbias) dbias[d] = (part[1][0][c] + part[1][1][c]) + (part[1][2][c] + part[1][3][c]);
   }
 }
 
@@ -631,9 +704,10 @@ int launch_bwd(const ss_desc_t& d, const BwdPlan& plan, const BwdArgs& a, void* 
                      0, st, p.pB, p.pC, a.dB, a.dC, rows, ndblk, int(d.dstate));
   e = hipGetLastError();
   if (e != hipSuccess) return int(e);
-  hipLaunchKernelGGL(reduce_chan_kernel, dim3(unsigned((d.dim * (d.dstate + 1) + 255) / 256)),
-                     dim3(256), 0, st, p.pA, p.pD, p.pbias, a.dA, a.dDskip, a.dbias, d.batch,
-                     d.dim, int(d.dstate), nc);
+  hipLaunchKernelGGL(reduce_chan_kernel,
+                     dim3(unsigned((d.dim * (d.dstate + 1) + kRedCols - 1) / kRedCols)),
+                     dim3(kRedCols * kRedGroups), 0, st, p.pA, p.pD, p.pbias, a.dA, a.dDskip,
+                     a.dbias, d.batch, d.dim, int(d.dstate), nc);
   return int(hipGetLastError());
 }
 
