@@ -187,8 +187,10 @@ def test_fwd_full_size_sampled(oracle, name):
 # ------------------------------------------------------------------ decode step
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("disc", ["zoh", "euler"])
-def test_step_parity(oracle, dtype, disc):
-    inp = synth.make_inputs(3, 1, 200, 16, seed=9, dtype=dtype, with_h0=True, a_mode="mixed")
+@pytest.mark.parametrize("N", [16, 5, 13])
+def test_step_parity(oracle, dtype, disc, N):
+    log("step case", dtype, disc, N)
+    inp = synth.make_inputs(3, 1, 200, N, seed=9, dtype=dtype, with_h0=True, a_mode="mixed")
     d = upload(inp)
     h = d["h0"].clone()
     y = B.scan_step(h, d["u"][:, 0].contiguous(), d["delta"][:, 0].contiguous(), d["A"],
@@ -200,6 +202,45 @@ def test_step_parity(oracle, dtype, disc):
                                disc=disc)
     check_f32(y.cpu().numpy(), ref_y, "step y")
     check_f32(h.cpu().numpy(), ref_h, "step h")
+
+
+def test_step_graph_replay():
+    """A decode loop of 4 steps captured in a graph: every replay (state reset by
+    an eager copy between replays) equals the eager loop bit for bit."""
+    inp = synth.make_inputs(2, 4, 192, 16, seed=12, dtype="bf16", with_h0=True, a_mode="random")
+    d = upload(inp)
+    steps = [{k: d[k][:, t].contiguous() for k in ("u", "delta", "B", "C", "z")} for t in range(4)]
+    desc = B.make_desc(2, 1, 192, 16, B.SS_BF16, B.SS_F32, B.SS_ZOH, True)
+    ys = [torch.empty(2, 192, device="cuda") for _ in range(4)]
+
+    def loop(h):
+        for t, s in enumerate(steps):
+            rc = B.ss_scan_step(desc, h, s["u"], s["delta"], d["A"], s["B"], s["C"], d["D"],
+                                d["delta_bias"], s["z"], ys[t])
+            assert rc == 0
+
+    h_eager = d["h0"].clone()
+    loop(h_eager)
+    torch.cuda.synchronize()
+    y_eager = [y.clone() for y in ys]
+    h = d["h0"].clone()
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        loop(h)                                   # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        loop(h)
+    for rep in range(3):
+        h.copy_(d["h0"])
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(h, h_eager), rep
+        for t in range(4):
+            assert torch.equal(ys[t], y_eager[t]), (rep, t)
 
 
 def test_step_continues_forward():
