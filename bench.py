@@ -150,6 +150,9 @@ def main():
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device copy (counter calibration)")
+    ap.add_argument("--only", choices=["bwd", "step"],
+                    help="only time the backward (Mamba-130M shape) or the decode step and "
+                         "print their figures (for profiling runs)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: the selective scan needs no communication "
@@ -165,6 +168,12 @@ def main():
     from selective_state_space_69_amd import synth
 
     Bnd.load_library()
+    if args.only == "bwd":
+        print(json.dumps(time_bwd(torch, Bnd, synth, args.steps, args.warmup)), flush=True)
+        return
+    if args.only == "step":
+        print(json.dumps(time_step(torch, Bnd, synth)), flush=True)
+        return
     w = synth.WORKLOADS[args.workload]
     inp = synth.make_workload(w.name, with_dy=False)
     d = upload(inp, torch)
@@ -243,44 +252,49 @@ def extras(torch, Bnd, synth, args):
                      "chunks": "workspace %d B" % nb}
         del d, y, ws, inp
         torch.cuda.empty_cache()
-    # backward
+    out.update(time_bwd(torch, Bnd, synth, steps, warm))
+    out.update(time_step(torch, Bnd, synth))
+    return out
+
+
+def time_bwd(torch, Bnd, synth, steps, warm):
+    """Backward (row a9) at the Mamba-130M shape, both discretisations."""
+    out = {}
     w = synth.WORKLOADS["bwd_130m_bf16_b8_l2048_d1536"]
     inp = synth.make_workload(w.name, with_dy=True)
     d = upload(inp, torch)
     for disc in ("euler", "zoh"):
-        try:
-            g = Bnd.scan_bwd(d["u"], d["delta"], d["A"], d["B"], d["C"], d["dy"], D=d["D"],
-                             delta_bias=d["delta_bias"], z=d["z"], disc=disc)
-            f = lambda: Bnd.scan_bwd(d["u"], d["delta"], d["A"], d["B"], d["C"], d["dy"],  # noqa
-                                     D=d["D"], delta_bias=d["delta_bias"], z=d["z"], disc=disc)
-            total, per, mn, _ = time_calls(f, steps, warm, torch)
-            bld, bln = w.B * w.L * w.D, w.B * w.L * w.N
-            alg = bld * (4 * 2 + 3 * 4) + bln * (2 * 2 + 2 * 4) + w.D * (2 * w.N + 4) * 4
-            out["bwd_130m:" + disc] = {"ms": round(per, 4),
-                                       "elements_per_s": w.elements / (per * 1e-3),
-                                       "hbm_gbs": round(alg / (per * 1e-3) / 1e9, 1)}
-            del g
-        except Exception as e:  # backward not available in this build
-            out["bwd_130m:" + disc] = {"error": str(e)}
+        f = lambda: Bnd.scan_bwd(d["u"], d["delta"], d["A"], d["B"], d["C"], d["dy"],  # noqa
+                                 D=d["D"], delta_bias=d["delta_bias"], z=d["z"], disc=disc)
+        total, per, mn, _ = time_calls(f, steps, warm, torch)
+        bld, bln = w.B * w.L * w.D, w.B * w.L * w.N
+        alg = bld * (4 * 2 + 3 * 4) + bln * (2 * 2 + 2 * 4) + w.D * (2 * w.N + 4) * 4
+        out["bwd_130m:" + disc] = {"ms": round(per, 4), "elements_per_s": w.elements / (per * 1e-3),
+                                   "hbm_gbs": round(alg / (per * 1e-3) / 1e9, 1)}
     del d, inp
     torch.cuda.empty_cache()
-    # decode step at the Mamba-2.8B width
+    return out
+
+
+def time_step(torch, Bnd, synth):
+    """Decode step (row a10) at the Mamba-2.8B width: a 100-step decode loop
+    captured in one graph, so the figure is GPU time per step without the host's
+    per-launch cost."""
     Bt, D, N = 8, 5120, 16
     inp = synth.make_inputs(Bt, 1, D, N, seed=77, dtype="bf16", with_h0=True)
     d = upload(inp, torch)
     h = torch.from_numpy(inp.h0).cuda()
-    args1 = [d[k][:, 0].contiguous() for k in ("u", "delta")]
+    u1, dl1 = (d[k][:, 0].contiguous() for k in ("u", "delta"))
     Bc, Cc, zc = (d[k][:, 0].contiguous() for k in ("B", "C", "z"))
     y1 = torch.empty(Bt, D, dtype=torch.float32, device="cuda")
     sdesc = Bnd.make_desc(Bt, 1, D, N, Bnd.SS_BF16, Bnd.SS_F32, Bnd.SS_ZOH, True)
 
     def steps(k):
         for _ in range(k):
-            Bnd.ss_scan_step(sdesc, h, args1[0], args1[1], d["A"], Bc, Cc, d["D"],
-                             d["delta_bias"], zc, y1)
+            rc = Bnd.ss_scan_step(sdesc, h, u1, dl1, d["A"], Bc, Cc, d["D"], d["delta_bias"], zc, y1)
+            if rc != 0:
+                raise RuntimeError(Bnd.ss_scan_strerror(rc))
 
-    # a decode loop of 100 steps captured in a graph: GPU time per step without
-    # the host's per-launch cost
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
@@ -291,11 +305,10 @@ def extras(torch, Bnd, synth, args):
         steps(100)
     total, per, mn, _ = time_calls(g.replay, 10, 2, torch)
     sbytes = Bt * D * N * 4 * 2
-    out["step_b8_d5120"] = {"us_per_step": round(per * 10, 3), "state_bytes": sbytes,
-                            "state_gbs": round(sbytes / (per * 1e-5) / 1e9, 1),
-                            "how": "100 steps captured in one graph, 10 replays"}
     del g
-    return out
+    return {"step_b8_d5120": {"us_per_step": round(per * 10, 3), "state_bytes": sbytes,
+                              "state_gbs": round(sbytes / (per * 1e-5) / 1e9, 1),
+                              "how": "100 steps captured in one graph, 10 replays"}}
 
 
 if __name__ == "__main__":
