@@ -6,7 +6,7 @@
 // chunks of 32 steps.  Per chunk:
 //   - its start state comes from the forward's summary pass + carry scan;
 //   - the adjoint carry entering it from its end comes from a reverse summary
-//     pass + reverse carry scan (the adjoint recurrence
+//     pass + reverse carry scan (ss_carry.hip; the adjoint recurrence
 //     lambda_t = gy_t C_t + A_bar_{t+1} lambda_{t+1} is the same linear scan run
 //     backwards in time);
 //   - a workgroup of 4 waves (lane = channel d, 4 states per wave) stages the
@@ -524,32 +524,6 @@ __global__ __launch_bounds__(kWave) void rev_summary_kernel(BwdParams p) {
     if (n < N) ls[int64_t(n) * D] = nu[n];
 }
 
-// Adjoint carries, last chunk to first, one lane per (b, n, d): slot c of lam
-// becomes the adjoint entering chunk c from its end:
-//   nu_end(nc-1) = 0,  nu_end(c-1) = P_c nu_end(c) + R_c,  P_c = exp2(A sum_c dt log2 e).
-__global__ __launch_bounds__(256) void rev_carry_kernel(float* __restrict__ lam,
-                                                        const float* __restrict__ dsum,
-                                                        const float* __restrict__ A, int64_t B,
-                                                        int64_t D, int N, int nchunks) {
-  const int64_t gid = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (gid >= B * N * D) return;
-  const int64_t d = gid % D;
-  const int n = int((gid / D) % N);
-  const int64_t b = gid / (D * N);
-  const float a = A[d * N + n];
-  const int64_t sstride = int64_t(N) * D;
-  float* ls = lam + (b * nchunks) * sstride + int64_t(n) * D + d;
-  const float* ds = dsum + (b * nchunks) * D + d;
-  float carry = ls[(nchunks - 1) * sstride];     // R of the last chunk
-  ls[(nchunks - 1) * sstride] = 0.0f;
-  for (int c = nchunks - 2; c >= 1; --c) {
-    const float R = ls[c * sstride];
-    ls[c * sstride] = carry;
-    carry = __builtin_fmaf(hw_exp2(a * ds[c * D]), carry, R);
-  }
-  ls[0] = carry;
-}
-
 // ---------------------------------------------------------------- reductions
 __global__ __launch_bounds__(256) void reduce_rows_kernel(const float* __restrict__ pB,
                                                           const float* __restrict__ pC,
@@ -690,11 +664,9 @@ int launch_bwd(const ss_desc_t& d, const BwdPlan& plan, const BwdArgs& a, void* 
     e = d.in_dtype == SS_BF16 ? dispatch_bwd<uint16_t>(d, p, true, cols * (nc - 1), st)
                               : dispatch_bwd<float>(d, p, true, cols * (nc - 1), st);
     if (e != hipSuccess) return int(e);
-    const int64_t total = d.batch * d.dstate * d.dim;
-    hipLaunchKernelGGL(rev_carry_kernel, dim3(unsigned((total + 255) / 256)), dim3(256), 0, st,
-                       lam, dsum, a.A, d.batch, d.dim, int(d.dstate), nc);
-    e = hipGetLastError();
-    if (e != hipSuccess) return int(e);
+    const int ec = launch_chunk_carry(lam, dsum, a.A, nullptr, d.batch, d.dim, int(d.dstate), nc,
+                                      true, stream);
+    if (ec != 0) return ec;
   }
   e = d.in_dtype == SS_BF16 ? dispatch_bwd<uint16_t>(d, p, false, cols * nc, st)
                             : dispatch_bwd<float>(d, p, false, cols * nc, st);

@@ -426,48 +426,6 @@ __global__ __launch_bounds__(256) void pack_rows_kernel(const In* __restrict__ B
   Cp[gid] = n < N ? Cm[r * N + n] : In(0);
 }
 
-// Carry scan over chunks, one lane per (b, n, d).  In place on hend: slot c of
-// a chunk summary becomes the start state of chunk c (slot 0 is unused: chunk 0
-// starts from h0).  The decay of chunk c is exp2(A * sum of dt*log2e).
-__global__ __launch_bounds__(256) void carry_scan_kernel(float* __restrict__ hend,
-                                                         const float* __restrict__ dsum,
-                                                         const float* __restrict__ A,
-                                                         const float* __restrict__ h0,
-                                                         int64_t B, int64_t D, int N, int nchunks) {
-  const int64_t gid = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
-  const int64_t total = B * N * D;
-  if (gid >= total) return;
-  const int64_t d = gid % D;
-  const int n = int((gid / D) % N);
-  const int64_t b = gid / (D * N);
-  const float a = A[d * N + n];
-  float carry = h0 ? h0[(b * D + d) * N + n] : 0.0f;
-  const int64_t sstride = int64_t(N) * D;
-  float* hs = hend + (b * nchunks) * sstride + int64_t(n) * D + d;
-  const float* ds = dsum + (b * nchunks) * D + d;
-  int c = 0;
-  for (; c + 4 <= nchunks - 1; c += 4) {
-    float S[4], P[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      S[k] = hs[(c + k) * sstride];
-      P[k] = hw_exp2(a * ds[(c + k) * D]);
-    }
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      if (c + k >= 1) hs[(c + k) * sstride] = carry;
-      carry = __builtin_fmaf(P[k], carry, S[k]);
-    }
-  }
-  for (; c < nchunks - 1; ++c) {
-    const float S = hs[c * sstride];
-    const float P = hw_exp2(a * ds[c * D]);
-    if (c >= 1) hs[c * sstride] = carry;
-    carry = __builtin_fmaf(P, carry, S);
-  }
-  hs[(nchunks - 1) * sstride] = carry;
-}
-
 template <typename In, typename Out, int DISC, bool HAS_Z, bool SOFTPLUS, bool SUMMARY, int NSPLIT>
 hipError_t launch_one(const FwdParams& p, int64_t nblocks, hipStream_t st) {
   hipLaunchKernelGGL((fwd_kernel<In, Out, DISC, HAS_Z, SOFTPLUS, SUMMARY, NSPLIT>),
@@ -565,10 +523,8 @@ int launch_fwd_carries(const ss_desc_t& d, const TimePlan& tp, const FwdArgs& a,
                      ? launch_fwd_hw(d, p, true, cols * p.grid_chunks, st)
                      : dispatch(d, p, tp.nsplit, true, cols * p.grid_chunks, st);
   if (e != hipSuccess) return int(e);
-  const int64_t total = d.batch * d.dstate * d.dim;
-  hipLaunchKernelGGL(carry_scan_kernel, dim3(unsigned((total + 255) / 256)), dim3(256), 0, st,
-                     a.hend, a.dsum, a.A, a.h0, d.batch, d.dim, int(d.dstate), p.nchunks);
-  return int(hipGetLastError());
+  return launch_chunk_carry(a.hend, a.dsum, a.A, a.h0, d.batch, d.dim, int(d.dstate), p.nchunks,
+                            false, stream);
 }
 
 int launch_fwd(const ss_desc_t& d, const FwdPlan& plan, const FwdArgs& args, void* stream) {

@@ -122,6 +122,11 @@ int launch_pack_rows(const ss_desc_t& d, const void* Bm, const void* Cm, void* B
 // a.hend / a.dsum; a.Brow / a.Crow must hold the 16-wide rows.
 int launch_fwd_carries(const ss_desc_t& d, const TimePlan& tp, const FwdArgs& a, void* stream);
 int launch_bwd(const ss_desc_t& d, const BwdPlan& p, const BwdArgs& a, void* stream);
+// Chunk carries (ss_carry.hip), in place on states (B, nc, N, D): forward turns
+// chunk summaries into chunk start states (h0 may be null), reverse turns local
+// adjoints into the adjoints entering each chunk from its end.
+int launch_chunk_carry(float* states, const float* dsum, const float* A, const float* h0,
+                       int64_t batch, int64_t D, int N, int nc, bool reverse, void* stream);
 int launch_step(const ss_desc_t& d, const StepArgs& a, void* stream);
 
 }  // namespace ss

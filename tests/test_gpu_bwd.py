@@ -83,6 +83,21 @@ def test_bwd_fp32_parity(oracle, case):
     log("  worst rel err", {k: "%.2e" % v for k, v in worst.items()})
 
 
+@pytest.mark.parametrize("disc", ["zoh", "euler"])
+def test_bwd_many_chunks(oracle, disc):
+    """L = 8230: 258 chunks of 32 steps, so the forward and adjoint carries run
+    as the lane-parallel scan (five 64-chunk tiles, the last one ragged)."""
+    inp = synth.make_inputs(1, 8230, 70, 16, seed=3100, dtype="f32", with_dy=True, with_h0=True,
+                            a_mode="random")
+    d = upload(inp)
+    log("bwd many chunks", disc)
+    g = run_gpu(d, disc)
+    torch.cuda.synchronize()
+    ref = run_oracle(oracle, inp, disc)
+    worst = compare(g, ref, what="many chunks " + disc)
+    log("  worst rel err", {k: "%.2e" % v for k, v in worst.items()})
+
+
 def test_bwd_deterministic():
     inp = synth.make_inputs(2, 300, 200, 16, seed=31, dtype="bf16", with_dy=True)
     d = upload(inp)

@@ -122,6 +122,25 @@ def test_chunked_equals_sequential(monkeypatch):
         assert float((h1 - h2).abs().max()) <= 1e-4 * float(h1.abs().max()), chunk
 
 
+@pytest.mark.parametrize("chunk", ["16", "40"])
+def test_fwd_many_chunks(oracle, monkeypatch, chunk):
+    """Enough chunks (>= 256) that the chunk carries run as the lane-parallel
+    scan, over several 64-chunk tiles with a ragged last tile.  A is the
+    workloads' -(n+1): with A = -exp(N(0,1)) some |dt A| fall near 1e-4, where
+    the fp32 (exp(dt A) - 1) / A alone errs by ~1e-3 relative and, over 10^4
+    steps, the one-pass kernel already exceeds the elementwise fp32 bound."""
+    monkeypatch.setenv("SS_SCAN_CHUNK", chunk)
+    inp = synth.make_inputs(2, 10250, 40, 16, seed=14, dtype="f32", with_h0=True,
+                            a_mode="s4d_real")
+    d = upload(inp)
+    log("many chunks", chunk)
+    y, hl = gpu_fwd(d, "zoh", return_last_state=True)
+    torch.cuda.synchronize()
+    ref, href = _full_oracle(oracle, inp, "zoh")
+    check_f32(y.cpu().numpy(), ref, "y")
+    check_f32(hl.cpu().numpy(), href, "h_last")
+
+
 def test_fwd_deterministic():
     inp = synth.make_inputs(4, 512, 320, 16, seed=6, dtype="bf16")
     d = upload(inp)
