@@ -263,3 +263,103 @@ int oracle_step(int64_t Bt, int64_t D, int64_t N, int disc, int softplus,
   }
   return 0;
 }
+
+/*
+ * Causal depthwise convolution of width K along time, then SiLU: the step that
+ * turns the expanded input x into the scan's u (Gu & Dao wiki note, "Mamba
+ * architecture": Linear(expand) -> Conv1d -> SiLU -> SSM; "A Visual Guide to
+ * Mamba" summary, "Mamba block": a convolution before the selective SSM so
+ * that tokens are not processed independently).
+ * Readings: one filter per channel (depthwise: the scan is per channel), causal
+ * (output t sees inputs t-K+1 .. t, zero before t = 0), width 1 <= K <= 4, an
+ * optional per-channel bias; silu = 0 leaves the activation out.
+ *   pre[b,t,d] = bias[d] + sum_k w[d,k] x[b, t-K+1+k, d]
+ *   u[b,t,d]   = pre * sigma(pre)   (or pre)
+ * x, u: (Bt, L, D); w: (D, K); bias: (D) or NULL.
+ */
+static double conv_pre(const double* x, const double* w, const double* bias, int64_t L, int64_t D,
+                       int64_t K, int64_t b, int64_t t, int64_t d) {
+  double s = bias ? bias[d] : 0.0;
+  for (int64_t k = 0; k < K; ++k) {
+    int64_t tt = t - K + 1 + k;
+    if (tt >= 0) s += w[d * K + k] * x[(b * L + tt) * D + d];
+  }
+  return s;
+}
+
+int oracle_conv1d_fwd(int64_t Bt, int64_t L, int64_t D, int64_t K, int silu, const double* x,
+                      const double* w, const double* bias, double* u) {
+  if (Bt < 0 || L < 0 || D < 0 || K < 1) return -1;
+  for (int64_t b = 0; b < Bt; ++b)
+    for (int64_t t = 0; t < L; ++t)
+      for (int64_t d = 0; d < D; ++d) {
+        double p = conv_pre(x, w, bias, L, D, K, b, t, d);
+        u[(b * L + t) * D + d] = silu ? p * sigmoid(p) : p;
+      }
+  return 0;
+}
+
+/*
+ * Backward of the above by the chain rule.  Given g = dLoss/du:
+ *   gp[b,t,d] = g * d silu(p)/dp = g * s (1 + p (1 - s)),  s = sigma(p)  (or g)
+ *   dx[b,t,d] = sum_k w[d,k] gp[b, t+K-1-k, d]   (terms past L - 1 are 0)
+ *   dw[d,k]   = sum_{b,t} gp[b,t,d] x[b, t-K+1+k, d]
+ *   dbias[d]  = sum_{b,t} gp[b,t,d]
+ * dw and dbias are written (not accumulated into); dbias may be NULL.
+ */
+int oracle_conv1d_bwd(int64_t Bt, int64_t L, int64_t D, int64_t K, int silu, const double* x,
+                      const double* w, const double* bias, const double* g, double* dx,
+                      double* dw, double* dbias) {
+  if (Bt < 0 || L < 0 || D < 0 || K < 1) return -1;
+  double* gp = (double*)malloc(sizeof(double) * (size_t)(Bt * L * D > 0 ? Bt * L * D : 1));
+  if (!gp) return -2;
+  for (int64_t b = 0; b < Bt; ++b)
+    for (int64_t t = 0; t < L; ++t)
+      for (int64_t d = 0; d < D; ++d) {
+        int64_t i = (b * L + t) * D + d;
+        double p = conv_pre(x, w, bias, L, D, K, b, t, d);
+        double s = sigmoid(p);
+        gp[i] = silu ? g[i] * s * (1.0 + p * (1.0 - s)) : g[i];
+      }
+  for (int64_t d = 0; d < D; ++d) {
+    for (int64_t k = 0; k < K; ++k) dw[d * K + k] = 0.0;
+    if (dbias) dbias[d] = 0.0;
+  }
+  for (int64_t b = 0; b < Bt; ++b)
+    for (int64_t t = 0; t < L; ++t)
+      for (int64_t d = 0; d < D; ++d) {
+        int64_t i = (b * L + t) * D + d;
+        double acc = 0.0;
+        for (int64_t k = 0; k < K; ++k) {
+          int64_t to = t + K - 1 - k;     /* output step that read x[t] through tap k */
+          if (to < L) acc += w[d * K + k] * gp[(b * L + to) * D + d];
+          int64_t ti = t - K + 1 + k;     /* input step that tap k of output t read */
+          if (ti >= 0) dw[d * K + k] += gp[i] * x[(b * L + ti) * D + d];
+        }
+        dx[i] = acc;
+        if (dbias) dbias[d] += gp[i];
+      }
+  free(gp);
+  return 0;
+}
+
+/*
+ * One decode step of the convolution: state (Bt, D, K-1) holds the last K-1
+ * inputs of each channel, oldest first; x, u: (Bt, D).  The window is
+ * [state, x]; afterwards the state holds its last K-1 entries.
+ */
+int oracle_conv1d_step(int64_t Bt, int64_t D, int64_t K, int silu, double* state,
+                       const double* x, const double* w, const double* bias, double* u) {
+  if (Bt < 0 || D < 0 || K < 1) return -1;
+  for (int64_t b = 0; b < Bt; ++b)
+    for (int64_t d = 0; d < D; ++d) {
+      double* st = state + (b * D + d) * (K - 1);
+      double p = bias ? bias[d] : 0.0;
+      for (int64_t k = 0; k < K - 1; ++k) p += w[d * K + k] * st[k];
+      p += w[d * K + K - 1] * x[b * D + d];
+      for (int64_t k = 0; k + 1 < K - 1; ++k) st[k] = st[k + 1];
+      if (K > 1) st[K - 2] = x[b * D + d];
+      u[b * D + d] = silu ? p * sigmoid(p) : p;
+    }
+  return 0;
+}

@@ -57,6 +57,12 @@ def _load():
         lib.oracle_fwd.restype = I
         lib.oracle_bwd.argtypes = [I64, I64, I64, I64, I, I] + [P] * 19
         lib.oracle_bwd.restype = I
+        lib.oracle_conv1d_fwd.argtypes = [I64, I64, I64, I64, I] + [P] * 4
+        lib.oracle_conv1d_fwd.restype = I
+        lib.oracle_conv1d_bwd.argtypes = [I64, I64, I64, I64, I] + [P] * 7
+        lib.oracle_conv1d_bwd.restype = I
+        lib.oracle_conv1d_step.argtypes = [I64, I64, I64, I] + [P] * 5
+        lib.oracle_conv1d_step.restype = I
         lib.oracle_step.argtypes = [I64, I64, I64, I, I] + [P] * 10
         lib.oracle_step.restype = I
         _lib = lib
@@ -149,3 +155,43 @@ def step(h, u, delta, A, B, C, D=None, delta_bias=None, z=None, disc="zoh", soft
     if rc != 0:
         raise ValueError("oracle_step failed: %d" % rc)
     return out, h
+
+
+# ---------------------------------------------------------------- conv1d + SiLU
+def conv1d_fwd(x, w, bias=None, silu=True):
+    """Causal depthwise conv of width K = w.shape[1] along time, then SiLU.
+    x: (B, L, D); w: (D, K); bias: (D,) or None.  Returns u (B, L, D) float64."""
+    x = _f64(x); w = _f64(w); bias = None if bias is None else _f64(bias)
+    Bt, L, D = x.shape
+    K = w.shape[1]
+    u = np.empty((Bt, L, D))
+    rc = _load().oracle_conv1d_fwd(Bt, L, D, K, int(bool(silu)), _ptr(x), _ptr(w), _ptr(bias),
+                                   _ptr(u))
+    assert rc == 0
+    return u
+
+
+def conv1d_bwd(x, w, g, bias=None, silu=True):
+    """Gradients of sum(g * conv1d_fwd(x, w, bias)): dict dx, dw, dbias."""
+    x = _f64(x); w = _f64(w); g = _f64(g); bias = None if bias is None else _f64(bias)
+    Bt, L, D = x.shape
+    K = w.shape[1]
+    dx = np.empty((Bt, L, D)); dw = np.empty((D, K)); db = np.empty(D)
+    rc = _load().oracle_conv1d_bwd(Bt, L, D, K, int(bool(silu)), _ptr(x), _ptr(w), _ptr(bias),
+                                   _ptr(g), _ptr(dx), _ptr(dw), _ptr(db))
+    assert rc == 0
+    return {"dx": dx, "dw": dw, "dbias": db if bias is not None else None}
+
+
+def conv1d_step(state, x, w, bias=None, silu=True):
+    """One decode step: state (B, D, K-1) (copied, not modified), x (B, D).
+    Returns (u (B, D), new state)."""
+    st = _f64(state).copy(); x = _f64(x); w = _f64(w)
+    bias = None if bias is None else _f64(bias)
+    Bt, D = x.shape
+    K = w.shape[1]
+    u = np.empty((Bt, D))
+    rc = _load().oracle_conv1d_step(Bt, D, K, int(bool(silu)), _ptr(st), _ptr(x), _ptr(w),
+                                    _ptr(bias), _ptr(u))
+    assert rc == 0
+    return u, st
