@@ -150,9 +150,9 @@ def main():
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device copy (counter calibration)")
-    ap.add_argument("--only", choices=["bwd", "step"],
-                    help="only time the backward (Mamba-130M shape) or the decode step and "
-                         "print their figures (for profiling runs)")
+    ap.add_argument("--only", choices=["bwd", "step", "conv"],
+                    help="only time the backward (Mamba-130M shape), the decode step or the "
+                         "Conv1d + SiLU and print their figures (for profiling runs)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: the selective scan needs no communication "
@@ -173,6 +173,9 @@ def main():
         return
     if args.only == "step":
         print(json.dumps(time_step(torch, Bnd, synth)), flush=True)
+        return
+    if args.only == "conv":
+        print(json.dumps(time_conv(torch, Bnd, synth, args.steps, args.warmup)), flush=True)
         return
     w = synth.WORKLOADS[args.workload]
     inp = synth.make_workload(w.name, with_dy=False)
@@ -254,6 +257,47 @@ def extras(torch, Bnd, synth, args):
         torch.cuda.empty_cache()
     out.update(time_bwd(torch, Bnd, synth, steps, warm))
     out.update(time_step(torch, Bnd, synth))
+    out.update(time_conv(torch, Bnd, synth, steps, warm))
+    return out
+
+
+def time_conv(torch, Bnd, synth, steps, warm):
+    """Causal depthwise Conv1d (width 4) + SiLU at the Mamba-2.8B shape (B=8,
+    L=2048, D=5120): forward bf16 -> bf16, backward (fp32 du and dx), and the
+    decode step.  HBM-bound: reported against the algorithmic bytes."""
+    import numpy as np
+    Bt, L, D, K = 8, 2048, 5120, 4
+    rng = np.random.default_rng(1002)
+    x = torch.from_numpy(synth.round_to_bf16(rng.standard_normal((Bt, L, D)).astype(np.float32)))
+    x = x.to("cuda").to(torch.bfloat16)
+    w = torch.from_numpy((rng.standard_normal((D, K)) * 0.5).astype(np.float32)).cuda()
+    b = torch.from_numpy((rng.standard_normal(D) * 0.3).astype(np.float32)).cuda()
+    du = torch.randn((Bt, L, D), device="cuda")
+    u = torch.empty_like(x)
+    desc = Bnd.make_conv_desc(Bt, L, D, K, Bnd.SS_BF16, Bnd.SS_BF16, True)
+    f = lambda: Bnd.ss_conv1d_fwd(desc, x, w, b, u)  # noqa
+    total, per, mn, _ = time_calls(f, steps, warm, torch)
+    n = Bt * L * D
+    alg_f = n * (2 + 2) + D * (K + 1) * 4
+    out = {"conv1d_fwd_b8_l2048_d5120": {"ms": round(per, 4), "ms_min": round(mn, 4),
+                                          "hbm_gbs": round(alg_f / (per * 1e-3) / 1e9, 1),
+                                          "hbm_frac": round(alg_f / (per * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                                          "algorithmic_bytes": alg_f}}
+    dx = torch.empty((Bt, L, D), device="cuda")
+    dw = torch.empty((D, K), device="cuda")
+    db = torch.empty(D, device="cuda")
+    bdesc = Bnd.make_conv_desc(Bt, L, D, K, Bnd.SS_BF16, Bnd.SS_F32, True)
+    nb = Bnd.ss_conv1d_workspace_bytes(bdesc)
+    ws = Bnd.workspace(nb, "cuda")
+    f = lambda: Bnd.ss_conv1d_bwd(bdesc, x, w, b, du, dx, dw, db, ws, nb)  # noqa
+    total, per, mn, _ = time_calls(f, steps, warm, torch)
+    alg_b = n * (2 + 4 + 4) + D * (K + 1) * 4 * 2
+    out["conv1d_bwd_b8_l2048_d5120"] = {"ms": round(per, 4), "ms_min": round(mn, 4),
+                                         "hbm_gbs": round(alg_b / (per * 1e-3) / 1e9, 1),
+                                         "hbm_frac": round(alg_b / (per * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                                         "algorithmic_bytes": alg_b}
+    del x, u, du, dx, ws
+    torch.cuda.empty_cache()
     return out
 
 

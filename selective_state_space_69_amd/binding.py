@@ -1,11 +1,14 @@
-"""Thin ctypes binding of libssscan.so (C ABI declared in include/ss_scan.h).
+"""Thin ctypes binding of libssscan.so (C ABI declared in include/ss_scan.h and
+include/ss_conv.h).
 
 The functions named like the C entry points (ss_scan_fwd, ss_scan_bwd,
-ss_scan_step, ss_scan_workspace_bytes, ss_scan_strerror, ss_scan_version) only
+ss_scan_step, ss_scan_workspace_bytes, ss_scan_strerror, ss_scan_version,
+ss_conv1d_fwd, ss_conv1d_bwd, ss_conv1d_step, ss_conv1d_workspace_bytes) only
 marshal arguments: torch tensors become device pointers, None becomes NULL and
-the stream defaults to torch's current HIP stream.  Every step of the scan runs
-in the HIP kernels; there is no fallback.  The convenience wrappers scan_fwd,
-scan_bwd and scan_step additionally allocate outputs and workspace with torch.
+the stream defaults to torch's current HIP stream.  Every step runs in the HIP
+kernels; there is no fallback.  The convenience wrappers scan_fwd, scan_bwd,
+scan_step, conv1d_fwd, conv1d_bwd and conv1d_step additionally allocate
+outputs and workspace with torch.
 """
 from __future__ import annotations
 
@@ -31,6 +34,12 @@ class ss_desc_t(ctypes.Structure):
                 ("dstate", ctypes.c_int64), ("in_dtype", ctypes.c_int32),
                 ("out_dtype", ctypes.c_int32), ("disc", ctypes.c_int32),
                 ("delta_softplus", ctypes.c_int32)]
+
+
+class ss_conv_desc_t(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int64), ("seqlen", ctypes.c_int64), ("dim", ctypes.c_int64),
+                ("width", ctypes.c_int32), ("in_dtype", ctypes.c_int32),
+                ("out_dtype", ctypes.c_int32), ("silu", ctypes.c_int32)]
 
 
 class ScanError(RuntimeError):
@@ -60,6 +69,15 @@ def load_library():
         lib.ss_scan_bwd.restype = I
         lib.ss_scan_step.argtypes = [D] + [P] * 10 + [P]
         lib.ss_scan_step.restype = I
+        C = ctypes.POINTER(ss_conv_desc_t)
+        lib.ss_conv1d_workspace_bytes.argtypes = [C]
+        lib.ss_conv1d_workspace_bytes.restype = SZ
+        lib.ss_conv1d_fwd.argtypes = [C] + [P] * 4 + [P]
+        lib.ss_conv1d_fwd.restype = I
+        lib.ss_conv1d_bwd.argtypes = [C] + [P] * 7 + [P, SZ, P]
+        lib.ss_conv1d_bwd.restype = I
+        lib.ss_conv1d_step.argtypes = [C] + [P] * 5 + [P]
+        lib.ss_conv1d_step.restype = I
         lib.ss_scan_strerror.argtypes = [I]
         lib.ss_scan_strerror.restype = ctypes.c_char_p
         lib.ss_scan_version.argtypes = []
@@ -123,6 +141,31 @@ def ss_scan_step(desc, h, u, delta, A, Bm, Cm, D_skip, delta_bias, z, y, stream=
     return load_library().ss_scan_step(ctypes.byref(desc), _p(h), _p(u), _p(delta), _p(A), _p(Bm),
                                        _p(Cm), _p(D_skip), _p(delta_bias), _p(z), _p(y),
                                        _stream(stream))
+
+
+def make_conv_desc(batch, seqlen, dim, width, in_dtype=SS_F32, out_dtype=SS_F32, silu=True):
+    return ss_conv_desc_t(int(batch), int(seqlen), int(dim), int(width), int(in_dtype),
+                          int(out_dtype), int(bool(silu)))
+
+
+def ss_conv1d_workspace_bytes(desc: ss_conv_desc_t) -> int:
+    return int(load_library().ss_conv1d_workspace_bytes(ctypes.byref(desc)))
+
+
+def ss_conv1d_fwd(desc, x, w, bias, u, stream=None) -> int:
+    return load_library().ss_conv1d_fwd(ctypes.byref(desc), _p(x), _p(w), _p(bias), _p(u),
+                                        _stream(stream))
+
+
+def ss_conv1d_bwd(desc, x, w, bias, du, dx, dw, dbias, workspace, ws_bytes, stream=None) -> int:
+    return load_library().ss_conv1d_bwd(ctypes.byref(desc), _p(x), _p(w), _p(bias), _p(du),
+                                        _p(dx), _p(dw), _p(dbias), _p(workspace), int(ws_bytes),
+                                        _stream(stream))
+
+
+def ss_conv1d_step(desc, state, x, w, bias, u, stream=None) -> int:
+    return load_library().ss_conv1d_step(ctypes.byref(desc), _p(state), _p(x), _p(w), _p(bias),
+                                         _p(u), _stream(stream))
 
 
 # ---------------------------------------------------------------- allocating wrappers
@@ -189,3 +232,37 @@ def scan_step(h, u, delta, A, B, C, D=None, delta_bias=None, z=None, disc="zoh",
     y = torch.empty(u.shape, dtype=out_dtype, device=u.device)
     _check(ss_scan_step(desc, h, u, delta, A, B, C, D, delta_bias, z, y, stream), "ss_scan_step")
     return y
+
+
+def conv1d_fwd(x, w, bias=None, silu=True, out_dtype=None, stream=None):
+    """Causal depthwise conv of width w.shape[1] (+ SiLU) over x (B, L, D);
+    returns u (B, L, D) in out_dtype (default: x's dtype)."""
+    Bt, L, Dd = x.shape
+    out_dtype = x.dtype if out_dtype is None else out_dtype
+    desc = make_conv_desc(Bt, L, Dd, w.shape[1], _DTYPE[x.dtype], _DTYPE[out_dtype], silu)
+    u = torch.empty(x.shape, dtype=out_dtype, device=x.device)
+    _check(ss_conv1d_fwd(desc, x, w, bias, u, stream), "ss_conv1d_fwd")
+    return u
+
+
+def conv1d_bwd(x, w, du, bias=None, silu=True, stream=None):
+    """Backward of conv1d_fwd given du (fp32); returns dict dx, dw, dbias (fp32)."""
+    Bt, L, Dd = x.shape
+    desc = make_conv_desc(Bt, L, Dd, w.shape[1], _DTYPE[x.dtype], SS_F32, silu)
+    f32 = dict(dtype=torch.float32, device=x.device)
+    g = {"dx": torch.empty(x.shape, **f32), "dw": torch.empty(w.shape, **f32),
+         "dbias": torch.empty(bias.shape, **f32) if bias is not None else None}
+    nb = ss_conv1d_workspace_bytes(desc)
+    ws = workspace(nb, x.device)
+    _check(ss_conv1d_bwd(desc, x, w, bias, du, g["dx"], g["dw"], g["dbias"], ws, nb, stream),
+           "ss_conv1d_bwd")
+    return g
+
+
+def conv1d_step(state, x, w, bias=None, silu=True, out_dtype=torch.float32, stream=None):
+    """One decode step: state (B, D, K-1) fp32 updated in place, x (B, D); returns u."""
+    Bt, Dd = x.shape
+    desc = make_conv_desc(Bt, 1, Dd, w.shape[1], _DTYPE[x.dtype], _DTYPE[out_dtype], silu)
+    u = torch.empty(x.shape, dtype=out_dtype, device=x.device)
+    _check(ss_conv1d_step(desc, state, x, w, bias, u, stream), "ss_conv1d_step")
+    return u

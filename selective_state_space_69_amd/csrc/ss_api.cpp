@@ -154,6 +154,35 @@ BwdPlan plan_bwd(const ss_desc_t& d) {
   return p;
 }
 
+namespace {
+
+// Conv1d descriptions: positive sizes, width 1..4, 32-bit segment count.
+int check_conv(const ss_conv_desc_t* d, bool need_len) {
+  if (!d) return SS_ERR_INVALID_ARG;
+  if (d->batch < 1 || d->dim < 1 || d->width < 1 || d->width > 4) return SS_ERR_INVALID_ARG;
+  if (need_len && d->seqlen < 1) return SS_ERR_INVALID_ARG;
+  const int64_t lim = int64_t(1) << 40;
+  const int64_t L = need_len ? d->seqlen : 1;
+  if (d->batch > lim || d->dim > lim || L > (int64_t(INT32_MAX) - 64) ||
+      d->batch > lim / L || d->batch * L > lim / d->dim)
+    return SS_ERR_INVALID_ARG;
+  if (!valid_dtype(d->in_dtype) || !valid_dtype(d->out_dtype)) return SS_ERR_UNSUPPORTED;
+  return SS_OK;
+}
+
+}  // namespace
+
+ConvPlan plan_conv(const ss_conv_desc_t& d) {
+  ConvPlan p;
+  p.nseg = (d.seqlen + kConvSeg - 1) / kConvSeg;
+  p.vec = d.dim % 4 == 0 ? 4 : 1;
+  const size_t parts = size_t(d.batch) * size_t(p.nseg), D = size_t(d.dim);
+  p.off_dw = 0;
+  p.off_db = align_up(parts * D * size_t(d.width) * sizeof(float));
+  p.bytes = p.off_db + align_up(parts * D * sizeof(float));
+  return p;
+}
+
 }  // namespace ss
 
 using namespace ss;
@@ -246,6 +275,52 @@ int ss_scan_step(const ss_desc_t* desc, float* h, const void* u, const void* del
     if (p && !aligned(p, kPtrAlign)) return SS_ERR_INVALID_ARG;
   StepArgs a{h, u, delta, A, Bm, Cm, D_skip, delta_bias, z, y};
   return launch_step(*desc, a, stream) == 0 ? SS_OK : SS_ERR_HIP;
+}
+
+size_t ss_conv1d_workspace_bytes(const ss_conv_desc_t* desc) {
+  if (check_conv(desc, true) != SS_OK) return 0;
+  return plan_conv(*desc).bytes;
+}
+
+int ss_conv1d_fwd(const ss_conv_desc_t* desc, const void* x, const float* w, const float* bias,
+                  void* u, void* stream) {
+  int rc = check_conv(desc, true);
+  if (rc != SS_OK) return rc;
+  if (!x || !w || !u || x == u) return SS_ERR_INVALID_ARG;
+  const void* ptrs[] = {x, w, bias, u};
+  for (const void* p : ptrs)
+    if (p && !aligned(p, kPtrAlign)) return SS_ERR_INVALID_ARG;
+  return launch_conv_fwd(*desc, plan_conv(*desc), x, w, bias, u, stream) == 0 ? SS_OK : SS_ERR_HIP;
+}
+
+int ss_conv1d_bwd(const ss_conv_desc_t* desc, const void* x, const float* w, const float* bias,
+                  const float* du, float* dx, float* dw, float* dbias, void* workspace,
+                  size_t ws_bytes, void* stream) {
+  int rc = check_conv(desc, true);
+  if (rc != SS_OK) return rc;
+  if (!x || !w || !du || !dx || !dw) return SS_ERR_INVALID_ARG;
+  if ((bias != nullptr) != (dbias != nullptr)) return SS_ERR_INVALID_ARG;
+  if (static_cast<const void*>(dx) == x || dx == du) return SS_ERR_INVALID_ARG;
+  const void* ptrs[] = {x, w, bias, du, dx, dw, dbias};
+  for (const void* p : ptrs)
+    if (p && !aligned(p, kPtrAlign)) return SS_ERR_INVALID_ARG;
+  const ConvPlan plan = plan_conv(*desc);
+  if (!workspace || ws_bytes < plan.bytes || !aligned(workspace, kAlign)) return SS_ERR_WORKSPACE;
+  return launch_conv_bwd(*desc, plan, x, w, bias, du, dx, dw, dbias,
+                         static_cast<char*>(workspace), stream) == 0
+             ? SS_OK
+             : SS_ERR_HIP;
+}
+
+int ss_conv1d_step(const ss_conv_desc_t* desc, float* state, const void* x, const float* w,
+                   const float* bias, void* u, void* stream) {
+  int rc = check_conv(desc, false);
+  if (rc != SS_OK) return rc;
+  if (!x || !w || !u || (!state && desc->width > 1)) return SS_ERR_INVALID_ARG;
+  const void* ptrs[] = {state, x, w, bias, u};
+  for (const void* p : ptrs)
+    if (p && !aligned(p, kPtrAlign)) return SS_ERR_INVALID_ARG;
+  return launch_conv_step(*desc, state, x, w, bias, u, stream) == 0 ? SS_OK : SS_ERR_HIP;
 }
 
 }  // extern "C"

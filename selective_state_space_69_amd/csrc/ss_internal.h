@@ -6,6 +6,7 @@
 #include <cstddef>
 #include <cstdint>
 
+#include "ss_conv.h"
 #include "ss_scan.h"
 
 namespace ss {
@@ -122,6 +123,25 @@ int launch_pack_rows(const ss_desc_t& d, const void* Bm, const void* Cm, void* B
 // a.hend / a.dsum; a.Brow / a.Crow must hold the 16-wide rows.
 int launch_fwd_carries(const ss_desc_t& d, const TimePlan& tp, const FwdArgs& a, void* stream);
 int launch_bwd(const ss_desc_t& d, const BwdPlan& p, const BwdArgs& a, void* stream);
+// Conv1d + SiLU (ss_conv.hip).  Time runs in independent segments of
+// kConvSeg steps; vec = 4 channels per thread when D % 4 == 0, else 1.
+// Backward workspace: per-segment partials of dw (B * nseg, D, K) and dbias
+// (B * nseg, D), fp32, 256-byte aligned.
+constexpr int kConvSeg = 64;
+struct ConvPlan {
+  int64_t nseg = 1;
+  int vec = 1;
+  size_t off_dw = 0, off_db = 0, bytes = 0;
+};
+ConvPlan plan_conv(const ss_conv_desc_t& d);
+int launch_conv_fwd(const ss_conv_desc_t& d, const ConvPlan& plan, const void* x, const float* w,
+                    const float* bias, void* u, void* stream);
+int launch_conv_bwd(const ss_conv_desc_t& d, const ConvPlan& plan, const void* x, const float* w,
+                    const float* bias, const float* du, float* dx, float* dw, float* dbias,
+                    char* ws, void* stream);
+int launch_conv_step(const ss_conv_desc_t& d, float* state, const void* x, const float* w,
+                     const float* bias, void* u, void* stream);
+
 // Chunk carries (ss_carry.hip), in place on states (B, nc, N, D): forward turns
 // chunk summaries into chunk start states (h0 may be null), reverse turns local
 // adjoints into the adjoints entering each chunk from its end.

@@ -9,7 +9,7 @@ import pytest
 from selective_state_space_69_amd import binding as B
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "ss_scan.h")
+INCLUDE = os.path.join(ROOT, "include")
 
 
 @pytest.fixture(scope="module")
@@ -21,15 +21,21 @@ def lib():
 
 
 def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(ss_scan_\w+)\s*\(", text)))
+    """Every function declared in include/*.h (comments stripped)."""
+    names = set()
+    for h in sorted(os.listdir(INCLUDE)):
+        if not h.endswith(".h"):
+            continue
+        text = re.sub(r"/\*.*?\*/", "", open(os.path.join(INCLUDE, h)).read(), flags=re.S)
+        names |= set(re.findall(r"\b(ss_\w+)\s*\(", text))
+    return sorted(names)
 
 
 def test_header_declares_entry_points():
     names = declared_functions()
     for n in ("ss_scan_fwd", "ss_scan_bwd", "ss_scan_step", "ss_scan_workspace_bytes",
-              "ss_scan_strerror", "ss_scan_version"):
+              "ss_scan_strerror", "ss_scan_version", "ss_conv1d_fwd", "ss_conv1d_bwd",
+              "ss_conv1d_step", "ss_conv1d_workspace_bytes"):
         assert n in names
 
 
@@ -122,3 +128,43 @@ def test_bwd_and_step_validation(lib):
         B.SS_ERR_INVALID_ARG
     assert B.ss_scan_step(d, None, P, P, P, P, P, None, None, None, P, stream=0) == \
         B.SS_ERR_INVALID_ARG
+
+
+# ---------------------------------------------------------------- conv1d entry points
+def cdesc(**kw):
+    base = dict(batch=2, seqlen=100, dim=64, width=4, in_dtype=B.SS_BF16, out_dtype=B.SS_BF16,
+                silu=True)
+    base.update(kw)
+    return B.make_conv_desc(**base)
+
+
+def test_conv_validation(lib):
+    P = FAKE
+    ok = cdesc()
+    for bad in (cdesc(width=0), cdesc(width=5), cdesc(batch=0), cdesc(seqlen=0), cdesc(dim=0)):
+        assert B.ss_conv1d_fwd(bad, P, P, None, P + 4096, stream=0) == B.SS_ERR_INVALID_ARG
+    assert B.ss_conv1d_fwd(cdesc(in_dtype=7), P, P, None, P + 4096, stream=0) == B.SS_ERR_UNSUPPORTED
+    assert B.ss_conv1d_fwd(ok, None, P, None, P, stream=0) == B.SS_ERR_INVALID_ARG
+    assert B.ss_conv1d_fwd(ok, P, P, None, P, stream=0) == B.SS_ERR_INVALID_ARG      # u aliases x
+    assert B.ss_conv1d_fwd(ok, P + 2, P, None, P + 4096, stream=0) == B.SS_ERR_INVALID_ARG
+    nb = B.ss_conv1d_workspace_bytes(ok)
+    assert nb > 0 and nb % 256 == 0
+    args = (P, P, None, P + 8192, P + 4096, P + 12288, None)
+    assert B.ss_conv1d_bwd(ok, *args, None, 0, stream=0) == B.SS_ERR_WORKSPACE
+    assert B.ss_conv1d_bwd(ok, *args, P, nb - 1, stream=0) == B.SS_ERR_WORKSPACE
+    # bias without dbias, dx aliasing du
+    assert B.ss_conv1d_bwd(ok, P, P, P, P + 8192, P + 4096, P + 12288, None, P, nb,
+                           stream=0) == B.SS_ERR_INVALID_ARG
+    assert B.ss_conv1d_bwd(ok, P, P, None, P + 8192, P + 8192, P + 12288, None, P, nb,
+                           stream=0) == B.SS_ERR_INVALID_ARG
+    # the decode step needs a state unless the width is 1
+    assert B.ss_conv1d_step(ok, None, P, P, None, P + 4096, stream=0) == B.SS_ERR_INVALID_ARG
+    assert B.ss_conv1d_workspace_bytes(cdesc(width=9)) == 0
+
+
+def test_conv_workspace_size(lib):
+    # per-segment (64 steps) partials of dw (B*nseg, D, K) and dbias (B*nseg, D), fp32
+    d = cdesc(batch=8, seqlen=2048, dim=5120, width=4)
+    parts = 8 * 32
+    want = parts * 5120 * 4 * 4 + parts * 5120 * 4
+    assert B.ss_conv1d_workspace_bytes(d) == want
