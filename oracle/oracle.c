@@ -363,3 +363,54 @@ int oracle_conv1d_step(int64_t Bt, int64_t D, int64_t K, int silu, double* state
     }
   return 0;
 }
+
+/*
+ * Structured state-space duality (SSD) layer, sequential reference ("A Survey
+ * of Mamba" summary, section "Mamba-2: state space duality": the SSM as a
+ * semiseparable matrix M_ji = C_j^T A_{j:i} B_i, computed by block
+ * decomposition with diagonal blocks inside chunks and off-diagonal blocks
+ * through hidden states).  Per batch row b and head h the state is an N x P
+ * matrix and A_t is a scalar (times the identity), shared by the head's P
+ * channels; B and C are shared by the heads of a group.
+ * Readings: A_h is a per-head scalar (it is what makes M a matrix shared by the
+ * head's channels); dt_t = softplus(dt_raw[b,t,h] + dt_bias[h]) as in the
+ * selective scan; the input coefficient is dt (B_bar = dt B); D_h is a per-head
+ * skip; no gate (the gate is applied outside the layer).
+ *   a_t  = exp(dt_t A_h)
+ *   H_t  = a_t H_{t-1} + dt_t B_t x_t^T              (N x P)
+ *   y_t  = H_t^T C_t + D_h x_t                       (P)
+ * x, y: (Bt, L, Hh, P); dt: (Bt, L, Hh); A, D, dt_bias: (Hh);
+ * Bm, Cm: (Bt, L, G, N), head h uses group h / (Hh / G).
+ */
+int oracle_ssd_fwd(int64_t Bt, int64_t L, int64_t Hh, int64_t P, int64_t N, int64_t G,
+                   int softplus, const double* x, const double* dt_raw, const double* A,
+                   const double* Bm, const double* Cm, const double* Dh, const double* dt_bias,
+                   double* y, int nthreads) {
+  if (Bt < 0 || L < 0 || Hh < 1 || P < 1 || N < 1 || G < 1 || Hh % G) return -1;
+  const int64_t hpg = Hh / G;
+#pragma omp parallel for collapse(2) schedule(dynamic) num_threads(nthreads > 0 ? nthreads : 1)
+  for (int64_t b = 0; b < Bt; ++b) {
+    for (int64_t h = 0; h < Hh; ++h) {
+      double* H = (double*)calloc((size_t)(N * P), sizeof(double));
+      const int64_t g = h / hpg;
+      for (int64_t t = 0; t < L; ++t) {
+        double dt = step_size(dt_raw[(b * L + t) * Hh + h], dt_bias ? dt_bias[h] : 0.0, softplus);
+        double a = exp(dt * A[h]);
+        const double* Bt_ = Bm + ((b * L + t) * G + g) * N;
+        const double* Ct = Cm + ((b * L + t) * G + g) * N;
+        const double* xt = x + ((b * L + t) * Hh + h) * P;
+        double* yt = y + ((b * L + t) * Hh + h) * P;
+        for (int64_t n = 0; n < N; ++n)
+          for (int64_t p = 0; p < P; ++p)
+            H[n * P + p] = a * H[n * P + p] + dt * Bt_[n] * xt[p];
+        for (int64_t p = 0; p < P; ++p) {
+          double s = 0.0;
+          for (int64_t n = 0; n < N; ++n) s += Ct[n] * H[n * P + p];
+          yt[p] = s + (Dh ? Dh[h] : 0.0) * xt[p];
+        }
+      }
+      free(H);
+    }
+  }
+  return 0;
+}
