@@ -1,13 +1,13 @@
-"""Thin ctypes binding of libssscan.so (C ABI declared in include/ss_scan.h and
-include/ss_conv.h).
+"""Thin ctypes binding of libssscan.so (C ABI declared in include/ss_scan.h,
+include/ss_conv.h and include/ss_ssd.h).
 
 The functions named like the C entry points (ss_scan_fwd, ss_scan_bwd,
 ss_scan_step, ss_scan_workspace_bytes, ss_scan_strerror, ss_scan_version,
-ss_conv1d_fwd, ss_conv1d_bwd, ss_conv1d_step, ss_conv1d_workspace_bytes) only
+ss_conv1d_fwd, ss_conv1d_bwd, ss_conv1d_step, ss_conv1d_workspace_bytes, ss_ssd_fwd) only
 marshal arguments: torch tensors become device pointers, None becomes NULL and
 the stream defaults to torch's current HIP stream.  Every step runs in the HIP
 kernels; there is no fallback.  The convenience wrappers scan_fwd, scan_bwd,
-scan_step, conv1d_fwd, conv1d_bwd and conv1d_step additionally allocate
+scan_step, conv1d_fwd, conv1d_bwd, conv1d_step and ssd_fwd additionally allocate
 outputs and workspace with torch.
 """
 from __future__ import annotations
@@ -40,6 +40,14 @@ class ss_conv_desc_t(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int64), ("seqlen", ctypes.c_int64), ("dim", ctypes.c_int64),
                 ("width", ctypes.c_int32), ("in_dtype", ctypes.c_int32),
                 ("out_dtype", ctypes.c_int32), ("silu", ctypes.c_int32)]
+
+
+class ss_ssd_desc_t(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int64), ("seqlen", ctypes.c_int64), ("nheads", ctypes.c_int64),
+                ("headdim", ctypes.c_int64), ("dstate", ctypes.c_int64),
+                ("ngroups", ctypes.c_int64), ("in_dtype", ctypes.c_int32),
+                ("out_dtype", ctypes.c_int32), ("dt_softplus", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
 
 
 class ScanError(RuntimeError):
@@ -78,6 +86,8 @@ def load_library():
         lib.ss_conv1d_bwd.restype = I
         lib.ss_conv1d_step.argtypes = [C] + [P] * 5 + [P]
         lib.ss_conv1d_step.restype = I
+        lib.ss_ssd_fwd.argtypes = [ctypes.POINTER(ss_ssd_desc_t)] + [P] * 8 + [P]
+        lib.ss_ssd_fwd.restype = I
         lib.ss_scan_strerror.argtypes = [I]
         lib.ss_scan_strerror.restype = ctypes.c_char_p
         lib.ss_scan_version.argtypes = []
@@ -169,6 +179,17 @@ def ss_conv1d_step(desc, state, x, w, bias, u, stream=None) -> int:
 
 
 # ---------------------------------------------------------------- allocating wrappers
+def make_ssd_desc(batch, seqlen, nheads, headdim, dstate, ngroups=1, in_dtype=SS_BF16,
+                  out_dtype=SS_F32, dt_softplus=True) -> ss_ssd_desc_t:
+    return ss_ssd_desc_t(int(batch), int(seqlen), int(nheads), int(headdim), int(dstate),
+                         int(ngroups), int(in_dtype), int(out_dtype), int(bool(dt_softplus)), 0)
+
+
+def ss_ssd_fwd(desc, x, dt, A, Bm, Cm, D, dt_bias, y, stream=None) -> int:
+    return load_library().ss_ssd_fwd(ctypes.byref(desc), _p(x), _p(dt), _p(A), _p(Bm), _p(Cm),
+                                      _p(D), _p(dt_bias), _p(y), _stream(stream))
+
+
 def _check(rc, where):
     if rc != SS_OK:
         raise ScanError(rc, where)
@@ -266,3 +287,15 @@ def conv1d_step(state, x, w, bias=None, silu=True, out_dtype=torch.float32, stre
     u = torch.empty(x.shape, dtype=out_dtype, device=x.device)
     _check(ss_conv1d_step(desc, state, x, w, bias, u, stream), "ss_conv1d_step")
     return u
+
+
+def ssd_fwd(x, dt, A, B, C, D=None, dt_bias=None, softplus=True, out_dtype=torch.float32,
+            stream=None):
+    """SSD (Mamba-2) layer forward: x (Bt, L, H, P), dt (Bt, L, H), B and C
+    (Bt, L, G, N) in bf16; A, D, dt_bias (H,) fp32.  Returns y (Bt, L, H, P)."""
+    Bt, L, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    desc = make_ssd_desc(Bt, L, H, P, N, G, _DTYPE[x.dtype], _DTYPE[out_dtype], softplus)
+    y = torch.empty(x.shape, dtype=out_dtype, device=x.device)
+    _check(ss_ssd_fwd(desc, x, dt, A, B, C, D, dt_bias, y, stream), "ss_ssd_fwd")
+    return y

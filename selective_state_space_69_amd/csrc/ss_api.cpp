@@ -170,6 +170,21 @@ int check_conv(const ss_conv_desc_t* d, bool need_len) {
   return SS_OK;
 }
 
+// SSD descriptions: positive sizes, heads divisible into groups, 32-bit grid.
+int check_ssd(const ss_ssd_desc_t* d) {
+  if (!d || d->reserved != 0) return SS_ERR_INVALID_ARG;
+  if (d->batch < 1 || d->seqlen < 1 || d->nheads < 1 || d->headdim < 1 || d->dstate < 1 ||
+      d->ngroups < 1 || d->nheads % d->ngroups != 0)
+    return SS_ERR_INVALID_ARG;
+  const int64_t lim = int64_t(1) << 40;
+  if (d->batch > lim || d->seqlen > lim || d->nheads > lim || d->ngroups > lim ||
+      d->batch > (int64_t(INT32_MAX) / d->nheads) || d->batch * d->seqlen > lim / d->nheads)
+    return SS_ERR_INVALID_ARG;
+  if (d->headdim != 64 || d->dstate != 64) return SS_ERR_UNSUPPORTED;
+  if (d->in_dtype != SS_BF16 || !valid_dtype(d->out_dtype)) return SS_ERR_UNSUPPORTED;
+  return SS_OK;
+}
+
 }  // namespace
 
 ConvPlan plan_conv(const ss_conv_desc_t& d) {
@@ -321,6 +336,19 @@ int ss_conv1d_step(const ss_conv_desc_t* desc, float* state, const void* x, cons
   for (const void* p : ptrs)
     if (p && !aligned(p, kPtrAlign)) return SS_ERR_INVALID_ARG;
   return launch_conv_step(*desc, state, x, w, bias, u, stream) == 0 ? SS_OK : SS_ERR_HIP;
+}
+
+int ss_ssd_fwd(const ss_ssd_desc_t* desc, const void* x, const void* dt, const float* A,
+               const void* Bm, const void* Cm, const float* D, const float* dt_bias, void* y,
+               void* stream) {
+  int rc = check_ssd(desc);
+  if (rc != SS_OK) return rc;
+  if (!x || !dt || !A || !Bm || !Cm || !y) return SS_ERR_INVALID_ARG;
+  if (y == x || y == dt || y == Bm || y == Cm) return SS_ERR_INVALID_ARG;
+  const void* ptrs[] = {x, dt, A, Bm, Cm, D, dt_bias, y};
+  for (const void* p : ptrs)
+    if (p && !aligned(p, kPtrAlign)) return SS_ERR_INVALID_ARG;
+  return launch_ssd_fwd(*desc, x, dt, A, Bm, Cm, D, dt_bias, y, stream) == 0 ? SS_OK : SS_ERR_HIP;
 }
 
 }  // extern "C"

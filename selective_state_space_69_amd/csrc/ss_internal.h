@@ -7,6 +7,7 @@
 #include <cstdint>
 
 #include "ss_conv.h"
+#include "ss_ssd.h"
 #include "ss_scan.h"
 
 namespace ss {
@@ -148,5 +149,9 @@ int launch_conv_step(const ss_conv_desc_t& d, float* state, const void* x, const
 int launch_chunk_carry(float* states, const float* dsum, const float* A, const float* h0,
                        int64_t batch, int64_t D, int N, int nc, bool reverse, void* stream);
 int launch_step(const ss_desc_t& d, const StepArgs& a, void* stream);
+// SSD (Mamba-2) forward (ss_ssd.hip): one workgroup per (batch row, head).
+int launch_ssd_fwd(const ss_ssd_desc_t& d, const void* x, const void* dt, const float* A,
+                   const void* Bm, const void* Cm, const float* D, const float* dt_bias, void* y,
+                   void* stream);
 
 }  // namespace ss

@@ -157,3 +157,52 @@ def make_workload(name: str, with_dy: bool | None = None) -> Inputs:
     if with_dy is None:
         with_dy = w.op == "bwd"
     return make_inputs(w.B, w.L, w.D, w.N, w.seed, w.dtype, w.dt_range, with_dy=with_dy)
+
+
+# ---------------------------------------------------------------- SSD (Mamba-2) layer
+@dataclass
+class SsdInputs:
+    """Host arrays of one SSD problem (float32 holding the exact values both sides
+    receive): x (Bt, L, H, P), dt (Bt, L, H), B and C (Bt, L, G, N) as exact bf16
+    values; A, D, dt_bias (H,) float32."""
+    x: np.ndarray
+    dt: np.ndarray
+    A: np.ndarray
+    B: np.ndarray
+    C: np.ndarray
+    D: np.ndarray | None
+    dt_bias: np.ndarray | None
+    meta: dict = field(default_factory=dict)
+
+
+def make_ssd_inputs(Bt: int, L: int, H: int, P: int, N: int, G: int, seed: int,
+                    dt_range=(1e-3, 1e-1), a_range=(1.0, 16.0), dt_std: float = 0.1,
+                    with_D: bool = True, with_bias: bool = True) -> SsdInputs:
+    """Draw one seeded SSD problem.  Recipe: x, B, C ~ N(0, 1); raw dt ~ N(0, dt_std);
+    per head a step bias that is the inverse softplus of a log-uniform step in
+    dt_range; A_h = -U(a_range) (one scalar per head); D_h ~ U(0.5, 1.5).  x, dt,
+    B, C are rounded once to bf16.  Order of draws: x, B, C, dt, U (step), A, D."""
+    rng = np.random.default_rng(seed)
+    f32 = np.float32
+    x = rng.standard_normal((Bt, L, H, P), dtype=f32)
+    Bm = rng.standard_normal((Bt, L, G, N), dtype=f32)
+    Cm = rng.standard_normal((Bt, L, G, N), dtype=f32)
+    dt = rng.standard_normal((Bt, L, H), dtype=f32)
+    dt *= f32(dt_std)
+    U = rng.random(H)
+    a_lo, a_hi = a_range
+    A = (-(a_lo + (a_hi - a_lo) * rng.random(H))).astype(f32)
+    D = (0.5 + rng.random(H)).astype(f32)
+    lo, hi = dt_range
+    step = np.exp(math.log(lo) + U * (math.log(hi) - math.log(lo)))
+    bias = (step + np.log(-np.expm1(-step))).astype(f32)
+    x, Bm, Cm, dt = (round_to_bf16(v) for v in (x, Bm, Cm, dt))
+    return SsdInputs(x=x, dt=dt, A=A, B=Bm, C=Cm, D=D if with_D else None,
+                     dt_bias=bias if with_bias else None,
+                     meta=dict(Bt=Bt, L=L, H=H, P=P, N=N, G=G, seed=seed))
+
+
+# The SSD workload: 80 heads of 64 channels (width 5120, as the Mamba-2.8B scan
+# workload), 64 states, one B/C group.
+SSD_WORKLOAD = dict(name="ssd_bf16_b8_l2048_h80_p64_n64_g1", Bt=8, L=2048, H=80, P=64, N=64,
+                    G=1, seed=2001)

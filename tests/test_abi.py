@@ -35,7 +35,7 @@ def test_header_declares_entry_points():
     names = declared_functions()
     for n in ("ss_scan_fwd", "ss_scan_bwd", "ss_scan_step", "ss_scan_workspace_bytes",
               "ss_scan_strerror", "ss_scan_version", "ss_conv1d_fwd", "ss_conv1d_bwd",
-              "ss_conv1d_step", "ss_conv1d_workspace_bytes"):
+              "ss_conv1d_step", "ss_conv1d_workspace_bytes", "ss_ssd_fwd"):
         assert n in names
 
 
@@ -168,3 +168,38 @@ def test_conv_workspace_size(lib):
     parts = 8 * 32
     want = parts * 5120 * 4 * 4 + parts * 5120 * 4
     assert B.ss_conv1d_workspace_bytes(d) == want
+
+
+# ---------------------------------------------------------------- SSD entry point
+def sdesc(**kw):
+    base = dict(batch=2, seqlen=100, nheads=4, headdim=64, dstate=64, ngroups=2)
+    base.update(kw)
+    return B.make_ssd_desc(**base)
+
+
+def ssd(desc, **kw):
+    P = FAKE
+    args = dict(x=P, dt=P + 4096, A=P + 8192, Bm=P + 12288, Cm=P + 16384, D=None, dt_bias=None,
+                y=P + 20480)
+    args.update(kw)
+    return B.ss_ssd_fwd(desc, args["x"], args["dt"], args["A"], args["Bm"], args["Cm"], args["D"],
+                        args["dt_bias"], args["y"], stream=0)
+
+
+def test_ssd_validation(lib):
+    for bad in (sdesc(batch=0), sdesc(seqlen=0), sdesc(nheads=0), sdesc(ngroups=3),
+                sdesc(ngroups=0), sdesc(headdim=0), sdesc(batch=1 << 30, nheads=4)):
+        assert ssd(bad) == B.SS_ERR_INVALID_ARG
+    d = sdesc()
+    d.reserved = 1
+    assert ssd(d) == B.SS_ERR_INVALID_ARG
+    for uns in (sdesc(headdim=32), sdesc(dstate=128), sdesc(in_dtype=B.SS_F32),
+                sdesc(out_dtype=5)):
+        assert ssd(uns) == B.SS_ERR_UNSUPPORTED
+    ok = sdesc()
+    for name in ("x", "dt", "A", "Bm", "Cm", "y"):
+        assert ssd(ok, **{name: None}) == B.SS_ERR_INVALID_ARG, name
+    assert ssd(ok, y=FAKE) == B.SS_ERR_INVALID_ARG               # y aliases x
+    assert ssd(ok, D=FAKE + 2) == B.SS_ERR_INVALID_ARG           # misaligned
+    assert ssd(ok, y=FAKE + 20488) == B.SS_ERR_INVALID_ARG
+    assert B.load_library().ss_ssd_fwd(None, *([None] * 8), None) == B.SS_ERR_INVALID_ARG
