@@ -150,7 +150,7 @@ def main():
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device copy (counter calibration)")
-    ap.add_argument("--only", choices=["bwd", "step", "conv"],
+    ap.add_argument("--only", choices=["bwd", "step", "conv", "ssd"],
                     help="only time the backward (Mamba-130M shape), the decode step or the "
                          "Conv1d + SiLU and print their figures (for profiling runs)")
     args = ap.parse_args()
@@ -176,6 +176,9 @@ def main():
         return
     if args.only == "conv":
         print(json.dumps(time_conv(torch, Bnd, synth, args.steps, args.warmup)), flush=True)
+        return
+    if args.only == "ssd":
+        print(json.dumps(time_ssd(torch, Bnd, synth, args.steps, args.warmup)), flush=True)
         return
     w = synth.WORKLOADS[args.workload]
     inp = synth.make_workload(w.name, with_dy=False)
@@ -258,6 +261,7 @@ def extras(torch, Bnd, synth, args):
     out.update(time_bwd(torch, Bnd, synth, steps, warm))
     out.update(time_step(torch, Bnd, synth))
     out.update(time_conv(torch, Bnd, synth, steps, warm))
+    out.update(time_ssd(torch, Bnd, synth, steps, warm))
     return out
 
 
@@ -297,6 +301,39 @@ def time_conv(torch, Bnd, synth, steps, warm):
                                          "hbm_frac": round(alg_b / (per * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                                          "algorithmic_bytes": alg_b}
     del x, u, du, dx, ws
+    torch.cuda.empty_cache()
+    return out
+
+
+def time_ssd(torch, Bnd, synth, steps, warm):
+    """SSD (Mamba-2) layer forward, 8 x 2048 tokens, 80 heads of 64 channels,
+    64 states, one B/C group; fp32 and bf16 output.  Algorithmic bytes: x, dt,
+    B, C read once, y written once; algorithmic flops of the chunked form
+    (Q = 64): per token and head Q (N + P) for the causal C B^T and M x
+    blocks plus 4 N P for C H and the state update."""
+    w = synth.SSD_WORKLOAD
+    Bt, L, H, P, N, G = (w[k] for k in ("Bt", "L", "H", "P", "N", "G"))
+    inp = synth.make_ssd_inputs(Bt, L, H, P, N, G, w["seed"])
+    bf, f32 = torch.bfloat16, torch.float32
+    dev = lambda a, t: torch.from_numpy(a).to("cuda").to(t).contiguous()  # noqa
+    x, dt, Bm, Cm = (dev(a, bf) for a in (inp.x, inp.dt, inp.B, inp.C))
+    A, Dh, bias = (dev(a, f32) for a in (inp.A, inp.D, inp.dt_bias))
+    out = {}
+    toks = Bt * L
+    flops = toks * H * (64 * (N + P) + 4 * N * P)
+    for od, ob in ((Bnd.SS_F32, 4), (Bnd.SS_BF16, 2)):
+        y = torch.empty(x.shape, dtype=f32 if od == Bnd.SS_F32 else bf, device="cuda")
+        desc = Bnd.make_ssd_desc(Bt, L, H, P, N, G, Bnd.SS_BF16, od, True)
+        f = lambda: Bnd.ss_ssd_fwd(desc, x, dt, A, Bm, Cm, Dh, bias, y)  # noqa
+        total, per, mn, _ = time_calls(f, steps, warm, torch)
+        alg = toks * H * P * (2 + ob) + toks * H * 2 + 2 * toks * G * N * 2 + 3 * H * 4
+        out["%s:y_%s" % (w["name"], "f32" if od == Bnd.SS_F32 else "bf16")] = {
+            "ms": round(per, 4), "ms_min": round(mn, 4), "tokens_per_s": toks / (per * 1e-3),
+            "hbm_gbs": round(alg / (per * 1e-3) / 1e9, 1),
+            "hbm_frac": round(alg / (per * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "tflops": round(flops / (per * 1e-3) / 1e12, 1), "algorithmic_bytes": alg}
+        del y
+    del x, dt, Bm, Cm
     torch.cuda.empty_cache()
     return out
 

@@ -34,6 +34,11 @@
 // adjacent 16-row tiles are then exactly the k slots a lane must supply, for M
 // (from the G^T tiles) and for H alike, and the LDS operands are read in the
 // same order.
+//
+// Per chunk: the next chunk's x, B, C rows are fetched into registers (buffer
+// loads; rows past the end read as zero) while this one is computed, then
+// written to LDS as B and C rows and as B^T and x^T (4 x 4 transposes in
+// registers).  Three barriers: tiles written, C H exchanged, tiles free again.
 #include "ss_device.hpp"
 
 namespace ss {
@@ -48,34 +53,32 @@ constexpr int kDim = 64;        // P = N = 64
 constexpr int kNW = 4;          // waves per workgroup
 constexpr int kThreads = kNW * kWave;
 
-// LDS tiles: 64 rows of 16 units of 8 bytes (4 bf16).  Unit u of row r sits at
-// u ^ (4 * ((r >> 2) & 3)): the operand reads (16 rows x units 8j+g), the
-// row-major staging writes and the transposing staging writes all spread over
-// the banks evenly.
-struct Tile {
-  uint2 u[kDim][16];
-};
-__device__ __forceinline__ int swz(int row, int unit) { return unit ^ (((row >> 2) & 3) << 2); }
-
-struct Smem {
-  Tile bs;                    // B rows   [s][n]
-  Tile cs;                    // C rows   [t][n]
-  Tile bt;                    // B^T      [n][s]
-  Tile xt;                    // x^T      [p][s]
-  f32x4 yo[4][4][kWave];      // exp(l_t) C H, [t-tile][p-tile][lane]
-  float lam[kQ];              // l_t in log2 units (inclusive, from the chunk start)
-  float dts[kQ];              // dt_t
-};
-
-// MFMA operand of k block j from row `row` of a tile: 8 bf16 at columns
-// 32j + 4g .. +3 and 32j + 16 + 4g .. +3.
-__device__ __forceinline__ u32x4 ld_op(const Tile& t, int row, int j, int g) {
-  const uint2 a = t.u[row][swz(row, 8 * j + g)];
-  const uint2 b = t.u[row][swz(row, 8 * j + 4 + g)];
-  u32x4 r;
-  r.x = a.x; r.y = a.y; r.z = b.x; r.w = b.y;
-  return r;
+// LDS operand tiles: 64 rows x 8 units of 16 bytes.  Unit q = 4j + g of a row
+// holds the 8 k slots lane group g supplies for k block j (columns 32j + 4g .. +3
+// and 32j + 16 + 4g .. +3), so an operand is one 16-byte read; the unit sits at
+// q ^ ((row >> 1) & 7): the 16 rows one read touches (16 lanes per pass) then
+// cover all 64 banks exactly once (row parity picks the bank half, the XOR the
+// unit inside it).
+constexpr int kTileBytes = kDim * 128;
+__device__ __forceinline__ int op_off(int row, int q) {
+  return row * 128 + ((q ^ ((row >> 1) & 7)) << 4);
 }
+// columns 4 cb .. 4 cb + 3 of a row (8 bytes): unit 4 (cb >> 3) + (cb & 3), half (cb >> 2) & 1
+__device__ __forceinline__ int col_off(int row, int cb) {
+  return op_off(row, 4 * (cb >> 3) + (cb & 3)) + (((cb >> 2) & 1) << 3);
+}
+
+// LDS map (bytes)
+constexpr int kOffBs = 0;                        // B rows   [s][n]
+constexpr int kOffCs = kOffBs + kTileBytes;      // C rows   [t][n]
+constexpr int kOffBt = kOffCs + kTileBytes;      // B^T      [n][s]
+constexpr int kOffXt = kOffBt + kTileBytes;      // x^T      [p][s]
+constexpr int kOffYo = kOffXt + kTileBytes;      // exp(l_t) C H as [t-tile][p-tile][lane] x 16 B
+constexpr int kOffLam = kOffYo + 16 * kWave * 16;   // l_t, log2 units, inclusive from the chunk start
+constexpr int kOffElam = kOffLam + kQ * 4;       // exp2(l_t)
+constexpr int kOffWts = kOffElam + kQ * 4;       // exp2(l_end - l_s) dt_s
+constexpr int kOffDts = kOffWts + kQ * 4;        // dt_s
+constexpr int kSmemBytes = kOffDts + kQ * 4;
 
 __device__ __forceinline__ f32x4 mfma(u32x4 a, u32x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
@@ -102,15 +105,6 @@ __device__ __forceinline__ void split8(const float (&v)[8], u32x4& hi, u32x4& lo
   }
   hi.x = h[0]; hi.y = h[1]; hi.z = h[2]; hi.w = h[3];
   lo.x = l[0]; lo.y = l[1]; lo.z = l[2]; lo.w = l[3];
-}
-
-__device__ __forceinline__ void bf16x8_to_f32(u32x4 v, float (&f)[8]) {
-  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    f[2 * i] = __uint_as_float(w[i] << 16);
-    f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
-  }
 }
 
 template <int CTRL, int ROW_MASK>
@@ -141,6 +135,11 @@ __device__ __forceinline__ void transpose4(const uint2 (&in)[4], uint2 (&out)[4]
   out[3] = make_uint2(hi2(in[0].y, in[1].y), hi2(in[2].y, in[3].y));
 }
 
+__device__ __forceinline__ uint2 buf_load8(Rsrc r, uint32_t voff) {
+  const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, voff, 0, 0);
+  return make_uint2(v[0], v[1]);
+}
+
 struct SsdArgs {
   const uint16_t* x;       // (B, L, H, P) bf16
   const uint16_t* dt;      // (B, L, H) bf16
@@ -154,9 +153,24 @@ struct SsdArgs {
   int H, G;
 };
 
+template <typename Out>
+__device__ __forceinline__ void store_y4(Rsrc r, uint32_t voff, f32x4 v);
+template <>
+__device__ __forceinline__ void store_y4<float>(Rsrc r, uint32_t voff, f32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, voff, 0, 0);
+}
+template <>
+__device__ __forceinline__ void store_y4<uint16_t>(Rsrc r, uint32_t voff, f32x4 v) {
+  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+  u32x2 p;
+  p.x = pack_bf16(v[0], v[1]);
+  p.y = pack_bf16(v[2], v[3]);
+  __builtin_amdgcn_raw_buffer_store_b64(p, r, voff, 0, 0);
+}
+
 template <typename Out, bool SOFTPLUS>
 __global__ __launch_bounds__(kThreads, 3) void ssd_fwd_kernel(SsdArgs a) {
-  __shared__ Smem sm;
+  __shared__ __align__(16) char sm[kSmemBytes];
   const int tid = int(threadIdx.x);
   const int w = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int lane = tid % kWave;
@@ -166,80 +180,105 @@ __global__ __launch_bounds__(kThreads, 3) void ssd_fwd_kernel(SsdArgs a) {
   const int grp = h / (a.H / a.G);
   const int64_t L = a.L;
   const int nc = int((L + kQ - 1) / kQ);
-
   const float Dh = a.D ? a.D[h] : 0.0f;
   const float biash = a.dt_bias ? a.dt_bias[h] : 0.0f;
+  const float Ah = a.A[h];
+
+  // operand reads: row 16 tile + c16, unit 4j + g -> byte offset tile * 2048 + opj[j]
+  // (the swizzle depends on the row only through c16)
+  const int opj0 = op_off(c16, g), opj1 = op_off(c16, 4 + g);
+  auto ld_op = [&](int base, int tile, int j) -> u32x4 {
+    return *reinterpret_cast<const u32x4*>(sm + base + tile * (16 * 128) + (j ? opj1 : opj0));
+  };
+  auto ldf4 = [&](int off) -> f32x4 { return *reinterpret_cast<const f32x4*>(sm + off); };
 
   // staging: thread = 4 x 4 block (rows 4 rb .. +3, columns 4 cb .. +3) of each chunk tile
   const int rb = tid >> 4, cb = tid & 15;
-  const int64_t xrow = int64_t(a.H) * kDim, brow = int64_t(a.G) * kDim;   // row strides
-  const uint16_t* xg = a.x + (b * L * a.H + h) * kDim + 4 * cb;
-  const uint16_t* bg = a.Bm + (b * L * a.G + grp) * kDim + 4 * cb;
-  const uint16_t* cg = a.Cm + (b * L * a.G + grp) * kDim + 4 * cb;
-  const uint16_t* dtg = a.dt + b * L * a.H + h;
-  uint2 xr[4], br[4], cr[4];
-  uint16_t dtr = 0;
-  auto load_chunk = [&](int c) {
+  const uint32_t xrow_b = uint32_t(a.H) * kDim * 2, brow_b = uint32_t(a.G) * kDim * 2;
+  const uint16_t* xbase = a.x + (b * L * a.H + h) * kDim;
+  const uint16_t* bbase = a.Bm + (b * L * a.G + grp) * kDim;
+  const uint16_t* cbase = a.Cm + (b * L * a.G + grp) * kDim;
+  const uint16_t* dtbase = a.dt + b * L * a.H + h;
+  Out* ybase = static_cast<Out*>(a.y) + (b * L * a.H + h) * kDim;
+  // register set the next chunk is fetched into while this one is computed
+  struct Stage {
+    uint2 xr[4], br[4], cr[4];
+    uint32_t dtr;
+  };
+  Stage st0;
+  auto load_chunk = [&](int c, Stage& sg) __attribute__((always_inline)) {
+    const int64_t t0 = int64_t(c) * kQ;
+    const int64_t rows = L - t0;                       // valid rows of this chunk (> 0)
+    const Rsrc rx = make_rsrc(xbase + t0 * a.H * kDim);
+    const Rsrc rbm = make_rsrc(bbase + t0 * a.G * kDim);
+    const Rsrc rcm = make_rsrc(cbase + t0 * a.G * kDim);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int64_t s = int64_t(c) * kQ + 4 * rb + i;
-      if (s < L) {
-        xr[i] = *reinterpret_cast<const uint2*>(xg + s * xrow);
-        br[i] = *reinterpret_cast<const uint2*>(bg + s * brow);
-        cr[i] = *reinterpret_cast<const uint2*>(cg + s * brow);
-      } else {
-        xr[i] = br[i] = cr[i] = make_uint2(0u, 0u);
-      }
+      const bool ok = 4 * rb + i < rows;
+      const uint32_t ox = ok ? uint32_t(4 * rb + i) * xrow_b + 8 * cb : kOutOfRange;
+      const uint32_t ob = ok ? uint32_t(4 * rb + i) * brow_b + 8 * cb : kOutOfRange;
+      sg.xr[i] = buf_load8(rx, ox);
+      sg.br[i] = buf_load8(rbm, ob);
+      sg.cr[i] = buf_load8(rcm, ob);
     }
-    if (w == 0) {
-      const int64_t s = int64_t(c) * kQ + lane;
-      dtr = s < L ? dtg[s * a.H] : uint16_t(0);
-    }
+    // every wave loads the step sizes (only wave 0 uses them) so that all waves
+    // have the same memory operations in flight
+    const Rsrc rd = make_rsrc(dtbase + t0 * a.H);
+    sg.dtr = __builtin_amdgcn_raw_buffer_load_b16(
+        rd, lane < rows ? uint32_t(lane) * uint32_t(a.H) * 2 : kOutOfRange, 0, 0);
   };
+  // output rows 16 w + 4 g + r, columns 16 pi + c16
+  const uint32_t yrow_b = uint32_t(a.H) * kDim * uint32_t(sizeof(Out));
 
   // state H[n][p]: tile ni holds rows 16 ni + 4g + r, column 16 w + c16
   f32x4 hacc[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) hacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  load_chunk(0);
-  for (int c = 0; c < nc; ++c) {
+  // One chunk, from register set sg.  The first chunk is peeled off the loop
+  // below: every path into the loop head then has the previous chunk's output
+  // stores issued after its prefetch loads, so the wait at the head covers the
+  // loads only.
+  auto chunk = [&](int c, Stage& sg) __attribute__((always_inline)) {
+    const int64_t t0 = int64_t(c) * kQ;
+    const int64_t rows = L - t0;
     __syncthreads();   // the previous chunk's tiles are no longer read
     {
       uint2 tr[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = 4 * rb + i;
-        sm.bs.u[r][swz(r, cb)] = br[i];
-        sm.cs.u[r][swz(r, cb)] = cr[i];
+        *reinterpret_cast<uint2*>(sm + kOffBs + col_off(r, cb)) = sg.br[i];
+        *reinterpret_cast<uint2*>(sm + kOffCs + col_off(r, cb)) = sg.cr[i];
       }
-      transpose4(br, tr);
+      transpose4(sg.br, tr);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int r = 4 * cb + j;
-        sm.bt.u[r][swz(r, rb)] = tr[j];
-      }
-      transpose4(xr, tr);
+      for (int j = 0; j < 4; ++j)
+        *reinterpret_cast<uint2*>(sm + kOffBt + col_off(4 * cb + j, rb)) = tr[j];
+      transpose4(sg.xr, tr);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int r = 4 * cb + j;
-        sm.xt.u[r][swz(r, rb)] = tr[j];
-      }
+      for (int j = 0; j < 4; ++j)
+        *reinterpret_cast<uint2*>(sm + kOffXt + col_off(4 * cb + j, rb)) = tr[j];
       if (w == 0) {
-        // step sizes and the running log2 decay of the chunk (zero past the end)
-        const bool valid = int64_t(c) * kQ + lane < L;
-        const float v = to_f32(dtr) + biash;
+        // step sizes, the running log2 decay of the chunk (zero past the end) and
+        // the per-step factors every wave needs
+        const float v = __uint_as_float(sg.dtr << 16) + biash;
         float dt2;   // dt * log2(e)
         if constexpr (SOFTPLUS) dt2 = softplus_log2(v * kLog2e);
         else dt2 = v * kLog2e;
-        if (!valid) dt2 = 0.0f;
-        sm.lam[lane] = wave_inclusive_sum(dt2 * a.A[h]);
-        sm.dts[lane] = dt2 * kLn2;
+        if (lane >= rows) dt2 = 0.0f;
+        const float lam = wave_inclusive_sum(dt2 * Ah);
+        const float lend = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lam), kQ - 1));
+        const float dtn = dt2 * kLn2;
+        reinterpret_cast<float*>(sm + kOffLam)[lane] = lam;
+        reinterpret_cast<float*>(sm + kOffElam)[lane] = hw_exp2(lam);
+        reinterpret_cast<float*>(sm + kOffWts)[lane] = hw_exp2(lend - lam) * dtn;
+        reinterpret_cast<float*>(sm + kOffDts)[lane] = dtn;
       }
     }
     __syncthreads();
-    if (c + 1 < nc) load_chunk(c + 1);
-    const float lam_end = sm.lam[kQ - 1];
+    if (c + 1 < nc) load_chunk(c + 1, sg);
+    const float lam_end = reinterpret_cast<const float*>(sm + kOffLam)[kQ - 1];
 
     // p-role: off-diagonal outputs exp(l_t) C_t . H for p-tile w, every t-tile
     {
@@ -259,14 +298,12 @@ __global__ __launch_bounds__(kThreads, 3) void ssd_fwd_kernel(SsdArgs a) {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-          const u32x4 cop = ld_op(sm.cs, 16 * ti + c16, j, g);
+          const u32x4 cop = ld_op(kOffCs, ti, j);
           acc = mfma(cop, hh[j], acc);
           acc = mfma(cop, hl[j], acc);
         }
-        const f32x4 lt = *reinterpret_cast<const f32x4*>(&sm.lam[16 * ti + 4 * g]);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) acc[r] *= hw_exp2(lt[r]);
-        sm.yo[ti][w][lane] = acc;
+        acc *= ldf4(kOffElam + (16 * ti + 4 * g) * 4);
+        *reinterpret_cast<f32x4*>(sm + kOffYo + ((ti * 4 + w) * kWave + lane) * 16) = acc;
       }
     }
 
@@ -274,8 +311,8 @@ __global__ __launch_bounds__(kThreads, 3) void ssd_fwd_kernel(SsdArgs a) {
     u32x4 mh[2], ml[2];
     {
       const int t = 16 * w + c16;
-      const float lamt = sm.lam[t];
-      const u32x4 ct0 = ld_op(sm.cs, t, 0, g), ct1 = ld_op(sm.cs, t, 1, g);
+      const float lamt = reinterpret_cast<const float*>(sm + kOffLam)[t];
+      const u32x4 ct0 = ld_op(kOffCs, w, 0), ct1 = ld_op(kOffCs, w, 1);
       float m[4][4];
 #pragma unroll
       for (int si = 0; si < 4; ++si) {
@@ -285,10 +322,10 @@ __global__ __launch_bounds__(kThreads, 3) void ssd_fwd_kernel(SsdArgs a) {
           continue;
         }
         f32x4 gacc = {0.f, 0.f, 0.f, 0.f};
-        gacc = mfma(ld_op(sm.bs, 16 * si + c16, 0, g), ct0, gacc);
-        gacc = mfma(ld_op(sm.bs, 16 * si + c16, 1, g), ct1, gacc);
-        const f32x4 ls = *reinterpret_cast<const f32x4*>(&sm.lam[16 * si + 4 * g]);
-        const f32x4 ds = *reinterpret_cast<const f32x4*>(&sm.dts[16 * si + 4 * g]);
+        gacc = mfma(ld_op(kOffBs, si, 0), ct0, gacc);
+        gacc = mfma(ld_op(kOffBs, si, 1), ct1, gacc);
+        const f32x4 ls = ldf4(kOffLam + (16 * si + 4 * g) * 4);
+        const f32x4 ds = ldf4(kOffDts + (16 * si + 4 * g) * 4);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int s = 16 * si + 4 * g + r;
@@ -310,25 +347,47 @@ __global__ __launch_bounds__(kThreads, 3) void ssd_fwd_kernel(SsdArgs a) {
     }
     __syncthreads();   // yo complete
 
-    // t-role: Y = yo + M X for t-tile w, every p-tile; store
+    // t-role: Y = yo + M X for t-tile w, every p-tile.  The wave's 16 x 64
+    // outputs go through its own 4 KB of the exchange area (its yo tiles, read
+    // first) so that every lane stores 16 contiguous bytes and each store
+    // instruction writes 4 whole output rows.
     {
       const int nkb = (w >> 1) + 1;
+      char* ybuf = sm + kOffYo + w * 4 * kWave * 16;
+      f32x4 acc[4];
+#pragma unroll
+      for (int pi = 0; pi < 4; ++pi)
+        acc[pi] = *reinterpret_cast<const f32x4*>(ybuf + (pi * kWave + lane) * 16);
 #pragma unroll
       for (int pi = 0; pi < 4; ++pi) {
-        f32x4 acc = sm.yo[w][pi][lane];
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
           if (j >= nkb) continue;
-          const u32x4 xop = ld_op(sm.xt, 16 * pi + c16, j, g);
-          acc = mfma(mh[j], xop, acc);
-          acc = mfma(ml[j], xop, acc);
+          const u32x4 xop = ld_op(kOffXt, pi, j);
+          acc[pi] = mfma(mh[j], xop, acc[pi]);
+          acc[pi] = mfma(ml[j], xop, acc[pi]);
         }
-        Out* yp = static_cast<Out*>(a.y) +
-                  ((b * L + int64_t(c) * kQ + 16 * w + 4 * g) * a.H + h) * kDim + 16 * pi + c16;
+      }
+      __builtin_amdgcn_wave_barrier();
+      // row t (0..15) of 64 floats = 16 units of 16 bytes; unit u at u ^ (4 (t >> 2))
+#pragma unroll
+      for (int pi = 0; pi < 4; ++pi)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          if (int64_t(c) * kQ + 16 * w + 4 * g + r < L) store_out(yp + int64_t(r) * xrow, acc[r]);
+          const int t = 4 * g + r, u = 4 * pi + (c16 >> 2);
+          *reinterpret_cast<float*>(ybuf + t * 256 + ((u ^ (4 * g)) << 4) + (c16 & 3) * 4) =
+              acc[pi][r];
         }
+      __builtin_amdgcn_wave_barrier();
+      const Rsrc ry = make_rsrc(ybase + t0 * a.H * kDim);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int t = 4 * k + (lane >> 4), u = lane & 15;
+        const f32x4 v = *reinterpret_cast<const f32x4*>(ybuf + t * 256 + ((u ^ (4 * k)) << 4));
+        const int row = 16 * w + t;
+        const uint32_t off = row < rows ? uint32_t(row) * yrow_b + uint32_t(4 * u * sizeof(Out))
+                                        : kOutOfRange;
+        store_y4<Out>(ry, off, v);
       }
     }
 
@@ -337,17 +396,18 @@ __global__ __launch_bounds__(kThreads, 3) void ssd_fwd_kernel(SsdArgs a) {
       u32x4 xh[2], xl[2];
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
+        const u32x4 xv = ld_op(kOffXt, w, j);
+        const f32x4 w0 = ldf4(kOffWts + (32 * j + 4 * g) * 4);
+        const f32x4 w1 = ldf4(kOffWts + (32 * j + 16 + 4 * g) * 4);
         float v[8];
-        bf16x8_to_f32(ld_op(sm.xt, 16 * w + c16, j, g), v);
-        const f32x4 l0 = *reinterpret_cast<const f32x4*>(&sm.lam[32 * j + 4 * g]);
-        const f32x4 l1 = *reinterpret_cast<const f32x4*>(&sm.lam[32 * j + 16 + 4 * g]);
-        const f32x4 d0 = *reinterpret_cast<const f32x4*>(&sm.dts[32 * j + 4 * g]);
-        const f32x4 d1 = *reinterpret_cast<const f32x4*>(&sm.dts[32 * j + 16 + 4 * g]);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          v[r] *= hw_exp2(lam_end - l0[r]) * d0[r];
-          v[4 + r] *= hw_exp2(lam_end - l1[r]) * d1[r];
-        }
+        v[0] = __uint_as_float(xv.x << 16) * w0[0];
+        v[1] = __uint_as_float(xv.x & 0xffff0000u) * w0[1];
+        v[2] = __uint_as_float(xv.y << 16) * w0[2];
+        v[3] = __uint_as_float(xv.y & 0xffff0000u) * w0[3];
+        v[4] = __uint_as_float(xv.z << 16) * w1[0];
+        v[5] = __uint_as_float(xv.z & 0xffff0000u) * w1[1];
+        v[6] = __uint_as_float(xv.w << 16) * w1[2];
+        v[7] = __uint_as_float(xv.w & 0xffff0000u) * w1[3];
         split8(v, xh[j], xl[j]);
       }
       const float decay = hw_exp2(lam_end);
@@ -356,14 +416,17 @@ __global__ __launch_bounds__(kThreads, 3) void ssd_fwd_kernel(SsdArgs a) {
         f32x4 acc = hacc[ni] * decay;
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-          const u32x4 bop = ld_op(sm.bt, 16 * ni + c16, j, g);
+          const u32x4 bop = ld_op(kOffBt, ni, j);
           acc = mfma(bop, xh[j], acc);
           acc = mfma(bop, xl[j], acc);
         }
         hacc[ni] = acc;
       }
     }
-  }
+  };
+  load_chunk(0, st0);
+  chunk(0, st0);
+  for (int c = 1; c < nc; ++c) chunk(c, st0);
 }
 
 }  // namespace
