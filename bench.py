@@ -150,7 +150,7 @@ def main():
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device copy (counter calibration)")
-    ap.add_argument("--only", choices=["bwd", "step", "conv", "ssd"],
+    ap.add_argument("--only", choices=["bwd", "step", "conv", "ssd", "bidir"],
                     help="only time the backward (Mamba-130M shape), the decode step or the "
                          "Conv1d + SiLU and print their figures (for profiling runs)")
     args = ap.parse_args()
@@ -176,6 +176,9 @@ def main():
         return
     if args.only == "conv":
         print(json.dumps(time_conv(torch, Bnd, synth, args.steps, args.warmup)), flush=True)
+        return
+    if args.only == "bidir":
+        print(json.dumps(time_bidir(torch, Bnd, synth, args.steps, args.warmup)), flush=True)
         return
     if args.only == "ssd":
         print(json.dumps(time_ssd(torch, Bnd, synth, args.steps, args.warmup)), flush=True)
@@ -262,6 +265,7 @@ def extras(torch, Bnd, synth, args):
     out.update(time_step(torch, Bnd, synth))
     out.update(time_conv(torch, Bnd, synth, steps, warm))
     out.update(time_ssd(torch, Bnd, synth, steps, warm))
+    out.update(time_bidir(torch, Bnd, synth, steps, warm))
     return out
 
 
@@ -353,6 +357,31 @@ def time_bwd(torch, Bnd, synth, steps, warm):
         out["bwd_130m:" + disc] = {"ms": round(per, 4), "elements_per_s": w.elements / (per * 1e-3),
                                    "hbm_gbs": round(alg / (per * 1e-3) / 1e9, 1)}
     del d, inp
+    torch.cuda.empty_cache()
+    return out
+
+
+def time_bidir(torch, Bnd, synth, steps, warm):
+    """Bidirectional scan at the Mamba-2.8B shape: the forward call, then the
+    reverse-time call adding into y (two launches); the reverse call alone too."""
+    name = "fwd_2p8b_bf16_b8_l2048_d5120"
+    w = synth.WORKLOADS[name]
+    inp = synth.make_workload(name)
+    d = upload(inp, torch)
+    y = torch.empty((w.B, w.L, w.D), dtype=torch.float32, device="cuda")
+    desc = Bnd.make_desc(w.B, w.L, w.D, w.N, Bnd.SS_BF16, Bnd.SS_F32, Bnd._DISC[w.disc], True)
+    nb = Bnd.ss_scan_workspace_bytes(desc, Bnd.SS_OP_FWD)
+    ws = Bnd.workspace(nb, "cuda")
+    args = (d["u"], d["delta"], d["A"], d["B"], d["C"], d["D"], d["delta_bias"], d["z"], None, y,
+            None, ws, nb)
+    rev = lambda acc: Bnd.ss_scan_fwd_dir(desc, Bnd.SS_DIR_REVERSE, acc, *args)  # noqa
+    both = lambda: (Bnd.ss_scan_fwd_dir(desc, Bnd.SS_DIR_FORWARD, 0, *args), rev(1))  # noqa
+    out = {}
+    for key, f, mult in (("bidir_2p8b:fwd+rev_acc", both, 2), ("bidir_2p8b:rev", lambda: rev(0), 1)):
+        total, per, mn, _ = time_calls(f, steps, warm, torch)
+        out[key] = {"ms": round(per, 4), "ms_min": round(mn, 4),
+                    "elements_per_s": mult * w.elements / (per * 1e-3)}
+    del d, y, ws, inp
     torch.cuda.empty_cache()
     return out
 

@@ -107,6 +107,36 @@ int ss_scan_fwd(const ss_desc_t* desc,
                 void* y, float* h_last,
                 void* workspace, size_t ws_bytes, void* stream);
 
+/* Time directions of ss_scan_fwd_dir. */
+#define SS_DIR_FORWARD 0
+#define SS_DIR_REVERSE 1
+
+/*
+ * Forward selective scan in either time direction, optionally added to y.
+ * Scan modes: a scan that runs only forward in time sees no later tokens,
+ * which suits text but not images or video; flat scan modes therefore also
+ * scan the token sequence the other way and combine the results ("A Survey of
+ * Mamba" summary, section on scan modes).
+ *   direction = SS_DIR_FORWARD: exactly ss_scan_fwd.
+ *   direction = SS_DIR_REVERSE: the same system run from t = L-1 down to 0,
+ *       h_t = abar_t h_{t+1} + bbar_t u_t,  y_t = C_t h_t + D_skip u_t (gated),
+ *       i.e. ss_scan_fwd on the time-reversed sequence, reversed back.  h0 is
+ *       the state entering at t = L-1, h_last the state after t = 0.
+ *   accumulate != 0: y += result (y must hold valid values of out_dtype;
+ *       the addition is done in fp32).  A bidirectional scan is a forward call
+ *       followed by a reverse call with accumulate = 1 (each direction may use
+ *       its own A, D_skip, delta_bias).
+ * Other arguments, workspace size and status codes as ss_scan_fwd.
+ * Returns SS_ERR_INVALID_ARG for any other direction.
+ */
+int ss_scan_fwd_dir(const ss_desc_t* desc, int direction, int accumulate,
+                    const void* u, const void* delta, const float* A,
+                    const void* Bm, const void* Cm,
+                    const float* D_skip, const float* delta_bias, const void* z,
+                    const float* h0,
+                    void* y, float* h_last,
+                    void* workspace, size_t ws_bytes, void* stream);
+
 /*
  * Backward of ss_scan_fwd with recomputation: the states are rebuilt from the
  * inputs (chunk start states in the workspace, the rest on chip), never read

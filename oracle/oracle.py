@@ -117,6 +117,23 @@ def fwd(u, delta, A, B, C, D=None, delta_bias=None, z=None, h0=None,
     return out, h_last
 
 
+def _flip_t(x):
+    return None if x is None else np.ascontiguousarray(np.asarray(x)[:, ::-1])
+
+
+def fwd_reverse(u, delta, A, B, C, D=None, delta_bias=None, z=None, h0=None,
+                disc="zoh", softplus=True, nthreads=1):
+    """The same system run backwards in time ("A Survey of Mamba" summary, scan
+    modes: scanning the token sequence the other way), by definition the forward
+    scan of the time-reversed sequence, reversed back:
+    h_t = abar_t h_{t+1} + bbar_t u_t for t = L-1 .. 0; h0 enters at t = L-1 and
+    h_last is the state after t = 0.  Returns (out, h_last)."""
+    out, h_last = fwd(_flip_t(u), _flip_t(delta), A, _flip_t(B), _flip_t(C), D=D,
+                      delta_bias=delta_bias, z=_flip_t(z), h0=h0, disc=disc,
+                      softplus=softplus, nthreads=nthreads)
+    return np.ascontiguousarray(out[:, ::-1]), h_last
+
+
 def bwd(u, delta, A, B, C, D=None, delta_bias=None, z=None, h0=None, g=None,
         disc="zoh", softplus=True):
     """Backward scan. Returns a dict of float64 gradients

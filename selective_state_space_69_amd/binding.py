@@ -1,13 +1,13 @@
 """Thin ctypes binding of libssscan.so (C ABI declared in include/ss_scan.h,
 include/ss_conv.h and include/ss_ssd.h).
 
-The functions named like the C entry points (ss_scan_fwd, ss_scan_bwd,
-ss_scan_step, ss_scan_workspace_bytes, ss_scan_strerror, ss_scan_version,
+The functions named like the C entry points (ss_scan_fwd, ss_scan_fwd_dir,
+ss_scan_bwd, ss_scan_step, ss_scan_workspace_bytes, ss_scan_strerror, ss_scan_version,
 ss_conv1d_fwd, ss_conv1d_bwd, ss_conv1d_step, ss_conv1d_workspace_bytes, ss_ssd_fwd) only
 marshal arguments: torch tensors become device pointers, None becomes NULL and
 the stream defaults to torch's current HIP stream.  Every step runs in the HIP
 kernels; there is no fallback.  The convenience wrappers scan_fwd, scan_bwd,
-scan_step, conv1d_fwd, conv1d_bwd, conv1d_step and ssd_fwd additionally allocate
+scan_bidir, scan_step, conv1d_fwd, conv1d_bwd, conv1d_step and ssd_fwd additionally allocate
 outputs and workspace with torch.
 """
 from __future__ import annotations
@@ -24,6 +24,7 @@ SS_OK, SS_ERR_INVALID_ARG, SS_ERR_UNSUPPORTED, SS_ERR_WORKSPACE, SS_ERR_HIP = 0,
 SS_F32, SS_BF16 = 0, 1
 SS_ZOH, SS_EULER = 0, 1
 SS_OP_FWD, SS_OP_BWD = 0, 1
+SS_DIR_FORWARD, SS_DIR_REVERSE = 0, 1
 
 _DTYPE = {torch.float32: SS_F32, torch.bfloat16: SS_BF16}
 _DISC = {"zoh": SS_ZOH, "euler": SS_EULER}
@@ -73,6 +74,8 @@ def load_library():
         lib.ss_scan_workspace_bytes.restype = SZ
         lib.ss_scan_fwd.argtypes = [D] + [P] * 11 + [P, SZ, P]
         lib.ss_scan_fwd.restype = I
+        lib.ss_scan_fwd_dir.argtypes = [D, I, I] + [P] * 11 + [P, SZ, P]
+        lib.ss_scan_fwd_dir.restype = I
         lib.ss_scan_bwd.argtypes = [D] + [P] * 19 + [P, SZ, P]
         lib.ss_scan_bwd.restype = I
         lib.ss_scan_step.argtypes = [D] + [P] * 10 + [P]
@@ -136,6 +139,14 @@ def ss_scan_fwd(desc, u, delta, A, Bm, Cm, D_skip, delta_bias, z, h0, y, h_last,
     return load_library().ss_scan_fwd(ctypes.byref(desc), _p(u), _p(delta), _p(A), _p(Bm), _p(Cm),
                                       _p(D_skip), _p(delta_bias), _p(z), _p(h0), _p(y), _p(h_last),
                                       _p(workspace), int(ws_bytes), _stream(stream))
+
+
+def ss_scan_fwd_dir(desc, direction, accumulate, u, delta, A, Bm, Cm, D_skip, delta_bias, z, h0,
+                    y, h_last, workspace, ws_bytes, stream=None) -> int:
+    return load_library().ss_scan_fwd_dir(ctypes.byref(desc), int(direction), int(accumulate),
+                                          _p(u), _p(delta), _p(A), _p(Bm), _p(Cm), _p(D_skip),
+                                          _p(delta_bias), _p(z), _p(h0), _p(y), _p(h_last),
+                                          _p(workspace), int(ws_bytes), _stream(stream))
 
 
 def ss_scan_bwd(desc, u, delta, A, Bm, Cm, D_skip, delta_bias, z, h0, dy, du, ddelta, dA, dB, dC,
@@ -209,18 +220,36 @@ def workspace(nbytes: int, device) -> torch.Tensor | None:
 
 def scan_fwd(u, delta, A, B, C, D=None, delta_bias=None, z=None, h0=None, disc="zoh",
              softplus=True, out_dtype=torch.float32, return_last_state=False, stream=None,
-             ws=None):
-    """Forward scan on device tensors; returns y (and h_last)."""
-    desc = _desc_from(u, A, disc, softplus, out_dtype)
-    y = torch.empty(u.shape, dtype=out_dtype, device=u.device)
+             ws=None, reverse=False, y=None):
+    """Forward scan on device tensors; returns y (and h_last).  reverse=True runs
+    the system from the last step to the first; passing y adds the result to it
+    (in place) instead of allocating a new output."""
+    desc = _desc_from(u, A, disc, softplus, out_dtype if y is None else y.dtype)
+    acc = y is not None
+    if y is None:
+        y = torch.empty(u.shape, dtype=out_dtype, device=u.device)
     h_last = (torch.empty((u.shape[0], u.shape[2], A.shape[1]), dtype=torch.float32,
                           device=u.device) if return_last_state else None)
     nb = ss_scan_workspace_bytes(desc, SS_OP_FWD)
     if ws is None or ws.numel() < nb:
         ws = workspace(nb, u.device)
-    _check(ss_scan_fwd(desc, u, delta, A, B, C, D, delta_bias, z, h0, y, h_last, ws, nb, stream),
-           "ss_scan_fwd")
+    _check(ss_scan_fwd_dir(desc, SS_DIR_REVERSE if reverse else SS_DIR_FORWARD, int(acc), u, delta,
+                           A, B, C, D, delta_bias, z, h0, y, h_last, ws, nb, stream),
+           "ss_scan_fwd_dir")
     return (y, h_last) if return_last_state else y
+
+
+def scan_bidir(u, delta, A, B, C, D=None, delta_bias=None, z=None, disc="zoh", softplus=True,
+               A_rev=None, D_rev=None, delta_bias_rev=None, out_dtype=torch.float32, stream=None):
+    """Bidirectional scan: the forward scan plus the reverse-time scan (with its
+    own A, D, delta_bias when given), summed inside the second kernel."""
+    y = scan_fwd(u, delta, A, B, C, D=D, delta_bias=delta_bias, z=z, disc=disc,
+                 softplus=softplus, out_dtype=out_dtype, stream=stream)
+    scan_fwd(u, delta, A if A_rev is None else A_rev, B, C,
+             D=D if D_rev is None else D_rev,
+             delta_bias=delta_bias if delta_bias_rev is None else delta_bias_rev, z=z, disc=disc,
+             softplus=softplus, stream=stream, reverse=True, y=y)
+    return y
 
 
 def scan_bwd(u, delta, A, B, C, dy, D=None, delta_bias=None, z=None, h0=None, disc="zoh",

@@ -228,8 +228,17 @@ int ss_scan_fwd(const ss_desc_t* desc, const void* u, const void* delta, const f
                 const void* Bm, const void* Cm, const float* D_skip, const float* delta_bias,
                 const void* z, const float* h0, void* y, float* h_last, void* workspace,
                 size_t ws_bytes, void* stream) {
+  return ss_scan_fwd_dir(desc, SS_DIR_FORWARD, 0, u, delta, A, Bm, Cm, D_skip, delta_bias, z, h0,
+                         y, h_last, workspace, ws_bytes, stream);
+}
+
+int ss_scan_fwd_dir(const ss_desc_t* desc, int direction, int accumulate, const void* u,
+                    const void* delta, const float* A, const void* Bm, const void* Cm,
+                    const float* D_skip, const float* delta_bias, const void* z, const float* h0,
+                    void* y, float* h_last, void* workspace, size_t ws_bytes, void* stream) {
   int rc = check_desc(desc, true);
   if (rc != SS_OK) return rc;
+  if (direction != SS_DIR_FORWARD && direction != SS_DIR_REVERSE) return SS_ERR_INVALID_ARG;
   if (!u || !delta || !A || !Bm || !Cm || !y) return SS_ERR_INVALID_ARG;
   if (h_last && h0 && static_cast<const void*>(h_last) == static_cast<const void*>(h0))
     return SS_ERR_INVALID_ARG;
@@ -241,6 +250,8 @@ int ss_scan_fwd(const ss_desc_t* desc, const void* u, const void* delta, const f
     return SS_ERR_WORKSPACE;
   FwdArgs a{u, delta, A, Bm, Cm, D_skip, delta_bias, z, h0, y, h_last,
             nullptr, nullptr, nullptr, nullptr};
+  a.rev = direction == SS_DIR_REVERSE;
+  a.acc = accumulate != 0;
   char* ws = static_cast<char*>(workspace);
   if (plan.packed_rows) {
     a.Brow = ws + plan.off_brow;

@@ -56,7 +56,7 @@ struct Lds {
 // which alone computes its softplus step size (shared with the other waves
 // through LDS), its gate, and its final output.
 template <typename In, typename Out, int DISC, bool HAS_Z, bool SOFTPLUS, bool SUMMARY, bool SAFE,
-          int NSPLIT>
+          int NSPLIT, bool REV>
 struct Scan {
   static constexpr int NS = kMaxState / NSPLIT;
   static constexpr int OWN = kPrefetch / NSPLIT;   // steps owned per block
@@ -65,8 +65,9 @@ struct Scan {
   float (&h)[NS];
   float Dd, bias2;
   float dsum;
-  int64_t row0;          // b * L
-  const In* ub;          // wave-uniform base pointers of (b, t = 0, d = 64 * dblk)
+  int64_t bidx;          // batch row
+  TimeDir<REV> td;
+  const In* ub;          // wave-uniform base pointers of (b, logical t = 0, d = 64 * dblk)
   const In* db;
   const In* zb;
   Out* yb;
@@ -92,23 +93,27 @@ struct Scan {
   // the owned steps, B/C rows.  load_u issues one step's u, so that inside a
   // block each load can reuse the register its predecessor in the slot has
   // just released.
-  __device__ __forceinline__ Rsrc u_rsrc(int32_t t) const { return make_rsrc(ub + int64_t(t) * p.D); }
+  template <typename T>
+  __device__ __forceinline__ Rsrc at(const T* base, int32_t t) const {
+    return make_rsrc(base + int64_t(td.blk(t)) * td.ts);
+  }
+  __device__ __forceinline__ Rsrc u_rsrc(int32_t t) const { return at(ub, t); }
   template <int S>
   __device__ __forceinline__ void load_u(const Rsrc& ru, int k, int32_t lim, bool clamp) {
     int32_t tt = k;
     if (clamp) tt = tt < lim ? tt : lim;
-    ur[S][k] = buf_load<In>(ru, vin, uint32_t(tt) * rowb_in);
+    ur[S][k] = buf_load<In>(ru, vin, td.pos(tt) * rowb_in);
   }
   template <int S>
   __device__ __forceinline__ void load_owned(int32_t t, bool clamp) {
-    const Rsrc ru = u_rsrc(t), rd = make_rsrc(db + int64_t(t) * p.D);
-    const Rsrc rz = make_rsrc(HAS_Z ? zb + int64_t(t) * p.D : ub);
+    const Rsrc ru = u_rsrc(t), rd = at(db, t);
+    const Rsrc rz = at(HAS_Z ? zb : ub, t);
     const int32_t lim = tlast - t;    // last valid step, relative to t
 #pragma unroll
     for (int i = 0; i < OWN; ++i) {
       int32_t tt = owned(i);
       if (clamp) tt = tt < lim ? tt : lim;
-      const uint32_t so = uint32_t(tt) * rowb_in;
+      const uint32_t so = td.pos(tt) * rowb_in;
       dr[S][i] = buf_load<In>(rd, vin, so);
       if (HAS_Z && !SUMMARY) zr[S][i] = buf_load<In>(rz, vin, so);
       // a second read of u for the owned steps: the ring cannot be indexed by
@@ -154,8 +159,9 @@ struct Scan {
     const int k = int(l / G), g = int(l % G);
     int32_t tr = t + k;
     tr = tr < tlast ? tr : tlast;
+    const int64_t rw = REV ? bidx * p.L + (p.L - 1) - tr : bidx * p.L + tr;
     const In* src = static_cast<const In*>(g < G / 2 ? p.Brow : p.Crow) +
-                    (row0 + tr) * kMaxState + n0 + 4 * (g % (G / 2));
+                    rw * kMaxState + n0 + 4 * (g % (G / 2));
     rowq[S] = load_raw4(src);
   }
   template <int S>
@@ -202,7 +208,7 @@ struct Scan {
     load_owned<S>(tn, GUARD);
     fetch_rows<S>(tn);
     const Rsrc ru = u_rsrc(tn);
-    const Rsrc ry = make_rsrc(yb + int64_t(t) * p.D);
+    const Rsrc ry = at(yb, t);
     const float* dls = act + S * kPrefetch * kWave + lane;
     float* parts = part + (S * NSPLIT + wave) * kPrefetch * kWave + lane;
     // the recurrence, one step at a time (rows and step sizes read one step ahead)
@@ -261,7 +267,11 @@ struct Scan {
           // one wave holds every state: y of step k is complete
           float yv = __builtin_fmaf(Dd, uk, acc);                  // + D skip
           if (HAS_Z) yv *= g[k];                                   // silu(z) gate
-          if (!GUARD || t + k < t1) buf_store<Out>(ry, vout, uint32_t(k) * rowb_out, yv);
+          if (!GUARD || t + k < t1) {
+            const uint32_t so = td.pos(k) * rowb_out;
+            if (p.acc) yv += to_f32(buf_load<Out>(ry, vout, so));
+            buf_store<Out>(ry, vout, so, yv);
+          }
         }
       }
     }
@@ -280,7 +290,11 @@ struct Scan {
       for (int w = 0; w < NSPLIT; ++w) yv += part[((S * NSPLIT + w) * kPrefetch + k) * kWave + lane];
       yv = __builtin_fmaf(Dd, us[i], yv);                          // + D skip
       if (HAS_Z) yv *= g[i];                                       // silu(z) gate
-      if (!GUARD || t + k < t1) buf_store<Out>(ry, vout, uint32_t(k) * rowb_out, yv);
+      if (!GUARD || t + k < t1) {
+        const uint32_t so = td.pos(k) * rowb_out;
+        if (p.acc) yv += to_f32(buf_load<Out>(ry, vout, so));
+        buf_store<Out>(ry, vout, so, yv);
+      }
     }
   }
 
@@ -313,7 +327,8 @@ struct Scan {
 template <int NSPLIT>
 constexpr int kMinWaves = NSPLIT == 1 ? 2 : 3;
 
-template <typename In, typename Out, int DISC, bool HAS_Z, bool SOFTPLUS, bool SUMMARY, int NSPLIT>
+template <typename In, typename Out, int DISC, bool HAS_Z, bool SOFTPLUS, bool SUMMARY, int NSPLIT,
+          bool REV>
 __global__ __launch_bounds__(kWave * NSPLIT, kMinWaves<NSPLIT>) void fwd_kernel(FwdParams p) {
   constexpr int NS = kMaxState / NSPLIT;
   // wave-uniform by construction; readfirstlane lets the compiler keep it in an SGPR
@@ -361,7 +376,7 @@ __global__ __launch_bounds__(kWave * NSPLIT, kMinWaves<NSPLIT>) void fwd_kernel(
 
   __shared__ float4 lds4[(Lds<NSPLIT>::kFloats + 3) / 4];
   float* lds = reinterpret_cast<float*>(lds4);
-  const int64_t base = b * p.L * p.D + int64_t(dblk) * kWave;
+  const int64_t base = b * p.L * p.D + (REV ? (p.L - 1) * p.D : 0) + int64_t(dblk) * kWave;
   auto setup = [&](auto& sc) {
     sc.stage = lds + wave * Lds<NSPLIT>::kStage;
     sc.act = lds + NSPLIT * Lds<NSPLIT>::kStage;
@@ -372,7 +387,8 @@ __global__ __launch_bounds__(kWave * NSPLIT, kMinWaves<NSPLIT>) void fwd_kernel(
     sc.Dd = p.Dskip ? p.Dskip[dc] : 0.0f;
     sc.bias2 = (p.bias ? p.bias[dc] : 0.0f) * kLog2e;
     sc.dsum = 0.0f;
-    sc.row0 = b * p.L;
+    sc.bidx = b;
+    sc.td.ts = REV ? -p.D : p.D;
     sc.ub = static_cast<const In*>(p.u) + base;
     sc.db = static_cast<const In*>(p.delta) + base;
     sc.zb = p.z ? static_cast<const In*>(p.z) + base : nullptr;
@@ -390,10 +406,10 @@ __global__ __launch_bounds__(kWave * NSPLIT, kMinWaves<NSPLIT>) void fwd_kernel(
   // exact ZOH needs the dt * B fallback only where some A entry is exactly 0
   // (decided per wave; every wave still passes the same barriers)
   if (DISC == kZoh && __any(zero)) {
-    Scan<In, Out, DISC, HAS_Z, SOFTPLUS, SUMMARY, true, NSPLIT> sc{p, ch, h};
+    Scan<In, Out, DISC, HAS_Z, SOFTPLUS, SUMMARY, true, NSPLIT, REV> sc{p, ch, h};
     dsum = setup(sc);
   } else {
-    Scan<In, Out, DISC, HAS_Z, SOFTPLUS, SUMMARY, false, NSPLIT> sc{p, ch, h};
+    Scan<In, Out, DISC, HAS_Z, SOFTPLUS, SUMMARY, false, NSPLIT, REV> sc{p, ch, h};
     dsum = setup(sc);
   }
 
@@ -426,15 +442,20 @@ __global__ __launch_bounds__(256) void pack_rows_kernel(const In* __restrict__ B
   Cp[gid] = n < N ? Cm[r * N + n] : In(0);
 }
 
-template <typename In, typename Out, int DISC, bool HAS_Z, bool SOFTPLUS, bool SUMMARY, int NSPLIT>
+template <typename In, typename Out, int DISC, bool HAS_Z, bool SOFTPLUS, bool SUMMARY, int NSPLIT,
+          bool REV = false>
 hipError_t launch_one(const FwdParams& p, int64_t nblocks, hipStream_t st) {
-  hipLaunchKernelGGL((fwd_kernel<In, Out, DISC, HAS_Z, SOFTPLUS, SUMMARY, NSPLIT>),
+  hipLaunchKernelGGL((fwd_kernel<In, Out, DISC, HAS_Z, SOFTPLUS, SUMMARY, NSPLIT, REV>),
                      dim3(unsigned(nblocks)), dim3(kWave * NSPLIT), 0, st, p);
   return hipGetLastError();
 }
 
+// The reverse direction runs on the 4-wave layout only (its register use
+// leaves room for the mirrored addressing); the chunk plan, and with it the
+// workspace, is the forward one.
 template <typename In, typename Out, int DISC, bool HAS_Z, bool SOFTPLUS, bool SUMMARY>
 hipError_t dispatch_split(const FwdParams& p, int nsplit, int64_t nblocks, hipStream_t st) {
+  if (p.rev) return launch_one<In, Out, DISC, HAS_Z, SOFTPLUS, SUMMARY, 4, true>(p, nblocks, st);
   switch (nsplit) {
     case 4: return launch_one<In, Out, DISC, HAS_Z, SOFTPLUS, SUMMARY, 4>(p, nblocks, st);
     case 2: return launch_one<In, Out, DISC, HAS_Z, SOFTPLUS, SUMMARY, 2>(p, nblocks, st);
@@ -490,6 +511,8 @@ FwdParams make_params(const ss_desc_t& d, const TimePlan& tp, const FwdArgs& a) 
   p.L = d.seqlen; p.D = d.dim; p.N = int32_t(d.dstate);
   p.chunk_len = tp.chunk_len;
   p.nchunks = int32_t(tp.nchunks);
+  p.rev = a.rev ? 1 : 0;
+  p.acc = a.acc ? 1 : 0;
   const int64_t width = tp.nsplit == kHalfWaveSplit ? 32 : kWave;   // channels per workgroup
   p.ndblk = int32_t((d.dim + width - 1) / width);
   return p;

@@ -28,6 +28,28 @@ struct FwdParams {
   int64_t L, D;
   int64_t chunk_len;
   int32_t N, ndblk, nchunks, grid_chunks;
+  // Time direction.  Logical step t of a batch row is physical step t
+  // (forward) or L - 1 - t (reverse); the recurrence always runs over logical
+  // steps.  Buffer offsets cannot be negative, so in reverse a block of 8
+  // steps is addressed from its last logical step (its lowest address) and
+  // logical step t + k sits at position 7 - k.
+  int32_t rev;
+  int32_t acc;   // nonzero: y += result (the old y is read in the output type)
+};
+
+// Address helpers of the time direction (compile time; forward code is the
+// plain t * D addressing).
+template <bool REV>
+struct TimeDir {
+  int64_t ts;     // elements from logical step t to t + 1 (+D or -D)
+  __device__ __forceinline__ int32_t blk(int32_t t) const { return REV ? t + (kBlk - 1) : t; }
+  __device__ __forceinline__ uint32_t pos(int32_t k) const {
+    return uint32_t(REV ? (kBlk - 1) - k : k);
+  }
+  // row index (b * L + physical step) of the block base of logical step t
+  __device__ __forceinline__ int64_t row(int64_t b, int64_t L, int32_t t) const {
+    return REV ? b * L + (L - 1) - blk(t) : b * L + t;
+  }
 };
 
 // Launch of the 32-channel kernel over B * ndblk * grid_chunks workgroups

@@ -38,7 +38,8 @@ constexpr int kPartRow = (kBlk + 1) * kCh;
 constexpr int kPartF = kOwners * kPartRow;
 constexpr int kLdsF = 2 * (kActF + kStageF + kPartF);
 
-template <typename In, typename Out, int DISC, bool HAS_Z, bool SOFTPLUS, bool SUMMARY, bool SAFE>
+template <typename In, typename Out, int DISC, bool HAS_Z, bool SOFTPLUS, bool SUMMARY, bool SAFE,
+          bool REV>
 struct HalfScan {
   using Raw2 = typename std::conditional<sizeof(In) == 2, uint32_t, uint2>::type;
   const FwdParams& p;
@@ -46,8 +47,9 @@ struct HalfScan {
   float h[2];
   float Dd, bias2;
   float dsum;
-  int64_t row0;          // b * L
-  const In* ub;          // wave-uniform base pointers of (b, t = 0, d = 32 * dblk)
+  int64_t bidx;          // batch row
+  TimeDir<REV> td;
+  const In* ub;          // wave-uniform base pointers of (b, logical t = 0, d = 32 * dblk)
   const In* db;
   const In* zb;
   Out* yb;
@@ -76,29 +78,34 @@ struct HalfScan {
   // the owned step, this lane's B/C pair.  The u loads can be issued one step
   // at a time (load_u) so that each reuses the register its predecessor in
   // the slot has just released.
-  __device__ __forceinline__ Rsrc u_rsrc(int32_t t) const { return make_rsrc(ub + int64_t(t) * p.D); }
+  template <typename T>
+  __device__ __forceinline__ Rsrc at(const T* base, int32_t t) const {
+    return make_rsrc(base + int64_t(td.blk(t)) * td.ts);
+  }
+  __device__ __forceinline__ Rsrc u_rsrc(int32_t t) const { return at(ub, t); }
   template <int S>
   __device__ __forceinline__ void load_u(const Rsrc& ru, int k, int32_t lim, bool clamp) {
     int32_t tt = k;
     if (clamp) tt = tt < lim ? tt : lim;
-    ur[S][k] = buf_load<In>(ru, vin, uint32_t(tt) * rowb_in);
+    ur[S][k] = buf_load<In>(ru, vin, td.pos(tt) * rowb_in);
   }
   template <int S>
   __device__ __forceinline__ void load_rest(int32_t t, bool clamp) {
-    const Rsrc ru = u_rsrc(t), rd = make_rsrc(db + int64_t(t) * p.D);
-    const Rsrc rz = make_rsrc(HAS_Z ? zb + int64_t(t) * p.D : ub);
+    const Rsrc ru = u_rsrc(t), rd = at(db, t);
+    const Rsrc rz = at(HAS_Z ? zb : ub, t);
     const int32_t lim = tlast - t;
     uint32_t vo = vown;
-    if (clamp) vo = vin + uint32_t(o < lim ? o : lim) * rowb_in;
+    if (clamp) vo = vin + td.pos(o < lim ? o : lim) * rowb_in;
     dr[S] = buf_load<In>(rd, vo, 0);
     if (HAS_Z && !SUMMARY) zr[S] = buf_load<In>(rz, vo, 0);
     if (!SUMMARY) uo[S] = buf_load<In>(ru, vo, 0);
     // B/C pair: step k_row of the block, states 2 * (owner) .. + 1
-    const Rsrc rB = make_rsrc(brb + (row0 + t) * kMaxState);
-    const Rsrc rC = make_rsrc(crb + (row0 + t) * kMaxState);
+    const int64_t rw = td.row(bidx, p.L, t);
+    const Rsrc rB = make_rsrc(brb + rw * kMaxState);
+    const Rsrc rC = make_rsrc(crb + rw * kMaxState);
     uint32_t vr = vrow;
-    if (clamp) vr = vrow - uint32_t(k_row) * uint32_t(kMaxState * sizeof(In)) +
-                    uint32_t(k_row < lim ? k_row : lim) * uint32_t(kMaxState * sizeof(In));
+    if (clamp) vr = vrow - td.pos(k_row) * uint32_t(kMaxState * sizeof(In)) +
+                    td.pos(k_row < lim ? k_row : lim) * uint32_t(kMaxState * sizeof(In));
     rb[S] = load_pair(rB, vr);
     if (!SUMMARY) rc[S] = load_pair(rC, vr);
   }
@@ -198,7 +205,11 @@ struct HalfScan {
     for (int w = 0; w < kOwners; ++w) yv += part[S * kPartF + w * kPartRow + o * kCh + c];
     yv = __builtin_fmaf(Dd, us, yv);                                 // + D skip
     if (HAS_Z) yv *= g;                                              // silu(z) gate
-    if (!GUARD || t + o < t1) buf_store<Out>(make_rsrc(yb + int64_t(t) * p.D), vout, 0, yv);
+    if (!GUARD || t + o < t1) {
+      const Rsrc ry = at(yb, t);
+      if (p.acc) yv += to_f32(buf_load<Out>(ry, vout, 0));
+      buf_store<Out>(ry, vout, 0, yv);
+    }
   }
 
   __device__ __forceinline__ void run(int32_t t0) {
@@ -220,7 +231,7 @@ struct HalfScan {
   }
 };
 
-template <typename In, typename Out, int DISC, bool HAS_Z, bool SOFTPLUS, bool SUMMARY>
+template <typename In, typename Out, int DISC, bool HAS_Z, bool SOFTPLUS, bool SUMMARY, bool REV>
 // five waves per SIMD: five workgroups per compute unit
 __global__ __launch_bounds__(kWave * kWaves, 5) void fwd_hw_kernel(FwdParams p) {
   const int wave = __builtin_amdgcn_readfirstlane(int(threadIdx.x) / kWave);
@@ -249,7 +260,7 @@ __global__ __launch_bounds__(kWave * kWaves, 5) void fwd_hw_kernel(FwdParams p) 
 
   __shared__ float4 lds4[kLdsF / 4];
   float* lds = reinterpret_cast<float*>(lds4);
-  const int64_t base = b * p.L * p.D + int64_t(dblk) * kCh;
+  const int64_t base = b * p.L * p.D + (REV ? (p.L - 1) * p.D : 0) + int64_t(dblk) * kCh;
 
   float Av[2];
   bool zero = false;
@@ -278,7 +289,8 @@ __global__ __launch_bounds__(kWave * kWaves, 5) void fwd_hw_kernel(FwdParams p) 
     sc.Dd = p.Dskip ? p.Dskip[dc] : 0.0f;
     sc.bias2 = (p.bias ? p.bias[dc] : 0.0f) * kLog2e;
     sc.dsum = 0.0f;
-    sc.row0 = b * p.L;
+    sc.bidx = b;
+    sc.td.ts = REV ? -p.D : p.D;
     sc.ub = static_cast<const In*>(p.u) + base;
     sc.db = static_cast<const In*>(p.delta) + base;
     sc.zb = p.z ? static_cast<const In*>(p.z) + base : nullptr;
@@ -288,13 +300,13 @@ __global__ __launch_bounds__(kWave * kWaves, 5) void fwd_hw_kernel(FwdParams p) 
     sc.rowb_in = uint32_t(p.D) * uint32_t(sizeof(In));
     sc.rowb_out = uint32_t(p.D) * uint32_t(sizeof(Out));
     sc.vin = c_c * uint32_t(sizeof(In));
-    sc.vown = sc.vin + uint32_t(o) * sc.rowb_in;
-    sc.vout = active ? c_c * uint32_t(sizeof(Out)) + uint32_t(o) * sc.rowb_out : kOutOfRange;
+    sc.vown = sc.vin + sc.td.pos(o) * sc.rowb_in;
+    sc.vout = active ? c_c * uint32_t(sizeof(Out)) + sc.td.pos(o) * sc.rowb_out : kOutOfRange;
     // fetch slot of this lane: step k_row = l % 8 of the block, owner 2w + (l / 8) % 2
     // (lanes 16..63 repeat lanes 0..15)
     sc.k_row = lane % kBlk;
     const int fo = 2 * wave + (lane / kBlk) % 2;
-    sc.vrow = uint32_t(sc.k_row * kMaxState + 2 * fo) * uint32_t(sizeof(In));
+    sc.vrow = (sc.td.pos(sc.k_row) * kMaxState + 2 * fo) * uint32_t(sizeof(In));
     sc.t1 = t1;
     sc.tlast = t1 - 1;
     sc.o = o;
@@ -311,10 +323,10 @@ __global__ __launch_bounds__(kWave * kWaves, 5) void fwd_hw_kernel(FwdParams p) 
   // exact ZOH needs the dt * B fallback only where some A entry is exactly 0
   // (decided per wave; every wave still passes the same barriers)
   if (DISC == kZoh && __any(zero)) {
-    HalfScan<In, Out, DISC, HAS_Z, SOFTPLUS, SUMMARY, true> sc{p};
+    HalfScan<In, Out, DISC, HAS_Z, SOFTPLUS, SUMMARY, true, REV> sc{p};
     go(sc);
   } else {
-    HalfScan<In, Out, DISC, HAS_Z, SOFTPLUS, SUMMARY, false> sc{p};
+    HalfScan<In, Out, DISC, HAS_Z, SOFTPLUS, SUMMARY, false, REV> sc{p};
     go(sc);
   }
 
@@ -333,8 +345,12 @@ __global__ __launch_bounds__(kWave * kWaves, 5) void fwd_hw_kernel(FwdParams p) 
 
 template <typename In, typename Out, int DISC, bool HAS_Z, bool SOFTPLUS, bool SUMMARY>
 hipError_t launch_one(const FwdParams& p, int64_t nblocks, hipStream_t st) {
-  hipLaunchKernelGGL((fwd_hw_kernel<In, Out, DISC, HAS_Z, SOFTPLUS, SUMMARY>),
-                     dim3(unsigned(nblocks)), dim3(kWave * kWaves), 0, st, p);
+  if (p.rev)
+    hipLaunchKernelGGL((fwd_hw_kernel<In, Out, DISC, HAS_Z, SOFTPLUS, SUMMARY, true>),
+                       dim3(unsigned(nblocks)), dim3(kWave * kWaves), 0, st, p);
+  else
+    hipLaunchKernelGGL((fwd_hw_kernel<In, Out, DISC, HAS_Z, SOFTPLUS, SUMMARY, false>),
+                       dim3(unsigned(nblocks)), dim3(kWave * kWaves), 0, st, p);
   return hipGetLastError();
 }
 

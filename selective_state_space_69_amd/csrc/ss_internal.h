@@ -77,6 +77,8 @@ struct FwdArgs {
   void* Crow;
   float* hend;
   float* dsum;
+  int rev = 0;   // reverse time: h_t from h_{t+1}, t = L-1 .. 0
+  int acc = 0;   // add the result to y instead of overwriting it
 };
 
 struct BwdArgs {

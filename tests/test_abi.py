@@ -35,7 +35,7 @@ def test_header_declares_entry_points():
     names = declared_functions()
     for n in ("ss_scan_fwd", "ss_scan_bwd", "ss_scan_step", "ss_scan_workspace_bytes",
               "ss_scan_strerror", "ss_scan_version", "ss_conv1d_fwd", "ss_conv1d_bwd",
-              "ss_conv1d_step", "ss_conv1d_workspace_bytes", "ss_ssd_fwd"):
+              "ss_conv1d_step", "ss_conv1d_workspace_bytes", "ss_ssd_fwd", "ss_scan_fwd_dir"):
         assert n in names
 
 
@@ -203,3 +203,14 @@ def test_ssd_validation(lib):
     assert ssd(ok, D=FAKE + 2) == B.SS_ERR_INVALID_ARG           # misaligned
     assert ssd(ok, y=FAKE + 20488) == B.SS_ERR_INVALID_ARG
     assert B.load_library().ss_ssd_fwd(None, *([None] * 8), None) == B.SS_ERR_INVALID_ARG
+
+
+def test_fwd_dir_validation(lib):
+    d = B.make_desc(2, 64, 32, 16, B.SS_F32, B.SS_F32)
+    P = FAKE
+    for bad_dir in (-1, 2, 7):
+        assert B.ss_scan_fwd_dir(d, bad_dir, 0, P, P, P, P, P, None, None, None, None, P + 4096,
+                                 None, None, 0, stream=0) == B.SS_ERR_INVALID_ARG
+    # the rest of the validation is shared with ss_scan_fwd
+    assert B.ss_scan_fwd_dir(d, B.SS_DIR_REVERSE, 1, None, P, P, P, P, None, None, None, None,
+                             P + 4096, None, None, 0, stream=0) == B.SS_ERR_INVALID_ARG
