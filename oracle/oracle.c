@@ -35,6 +35,7 @@
  *  - initial state 0 unless h0 is given; out = y * silu(z) with the D skip inside
  *    the gate.
  */
+#include <complex.h>
 #include <math.h>
 #include <stdint.h>
 #include <stdlib.h>
@@ -412,5 +413,70 @@ int oracle_ssd_fwd(int64_t Bt, int64_t L, int64_t Hh, int64_t P, int64_t N, int6
       free(H);
     }
   }
+  return 0;
+}
+
+/*
+ * Complex diagonal A.  The pages name a complex diagonal initialisation
+ * (S4D-Lin) beside the real one (S4D-Real) ("A Survey of Mamba" summary,
+ * HiPPO-based memory initialisation) and compare complex with real decay in an
+ * ablation ("Mamba: S4 epic upgrade", ablation on A).  A (D,N), B, C (Bt,L,N),
+ * h0 and h_last (Bt,D,N) are complex, stored as (re, im) pairs in a last axis
+ * of 2.  Per channel and step, with the same step size as oracle_fwd:
+ *   abar  = exp(dt a)                                     complex exponential
+ *   bcoef = (exp(dt a) - 1) / a  (exact ZOH; dt when a == 0 or in Euler mode)
+ *   h_n   = abar h_n + bcoef B_n u
+ *   y     = 2 Re(sum_n C_n h_n) + D u      each complex state stands for itself
+ *                                          and its conjugate; the real output
+ *                                          adds both, i.e. twice the real part
+ *   out   = y * silu(z)
+ */
+int oracle_fwd_complex(int64_t Bt, int64_t L, int64_t D, int64_t N, int disc, int softplus,
+                       const double* u, const double* delta, const double* A,
+                       const double* Bm, const double* Cm, const double* Dskip,
+                       const double* bias, const double* z, const double* h0,
+                       double* out, double* h_last, int nthreads) {
+  if (Bt < 0 || L < 0 || D < 0 || N < 1 || N > 64) return -1;
+  int64_t nch = Bt * D;
+#ifdef _OPENMP
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads > 0 ? nthreads : 1)
+#endif
+  for (int64_t ch = 0; ch < nch; ++ch) {
+    int64_t b = ch / D, d = ch % D;
+    double complex h[64];
+    for (int64_t n = 0; n < N; ++n) {
+      int64_t k = ((b * D + d) * N + n) * 2;
+      h[n] = h0 ? h0[k] + I * h0[k + 1] : 0.0;
+    }
+    double dsk = Dskip ? Dskip[d] : 0.0;
+    double bi = bias ? bias[d] : 0.0;
+    for (int64_t t = 0; t < L; ++t) {
+      int64_t i = (b * L + t) * D + d;
+      double dt = step_size(delta[i], bi, softplus);
+      double ut = u[i];
+      double complex acc = 0.0;
+      for (int64_t n = 0; n < N; ++n) {
+        double complex a = A[(d * N + n) * 2] + I * A[(d * N + n) * 2 + 1];
+        double complex abar = cexp(dt * a);
+        double complex bcoef = (disc == ORACLE_EULER || a == 0.0) ? (double complex)dt
+                                                                  : (abar - 1.0) / a;
+        int64_t j = ((b * L + t) * N + n) * 2;
+        double complex Bn = Bm[j] + I * Bm[j + 1];
+        double complex Cn = Cm[j] + I * Cm[j + 1];
+        h[n] = abar * h[n] + bcoef * Bn * ut;     /* recurrence */
+        acc += Cn * h[n];                          /* output contraction */
+      }
+      double y = 2.0 * creal(acc) + dsk * ut;      /* conjugate pairs, skip D u */
+      if (z) y *= z[i] * sigmoid(z[i]);            /* silu(z) gate */
+      out[i] = y;
+    }
+    if (h_last)
+      for (int64_t n = 0; n < N; ++n) {
+        int64_t k = ((b * D + d) * N + n) * 2;
+        h_last[k] = creal(h[n]);
+        h_last[k + 1] = cimag(h[n]);
+      }
+  }
+  (void)nthreads;
   return 0;
 }

@@ -65,6 +65,8 @@ def _load():
         lib.oracle_conv1d_step.restype = I
         lib.oracle_ssd_fwd.argtypes = [I64] * 6 + [I] + [P] * 8 + [I]
         lib.oracle_ssd_fwd.restype = I
+        lib.oracle_fwd_complex.argtypes = [I64, I64, I64, I64, I, I] + [P] * 11 + [I]
+        lib.oracle_fwd_complex.restype = I
         lib.oracle_step.argtypes = [I64, I64, I64, I, I] + [P] * 10
         lib.oracle_step.restype = I
         _lib = lib
@@ -115,6 +117,38 @@ def fwd(u, delta, A, B, C, D=None, delta_bias=None, z=None, h0=None,
     if rc != 0:
         raise ValueError("oracle_fwd failed: %d" % rc)
     return out, h_last
+
+
+def _pairs(x):
+    """Complex arrays (any complex dtype, or real with a last axis of 2) as
+    float64 (..., 2) (re, im) pairs."""
+    if x is None:
+        return None
+    x = np.asarray(x)
+    if np.iscomplexobj(x):
+        x = np.stack([x.real, x.imag], axis=-1)
+    return np.ascontiguousarray(x, dtype=np.float64)
+
+
+def fwd_complex(u, delta, A, B, C, D=None, delta_bias=None, z=None, h0=None,
+                disc="zoh", softplus=True, nthreads=1):
+    """Forward scan with complex diagonal A: A (D,N), B and C (B,L,N), h0 (B,D,N)
+    complex (numpy complex or real with a last axis of 2).  Returns
+    (out (B,L,D) float64, h_last (B,D,N) complex128).  See oracle.c."""
+    u, delta = _f64(u), _f64(delta)
+    A, B, C, h0 = _pairs(A), _pairs(B), _pairs(C), _pairs(h0)
+    D, delta_bias, z = map(_f64, (D, delta_bias, z))
+    Bt, L, Dd = u.shape
+    N = A.shape[1]
+    out = np.empty((Bt, L, Dd), dtype=np.float64)
+    h_last = np.empty((Bt, Dd, N, 2), dtype=np.float64)
+    rc = _load().oracle_fwd_complex(Bt, L, Dd, N, _DISC[disc], int(bool(softplus)),
+                                    _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
+                                    _ptr(delta_bias), _ptr(z), _ptr(h0), _ptr(out), _ptr(h_last),
+                                    int(nthreads))
+    if rc != 0:
+        raise ValueError("oracle_fwd_complex failed: %d" % rc)
+    return out, h_last[..., 0] + 1j * h_last[..., 1]
 
 
 def _flip_t(x):
