@@ -150,7 +150,7 @@ def main():
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device copy (counter calibration)")
-    ap.add_argument("--only", choices=["bwd", "step", "conv", "ssd", "bidir"],
+    ap.add_argument("--only", choices=["bwd", "step", "conv", "ssd", "bidir", "complex"],
                     help="only time the backward (Mamba-130M shape), the decode step or the "
                          "Conv1d + SiLU and print their figures (for profiling runs)")
     args = ap.parse_args()
@@ -176,6 +176,9 @@ def main():
         return
     if args.only == "conv":
         print(json.dumps(time_conv(torch, Bnd, synth, args.steps, args.warmup)), flush=True)
+        return
+    if args.only == "complex":
+        print(json.dumps(time_complex(torch, Bnd, synth, args.steps, args.warmup)), flush=True)
         return
     if args.only == "bidir":
         print(json.dumps(time_bidir(torch, Bnd, synth, args.steps, args.warmup)), flush=True)
@@ -266,6 +269,7 @@ def extras(torch, Bnd, synth, args):
     out.update(time_conv(torch, Bnd, synth, steps, warm))
     out.update(time_ssd(torch, Bnd, synth, steps, warm))
     out.update(time_bidir(torch, Bnd, synth, steps, warm))
+    out.update(time_complex(torch, Bnd, synth, steps, warm))
     return out
 
 
@@ -382,6 +386,27 @@ def time_bidir(torch, Bnd, synth, steps, warm):
         out[key] = {"ms": round(per, 4), "ms_min": round(mn, 4),
                     "elements_per_s": mult * w.elements / (per * 1e-3)}
     del d, y, ws, inp
+    torch.cuda.empty_cache()
+    return out
+
+
+def time_complex(torch, Bnd, synth, steps, warm):
+    """Complex-A forward at the Mamba-2.8B shape (B=8, L=2048, D=5120, N=16
+    complex states, S4D-Lin A, bf16 in, fp32 out, exact ZOH, gate)."""
+    Bt, L, D, N = 8, 2048, 5120, 16
+    inp = synth.make_complex_inputs(Bt, L, D, N, seed=1002, dtype="bf16")
+    bf, f32 = torch.bfloat16, torch.float32
+    cv = lambda x, t: torch.from_numpy(x).to("cuda").to(t).contiguous()  # noqa
+    u, dl, Bm, Cm, z = (cv(a, bf) for a in (inp.u, inp.delta, inp.B, inp.C, inp.z))
+    A, Dk, bias = (cv(a, f32) for a in (inp.A, inp.D, inp.delta_bias))
+    y = torch.empty((Bt, L, D), dtype=f32, device="cuda")
+    desc = Bnd.make_desc(Bt, L, D, N, Bnd.SS_BF16, Bnd.SS_F32, Bnd.SS_ZOH, True)
+    f = lambda: Bnd.ss_scan_fwd_complex(desc, u, dl, A, Bm, Cm, Dk, bias, z, None, y, None)  # noqa
+    total, per, mn, _ = time_calls(f, steps, warm, torch)
+    el = Bt * L * D * N
+    out = {"complex_2p8b_s4dlin": {"ms": round(per, 4), "ms_min": round(mn, 4),
+                                   "elements_per_s": el / (per * 1e-3)}}
+    del u, dl, Bm, Cm, z, y
     torch.cuda.empty_cache()
     return out
 

@@ -138,6 +138,31 @@ int ss_scan_fwd_dir(const ss_desc_t* desc, int direction, int accumulate,
                     void* workspace, size_t ws_bytes, void* stream);
 
 /*
+ * Forward selective scan with a complex diagonal A (the S4D-Lin kind of
+ * system; "A Survey of Mamba" summary, HiPPO-based memory initialisation:
+ * complex and real diagonal initialisations; "Mamba: S4 epic upgrade",
+ * ablation on A: real and complex decay compared).  Per channel and complex
+ * state n:
+ *     abar  = exp(dt a)                   a = A[d,n] complex
+ *     bcoef = (abar - 1) / a              exact ZOH (dt when a == 0 or Euler)
+ *     h_n   = abar h_n + bcoef B_n u      B_n, C_n complex per (b, t)
+ *     y     = 2 Re(sum_n C_n h_n) + D_skip u      (each state stands for itself
+ *                                                  and its conjugate)
+ *     out   = y * silu(z)
+ * Complex tensors are stored as (re, im) pairs in a last axis of 2:
+ *     A : (D, N, 2) float32;  Bm, Cm : (B, L, N, 2) in in_dtype;
+ *     h0, h_last : (B, D, N, 2) float32.
+ * Everything else as ss_scan_fwd.  dstate = N complex states (1..16).  No
+ * workspace: one workgroup walks the whole sequence of its 64 channels.
+ */
+int ss_scan_fwd_complex(const ss_desc_t* desc,
+                        const void* u, const void* delta, const float* A,
+                        const void* Bm, const void* Cm,
+                        const float* D_skip, const float* delta_bias, const void* z,
+                        const float* h0,
+                        void* y, float* h_last, void* stream);
+
+/*
  * Backward of ss_scan_fwd with recomputation: the states are rebuilt from the
  * inputs (chunk start states in the workspace, the rest on chip), never read
  * from a stored (B,L,D,N) tensor ("A Visual Guide to Mamba" summary,

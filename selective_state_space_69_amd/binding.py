@@ -2,12 +2,12 @@
 include/ss_conv.h and include/ss_ssd.h).
 
 The functions named like the C entry points (ss_scan_fwd, ss_scan_fwd_dir,
-ss_scan_bwd, ss_scan_step, ss_scan_workspace_bytes, ss_scan_strerror, ss_scan_version,
+ss_scan_fwd_complex, ss_scan_bwd, ss_scan_step, ss_scan_workspace_bytes, ss_scan_strerror, ss_scan_version,
 ss_conv1d_fwd, ss_conv1d_bwd, ss_conv1d_step, ss_conv1d_workspace_bytes, ss_ssd_fwd) only
 marshal arguments: torch tensors become device pointers, None becomes NULL and
 the stream defaults to torch's current HIP stream.  Every step runs in the HIP
 kernels; there is no fallback.  The convenience wrappers scan_fwd, scan_bwd,
-scan_bidir, scan_step, conv1d_fwd, conv1d_bwd, conv1d_step and ssd_fwd additionally allocate
+scan_bidir, scan_fwd_complex, scan_step, conv1d_fwd, conv1d_bwd, conv1d_step and ssd_fwd additionally allocate
 outputs and workspace with torch.
 """
 from __future__ import annotations
@@ -76,6 +76,8 @@ def load_library():
         lib.ss_scan_fwd.restype = I
         lib.ss_scan_fwd_dir.argtypes = [D, I, I] + [P] * 11 + [P, SZ, P]
         lib.ss_scan_fwd_dir.restype = I
+        lib.ss_scan_fwd_complex.argtypes = [D] + [P] * 11 + [P]
+        lib.ss_scan_fwd_complex.restype = I
         lib.ss_scan_bwd.argtypes = [D] + [P] * 19 + [P, SZ, P]
         lib.ss_scan_bwd.restype = I
         lib.ss_scan_step.argtypes = [D] + [P] * 10 + [P]
@@ -147,6 +149,13 @@ def ss_scan_fwd_dir(desc, direction, accumulate, u, delta, A, Bm, Cm, D_skip, de
                                           _p(u), _p(delta), _p(A), _p(Bm), _p(Cm), _p(D_skip),
                                           _p(delta_bias), _p(z), _p(h0), _p(y), _p(h_last),
                                           _p(workspace), int(ws_bytes), _stream(stream))
+
+
+def ss_scan_fwd_complex(desc, u, delta, A, Bm, Cm, D_skip, delta_bias, z, h0, y, h_last,
+                        stream=None) -> int:
+    return load_library().ss_scan_fwd_complex(ctypes.byref(desc), _p(u), _p(delta), _p(A), _p(Bm),
+                                              _p(Cm), _p(D_skip), _p(delta_bias), _p(z), _p(h0),
+                                              _p(y), _p(h_last), _stream(stream))
 
 
 def ss_scan_bwd(desc, u, delta, A, Bm, Cm, D_skip, delta_bias, z, h0, dy, du, ddelta, dA, dB, dC,
@@ -236,6 +245,22 @@ def scan_fwd(u, delta, A, B, C, D=None, delta_bias=None, z=None, h0=None, disc="
     _check(ss_scan_fwd_dir(desc, SS_DIR_REVERSE if reverse else SS_DIR_FORWARD, int(acc), u, delta,
                            A, B, C, D, delta_bias, z, h0, y, h_last, ws, nb, stream),
            "ss_scan_fwd_dir")
+    return (y, h_last) if return_last_state else y
+
+
+def scan_fwd_complex(u, delta, A, B, C, D=None, delta_bias=None, z=None, h0=None, disc="zoh",
+                     softplus=True, out_dtype=torch.float32, return_last_state=False,
+                     stream=None):
+    """Complex-A forward: A (D, N, 2) float32, B and C (B, L, N, 2) in u's dtype,
+    h0 (B, D, N, 2) float32 ((re, im) pairs).  Returns y (and h_last (B, D, N, 2))."""
+    Bt, L, Dd = u.shape
+    N = A.shape[1]
+    desc = make_desc(Bt, L, Dd, N, _DTYPE[u.dtype], _DTYPE[out_dtype], _DISC[disc], softplus)
+    y = torch.empty(u.shape, dtype=out_dtype, device=u.device)
+    h_last = (torch.empty((Bt, Dd, N, 2), dtype=torch.float32, device=u.device)
+              if return_last_state else None)
+    _check(ss_scan_fwd_complex(desc, u, delta, A, B, C, D, delta_bias, z, h0, y, h_last, stream),
+           "ss_scan_fwd_complex")
     return (y, h_last) if return_last_state else y
 
 

@@ -264,6 +264,24 @@ int ss_scan_fwd_dir(const ss_desc_t* desc, int direction, int accumulate, const 
   return launch_fwd(*desc, plan, a, stream) == 0 ? SS_OK : SS_ERR_HIP;
 }
 
+int ss_scan_fwd_complex(const ss_desc_t* desc, const void* u, const void* delta, const float* A,
+                        const void* Bm, const void* Cm, const float* D_skip,
+                        const float* delta_bias, const void* z, const float* h0, void* y,
+                        float* h_last, void* stream) {
+  int rc = check_desc(desc, true);
+  if (rc != SS_OK) return rc;
+  if (!u || !delta || !A || !Bm || !Cm || !y) return SS_ERR_INVALID_ARG;
+  if (h_last && h0 && static_cast<const void*>(h_last) == static_cast<const void*>(h0))
+    return SS_ERR_INVALID_ARG;
+  const void* ptrs[] = {u, delta, Bm, Cm, z, A, D_skip, delta_bias, h0, h_last, y};
+  for (const void* p : ptrs)
+    if (p && !aligned(p, kPtrAlign)) return SS_ERR_INVALID_ARG;
+  return launch_fwd_complex(*desc, u, delta, A, Bm, Cm, D_skip, delta_bias, z, h0, y, h_last,
+                            stream) == 0
+             ? SS_OK
+             : SS_ERR_HIP;
+}
+
 int ss_scan_bwd(const ss_desc_t* desc, const void* u, const void* delta, const float* A,
                 const void* Bm, const void* Cm, const float* D_skip, const float* delta_bias,
                 const void* z, const float* h0, const void* dy, void* du, void* ddelta,

@@ -151,6 +151,10 @@ int launch_conv_step(const ss_conv_desc_t& d, float* state, const void* x, const
 int launch_chunk_carry(float* states, const float* dsum, const float* A, const float* h0,
                        int64_t batch, int64_t D, int N, int nc, bool reverse, void* stream);
 int launch_step(const ss_desc_t& d, const StepArgs& a, void* stream);
+// Complex-A forward (ss_complex.hip): A (D,N,2), B, C (B,L,N,2), h0 / h_last (B,D,N,2).
+int launch_fwd_complex(const ss_desc_t& d, const void* u, const void* delta, const float* A,
+                       const void* Bm, const void* Cm, const float* Dskip, const float* bias,
+                       const void* z, const float* h0, void* y, float* h_last, void* stream);
 // SSD (Mamba-2) forward (ss_ssd.hip): one workgroup per (batch row, head).
 int launch_ssd_fwd(const ss_ssd_desc_t& d, const void* x, const void* dt, const float* A,
                    const void* Bm, const void* Cm, const float* D, const float* dt_bias, void* y,

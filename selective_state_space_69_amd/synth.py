@@ -206,3 +206,44 @@ def make_ssd_inputs(Bt: int, L: int, H: int, P: int, N: int, G: int, seed: int,
 # workload), 64 states, one B/C group.
 SSD_WORKLOAD = dict(name="ssd_bf16_b8_l2048_h80_p64_n64_g1", Bt=8, L=2048, H=80, P=64, N=64,
                     G=1, seed=2001)
+
+
+# ---------------------------------------------------------------- complex diagonal A
+def make_A_complex(D: int, N: int, mode: str = "s4d_lin", rng: np.random.Generator | None = None):
+    """Complex diagonal A as (D, N, 2) float32 (re, im) pairs.
+    s4d_lin : A[d, n] = -1/2 + i pi n   (the S4D-Lin initialisation)
+    random  : re = -exp(N(0, 1)), im = pi * N(0, 2)
+    mixed   : random, with an exact zero and a purely imaginary entry"""
+    if mode == "s4d_lin":
+        re = np.full((D, N), -0.5)
+        im = np.tile(np.pi * np.arange(N), (D, 1))
+    else:
+        rng = rng or np.random.default_rng(8)
+        re = -np.exp(rng.standard_normal((D, N)))
+        im = np.pi * 2.0 * rng.standard_normal((D, N))
+        if mode == "mixed":
+            re[0, 0] = im[0, 0] = 0.0
+            if D > 1:
+                re[1, N - 1] = 0.0
+    return np.stack([re, im], axis=-1).astype(np.float32)
+
+
+def make_complex_inputs(B: int, L: int, D: int, N: int, seed: int, dtype: str = "f32",
+                        a_mode: str = "s4d_lin", with_h0: bool = False, with_z: bool = True,
+                        dt_range=(1e-3, 1e-1)) -> Inputs:
+    """Real-scan inputs of make_inputs with complex B, C (B, L, N, 2) (re and im
+    ~ N(0, 1/2), so |B_n| has unit second moment), A (D, N, 2) and h0 (B, D, N, 2)."""
+    base = make_inputs(B, L, D, N, seed, dtype="f32", dt_range=dt_range, with_z=with_z)
+    rng = np.random.default_rng(seed + 7919)
+    s = np.float32(np.sqrt(0.5))
+    Bm = rng.standard_normal((B, L, N, 2), dtype=np.float32) * s
+    Cm = rng.standard_normal((B, L, N, 2), dtype=np.float32) * s
+    h0 = rng.standard_normal((B, D, N, 2), dtype=np.float32) * s if with_h0 else None
+    A = make_A_complex(D, N, a_mode, rng)
+    u, z, delta = base.u, base.z, base.delta
+    if dtype == "bf16":
+        u, delta, Bm, Cm = (round_to_bf16(x) for x in (u, delta, Bm, Cm))
+        z = round_to_bf16(z) if z is not None else None
+    return Inputs(u=u, delta=delta, A=A, B=Bm, C=Cm, D=base.D, delta_bias=base.delta_bias, z=z,
+                  h0=h0, dtype=dtype, meta=dict(B=B, L=L, D=D, N=N, seed=seed, a_mode=a_mode,
+                                                complex=True))

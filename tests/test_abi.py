@@ -35,7 +35,7 @@ def test_header_declares_entry_points():
     names = declared_functions()
     for n in ("ss_scan_fwd", "ss_scan_bwd", "ss_scan_step", "ss_scan_workspace_bytes",
               "ss_scan_strerror", "ss_scan_version", "ss_conv1d_fwd", "ss_conv1d_bwd",
-              "ss_conv1d_step", "ss_conv1d_workspace_bytes", "ss_ssd_fwd", "ss_scan_fwd_dir"):
+              "ss_conv1d_step", "ss_conv1d_workspace_bytes", "ss_ssd_fwd", "ss_scan_fwd_dir", "ss_scan_fwd_complex"):
         assert n in names
 
 
@@ -214,3 +214,14 @@ def test_fwd_dir_validation(lib):
     # the rest of the validation is shared with ss_scan_fwd
     assert B.ss_scan_fwd_dir(d, B.SS_DIR_REVERSE, 1, None, P, P, P, P, None, None, None, None,
                              P + 4096, None, None, 0, stream=0) == B.SS_ERR_INVALID_ARG
+
+
+def test_fwd_complex_validation(lib):
+    P = FAKE
+    ok = B.make_desc(2, 64, 32, 16, B.SS_F32, B.SS_F32)
+    args = lambda **kw: [kw.get(k, v) for k, v in dict(u=P, delta=P, A=P, Bm=P, Cm=P, D=None,  # noqa
+                         bias=None, z=None, h0=None, y=P + 4096, hl=None).items()]
+    assert B.ss_scan_fwd_complex(B.make_desc(2, 64, 32, 17), *args(), stream=0) == B.SS_ERR_INVALID_ARG
+    assert B.ss_scan_fwd_complex(ok, *args(u=None), stream=0) == B.SS_ERR_INVALID_ARG
+    assert B.ss_scan_fwd_complex(ok, *args(A=P + 4), stream=0) == B.SS_ERR_INVALID_ARG
+    assert B.ss_scan_fwd_complex(ok, *args(h0=P + 8192, hl=P + 8192), stream=0) == B.SS_ERR_INVALID_ARG
