@@ -1,0 +1,13 @@
+// Instantiation of the 64-channel forward kernels for bf16 input, bf16 output
+// (one translation unit per element-type pair, so the build compiles them in
+// parallel).
+#include "ss_fwd_kernels.hpp"
+
+namespace ss {
+
+hipError_t fwd_dispatch_bf16_bf16(const FwdParams& p, int disc, int nsplit, bool has_z, bool softplus,
+                       bool summary, int64_t nblocks, hipStream_t st) {
+  return dispatch_disc<uint16_t, uint16_t>(p, disc, nsplit, has_z, softplus, summary, nblocks, st);
+}
+
+}  // namespace ss

@@ -52,6 +52,17 @@ struct TimeDir {
   }
 };
 
+// Launch of the 64-channel kernels for one element-type pair (input, output):
+// every discretisation, flag combination, layout (nsplit 1, 2, 4) and direction.
+hipError_t fwd_dispatch_bf16_f32(const FwdParams& p, int disc, int nsplit, bool has_z,
+                                 bool softplus, bool summary, int64_t nblocks, hipStream_t st);
+hipError_t fwd_dispatch_bf16_bf16(const FwdParams& p, int disc, int nsplit, bool has_z,
+                                  bool softplus, bool summary, int64_t nblocks, hipStream_t st);
+hipError_t fwd_dispatch_f32_f32(const FwdParams& p, int disc, int nsplit, bool has_z,
+                                bool softplus, bool summary, int64_t nblocks, hipStream_t st);
+hipError_t fwd_dispatch_f32_bf16(const FwdParams& p, int disc, int nsplit, bool has_z,
+                                 bool softplus, bool summary, int64_t nblocks, hipStream_t st);
+
 // Launch of the 32-channel kernel over B * ndblk * grid_chunks workgroups
 // (ndblk = ceil(D / 32)); summary = chunk summaries instead of outputs.
 hipError_t launch_fwd_hw(const ss_desc_t& d, const FwdParams& p, bool summary, int64_t nblocks,
