@@ -74,11 +74,23 @@ def upload(inp, torch):
                 dy=cv(inp.dy, it))
 
 
+# The GPU's clocks ramp up over the first ~50 ms of sustained load (a forward at
+# the Mamba-2.8B shape takes 0.8 ms per call for the first 20 calls, 0.44 ms from
+# about the 100th).  Every timed region is therefore preceded by at least
+# `warmup` untimed calls and at least WARM["min_s"] seconds of them.
+WARM = {"min_s": 0.3, "last_calls": 0}
+
+
 def time_calls(fn, steps, warmup, torch):
     """Warm up, then time `steps` calls: total wall (events around the whole region)
     and the mean per-call duration from events around each call (same stream)."""
-    for _ in range(warmup):
+    n, t0 = 0, time.perf_counter()
+    while n < warmup or time.perf_counter() - t0 < WARM["min_s"]:
         fn()
+        n += 1
+        if n % 8 == 0:
+            torch.cuda.synchronize()   # keep the host clock in step with the GPU
+    WARM["last_calls"] = n
     torch.cuda.synchronize()
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     t0 = time.perf_counter()
@@ -145,6 +157,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--min-warmup-s", type=float, default=WARM["min_s"],
+                    help="untimed warm-up lasts at least this long (GPU clock ramp)")
     ap.add_argument("--workload", default="fwd_2p8b_bf16_b8_l2048_d5120")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
@@ -154,6 +168,7 @@ def main():
                     help="only time the backward (Mamba-130M shape), the decode step or the "
                          "Conv1d + SiLU and print their figures (for profiling runs)")
     args = ap.parse_args()
+    WARM["min_s"] = args.min_warmup_s
     if args.gpus != 1:
         print("bench.py measures one GPU only: the selective scan needs no communication "
               "(every (b, d) channel is independent) and this build has no multi-GPU path; "
@@ -204,6 +219,7 @@ def main():
 
     torch.cuda.synchronize()
     total_ms, per_ms, min_ms, wall = time_calls(step, args.steps, args.warmup, torch)
+    warm_calls = WARM["last_calls"]
     torch.cuda.synchronize()
     elems = w.elements
     value = elems * args.steps / (total_ms * 1e-3)
@@ -219,7 +235,8 @@ def main():
             "hbm": {"achieved": round(hbm_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": round(hbm_gbs / HBM_PEAK_GBS, 4), "algorithmic_bytes": alg}}
     res = {"metric": "selective-scan elements (B*L*D*N)/s, 1 GPU", "value": value,
-           "unit": "elements/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "unit": "elements/s", "n_gpus": 1, "steps": args.steps, "warmup": warm_calls,
+           "warmup_requested": args.warmup, "warmup_min_s": WARM["min_s"],
            "ms_per_step": total_ms / args.steps, "higher_is_better": True, "scaling": "weak",
            "vs_baseline": None, "dtype": "f32", "data": "synthetic",
            "config": {"workload": w.name, "B": w.B, "L": w.L, "D": w.D, "N": w.N,
