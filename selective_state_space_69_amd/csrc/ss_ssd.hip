@@ -206,26 +206,42 @@ __global__ __launch_bounds__(kThreads, 3) void ssd_fwd_kernel(SsdArgs a) {
     uint32_t dtr;
   };
   Stage st0;
-  auto load_chunk = [&](int c, Stage& sg) __attribute__((always_inline)) {
+  // The next chunk is fetched in three parts (x and the step sizes, B, C) at
+  // three points of the current one, B and C while matrix products are in
+  // flight: the workgroups' waves leave each barrier together, and one burst
+  // of all their loads would hold every wave at the load issue until it
+  // drained.
+  // part 0: x and dt; part 1: B rows; part 2: C rows
+  auto load_part = [&](int part, int c, Stage& sg) __attribute__((always_inline)) {
     const int64_t t0 = int64_t(c) * kQ;
     const int64_t rows = L - t0;                       // valid rows of this chunk (> 0)
-    const Rsrc rx = make_rsrc(xbase + t0 * a.H * kDim);
-    const Rsrc rbm = make_rsrc(bbase + t0 * a.G * kDim);
-    const Rsrc rcm = make_rsrc(cbase + t0 * a.G * kDim);
+    if (part == 0) {
+      const Rsrc rx = make_rsrc(xbase + t0 * a.H * kDim);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const bool ok = 4 * rb + i < rows;
-      const uint32_t ox = ok ? uint32_t(4 * rb + i) * xrow_b + 8 * cb : kOutOfRange;
-      const uint32_t ob = ok ? uint32_t(4 * rb + i) * brow_b + 8 * cb : kOutOfRange;
-      sg.xr[i] = buf_load8(rx, ox);
-      sg.br[i] = buf_load8(rbm, ob);
-      sg.cr[i] = buf_load8(rcm, ob);
+      for (int i = 0; i < 4; ++i) {
+        const bool ok = 4 * rb + i < rows;
+        sg.xr[i] = buf_load8(rx, ok ? uint32_t(4 * rb + i) * xrow_b + 8 * cb : kOutOfRange);
+      }
+      // every wave loads the step sizes (only wave 0 uses them) so that all
+      // waves have the same memory operations in flight
+      const Rsrc rd = make_rsrc(dtbase + t0 * a.H);
+      sg.dtr = __builtin_amdgcn_raw_buffer_load_b16(
+          rd, lane < rows ? uint32_t(lane) * uint32_t(a.H) * 2 : kOutOfRange, 0, 0);
+    } else {
+      const Rsrc r = make_rsrc((part == 1 ? bbase : cbase) + t0 * a.G * kDim);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const bool ok = 4 * rb + i < rows;
+        const uint2 v = buf_load8(r, ok ? uint32_t(4 * rb + i) * brow_b + 8 * cb : kOutOfRange);
+        if (part == 1) sg.br[i] = v;
+        else sg.cr[i] = v;
+      }
     }
-    // every wave loads the step sizes (only wave 0 uses them) so that all waves
-    // have the same memory operations in flight
-    const Rsrc rd = make_rsrc(dtbase + t0 * a.H);
-    sg.dtr = __builtin_amdgcn_raw_buffer_load_b16(
-        rd, lane < rows ? uint32_t(lane) * uint32_t(a.H) * 2 : kOutOfRange, 0, 0);
+  };
+  auto load_chunk = [&](int c, Stage& sg) __attribute__((always_inline)) {
+    load_part(0, c, sg);
+    load_part(1, c, sg);
+    load_part(2, c, sg);
   };
   // output rows 16 w + 4 g + r, columns 16 pi + c16
   const uint32_t yrow_b = uint32_t(a.H) * kDim * uint32_t(sizeof(Out));
@@ -277,7 +293,7 @@ __global__ __launch_bounds__(kThreads, 3) void ssd_fwd_kernel(SsdArgs a) {
       }
     }
     __syncthreads();
-    if (c + 1 < nc) load_chunk(c + 1, sg);
+    if (c + 1 < nc) load_part(0, c + 1, sg);
     const float lam_end = reinterpret_cast<const float*>(sm + kOffLam)[kQ - 1];
 
     // p-role: off-diagonal outputs exp(l_t) C_t . H for p-tile w, every t-tile
@@ -293,18 +309,28 @@ __global__ __launch_bounds__(kThreads, 3) void ssd_fwd_kernel(SsdArgs a) {
         }
         split8(v, hh[j], hl[j]);
       }
+      // every operand read is issued before the first product, and the four
+      // row tiles' accumulation chains are interleaved
+      u32x4 cop[4][2];
+      f32x4 el[4], acc[4];
 #pragma unroll
       for (int ti = 0; ti < 4; ++ti) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const u32x4 cop = ld_op(kOffCs, ti, j);
-          acc = mfma(cop, hh[j], acc);
-          acc = mfma(cop, hl[j], acc);
-        }
-        acc *= ldf4(kOffElam + (16 * ti + 4 * g) * 4);
-        *reinterpret_cast<f32x4*>(sm + kOffYo + ((ti * 4 + w) * kWave + lane) * 16) = acc;
+        cop[ti][0] = ld_op(kOffCs, ti, 0);
+        cop[ti][1] = ld_op(kOffCs, ti, 1);
+        el[ti] = ldf4(kOffElam + (16 * ti + 4 * g) * 4);
+        acc[ti] = f32x4{0.f, 0.f, 0.f, 0.f};
       }
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+#pragma unroll
+        for (int ti = 0; ti < 4; ++ti) acc[ti] = mfma(cop[ti][j], hh[j], acc[ti]);
+#pragma unroll
+        for (int ti = 0; ti < 4; ++ti) acc[ti] = mfma(cop[ti][j], hl[j], acc[ti]);
+      }
+#pragma unroll
+      for (int ti = 0; ti < 4; ++ti)
+        *reinterpret_cast<f32x4*>(sm + kOffYo + ((ti * 4 + w) * kWave + lane) * 16) =
+            acc[ti] * el[ti];
     }
 
     // t-role: M^T tiles of t-tile w (s-tiles 0..w), masked and split
@@ -313,6 +339,29 @@ __global__ __launch_bounds__(kThreads, 3) void ssd_fwd_kernel(SsdArgs a) {
       const int t = 16 * w + c16;
       const float lamt = reinterpret_cast<const float*>(sm + kOffLam)[t];
       const u32x4 ct0 = ld_op(kOffCs, w, 0), ct1 = ld_op(kOffCs, w, 1);
+      // operands of all four column tiles first (in-bounds for every wave; the
+      // tiles past the diagonal are not used)
+      u32x4 bop[4][2];
+      f32x4 lsv[4], dsv[4], gacc[4];
+#pragma unroll
+      for (int si = 0; si < 4; ++si) {
+        bop[si][0] = ld_op(kOffBs, si, 0);
+        bop[si][1] = ld_op(kOffBs, si, 1);
+        gacc[si] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+      for (int si = 0; si < 4; ++si)
+        if (si <= w) gacc[si] = mfma(bop[si][0], ct0, gacc[si]);
+#pragma unroll
+      for (int si = 0; si < 4; ++si)
+        if (si <= w) gacc[si] = mfma(bop[si][1], ct1, gacc[si]);
+      if (c + 1 < nc) load_part(1, c + 1, sg);   // while the products run
+      // the decay factors are read while the products run
+#pragma unroll
+      for (int si = 0; si < 4; ++si) {
+        lsv[si] = ldf4(kOffLam + (16 * si + 4 * g) * 4);
+        dsv[si] = ldf4(kOffDts + (16 * si + 4 * g) * 4);
+      }
       float m[4][4];
 #pragma unroll
       for (int si = 0; si < 4; ++si) {
@@ -321,15 +370,11 @@ __global__ __launch_bounds__(kThreads, 3) void ssd_fwd_kernel(SsdArgs a) {
           for (int r = 0; r < 4; ++r) m[si][r] = 0.0f;
           continue;
         }
-        f32x4 gacc = {0.f, 0.f, 0.f, 0.f};
-        gacc = mfma(ld_op(kOffBs, si, 0), ct0, gacc);
-        gacc = mfma(ld_op(kOffBs, si, 1), ct1, gacc);
-        const f32x4 ls = ldf4(kOffLam + (16 * si + 4 * g) * 4);
-        const f32x4 ds = ldf4(kOffDts + (16 * si + 4 * g) * 4);
+        const f32x4 ls = lsv[si], ds = dsv[si];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int s = 16 * si + 4 * g + r;
-          float v = gacc[r] * (hw_exp2(lamt - ls[r]) * ds[r]);
+          float v = gacc[si][r] * (hw_exp2(lamt - ls[r]) * ds[r]);
           if (s == t) v += Dh;
           m[si][r] = s <= t ? v : 0.0f;
         }
@@ -355,19 +400,22 @@ __global__ __launch_bounds__(kThreads, 3) void ssd_fwd_kernel(SsdArgs a) {
       const int nkb = (w >> 1) + 1;
       char* ybuf = sm + kOffYo + w * 4 * kWave * 16;
       f32x4 acc[4];
-#pragma unroll
-      for (int pi = 0; pi < 4; ++pi)
-        acc[pi] = *reinterpret_cast<const f32x4*>(ybuf + (pi * kWave + lane) * 16);
+      u32x4 xop[4][2];
 #pragma unroll
       for (int pi = 0; pi < 4; ++pi) {
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          if (j >= nkb) continue;
-          const u32x4 xop = ld_op(kOffXt, pi, j);
-          acc[pi] = mfma(mh[j], xop, acc[pi]);
-          acc[pi] = mfma(ml[j], xop, acc[pi]);
-        }
+        acc[pi] = *reinterpret_cast<const f32x4*>(ybuf + (pi * kWave + lane) * 16);
+        xop[pi][0] = ld_op(kOffXt, pi, 0);
+        xop[pi][1] = ld_op(kOffXt, pi, 1);
       }
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        if (j >= nkb) continue;
+#pragma unroll
+        for (int pi = 0; pi < 4; ++pi) acc[pi] = mfma(mh[j], xop[pi][j], acc[pi]);
+#pragma unroll
+        for (int pi = 0; pi < 4; ++pi) acc[pi] = mfma(ml[j], xop[pi][j], acc[pi]);
+      }
+      if (c + 1 < nc) load_part(2, c + 1, sg);   // while the products run
       __builtin_amdgcn_wave_barrier();
       // row t (0..15) of 64 floats = 16 units of 16 bytes; unit u at u ^ (4 (t >> 2))
 #pragma unroll
@@ -393,12 +441,23 @@ __global__ __launch_bounds__(kThreads, 3) void ssd_fwd_kernel(SsdArgs a) {
 
     // p-role: H <- exp(l_end) H + B^T X', X' = exp(l_end - l_s) dt_s x_s (p-tile w)
     {
-      u32x4 xh[2], xl[2];
+      u32x4 xh[2], xl[2], bop[4][2], xvv[2];
+      f32x4 wv[2][2];
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        const u32x4 xv = ld_op(kOffXt, w, j);
-        const f32x4 w0 = ldf4(kOffWts + (32 * j + 4 * g) * 4);
-        const f32x4 w1 = ldf4(kOffWts + (32 * j + 16 + 4 * g) * 4);
+        xvv[j] = ld_op(kOffXt, w, j);
+        wv[j][0] = ldf4(kOffWts + (32 * j + 4 * g) * 4);
+        wv[j][1] = ldf4(kOffWts + (32 * j + 16 + 4 * g) * 4);
+      }
+#pragma unroll
+      for (int ni = 0; ni < 4; ++ni) {
+        bop[ni][0] = ld_op(kOffBt, ni, 0);
+        bop[ni][1] = ld_op(kOffBt, ni, 1);
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const u32x4 xv = xvv[j];
+        const f32x4 w0 = wv[j][0], w1 = wv[j][1];
         float v[8];
         v[0] = __uint_as_float(xv.x << 16) * w0[0];
         v[1] = __uint_as_float(xv.x & 0xffff0000u) * w0[1];
@@ -412,15 +471,13 @@ __global__ __launch_bounds__(kThreads, 3) void ssd_fwd_kernel(SsdArgs a) {
       }
       const float decay = hw_exp2(lam_end);
 #pragma unroll
-      for (int ni = 0; ni < 4; ++ni) {
-        f32x4 acc = hacc[ni] * decay;
+      for (int ni = 0; ni < 4; ++ni) hacc[ni] *= decay;
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const u32x4 bop = ld_op(kOffBt, ni, j);
-          acc = mfma(bop, xh[j], acc);
-          acc = mfma(bop, xl[j], acc);
-        }
-        hacc[ni] = acc;
+      for (int j = 0; j < 2; ++j) {
+#pragma unroll
+        for (int ni = 0; ni < 4; ++ni) hacc[ni] = mfma(bop[ni][j], xh[j], hacc[ni]);
+#pragma unroll
+        for (int ni = 0; ni < 4; ++ni) hacc[ni] = mfma(bop[ni][j], xl[j], hacc[ni]);
       }
     }
   };
