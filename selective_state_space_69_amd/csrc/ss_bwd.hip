@@ -18,8 +18,9 @@
 // reduce-scatter (permlane swaps and DPP), then over channel blocks; dA, dD_skip
 // and ddelta_bias per channel over the chunk, then over chunks and batch rows.
 // All partial sums are added in a fixed order: the backward is deterministic.
-// The register footprint (about 150 VGPRs) leaves room for three waves per
-// SIMD, which hides the latency of the transcendental unit and of LDS.
+// The chunk's inputs are all fetched at its start (one round trip to memory)
+// and kept in LDS; the footprint (about 175 VGPRs for Euler, 205 for ZOH and
+// 57 KB of LDS) allows two workgroups per CU.
 #include "ss_device.hpp"
 
 namespace ss {
@@ -158,13 +159,16 @@ __device__ __forceinline__ float reduce_scatter16(const float (&v)[16], uint32_t
 }
 
 // ---------------------------------------------------------------- main kernel
-// LDS (floats): step sizes and gated output gradients [32 steps][64 lanes],
-// B/C rows [32 steps][B 16, C 16], per-step partials of du, d(dt) and y
-// [4 waves][3][4 steps][64 lanes].
+// LDS (floats): step sizes, gated output gradients and inputs u
+// [32 steps][64 lanes], B/C rows [32 steps][B 16, C 16], per-step partials of
+// du, d(dt) and y [4 waves][3][4 steps][64 lanes], and the factors of dz and
+// d(delta) of the 8 steps a thread owns [8][2][256 threads] (written and read
+// back by the same thread).
 constexpr int kActF = kChunk * kWave;
 constexpr int kRowF = kChunk * 2 * kMaxState;
 constexpr int kXchF = kNW * 3 * kKB * kWave;
-constexpr int kLdsFloats = 2 * kActF + kRowF + kXchF;
+constexpr int kOwnF = kNB * 2 * kNW * kWave;
+constexpr int kLdsFloats = 3 * kActF + kRowF + kXchF + kOwnF;
 
 template <typename In, int DISC, bool HAS_Z, bool SOFTPLUS, bool SAFE>
 __device__ __forceinline__ void bwd_chunk(const BwdParams& p, float* lds, int64_t b, int dblk,
@@ -195,44 +199,32 @@ __device__ __forceinline__ void bwd_chunk(const BwdParams& p, float* lds, int64_
 
   float* actDl = lds;                            // [32 steps][64 lanes]
   float* actGy = lds + kActF;                    // [32 steps][64 lanes]
-  float* rows = lds + 2 * kActF;                 // [32 steps][B 16, C 16]
+  float* actU = lds + 2 * kActF;                 // [32 steps][64 lanes]
+  float* rows = lds + 3 * kActF;                 // [32 steps][B 16, C 16]
   float* xch = rows + kRowF;                     // [4 waves][3][4 steps][64 lanes]
+  float* own = xch + kXchF;                      // [8][2][256 threads]
+  const int tid = wave * kWave + int(lane);
 
-  // ---- phase A1: step sizes and gated upstream gradients of the chunk, each
-  //      wave computing the steps k with k % 4 == wave; the chunk's B/C rows
+  // ---- phase A1: step sizes, gated upstream gradients and inputs of the
+  //      chunk, each wave computing the steps k with k % 4 == wave; the
+  //      chunk's B/C rows.  Every load is issued before any is used.
+  In rdl[kNB], rdy[kNB], rz[kNB], ru[kNB];
 #pragma unroll
-  for (int s = 0; s < kChunk / kNW; ++s) {
-    const int k = s * kNW + wave;
-    const int32_t t = t0 + k;
-    float dl = 0.0f, gy = 0.0f;
-    if (t < t1) {
-      const int64_t i = ibase + int64_t(t) * D;
-      dl = step_log2<SOFTPLUS>(__builtin_fmaf(ld<In>(p.delta, i), kLog2e, bias2));
-      gy = ld<In>(p.dy, i);
-      if (HAS_Z) gy *= silu(ld<In>(p.z, i));
-    }
-    actDl[k * kWave + lane] = dl;
-    actGy[k * kWave + lane] = gy * amask;
+  for (int s = 0; s < kNB; ++s) {
+    const int32_t t = t0 + s * kNW + wave;
+    const int64_t i = ibase + int64_t(t < t1 ? t : t1 - 1) * D;
+    rdl[s] = static_cast<const In*>(p.delta)[i];
+    rdy[s] = static_cast<const In*>(p.dy)[i];
+    if (HAS_Z) rz[s] = static_cast<const In*>(p.z)[i];
+    ru[s] = static_cast<const In*>(p.u)[i];
   }
-  {
-    // 256 threads, 4 values each: step tid / 8, B (parts 0-3) or C (4-7)
-    const int tid = wave * kWave + int(lane);
-    const int k = tid / 8, part = tid % 8;
-    int32_t tr = t0 + k;
-    tr = tr < t1 ? tr : t1 - 1;
-    const In* src = static_cast<const In*>(part < 4 ? p.Brow : p.Crow) + (row0 + tr) * kMaxState +
-                    4 * (part % 4);
-    *reinterpret_cast<float4*>(rows + k * 2 * kMaxState + 4 * part) = unpack4(load_raw4(src));
-  }
-  __syncthreads();
-  // this wave's 4 states of the B (m = 0) or C (m = 1) row of step kk
-  auto row_of = [&](int kk, int m) -> float4 {
-    return *reinterpret_cast<const float4*>(rows + kk * 2 * kMaxState + m * kMaxState + n0);
-  };
-
-
-  // ---- phase A2: forward over the chunk, one checkpoint per block
-  float h[kNS];
+  // 256 threads, 4 values each: step tid / 8, B (parts 0-3) or C (4-7)
+  const int rk8 = tid / 8, rpart = tid % 8;
+  const auto rraw = load_raw4(static_cast<const In*>(rpart < 4 ? p.Brow : p.Crow) +
+                              (row0 + (t0 + rk8 < t1 ? t0 + rk8 : t1 - 1)) * kMaxState +
+                              4 * (rpart % 4));
+  // start state of the chunk and the adjoint carry entering it from its end
+  float h[kNS], nu[kNS];
   if (chunk == 0) {
 #pragma unroll
     for (int j = 0; j < kNS; ++j) h[j] = (p.h0 && n0 + j < N) ? p.h0[(b * D + dc) * N + n0 + j] : 0.0f;
@@ -241,6 +233,42 @@ __device__ __forceinline__ void bwd_chunk(const BwdParams& p, float* lds, int64_
 #pragma unroll
     for (int j = 0; j < kNS; ++j) h[j] = n0 + j < N ? hs[int64_t(n0 + j) * D] : 0.0f;
   }
+  if (chunk == p.nchunks - 1) {
+#pragma unroll
+    for (int j = 0; j < kNS; ++j) nu[j] = 0.0f;
+  } else {
+    const float* ls = p.lam + (b * p.nchunks + chunk) * int64_t(N) * D + dc;
+#pragma unroll
+    for (int j = 0; j < kNS; ++j) nu[j] = n0 + j < N ? ls[int64_t(n0 + j) * D] : 0.0f;
+  }
+#pragma unroll
+  for (int s = 0; s < kNB; ++s) {
+    const int k = s * kNW + wave;
+    const bool valid = t0 + k < t1;
+    const float x2 = __builtin_fmaf(to_f32(rdl[s]), kLog2e, bias2);
+    const float g = to_f32(rdy[s]);
+    float gy = g;
+    if (HAS_Z) {
+      const float zf = to_f32(rz[s]);
+      const float sz = sigmoid_log2(zf * kLog2e);
+      gy = g * zf * sz;
+      // dz = dy * y * d silu(z) / dz, y the pre-gate output
+      own[(s * 2 + 0) * (kNW * kWave) + tid] = g * sz * __builtin_fmaf(zf, 1.0f - sz, 1.0f);
+    }
+    if (SOFTPLUS) own[(s * 2 + 1) * (kNW * kWave) + tid] = sigmoid_log2(x2);   // d softplus
+    actDl[k * kWave + lane] = valid ? step_log2<SOFTPLUS>(x2) : 0.0f;
+    actGy[k * kWave + lane] = valid ? gy * amask : 0.0f;
+    actU[k * kWave + lane] = valid ? to_f32(ru[s]) * amask : 0.0f;
+  }
+  *reinterpret_cast<float4*>(rows + rk8 * 2 * kMaxState + 4 * rpart) = unpack4(rraw);
+  __syncthreads();
+  // this wave's 4 states of the B (m = 0) or C (m = 1) row of step kk
+  auto row_of = [&](int kk, int m) -> float4 {
+    return *reinterpret_cast<const float4*>(rows + kk * 2 * kMaxState + m * kMaxState + n0);
+  };
+
+
+  // ---- phase A2: forward over the chunk, one checkpoint per block
   float ck[kNB][kNS];
 #pragma unroll
   for (int jb = 0; jb < kNB; ++jb) {
@@ -249,10 +277,8 @@ __device__ __forceinline__ void bwd_chunk(const BwdParams& p, float* lds, int64_
 #pragma unroll
     for (int k = 0; k < kKB; ++k) {
       const int kk = jb * kKB + k;
-      const int32_t t = t0 + kk;
-      const int32_t tr = t < t1 ? t : t1 - 1;
       const float dl = actDl[kk * kWave + lane];
-      const float uf = ld<In>(p.u, ibase + int64_t(tr) * D);
+      const float uf = actU[kk * kWave + lane];
       const float4 B4 = row_of(kk, 0);
       const float Bv[kNS] = {B4.x, B4.y, B4.z, B4.w};
 #pragma unroll
@@ -271,15 +297,7 @@ __device__ __forceinline__ void bwd_chunk(const BwdParams& p, float* lds, int64_
   }
 
   // ---- phase B: blocks in reverse
-  float nu[kNS];   // adjoint carried from later steps: A_bar_{t+1} lambda_{t+1}
-  if (chunk == p.nchunks - 1) {
-#pragma unroll
-    for (int j = 0; j < kNS; ++j) nu[j] = 0.0f;
-  } else {
-    const float* ls = p.lam + (b * p.nchunks + chunk) * int64_t(N) * D + dc;
-#pragma unroll
-    for (int j = 0; j < kNS; ++j) nu[j] = n0 + j < N ? ls[int64_t(n0 + j) * D] : 0.0f;
-  }
+  // nu: adjoint carried from later steps, A_bar_{t+1} lambda_{t+1}
   float dA[kNS];
 #pragma unroll
   for (int j = 0; j < kNS; ++j) dA[j] = 0.0f;
@@ -300,11 +318,9 @@ __device__ __forceinline__ void bwd_chunk(const BwdParams& p, float* lds, int64_
 #pragma unroll
     for (int k = 0; k < kKB; ++k) {
       const int kk = jb * kKB + k;
-      const int32_t t = t0 + kk;
-      const int32_t tr = t < t1 ? t : t1 - 1;
       dl[k] = actDl[kk * kWave + lane];
       gy[k] = actGy[kk * kWave + lane];
-      uf[k] = ld<In>(p.u, ibase + int64_t(tr) * D) * amask;
+      uf[k] = actU[kk * kWave + lane];
       const float4 B4 = row_of(kk, 0), C4 = row_of(kk, 1);
       const float Bv[kNS] = {B4.x, B4.y, B4.z, B4.w}, Cv[kNS] = {C4.x, C4.y, C4.z, C4.w};
       float y0 = 0.0f;
@@ -395,23 +411,17 @@ __device__ __forceinline__ void bwd_chunk(const BwdParams& p, float* lds, int64_
         sy += xch[((w * 3 + 2) * kKB + k) * kWave + lane];
       }
       if (t < t1 && active) {
+        // the owned step of block jb is step jb of this thread in phase A1
         const int64_t i = ibase + int64_t(t) * D;
-        const float ui = ld<In>(p.u, i), g = ld<In>(p.dy, i);
-        float gyk = g, dzv = 0.0f;
+        const int kk = jb * kKB + k;
+        const float ui = actU[kk * kWave + lane], gyk = actGy[kk * kWave + lane];
         if (HAS_Z) {
-          const float zf = ld<In>(p.z, i);
-          const float sz = sigmoid_log2(zf * kLog2e);
-          gyk = g * zf * sz;
           const float y = __builtin_fmaf(Dd, ui, sy);   // pre-gate output
-          dzv = g * y * sz * __builtin_fmaf(zf, 1.0f - sz, 1.0f);
-          p.dz[i] = dzv;
+          p.dz[i] = own[(jb * 2 + 0) * (kNW * kWave) + tid] * y;
         }
         p.du[i] = __builtin_fmaf(gyk, Dd, sdu);
         float ddv = sdd;                                 // d loss / d dt
-        if (SOFTPLUS) {
-          const float x2 = __builtin_fmaf(ld<In>(p.delta, i), kLog2e, bias2);
-          ddv *= sigmoid_log2(x2);                       // through softplus
-        }
+        if (SOFTPLUS) ddv *= own[(jb * 2 + 1) * (kNW * kWave) + tid];   // through softplus
         p.ddelta[i] = ddv;
         dDacc = __builtin_fmaf(gyk, ui, dDacc);
         dbacc += ddv;
