@@ -61,22 +61,6 @@ struct BwdParams {
   int32_t N, ndblk, nchunks;
 };
 
-using ConstU32 = __attribute__((address_space(4))) const uint32_t;
-
-// This wave's 4 values of a B or C row: a scalar load (same address in every lane).
-template <typename In>
-__device__ __forceinline__ void row4(const void* rows, int64_t row, int n0, float (&v)[kNS]) {
-  ConstU32* q = (ConstU32*)(static_cast<const In*>(rows) + row * kMaxState + n0);
-  if constexpr (sizeof(In) == 2) {
-    const uint32_t w0 = q[0], w1 = q[1];
-    v[0] = __uint_as_float(w0 << 16); v[1] = __uint_as_float(w0 & 0xffff0000u);
-    v[2] = __uint_as_float(w1 << 16); v[3] = __uint_as_float(w1 & 0xffff0000u);
-  } else {
-#pragma unroll
-    for (int j = 0; j < kNS; ++j) v[j] = __uint_as_float(q[j]);
-  }
-}
-
 template <typename In>
 __device__ __forceinline__ float ld(const void* base, int64_t i) {
   return to_f32(static_cast<const In*>(base)[i]);
@@ -485,9 +469,12 @@ __global__ __launch_bounds__(kWave * kNW, 2) void bwd_kernel(BwdParams p) {
 // ---------------------------------------------------------------- reverse summaries
 // Local adjoint of chunk c (c >= 1) with nothing entering from its end:
 // R_c = A_bar-weighted sum of gy C over the chunk, one lane per (b, d), all N
-// states.  Stored in lam[b][c].
+// states.  Stored in lam[b][c].  The chunk's C rows go to LDS and every input
+// of the lane's 32 steps is fetched before the walk starts.
 template <typename In, bool HAS_Z, bool SOFTPLUS>
 __global__ __launch_bounds__(kWave) void rev_summary_kernel(BwdParams p) {
+  __shared__ float4 crow4[kChunk * kMaxState / 4];
+  float* crow = reinterpret_cast<float*>(crow4);   // [32 steps][16 states]
   const uint32_t lane = threadIdx.x;
   int64_t bid = blockIdx.x;
   const int dblk = int(bid % p.ndblk);
@@ -503,6 +490,23 @@ __global__ __launch_bounds__(kWave) void rev_summary_kernel(BwdParams p) {
   const int32_t t1 = int32_t(t0 + kChunk < p.L ? t0 + kChunk : p.L);
   const int64_t row0 = b * p.L;
   const int64_t ibase = row0 * D + dc;
+  In rdl[kChunk], rdy[kChunk], rz[kChunk];
+#pragma unroll
+  for (int k = 0; k < kChunk; ++k) {
+    const int64_t i = ibase + int64_t(t0 + k < t1 ? t0 + k : t1 - 1) * D;
+    rdl[k] = static_cast<const In*>(p.delta)[i];
+    rdy[k] = static_cast<const In*>(p.dy)[i];
+    if (HAS_Z) rz[k] = static_cast<const In*>(p.z)[i];
+  }
+  {
+    // 64 lanes x 8 values: row lane / 2, states 8 (lane % 2) .. + 7
+    const int k = int(lane / 2), q = 8 * int(lane % 2);
+    const In* src = static_cast<const In*>(p.Crow) +
+                    (row0 + (t0 + k < t1 ? t0 + k : t1 - 1)) * kMaxState + q;
+    const auto r0 = load_raw4(src), r1 = load_raw4(src + 4);
+    crow4[(k * kMaxState + q) / 4] = unpack4(r0);
+    crow4[(k * kMaxState + q) / 4 + 1] = unpack4(r1);
+  }
   const float bias2 = (p.bias ? p.bias[dc] : 0.0f) * kLog2e;
   float A[kMaxState], nu[kMaxState];
 #pragma unroll
@@ -510,22 +514,16 @@ __global__ __launch_bounds__(kWave) void rev_summary_kernel(BwdParams p) {
     A[n] = n < N ? p.A[dc * N + n] : -1.0f;
     nu[n] = 0.0f;
   }
-  for (int32_t t = t1 - 1; t >= t0; --t) {
-    const int64_t i = ibase + int64_t(t) * D;
-    const float dl = step_log2<SOFTPLUS>(__builtin_fmaf(ld<In>(p.delta, i), kLog2e, bias2));
-    float gy = ld<In>(p.dy, i);
-    if (HAS_Z) gy *= silu(ld<In>(p.z, i));
-    float c[kMaxState];
+  __syncthreads();
 #pragma unroll
-    for (int q = 0; q < kNW; ++q) {
-      float v[kNS];
-      row4<In>(p.Crow, row0 + t, q * kNS, v);
-#pragma unroll
-      for (int j = 0; j < kNS; ++j) c[q * kNS + j] = v[j];
-    }
+  for (int k = kChunk - 1; k >= 0; --k) {
+    if (t0 + k >= t1) continue;                  // uniform: steps past the end
+    const float dl = step_log2<SOFTPLUS>(__builtin_fmaf(to_f32(rdl[k]), kLog2e, bias2));
+    float gy = to_f32(rdy[k]);
+    if (HAS_Z) gy *= silu(to_f32(rz[k]));
 #pragma unroll
     for (int n = 0; n < kMaxState; ++n)
-      nu[n] = hw_exp2(dl * A[n]) * __builtin_fmaf(gy, c[n], nu[n]);
+      nu[n] = hw_exp2(dl * A[n]) * __builtin_fmaf(gy, crow[k * kMaxState + n], nu[n]);
   }
   if (!active) return;
   float* ls = p.lam + (b * p.nchunks + chunk) * int64_t(N) * D + d;
@@ -547,6 +545,7 @@ __global__ __launch_bounds__(256) void reduce_rows_kernel(const float* __restric
   const float* qb = pB + r * nblk * N + n;
   const float* qc = pC + r * nblk * N + n;
   float sb = 0.0f, sc = 0.0f;
+#pragma unroll 8
   for (int k = 0; k < nblk; ++k) {
     sb += qb[k * N];
     sc += qc[k * N];
@@ -557,10 +556,10 @@ __global__ __launch_bounds__(256) void reduce_rows_kernel(const float* __restric
 
 // dA (D, N), dD_skip and ddelta_bias (D): sums over (batch row, chunk) of the
 // per-chunk partials.  A workgroup takes 64 columns (column = n * D + d; n == N
-// holds the two per-channel vectors) and splits the terms over 4 thread
-// groups, each with 4 interleaved running sums, so 16 loads per column are in
+// holds the two per-channel vectors) and splits the terms over 16 thread
+// groups, each with 8 interleaved running sums, so 128 loads per column are in
 // flight.  Every addition happens in a fixed order: the result is deterministic.
-constexpr int kRedCols = 64, kRedGroups = 4;
+constexpr int kRedCols = 64, kRedGroups = 16, kRedAcc = 8;
 __global__ __launch_bounds__(kRedCols * kRedGroups) void reduce_chan_kernel(
     const float* __restrict__ pA, const float* __restrict__ pD, const float* __restrict__ pbias,
     float* __restrict__ dA, float* __restrict__ dD, float* __restrict__ dbias, int64_t B,
@@ -572,15 +571,18 @@ __global__ __launch_bounds__(kRedCols * kRedGroups) void reduce_chan_kernel(
   const int64_t d = valid ? col % D : 0;
   const int n = valid ? int(col / D) : 0;
   const int64_t terms = B * nchunks;
+  // group g adds terms g, g + 16, g + 32, ...; running sum m takes every 8th of them
   auto sum = [&](const float* x, int64_t stride) {
-    float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    int64_t k = g;
-    for (; k + 3 * kRedGroups < terms; k += 4 * kRedGroups) {
+    float acc[kRedAcc];
 #pragma unroll
-      for (int m = 0; m < 4; ++m) acc[m] += x[(k + m * kRedGroups) * stride];
+    for (int m = 0; m < kRedAcc; ++m) acc[m] = 0.0f;
+    int64_t k = g;
+    for (; k + (kRedAcc - 1) * kRedGroups < terms; k += kRedAcc * kRedGroups) {
+#pragma unroll
+      for (int m = 0; m < kRedAcc; ++m) acc[m] += x[(k + m * kRedGroups) * stride];
     }
     for (int m = 0; k < terms; k += kRedGroups, ++m) acc[m] += x[k * stride];
-    return (acc[0] + acc[1]) + (acc[2] + acc[3]);
+    return ((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7]));
   };
   float s0 = 0.0f, s1 = 0.0f;
   if (valid) {
@@ -595,12 +597,17 @@ __global__ __launch_bounds__(kRedCols * kRedGroups) void reduce_chan_kernel(
   part[1][g][c] = s1;
   __syncthreads();
   if (g != 0 || !valid) return;
-  const float t0 = (part[0][0][c] + part[0][1][c]) + (part[0][2][c] + part[0][3][c]);
+  float t0 = 0.0f, t1 = 0.0f;
+#pragma unroll
+  for (int q = 0; q < kRedGroups; ++q) {
+    t0 += part[0][q][c];
+    t1 += part[1][q][c];
+  }
   if (n < N) {
     dA[d * N + n] = t0;
   } else {
     if (dD) dD[d] = t0;
-    if (dbias) dbias[d] = (part[1][0][c] + part[1][1][c]) + (part[1][2][c] + part[1][3][c]);
+    if (dbias) dbias[d] = t1;
   }
 }
 

@@ -157,7 +157,11 @@ __global__ __launch_bounds__(kWave * kWaves) void chunk_carry_kernel(float* __re
   if (REVERSE && active && trow == 0) st[int64_t(nc - 1) * sstride] = 0.0f;
 }
 
-// The in-order walk: one lane per (b, n, d), same slots and semantics.
+// The in-order walk: one lane per (b, n, d), same slots and semantics.  The
+// chunks are taken in groups of kWalkG; a group's inputs are all fetched before
+// its chain runs, so a lane waits on memory once per group, not once per chunk.
+constexpr int kWalkG = 16;
+
 template <bool REVERSE>
 __global__ __launch_bounds__(256) void chunk_walk_kernel(float* __restrict__ states,
                                                          const float* __restrict__ dsum,
@@ -173,24 +177,44 @@ __global__ __launch_bounds__(256) void chunk_walk_kernel(float* __restrict__ sta
   const int64_t sstride = int64_t(N) * D;
   float* st = states + (b * nc) * sstride + int64_t(n) * D + d;
   const float* ds = dsum + (b * nc) * D + d;
-  float h = (!REVERSE && h0) ? h0[(b * D + d) * N + n] : 0.0f;
+  float sv[kWalkG], dv[kWalkG];
   if (!REVERSE) {
-    // slot c <- start of chunk c;  h <- a_c h + s_c
-    for (int c = 0; c < nc - 1; ++c) {
-      const float sc = st[int64_t(c) * sstride];
-      const float ac = hw_exp2(An * ds[int64_t(c) * D]);
-      if (c >= 1) st[int64_t(c) * sstride] = h;
-      h = __builtin_fmaf(ac, h, sc);
+    // slot c <- start of chunk c;  h <- a_c h + s_c, c = 0 .. nc - 2
+    float h = h0 ? h0[(b * D + d) * N + n] : 0.0f;
+    for (int c0 = 0; c0 < nc - 1; c0 += kWalkG) {
+#pragma unroll
+      for (int g = 0; g < kWalkG; ++g) {
+        const int c = c0 + g < nc - 1 ? c0 + g : nc - 2;
+        sv[g] = st[int64_t(c) * sstride];
+        dv[g] = ds[int64_t(c) * D];
+      }
+#pragma unroll
+      for (int g = 0; g < kWalkG; ++g) {
+        const int c = c0 + g;
+        if (c >= nc - 1) break;
+        if (c >= 1) st[int64_t(c) * sstride] = h;
+        h = __builtin_fmaf(hw_exp2(An * dv[g]), h, sv[g]);
+      }
     }
     st[int64_t(nc - 1) * sstride] = h;
   } else {
-    // slot c <- adjoint entering chunk c from its end;  h <- a_c h + r_c, c descending
-    h = st[int64_t(nc - 1) * sstride];
+    // slot c <- adjoint entering chunk c from its end;  h <- a_c h + r_c, c = nc - 2 .. 1
+    float h = st[int64_t(nc - 1) * sstride];
     st[int64_t(nc - 1) * sstride] = 0.0f;
-    for (int c = nc - 2; c >= 1; --c) {
-      const float rc = st[int64_t(c) * sstride];
-      st[int64_t(c) * sstride] = h;
-      h = __builtin_fmaf(hw_exp2(An * ds[int64_t(c) * D]), h, rc);
+    for (int c0 = nc - 2; c0 >= 1; c0 -= kWalkG) {
+#pragma unroll
+      for (int g = 0; g < kWalkG; ++g) {
+        const int c = c0 - g >= 1 ? c0 - g : 1;
+        sv[g] = st[int64_t(c) * sstride];
+        dv[g] = ds[int64_t(c) * D];
+      }
+#pragma unroll
+      for (int g = 0; g < kWalkG; ++g) {
+        const int c = c0 - g;
+        if (c < 1) break;
+        st[int64_t(c) * sstride] = h;
+        h = __builtin_fmaf(hw_exp2(An * dv[g]), h, sv[g]);
+      }
     }
     st[0] = h;
   }
