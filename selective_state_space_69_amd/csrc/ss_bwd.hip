@@ -145,14 +145,11 @@ __device__ __forceinline__ float reduce_scatter16(const float (&v)[16], uint32_t
 // ---------------------------------------------------------------- main kernel
 // LDS (floats): step sizes, gated output gradients and inputs u
 // [32 steps][64 lanes], B/C rows [32 steps][B 16, C 16], per-step partials of
-// du, d(dt) and y [4 waves][3][4 steps][64 lanes], and the factors of dz and
-// d(delta) of the 8 steps a thread owns [8][2][256 threads] (written and read
-// back by the same thread).
+// du, d(dt) and y [4 waves][3][4 steps][64 lanes]: 41 KB, three workgroups per CU.
 constexpr int kActF = kChunk * kWave;
 constexpr int kRowF = kChunk * 2 * kMaxState;
 constexpr int kXchF = kNW * 3 * kKB * kWave;
-constexpr int kOwnF = kNB * 2 * kNW * kWave;
-constexpr int kLdsFloats = 3 * kActF + kRowF + kXchF + kOwnF;
+constexpr int kLdsFloats = 3 * kActF + kRowF + kXchF;
 
 template <typename In, int DISC, bool HAS_Z, bool SOFTPLUS, bool SAFE>
 __device__ __forceinline__ void bwd_chunk(const BwdParams& p, float* lds, int64_t b, int dblk,
@@ -186,7 +183,6 @@ __device__ __forceinline__ void bwd_chunk(const BwdParams& p, float* lds, int64_
   float* actU = lds + 2 * kActF;                 // [32 steps][64 lanes]
   float* rows = lds + 3 * kActF;                 // [32 steps][B 16, C 16]
   float* xch = rows + kRowF;                     // [4 waves][3][4 steps][64 lanes]
-  float* own = xch + kXchF;                      // [8][2][256 threads]
   const int tid = wave * kWave + int(lane);
 
   // ---- phase A1: step sizes, gated upstream gradients and inputs of the
@@ -236,10 +232,7 @@ __device__ __forceinline__ void bwd_chunk(const BwdParams& p, float* lds, int64_
       const float zf = to_f32(rz[s]);
       const float sz = sigmoid_log2(zf * kLog2e);
       gy = g * zf * sz;
-      // dz = dy * y * d silu(z) / dz, y the pre-gate output
-      own[(s * 2 + 0) * (kNW * kWave) + tid] = g * sz * __builtin_fmaf(zf, 1.0f - sz, 1.0f);
     }
-    if (SOFTPLUS) own[(s * 2 + 1) * (kNW * kWave) + tid] = sigmoid_log2(x2);   // d softplus
     actDl[k * kWave + lane] = valid ? step_log2<SOFTPLUS>(x2) : 0.0f;
     actGy[k * kWave + lane] = valid ? gy * amask : 0.0f;
     actU[k * kWave + lane] = valid ? to_f32(ru[s]) * amask : 0.0f;
@@ -263,28 +256,31 @@ __device__ __forceinline__ void bwd_chunk(const BwdParams& p, float* lds, int64_
       const int kk = jb * kKB + k;
       const float dl = actDl[kk * kWave + lane];
       const float uf = actU[kk * kWave + lane];
+      const float dtu = dl * kLn2 * uf;            // Euler: B_bar u = dt u B
       const float4 B4 = row_of(kk, 0);
       const float Bv[kNS] = {B4.x, B4.y, B4.z, B4.w};
 #pragma unroll
       for (int j = 0; j < kNS; ++j) {
         const float a = hw_exp2(dl * A[j]);
-        float coef;
+        float bu;
         if (DISC == kEuler) {
-          coef = dl * kLn2;
+          bu = dtu * Bv[j];
         } else {
-          coef = __builtin_fmaf(a, iA[j], -iA[j]);
+          float coef = __builtin_fmaf(a, iA[j], -iA[j]);
           if (SAFE) coef = __builtin_fmaf(dl * kLn2, zm[j], coef);
+          bu = coef * (Bv[j] * uf);
         }
-        h[j] = __builtin_fmaf(a, h[j], coef * (Bv[j] * uf));
+        h[j] = __builtin_fmaf(a, h[j], bu);
       }
     }
   }
 
   // ---- phase B: blocks in reverse
   // nu: adjoint carried from later steps, A_bar_{t+1} lambda_{t+1}
-  float dA[kNS];
+  // dA = dA + dAc / A (dAc: exact ZOH's term through d coef / dA)
+  float dA[kNS], dAc[kNS];
 #pragma unroll
-  for (int j = 0; j < kNS; ++j) dA[j] = 0.0f;
+  for (int j = 0; j < kNS; ++j) dA[j] = dAc[j] = 0.0f;
   float dDacc = 0.0f, dbacc = 0.0f;
   // the value a lane holds after a reduce-scatter of [4 steps][4 states]
   const int rk = int(lane >> 4), rj = int((lane >> 2) & 3u);
@@ -293,6 +289,18 @@ __device__ __forceinline__ void bwd_chunk(const BwdParams& p, float* lds, int64_
 #pragma unroll
   for (int jb = kNB - 1; jb >= 0; --jb) {
     if (t0 + jb * kKB >= t1) continue;          // wave-uniform: block past the end
+    // raw inputs of the step this wave owns in the block (k = wave), fetched
+    // now and used by the block's outputs at its end
+    In zo{}, go{}, dlo{};
+    {
+      const int32_t tw = t0 + jb * kKB + wave;
+      const int64_t iw = ibase + int64_t(tw < t1 ? tw : t1 - 1) * D;
+      if (HAS_Z) {
+        zo = static_cast<const In*>(p.z)[iw];
+        go = static_cast<const In*>(p.dy)[iw];
+      }
+      if (SOFTPLUS) dlo = static_cast<const In*>(p.delta)[iw];
+    }
     float uf[kKB], dl[kKB], gy[kKB], yp[kKB];
     float hs[kKB][kNS];
     float red[kKB * kNS];
@@ -307,18 +315,20 @@ __device__ __forceinline__ void bwd_chunk(const BwdParams& p, float* lds, int64_
       uf[k] = actU[kk * kWave + lane];
       const float4 B4 = row_of(kk, 0), C4 = row_of(kk, 1);
       const float Bv[kNS] = {B4.x, B4.y, B4.z, B4.w}, Cv[kNS] = {C4.x, C4.y, C4.z, C4.w};
+      const float dtu = dl[k] * kLn2 * uf[k];
       float y0 = 0.0f;
 #pragma unroll
       for (int j = 0; j < kNS; ++j) {
         const float a = hw_exp2(dl[k] * A[j]);
-        float coef;
+        float bu;
         if (DISC == kEuler) {
-          coef = dl[k] * kLn2;
+          bu = dtu * Bv[j];
         } else {
-          coef = __builtin_fmaf(a, iA[j], -iA[j]);
+          float coef = __builtin_fmaf(a, iA[j], -iA[j]);
           if (SAFE) coef = __builtin_fmaf(dl[k] * kLn2, zm[j], coef);
+          bu = coef * (Bv[j] * uf[k]);
         }
-        h[j] = __builtin_fmaf(a, h[j], coef * (Bv[j] * uf[k]));
+        h[j] = __builtin_fmaf(a, h[j], bu);
         hs[k][j] = h[j];
         y0 = __builtin_fmaf(Cv[j], h[j], y0);
         red[k * kNS + j] = gy[k] * h[j];                       // dC
@@ -330,7 +340,12 @@ __device__ __forceinline__ void bwd_chunk(const BwdParams& p, float* lds, int64_
       const int32_t t = t0 + jb * kKB + rk;
       if (rwrite && t < t1) p.pC[((row0 + t) * p.ndblk + dblk) * N + n0 + rj] = r;
     }
-    // reverse sweep
+    // reverse sweep.  Per step, with lam = d loss / d h_t and nu = A_bar lam:
+    //   dB = lam coef u (coef = dt for Euler, (A_bar - 1) / A for exact ZOH)
+    //   du = sum_n lam coef B
+    //   d(dt) = sum_n nu h_{t-1} A + u sum_n (lam B [Euler] | nu B [ZOH])
+    //   dA += nu h_{t-1} dt  (+ lam B u d coef / dA for ZOH, with
+    //         d coef / dA = (dt A_bar - coef) / A; the 1 / A is applied once per chunk)
     float dup[kKB], ddp[kKB];
 #pragma unroll
     for (int k = kKB - 1; k >= 0; --k) {
@@ -338,37 +353,35 @@ __device__ __forceinline__ void bwd_chunk(const BwdParams& p, float* lds, int64_
       const float4 B4 = row_of(kk, 0), C4 = row_of(kk, 1);
       const float Bv[kNS] = {B4.x, B4.y, B4.z, B4.w}, Cv[kNS] = {C4.x, C4.y, C4.z, C4.w};
       const float dtn = dl[k] * kLn2;           // dt
-      float du0 = 0.0f, dd0 = 0.0f;
+      const float udt = uf[k] * dtn;            // u dt
+      float sLB = 0.0f, sdd = 0.0f, sdu = 0.0f;
 #pragma unroll
       for (int j = 0; j < kNS; ++j) {
         const float a = hw_exp2(dl[k] * A[j]);     // same value as in the recompute
         const float hp = k > 0 ? hs[k - 1][j] : ck[jb][j];
-        const float lam = __builtin_fmaf(gy[k], Cv[j], nu[j]);   // d loss / d h_t
-        float coef;
-        if (DISC == kEuler) {
-          coef = dtn;
-        } else {
-          coef = __builtin_fmaf(a, iA[j], -iA[j]);
-          if (SAFE) coef = __builtin_fmaf(dtn, zm[j], coef);
-        }
-        const float pu = lam * uf[k];                 // d loss / d (coef B)
-        const float q = pu * Bv[j];                   // d loss / d coef
-        red[k * kNS + j] = pu * coef;                 // dB
-        du0 = __builtin_fmaf(lam, coef * Bv[j], du0);
-        const float da = lam * hp;                    // d loss / d A_bar
-        if (DISC == kEuler) {
-          dd0 = __builtin_fmaf(da * a, A[j], dd0 + q);
-          dA[j] = __builtin_fmaf(da, a * dtn, dA[j]);
-        } else {
-          dd0 = __builtin_fmaf(a, __builtin_fmaf(da, A[j], q), dd0);
-          dA[j] = __builtin_fmaf(a * dtn, __builtin_fmaf(q, iA[j], da), dA[j]);
-          dA[j] = __builtin_fmaf(-(q * coef), iA[j], dA[j]);
-          if (SAFE) dA[j] = __builtin_fmaf(q * zm[j], 0.5f * dtn * dtn, dA[j]);
-        }
+        const float lam = __builtin_fmaf(gy[k], Cv[j], nu[j]);
         nu[j] = a * lam;
+        const float nh = nu[j] * hp;
+        sdd = __builtin_fmaf(nh, A[j], sdd);
+        dA[j] = __builtin_fmaf(nh, dtn, dA[j]);
+        if (DISC == kEuler) {
+          red[k * kNS + j] = lam * udt;                   // dB
+          sLB = __builtin_fmaf(lam, Bv[j], sLB);
+        } else {
+          float coef = __builtin_fmaf(a, iA[j], -iA[j]);
+          if (SAFE) coef = __builtin_fmaf(dtn, zm[j], coef);
+          const float cl = lam * coef;
+          const float db = cl * uf[k];
+          red[k * kNS + j] = db;                          // dB
+          sdu = __builtin_fmaf(cl, Bv[j], sdu);
+          sLB = __builtin_fmaf(nu[j], Bv[j], sLB);
+          dAc[j] = __builtin_fmaf(Bv[j], __builtin_fmaf(udt, nu[j], -db), dAc[j]);
+          // A == 0: coef = dt and d coef / dA = dt^2 / 2
+          if (SAFE) dA[j] = __builtin_fmaf(lam * zm[j], Bv[j] * (0.5f * udt * dtn), dA[j]);
+        }
       }
-      dup[k] = du0;
-      ddp[k] = dd0;
+      dup[k] = DISC == kEuler ? dtn * sLB : sdu;
+      ddp[k] = __builtin_fmaf(uf[k], sLB, sdd);
     }
     {
       const float r = reduce_scatter16(red, lane);
@@ -395,17 +408,19 @@ __device__ __forceinline__ void bwd_chunk(const BwdParams& p, float* lds, int64_
         sy += xch[((w * 3 + 2) * kKB + k) * kWave + lane];
       }
       if (t < t1 && active) {
-        // the owned step of block jb is step jb of this thread in phase A1
         const int64_t i = ibase + int64_t(t) * D;
         const int kk = jb * kKB + k;
         const float ui = actU[kk * kWave + lane], gyk = actGy[kk * kWave + lane];
         if (HAS_Z) {
-          const float y = __builtin_fmaf(Dd, ui, sy);   // pre-gate output
-          p.dz[i] = own[(jb * 2 + 0) * (kNW * kWave) + tid] * y;
+          // dz = dy * y * d silu(z) / dz, y the pre-gate output
+          const float zf = to_f32(zo), g = to_f32(go);
+          const float sz = sigmoid_log2(zf * kLog2e);
+          const float y = __builtin_fmaf(Dd, ui, sy);
+          p.dz[i] = g * y * sz * __builtin_fmaf(zf, 1.0f - sz, 1.0f);
         }
         p.du[i] = __builtin_fmaf(gyk, Dd, sdu);
         float ddv = sdd;                                 // d loss / d dt
-        if (SOFTPLUS) ddv *= own[(jb * 2 + 1) * (kNW * kWave) + tid];   // through softplus
+        if (SOFTPLUS) ddv *= sigmoid_log2(__builtin_fmaf(to_f32(dlo), kLog2e, bias2));   // through softplus
         p.ddelta[i] = ddv;
         dDacc = __builtin_fmaf(gyk, ui, dDacc);
         dbacc += ddv;
@@ -423,7 +438,7 @@ __device__ __forceinline__ void bwd_chunk(const BwdParams& p, float* lds, int64_
     float* pa = p.pA + (b * p.nchunks + chunk) * int64_t(N) * D + d;
 #pragma unroll
     for (int j = 0; j < kNS; ++j)
-      if (n0 + j < N) pa[int64_t(n0 + j) * D] = dA[j];
+      if (n0 + j < N) pa[int64_t(n0 + j) * D] = DISC == kEuler ? dA[j] : __builtin_fmaf(iA[j], dAc[j], dA[j]);
   }
   // dD_skip and ddelta_bias: the four waves' per-channel sums, added by wave 0
   xch[(wave * 2 + 0) * kWave + lane] = dDacc;
@@ -441,9 +456,9 @@ __device__ __forceinline__ void bwd_chunk(const BwdParams& p, float* lds, int64_
   }
 }
 
-// two waves per SIMD: at most 256 VGPRs
+// Euler: three waves per SIMD (at most 168 VGPRs); exact ZOH: two (256)
 template <typename In, int DISC, bool HAS_Z, bool SOFTPLUS>
-__global__ __launch_bounds__(kWave * kNW, 2) void bwd_kernel(BwdParams p) {
+__global__ __launch_bounds__(kWave * kNW, DISC == kEuler ? 3 : 2) void bwd_kernel(BwdParams p) {
   __shared__ float4 lds4[kLdsFloats / 4];
   float* lds = reinterpret_cast<float*>(lds4);
   const int wave = __builtin_amdgcn_readfirstlane(int(threadIdx.x) / kWave);
