@@ -4,14 +4,16 @@
 // ("A Visual Guide to Mamba" summary, Hardware-aware Algorithm: recomputation;
 // "A Survey of Mamba" summary, hardware-aware computation).  Time is cut into
 // chunks of 32 steps.  Per chunk:
-//   - its start state comes from the forward's summary pass + carry scan;
-//   - the adjoint carry entering it from its end comes from a reverse summary
-//     pass + reverse carry scan (ss_carry.hip; the adjoint recurrence
+//   - one summary pass gives its zero-start end state and its local adjoint
+//     (what it sends back to the chunk before it with nothing entering from
+//     its end);
+//   - carry scans turn those into its true start state and the adjoint carry
+//     entering it from its end (ss_carry.hip; the adjoint recurrence
 //     lambda_t = gy_t C_t + A_bar_{t+1} lambda_{t+1} is the same linear scan run
 //     backwards in time);
 //   - a workgroup of 4 waves (lane = channel d, 4 states per wave) stages the
-//     chunk's step sizes, gated output gradients and B/C rows in LDS, runs the
-//     chunk forward keeping one state checkpoint per 4-step block in
+//     chunk's step sizes, gated output gradients, inputs and B/C rows in LDS,
+//     runs the chunk forward keeping one state checkpoint per 4-step block in
 //     registers, then walks the blocks backwards: recompute the block (A_bar
 //     and h kept in registers), reverse sweep, gradients.
 // Reductions: dB, dC over the 64 channels of a block by a cross-lane
@@ -19,8 +21,8 @@
 // and ddelta_bias per channel over the chunk, then over chunks and batch rows.
 // All partial sums are added in a fixed order: the backward is deterministic.
 // The chunk's inputs are all fetched at its start (one round trip to memory)
-// and kept in LDS; the footprint (about 175 VGPRs for Euler, 205 for ZOH and
-// 57 KB of LDS) allows two workgroups per CU.
+// and kept in LDS (41 KB); the main kernel holds about 165 VGPRs for Euler (three
+// waves per SIMD) and 210 for exact ZOH (two).
 #include "ss_device.hpp"
 
 namespace ss {
@@ -45,8 +47,8 @@ struct BwdParams {
   const float* Dskip;
   const float* bias;
   const float* h0;
-  const float* hstart;   // (B, nc, N, D): start state of chunk c (c >= 1)
-  const float* dsum;     // (B, nc, D): sum of dt * log2 e over chunk c (c <= nc - 2)
+  float* hstart;         // (B, nc, N, D): start state of chunk c (c >= 1)
+  float* dsum;           // (B, nc, D): sum of dt * log2 e over chunk c (c <= nc - 2)
   float* lam;            // (B, nc, N, D): adjoint carry entering chunk c from its end
   float* du;
   float* ddelta;
@@ -151,6 +153,53 @@ constexpr int kRowF = kChunk * 2 * kMaxState;
 constexpr int kXchF = kNW * 3 * kKB * kWave;
 constexpr int kLdsFloats = 3 * kActF + kRowF + kXchF;
 
+// Stages chunk [t0, t1) in LDS: per step and lane the step size dt log2 e, the
+// gated upstream gradient gy and the input u (all 0 past t1, gy and u 0 on idle
+// lanes), and the chunk's B/C rows.  Wave w prepares the steps k with
+// k % 4 == w; every load is issued before any is used.  The caller places the
+// barrier.
+template <typename In, bool HAS_Z, bool SOFTPLUS>
+__device__ __forceinline__ void stage_chunk(const BwdParams& p, float* lds, int64_t ibase,
+                                            int64_t row0, int32_t t0, int32_t t1, int wave,
+                                            uint32_t lane, float bias2, float amask) {
+  const int64_t D = p.D;
+  float* actDl = lds;                            // [32 steps][64 lanes]
+  float* actGy = lds + kActF;
+  float* actU = lds + 2 * kActF;
+  float* rows = lds + 3 * kActF;                 // [32 steps][B 16, C 16]
+  In rdl[kNB], rdy[kNB], rz[kNB], ru[kNB];
+#pragma unroll
+  for (int s = 0; s < kNB; ++s) {
+    const int32_t t = t0 + s * kNW + wave;
+    const int64_t i = ibase + int64_t(t < t1 ? t : t1 - 1) * D;
+    rdl[s] = static_cast<const In*>(p.delta)[i];
+    rdy[s] = static_cast<const In*>(p.dy)[i];
+    if (HAS_Z) rz[s] = static_cast<const In*>(p.z)[i];
+    ru[s] = static_cast<const In*>(p.u)[i];
+  }
+  // 256 threads, 4 values each: step tid / 8, B (parts 0-3) or C (4-7)
+  const int tid = wave * kWave + int(lane);
+  const int rk8 = tid / 8, rpart = tid % 8;
+  const auto rraw = load_raw4(static_cast<const In*>(rpart < 4 ? p.Brow : p.Crow) +
+                              (row0 + (t0 + rk8 < t1 ? t0 + rk8 : t1 - 1)) * kMaxState +
+                              4 * (rpart % 4));
+#pragma unroll
+  for (int s = 0; s < kNB; ++s) {
+    const int k = s * kNW + wave;
+    const bool valid = t0 + k < t1;
+    const float x2 = __builtin_fmaf(to_f32(rdl[s]), kLog2e, bias2);
+    float gy = to_f32(rdy[s]);
+    if (HAS_Z) {
+      const float zf = to_f32(rz[s]);
+      gy *= zf * sigmoid_log2(zf * kLog2e);      // dy silu(z)
+    }
+    actDl[k * kWave + lane] = valid ? step_log2<SOFTPLUS>(x2) : 0.0f;
+    actGy[k * kWave + lane] = valid ? gy * amask : 0.0f;
+    actU[k * kWave + lane] = valid ? to_f32(ru[s]) * amask : 0.0f;
+  }
+  *reinterpret_cast<float4*>(rows + rk8 * 2 * kMaxState + 4 * rpart) = unpack4(rraw);
+}
+
 template <typename In, int DISC, bool HAS_Z, bool SOFTPLUS, bool SAFE>
 __device__ __forceinline__ void bwd_chunk(const BwdParams& p, float* lds, int64_t b, int dblk,
                                           int chunk, int wave, uint32_t lane) {
@@ -183,27 +232,8 @@ __device__ __forceinline__ void bwd_chunk(const BwdParams& p, float* lds, int64_
   float* actU = lds + 2 * kActF;                 // [32 steps][64 lanes]
   float* rows = lds + 3 * kActF;                 // [32 steps][B 16, C 16]
   float* xch = rows + kRowF;                     // [4 waves][3][4 steps][64 lanes]
-  const int tid = wave * kWave + int(lane);
-
-  // ---- phase A1: step sizes, gated upstream gradients and inputs of the
-  //      chunk, each wave computing the steps k with k % 4 == wave; the
-  //      chunk's B/C rows.  Every load is issued before any is used.
-  In rdl[kNB], rdy[kNB], rz[kNB], ru[kNB];
-#pragma unroll
-  for (int s = 0; s < kNB; ++s) {
-    const int32_t t = t0 + s * kNW + wave;
-    const int64_t i = ibase + int64_t(t < t1 ? t : t1 - 1) * D;
-    rdl[s] = static_cast<const In*>(p.delta)[i];
-    rdy[s] = static_cast<const In*>(p.dy)[i];
-    if (HAS_Z) rz[s] = static_cast<const In*>(p.z)[i];
-    ru[s] = static_cast<const In*>(p.u)[i];
-  }
-  // 256 threads, 4 values each: step tid / 8, B (parts 0-3) or C (4-7)
-  const int rk8 = tid / 8, rpart = tid % 8;
-  const auto rraw = load_raw4(static_cast<const In*>(rpart < 4 ? p.Brow : p.Crow) +
-                              (row0 + (t0 + rk8 < t1 ? t0 + rk8 : t1 - 1)) * kMaxState +
-                              4 * (rpart % 4));
-  // start state of the chunk and the adjoint carry entering it from its end
+  // ---- phase A1: the chunk's inputs and rows to LDS, with the loads of the
+  //      chunk's start state and of the adjoint carry entering it from its end
   float h[kNS], nu[kNS];
   if (chunk == 0) {
 #pragma unroll
@@ -221,23 +251,7 @@ __device__ __forceinline__ void bwd_chunk(const BwdParams& p, float* lds, int64_
 #pragma unroll
     for (int j = 0; j < kNS; ++j) nu[j] = n0 + j < N ? ls[int64_t(n0 + j) * D] : 0.0f;
   }
-#pragma unroll
-  for (int s = 0; s < kNB; ++s) {
-    const int k = s * kNW + wave;
-    const bool valid = t0 + k < t1;
-    const float x2 = __builtin_fmaf(to_f32(rdl[s]), kLog2e, bias2);
-    const float g = to_f32(rdy[s]);
-    float gy = g;
-    if (HAS_Z) {
-      const float zf = to_f32(rz[s]);
-      const float sz = sigmoid_log2(zf * kLog2e);
-      gy = g * zf * sz;
-    }
-    actDl[k * kWave + lane] = valid ? step_log2<SOFTPLUS>(x2) : 0.0f;
-    actGy[k * kWave + lane] = valid ? gy * amask : 0.0f;
-    actU[k * kWave + lane] = valid ? to_f32(ru[s]) * amask : 0.0f;
-  }
-  *reinterpret_cast<float4*>(rows + rk8 * 2 * kMaxState + 4 * rpart) = unpack4(rraw);
+  stage_chunk<In, HAS_Z, SOFTPLUS>(p, lds, ibase, row0, t0, t1, wave, lane, bias2, amask);
   __syncthreads();
   // this wave's 4 states of the B (m = 0) or C (m = 1) row of step kk
   auto row_of = [&](int kk, int m) -> float4 {
@@ -481,70 +495,115 @@ __global__ __launch_bounds__(kWave * kNW, DISC == kEuler ? 3 : 2) void bwd_kerne
     bwd_chunk<In, DISC, HAS_Z, SOFTPLUS, false>(p, lds, b, dblk, chunk, wave, lane);
 }
 
-// ---------------------------------------------------------------- reverse summaries
-// Local adjoint of chunk c (c >= 1) with nothing entering from its end:
-// R_c = A_bar-weighted sum of gy C over the chunk, one lane per (b, d), all N
-// states.  Stored in lam[b][c].  The chunk's C rows go to LDS and every input
-// of the lane's 32 steps is fetched before the walk starts.
-template <typename In, bool HAS_Z, bool SOFTPLUS>
-__global__ __launch_bounds__(kWave) void rev_summary_kernel(BwdParams p) {
-  __shared__ float4 crow4[kChunk * kMaxState / 4];
-  float* crow = reinterpret_cast<float*>(crow4);   // [32 steps][16 states]
-  const uint32_t lane = threadIdx.x;
-  int64_t bid = blockIdx.x;
-  const int dblk = int(bid % p.ndblk);
-  bid /= p.ndblk;
-  const int chunk = 1 + int(bid % (p.nchunks - 1));
-  const int64_t b = bid / (p.nchunks - 1);
-  const int64_t D = p.D;
+// ---------------------------------------------------------------- chunk summaries
+// One pass over chunk c yields what both carry scans need, for the 4 states of
+// each wave and the 64 channels of the workgroup:
+//  - forward (c <= nc - 2): the end state from a zero start, into hstart[b][c],
+//    and the chunk's sum of dt log2 e, into dsum[b][c];
+//  - reverse (c >= 1): the adjoint at the chunk's start with nothing entering
+//    from its end, sum over t of (A_bar_t0 ... A_bar_t) gy_t C_t, into
+//    lam[b][c]; it is accumulated forward in time with a running product of
+//    A_bar, so the two summaries share one exponential per (t, n).
+template <typename In, int DISC, bool HAS_Z, bool SOFTPLUS, bool SAFE>
+__device__ __forceinline__ void summary_chunk(const BwdParams& p, float* lds, int64_t b, int dblk,
+                                              int chunk, int wave, uint32_t lane) {
+  const int n0 = wave * kNS;
   const int N = p.N;
+  const int64_t D = p.D;
   const int64_t d = int64_t(dblk) * kWave + lane;
   const bool active = d < D;
   const int64_t dc = active ? d : D - 1;
   const int32_t t0 = chunk * kChunk;
   const int32_t t1 = int32_t(t0 + kChunk < p.L ? t0 + kChunk : p.L);
   const int64_t row0 = b * p.L;
-  const int64_t ibase = row0 * D + dc;
-  In rdl[kChunk], rdy[kChunk], rz[kChunk];
-#pragma unroll
-  for (int k = 0; k < kChunk; ++k) {
-    const int64_t i = ibase + int64_t(t0 + k < t1 ? t0 + k : t1 - 1) * D;
-    rdl[k] = static_cast<const In*>(p.delta)[i];
-    rdy[k] = static_cast<const In*>(p.dy)[i];
-    if (HAS_Z) rz[k] = static_cast<const In*>(p.z)[i];
-  }
-  {
-    // 64 lanes x 8 values: row lane / 2, states 8 (lane % 2) .. + 7
-    const int k = int(lane / 2), q = 8 * int(lane % 2);
-    const In* src = static_cast<const In*>(p.Crow) +
-                    (row0 + (t0 + k < t1 ? t0 + k : t1 - 1)) * kMaxState + q;
-    const auto r0 = load_raw4(src), r1 = load_raw4(src + 4);
-    crow4[(k * kMaxState + q) / 4] = unpack4(r0);
-    crow4[(k * kMaxState + q) / 4 + 1] = unpack4(r1);
-  }
   const float bias2 = (p.bias ? p.bias[dc] : 0.0f) * kLog2e;
-  float A[kMaxState], nu[kMaxState];
+  stage_chunk<In, HAS_Z, SOFTPLUS>(p, lds, row0 * D + dc, row0, t0, t1, wave, lane, bias2,
+                                   active ? 1.0f : 0.0f);
+  float A[kNS], iA[kNS], zm[kNS];
 #pragma unroll
-  for (int n = 0; n < kMaxState; ++n) {
-    A[n] = n < N ? p.A[dc * N + n] : -1.0f;
-    nu[n] = 0.0f;
+  for (int j = 0; j < kNS; ++j) {
+    const int n = n0 + j;
+    const float a = n < N ? p.A[dc * N + n] : -1.0f;
+    A[j] = a;
+    iA[j] = a == 0.0f ? 0.0f : 1.0f / a;
+    zm[j] = a == 0.0f ? 1.0f : 0.0f;
   }
   __syncthreads();
+  const float* actDl = lds;
+  const float* actGy = lds + kActF;
+  const float* actU = lds + 2 * kActF;
+  const float* rows = lds + 3 * kActF;
+  float h[kNS], P[kNS], R[kNS];
 #pragma unroll
-  for (int k = kChunk - 1; k >= 0; --k) {
-    if (t0 + k >= t1) continue;                  // uniform: steps past the end
-    const float dl = step_log2<SOFTPLUS>(__builtin_fmaf(to_f32(rdl[k]), kLog2e, bias2));
-    float gy = to_f32(rdy[k]);
-    if (HAS_Z) gy *= silu(to_f32(rz[k]));
+  for (int j = 0; j < kNS; ++j) {
+    h[j] = 0.0f;
+    P[j] = 1.0f;
+    R[j] = 0.0f;
+  }
+  float dsum = 0.0f;
+#pragma unroll 8
+  for (int k = 0; k < kChunk; ++k) {
+    const float dl = actDl[k * kWave + lane];
+    const float uf = actU[k * kWave + lane];
+    const float gy = actGy[k * kWave + lane];
+    const float4 B4 = *reinterpret_cast<const float4*>(rows + k * 2 * kMaxState + n0);
+    const float4 C4 = *reinterpret_cast<const float4*>(rows + k * 2 * kMaxState + kMaxState + n0);
+    const float Bv[kNS] = {B4.x, B4.y, B4.z, B4.w}, Cv[kNS] = {C4.x, C4.y, C4.z, C4.w};
+    const float dtu = dl * kLn2 * uf;
 #pragma unroll
-    for (int n = 0; n < kMaxState; ++n)
-      nu[n] = hw_exp2(dl * A[n]) * __builtin_fmaf(gy, crow[k * kMaxState + n], nu[n]);
+    for (int j = 0; j < kNS; ++j) {
+      const float a = hw_exp2(dl * A[j]);
+      float bu;
+      if (DISC == kEuler) {
+        bu = dtu * Bv[j];
+      } else {
+        float coef = __builtin_fmaf(a, iA[j], -iA[j]);
+        if (SAFE) coef = __builtin_fmaf(dl * kLn2, zm[j], coef);
+        bu = coef * (Bv[j] * uf);
+      }
+      h[j] = __builtin_fmaf(a, h[j], bu);
+      P[j] *= a;
+      R[j] = __builtin_fmaf(P[j], gy * Cv[j], R[j]);
+    }
+    dsum += dl;
   }
   if (!active) return;
-  float* ls = p.lam + (b * p.nchunks + chunk) * int64_t(N) * D + d;
+  const int64_t slot = (b * p.nchunks + chunk) * int64_t(N) * D + d;
+  if (chunk <= p.nchunks - 2) {
 #pragma unroll
-  for (int n = 0; n < kMaxState; ++n)
-    if (n < N) ls[int64_t(n) * D] = nu[n];
+    for (int j = 0; j < kNS; ++j)
+      if (n0 + j < N) p.hstart[slot + int64_t(n0 + j) * D] = h[j];
+    if (wave == 0) p.dsum[(b * p.nchunks + chunk) * D + d] = dsum;
+  }
+  if (chunk >= 1) {
+#pragma unroll
+    for (int j = 0; j < kNS; ++j)
+      if (n0 + j < N) p.lam[slot + int64_t(n0 + j) * D] = R[j];
+  }
+}
+
+// five workgroups per CU (LDS 28 KB each): at most 96 VGPRs
+template <typename In, int DISC, bool HAS_Z, bool SOFTPLUS>
+__global__ __launch_bounds__(kWave * kNW, 5) void summary_kernel(BwdParams p) {
+  __shared__ float4 lds4[(3 * kActF + kRowF) / 4];
+  float* lds = reinterpret_cast<float*>(lds4);
+  const int wave = __builtin_amdgcn_readfirstlane(int(threadIdx.x) / kWave);
+  const uint32_t lane = threadIdx.x % kWave;
+  int64_t bid = blockIdx.x;
+  const int dblk = int(bid % p.ndblk);
+  bid /= p.ndblk;
+  const int chunk = int(bid % p.nchunks);
+  const int64_t b = bid / p.nchunks;
+  bool zero = false;
+  if (DISC == kZoh) {
+    const int64_t d = int64_t(dblk) * kWave + lane;
+    const int64_t dc = d < p.D ? d : p.D - 1;
+    for (int n = 0; n < p.N; ++n) zero |= p.A[dc * p.N + n] == 0.0f;
+  }
+  if (DISC == kZoh && __syncthreads_or(zero))
+    summary_chunk<In, DISC, HAS_Z, SOFTPLUS, true>(p, lds, b, dblk, chunk, wave, lane);
+  else
+    summary_chunk<In, DISC, HAS_Z, SOFTPLUS, false>(p, lds, b, dblk, chunk, wave, lane);
 }
 
 // ---------------------------------------------------------------- reductions
@@ -638,19 +697,23 @@ hipError_t launch_main(const ss_desc_t& d, const BwdParams& p, int64_t blocks, h
 }
 
 template <typename In, bool HAS_Z, bool SOFTPLUS>
-hipError_t launch_rev(const BwdParams& p, int64_t blocks, hipStream_t st) {
-  hipLaunchKernelGGL((rev_summary_kernel<In, HAS_Z, SOFTPLUS>), dim3(unsigned(blocks)),
-                     dim3(kWave), 0, st, p);
+hipError_t launch_summary(const ss_desc_t& d, const BwdParams& p, int64_t blocks, hipStream_t st) {
+  if (d.disc == SS_ZOH)
+    hipLaunchKernelGGL((summary_kernel<In, kZoh, HAS_Z, SOFTPLUS>), dim3(unsigned(blocks)),
+                       dim3(kWave * kNW), 0, st, p);
+  else
+    hipLaunchKernelGGL((summary_kernel<In, kEuler, HAS_Z, SOFTPLUS>), dim3(unsigned(blocks)),
+                       dim3(kWave * kNW), 0, st, p);
   return hipGetLastError();
 }
 
 template <typename In>
-hipError_t dispatch_bwd(const ss_desc_t& d, const BwdParams& p, bool rev, int64_t blocks,
+hipError_t dispatch_bwd(const ss_desc_t& d, const BwdParams& p, bool summary, int64_t blocks,
                         hipStream_t st) {
   const bool z = p.z != nullptr, sp = d.delta_softplus != 0;
-  if (rev) {
-    if (z) return sp ? launch_rev<In, true, true>(p, blocks, st) : launch_rev<In, true, false>(p, blocks, st);
-    return sp ? launch_rev<In, false, true>(p, blocks, st) : launch_rev<In, false, false>(p, blocks, st);
+  if (summary) {
+    if (z) return sp ? launch_summary<In, true, true>(d, p, blocks, st) : launch_summary<In, true, false>(d, p, blocks, st);
+    return sp ? launch_summary<In, false, true>(d, p, blocks, st) : launch_summary<In, false, false>(d, p, blocks, st);
   }
   if (z) return sp ? launch_main<In, true, true>(d, p, blocks, st) : launch_main<In, true, false>(d, p, blocks, st);
   return sp ? launch_main<In, false, true>(d, p, blocks, st) : launch_main<In, false, false>(d, p, blocks, st);
@@ -673,12 +736,6 @@ int launch_bwd(const ss_desc_t& d, const BwdPlan& plan, const BwdArgs& a, void* 
   }
   const int nc = int(plan.tp.nchunks);
   const int ndblk = int(plan.nblk);
-  if (nc > 1) {
-    FwdArgs fa{a.u, a.delta, a.A, a.Bm, a.Cm, a.Dskip, a.bias, a.z, a.h0, nullptr, nullptr,
-               Brow, Crow, hend, dsum};
-    const int e = launch_fwd_carries(d, plan.tp, fa, stream);
-    if (e != 0) return e;
-  }
   BwdParams p{};
   p.u = a.u; p.delta = a.delta; p.z = a.z; p.dy = a.dy; p.A = a.A;
   p.Brow = Brow; p.Crow = Crow; p.Dskip = a.Dskip; p.bias = a.bias; p.h0 = a.h0;
@@ -693,11 +750,15 @@ int launch_bwd(const ss_desc_t& d, const BwdPlan& plan, const BwdArgs& a, void* 
   const int64_t cols = d.batch * ndblk;
   hipError_t e;
   if (nc > 1) {
-    e = d.in_dtype == SS_BF16 ? dispatch_bwd<uint16_t>(d, p, true, cols * (nc - 1), st)
-                              : dispatch_bwd<float>(d, p, true, cols * (nc - 1), st);
+    // both chunk summaries in one pass, then the forward and the reverse carry scans
+    e = d.in_dtype == SS_BF16 ? dispatch_bwd<uint16_t>(d, p, true, cols * nc, st)
+                              : dispatch_bwd<float>(d, p, true, cols * nc, st);
     if (e != hipSuccess) return int(e);
-    const int ec = launch_chunk_carry(lam, dsum, a.A, nullptr, d.batch, d.dim, int(d.dstate), nc,
-                                      true, stream);
+    int ec = launch_chunk_carry(hend, dsum, a.A, a.h0, d.batch, d.dim, int(d.dstate), nc, false,
+                                stream);
+    if (ec != 0) return ec;
+    ec = launch_chunk_carry(lam, dsum, a.A, nullptr, d.batch, d.dim, int(d.dstate), nc, true,
+                            stream);
     if (ec != 0) return ec;
   }
   e = d.in_dtype == SS_BF16 ? dispatch_bwd<uint16_t>(d, p, false, cols * nc, st)
