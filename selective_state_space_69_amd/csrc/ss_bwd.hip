@@ -93,11 +93,18 @@ __device__ __forceinline__ float swap_add16(float lo, float hi) {
   auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(lo), __float_as_uint(hi), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
+// x from the lane that DPP control CTRL selects (every control used here has a
+// source in range for every lane, so the bound-control zero never applies; it
+// lets the move fold into the consuming add)
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, true));
+}
 template <int CTRL>
 __device__ __forceinline__ float dpp_pair(float lo, float hi, bool upper) {
   const float send = upper ? lo : hi;
   const float keep = upper ? hi : lo;
-  return keep + __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(send), CTRL, 0xf, 0xf, false));
+  return keep + dpp<CTRL>(send);
 }
 constexpr int kDppRowRor8 = 0x128;
 constexpr int kDppRowHalfMirror = 0x141;
@@ -139,8 +146,8 @@ __device__ __forceinline__ float reduce_scatter16(const float (&v)[16], uint32_t
 #pragma unroll
   for (int i = 0; i < 2; ++i) c[i] = dpp_pair<kDppRowRor8>(b[i], b[i + 2], u3);
   float d = dpp_pair<kDppRowHalfMirror>(c[0], c[1], u2);
-  d += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(d), kDppQuadXor2, 0xf, 0xf, false));
-  d += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(d), kDppQuadXor1, 0xf, 0xf, false));
+  d += dpp<kDppQuadXor2>(d);
+  d += dpp<kDppQuadXor1>(d);
   return d;
 }
 
@@ -296,9 +303,14 @@ __device__ __forceinline__ void bwd_chunk(const BwdParams& p, float* lds, int64_
 #pragma unroll
   for (int j = 0; j < kNS; ++j) dA[j] = dAc[j] = 0.0f;
   float dDacc = 0.0f, dbacc = 0.0f;
-  // the value a lane holds after a reduce-scatter of [4 steps][4 states]
+  // the value a lane holds after a reduce-scatter of [4 steps][4 states]: step
+  // rk of the block, state n0 + rj; its rows of pB / pC for block 0
   const int rk = int(lane >> 4), rj = int((lane >> 2) & 3u);
   const bool rwrite = (lane & 3u) == 0 && n0 + rj < N;
+  const int64_t roff = ((row0 + t0 + rk) * p.ndblk + dblk) * N + n0 + rj;
+  float* const pBl = p.pB + roff;
+  float* const pCl = p.pC + roff;
+  const int64_t rstep = int64_t(kKB) * p.ndblk * N;   // between blocks
 
 #pragma unroll
   for (int jb = kNB - 1; jb >= 0; --jb) {
@@ -352,7 +364,7 @@ __device__ __forceinline__ void bwd_chunk(const BwdParams& p, float* lds, int64_
     {
       const float r = reduce_scatter16(red, lane);
       const int32_t t = t0 + jb * kKB + rk;
-      if (rwrite && t < t1) p.pC[((row0 + t) * p.ndblk + dblk) * N + n0 + rj] = r;
+      if (rwrite && t < t1) pCl[jb * rstep] = r;
     }
     // reverse sweep.  Per step, with lam = d loss / d h_t and nu = A_bar lam:
     //   dB = lam coef u (coef = dt for Euler, (A_bar - 1) / A for exact ZOH)
@@ -400,7 +412,7 @@ __device__ __forceinline__ void bwd_chunk(const BwdParams& p, float* lds, int64_
     {
       const float r = reduce_scatter16(red, lane);
       const int32_t t = t0 + jb * kKB + rk;
-      if (rwrite && t < t1) p.pB[((row0 + t) * p.ndblk + dblk) * N + n0 + rj] = r;
+      if (rwrite && t < t1) pBl[jb * rstep] = r;
     }
     // per-step partials of this wave -> LDS
 #pragma unroll
