@@ -11,16 +11,21 @@
 //                                                its conjugate
 //     out   = y * silu(z)
 //
-// Layout: a workgroup of 4 waves covers 64 channels; a wave covers 16
-// channels with 4 lanes each (a quad), and lane q of a quad holds the complex
-// states 4q .. 4q + 3 (N <= 16), so the problem has four times as many lanes
-// as channels.  The quad's partial sums of C h meet through two DPP quad
-// permutations.  Each step needs one v_exp_f32 (the modulus) and one
-// v_sin_f32 / v_cos_f32 pair (the phase, in revolutions, reduced to [0, 1)
-// first) per state.  B and C rows of a block of 8 steps are staged in LDS as
-// fp32 (re, im) pairs; u, delta and z of the next block are fetched into
-// registers while the current one runs.  No time chunks: one workgroup walks
-// the whole sequence of its channels.
+// Layout: a workgroup of 4 waves covers 32 channels; a wave covers 8 channels
+// with 8 lanes each, and lane q of a channel holds the complex states 2q and
+// 2q + 1 (N <= 16).  Time runs in blocks of 8 steps, and lane q also owns step
+// q of every block: it alone loads that step's u, delta and z, computes its
+// softplus and gate, publishes (dt, u) through LDS for the other lanes, and
+// stores its y.  The 8 per-step partial sums of C h a lane builds in a block
+// are reduce-scattered over the channel's 8 lanes (DPP half-row mirror, then
+// quad swaps), so lane q ends with the sum for its own step.  Each state and
+// step needs one v_exp_f32 (the modulus) and one v_sin_f32 / v_cos_f32 pair
+// (the phase, in revolutions, reduced to [0, 1) first).  B and C rows of a
+// block are staged in LDS as fp32 (re, im) pairs; the inputs of the next block
+// are fetched while the current one runs.  No time chunks: one workgroup walks
+// the whole sequence of its channels.  On the Mamba-2.8B width (B = 8,
+// D = 5120) the grid is 1280 workgroups: five per compute unit, five waves per
+// SIMD.
 #include <type_traits>
 
 #include "ss_device.hpp"
@@ -29,13 +34,14 @@ namespace ss {
 namespace {
 
 constexpr int kCBlk = 8;                 // steps per block
-constexpr int kSPL = 4;                  // complex states per lane
-constexpr int kQuad = 4;                 // lanes per channel
-constexpr int kChPerWave = kWave / kQuad;
+constexpr int kSPL = 2;                  // complex states per lane
+constexpr int kLPC = 8;                  // lanes per channel (= steps per block)
+constexpr int kChPerWave = kWave / kLPC;
 constexpr int kCWaves = 4;
 constexpr int kChPerGroup = kChPerWave * kCWaves;
-constexpr int kMaxC = kSPL * kQuad;      // 16 complex states
+constexpr int kMaxC = kSPL * kLPC;       // 16 complex states
 constexpr float kInv2Pi = 0.15915494309189535f;
+static_assert(kLPC == kCBlk, "lane q of a channel owns step q of a block");
 
 struct CParams {
   const void* u;
@@ -53,9 +59,31 @@ struct CParams {
   int32_t N, ndblk;
 };
 
+// x from the lane DPP control CTRL selects (every control used here has a
+// source in range for every lane)
 template <int CTRL>
-__device__ __forceinline__ float quad_dpp(float v) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+__device__ __forceinline__ float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, true));
+}
+// one stage of a reduce-scatter: the lane keeps the half of its values its
+// id bit selects (upper: hi) and adds the partner's copy of that half
+template <int CTRL>
+__device__ __forceinline__ float dpp_pair(float lo, float hi, bool upper) {
+  return (upper ? hi : lo) + dpp<CTRL>(upper ? lo : hi);
+}
+constexpr int kDppHalfMirror = 0x141;   // lane l <-> 7 - l inside each group of 8
+constexpr int kDppQuadXor2 = 0x4e;      // quad_perm [2, 3, 0, 1]
+constexpr int kDppQuadXor1 = 0xb1;      // quad_perm [1, 0, 3, 2]
+
+// 8 values per lane -> lane q of each group of 8 holds the group's sum of
+// value q.  Stage partners: l <-> 7 - l (keep by bit 2), then l ^ 2, l ^ 1.
+__device__ __forceinline__ float reduce_scatter8(const float (&v)[8], int q) {
+  float c[4], e[2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) c[i] = dpp_pair<kDppHalfMirror>(v[i], v[i + 4], (q & 4) != 0);
+#pragma unroll
+  for (int i = 0; i < 2; ++i) e[i] = dpp_pair<kDppQuadXor2>(c[i], c[i + 2], (q & 2) != 0);
+  return dpp_pair<kDppQuadXor1>(e[0], e[1], (q & 1) != 0);
 }
 
 template <typename In>
@@ -86,10 +114,11 @@ __global__ __launch_bounds__(kWave * kCWaves) void fwd_complex_kernel(CParams p)
   const int tid = int(threadIdx.x);
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int lane = tid % kWave;
-  const int q = lane % kQuad, cl = lane / kQuad;
+  const int q = lane % kLPC, cl = lane / kLPC;
+  const int chan = wave * kChPerWave + cl;                 // channel within the group
   const int dblk = int(blockIdx.x % unsigned(p.ndblk));
   const int64_t b = int64_t(blockIdx.x / unsigned(p.ndblk));
-  const int64_t d = int64_t(dblk) * kChPerGroup + wave * kChPerWave + cl;
+  const int64_t d = int64_t(dblk) * kChPerGroup + chan;
   const bool active = d < p.D;
   const int64_t dc = active ? d : p.D - 1;
   const int N = p.N;
@@ -123,8 +152,10 @@ __global__ __launch_bounds__(kWave * kCWaves) void fwd_complex_kernel(CParams p)
   const float Dd = p.Dskip ? p.Dskip[dc] : 0.0f;
   const float bias2 = (p.bias ? p.bias[dc] : 0.0f) * kLog2e;
 
-  // B and C rows of a block: [buffer][step][B | C][state] as (re, im)
+  // B and C rows of a block: [buffer][step][B | C][state] as (re, im); the
+  // owned steps' (dt log2 e, u): [buffer][step][channel]
   __shared__ __align__(16) float2 rows[2][kCBlk][2][kMaxC];
+  __shared__ __align__(16) float2 act[2][kCBlk][kChPerGroup];
   // staging thread: step sk, matrix sw (0 = B, 1 = C), state sn
   const int sk = tid / (2 * kMaxC), sw = (tid / kMaxC) % 2, sn = tid % kMaxC;
   const In* rbase = static_cast<const In*>(sw ? p.Cm : p.Bm);
@@ -134,44 +165,46 @@ __global__ __launch_bounds__(kWave * kCWaves) void fwd_complex_kernel(CParams p)
   Out* yb = static_cast<Out*>(p.y) + b * L * D + dc;
 
   typename Pair<In>::raw rw[2];
-  In ur[2][kCBlk], dr[2][kCBlk], zr[2][kCBlk];
+  In ur[2], dr[2], zr[2];        // the owned step's inputs, by block parity
+  float u_own[2], g_own[2];      // its u and gate
   // fetch block t0 into register set S (steps past the end read step L - 1;
-  // their step size is forced to 0 below)
+  // their step size and input are forced to 0 below)
   auto fetch = [&](auto S_, int64_t t0) {
     constexpr int S = decltype(S_)::value;
-#pragma unroll
-    for (int k = 0; k < kCBlk; ++k) {
-      const int64_t t = t0 + k < L ? t0 + k : L - 1;
-      ur[S][k] = ub[t * D];
-      dr[S][k] = db[t * D];
-      if (HAS_Z) zr[S][k] = zb[t * D];
-    }
+    const int64_t t = t0 + q < L ? t0 + q : L - 1;
+    ur[S] = ub[t * D];
+    dr[S] = db[t * D];
+    if (HAS_Z) zr[S] = zb[t * D];
     const int64_t tr = t0 + sk < L ? t0 + sk : L - 1;
     rw[S] = Pair<In>::load(rbase + ((b * L + tr) * N + (sn < N ? sn : 0)) * 2);
   };
+  // the block's rows and this lane's owned-step values into buffer S
   auto stage = [&](auto S_, int64_t t0) {
     constexpr int S = decltype(S_)::value;
     float2 v = Pair<In>::f32(rw[S]);
     if (sn >= N || t0 + sk >= L) v = make_float2(0.0f, 0.0f);
     rows[S][sk][sw][sn] = v;
+    const bool valid = t0 + q < L;
+    const float x2 = __builtin_fmaf(to_f32(dr[S]), kLog2e, bias2);
+    const float dl = valid ? (SOFTPLUS ? softplus_log2(x2) : x2) : 0.0f;   // dt log2 e
+    u_own[S] = valid ? to_f32(ur[S]) : 0.0f;
+    g_own[S] = HAS_Z ? silu(to_f32(zr[S])) : 1.0f;
+    act[S][q][chan] = make_float2(dl, u_own[S]);
   };
 
   auto block = [&](auto S_, int64_t t0) {
     constexpr int S = decltype(S_)::value;
     if (t0 + kCBlk < L) fetch(std::integral_constant<int, S ^ 1>{}, t0 + kCBlk);
+    float part[kCBlk];                                     // Re sum_n C h, per step
 #pragma unroll
     for (int k = 0; k < kCBlk; ++k) {
-      const bool valid = t0 + k < L;
-      float x2 = __builtin_fmaf(to_f32(dr[S][k]), kLog2e, bias2);
-      float dl = SOFTPLUS ? softplus_log2(x2) : x2;        // dt log2 e
-      if (!valid) dl = 0.0f;                               // abar = 1, no input
+      const float2 du = act[S][k][chan];
+      const float dl = du.x, uk = du.y;
       const float dt = dl * kLn2;
-      const float uk = valid ? to_f32(ur[S][k]) : 0.0f;
-      const float4* bq = reinterpret_cast<const float4*>(&rows[S][k][0][kSPL * q]);
-      const float4* cq = reinterpret_cast<const float4*>(&rows[S][k][1][kSPL * q]);
-      const float4 b01 = bq[0], b23 = bq[1], c01 = cq[0], c23 = cq[1];
-      const float Br[kSPL] = {b01.x, b01.z, b23.x, b23.z}, Bi[kSPL] = {b01.y, b01.w, b23.y, b23.w};
-      const float Cr[kSPL] = {c01.x, c01.z, c23.x, c23.z}, Ci[kSPL] = {c01.y, c01.w, c23.y, c23.w};
+      const float4 bq = *reinterpret_cast<const float4*>(&rows[S][k][0][kSPL * q]);
+      const float4 cq = *reinterpret_cast<const float4*>(&rows[S][k][1][kSPL * q]);
+      const float Br[kSPL] = {bq.x, bq.z}, Bi[kSPL] = {bq.y, bq.w};
+      const float Cr[kSPL] = {cq.x, cq.z}, Ci[kSPL] = {cq.y, cq.w};
       float acc = 0.0f;
 #pragma unroll
       for (int j = 0; j < kSPL; ++j) {
@@ -193,14 +226,16 @@ __global__ __launch_bounds__(kWave * kCWaves) void fwd_complex_kernel(CParams p)
         hi[j] = ni;
         acc = __builtin_fmaf(Cr[j], nr, __builtin_fmaf(-Ci[j], ni, acc));
       }
-      acc += quad_dpp<0xb1>(acc);   // quad_perm [1, 0, 3, 2]
-      acc += quad_dpp<0x4e>(acc);   // quad_perm [2, 3, 0, 1]
-      float yv = __builtin_fmaf(2.0f, acc, Dd * uk);
-      if (HAS_Z) yv *= silu(to_f32(zr[S][k]));
-      if (valid && active && q == 0) store_out<Out>(yb + (t0 + k) * D, yv);
+      part[k] = acc;
     }
-    // rows of the next block into the other buffer (last read by the previous
-    // block, which every wave finished before the barrier that ended it)
+    // y of the owned step: the channel's sum for step q, skip, gate
+    const float sum = reduce_scatter8(part, q);
+    float yv = __builtin_fmaf(2.0f, sum, Dd * u_own[S]);
+    if (HAS_Z) yv *= g_own[S];
+    if (t0 + q < L && active) store_out<Out>(yb + (t0 + q) * D, yv);
+    // the next block's rows and owned-step values into the other buffers (last
+    // read by the previous block, which every wave finished before the
+    // barrier that ended it)
     if (t0 + kCBlk < L) stage(std::integral_constant<int, S ^ 1>{}, t0 + kCBlk);
     __syncthreads();
   };
