@@ -110,6 +110,52 @@ def time_calls(fn, steps, warmup, torch):
     return total_ms, sum(per) / len(per), min(per), wall
 
 
+def time_flushed(fn, torch, runs=20, flush_bytes=512 << 20):
+    """Per-call times with the caches flushed: each run writes flush_bytes of scratch
+    memory, then times one call (events around the call only), then times a second
+    call right after it with nothing in between, as a control taken under the same
+    stop-and-go clock conditions.  Returns (flushed median, flushed min, control
+    median) in ms."""
+    scratch = torch.empty(flush_bytes // 4, dtype=torch.float32, device="cuda")
+
+    def one():
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1)
+
+    cold, ctrl = [], []
+    for i in range(runs):
+        scratch.fill_(float(i))
+        cold.append(one())
+        ctrl.append(one())
+    del scratch
+    cold.sort()
+    ctrl.sort()
+    return cold[len(cold) // 2], cold[0], ctrl[len(ctrl) // 2]
+
+
+def stream_gbs(torch, nbytes=1 << 30, reps=10):
+    """Device-to-device copy bandwidth (bytes read + written per second): the
+    achievable streaming rate of this GPU, a second reference beside the 8 TB/s peak."""
+    a = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del a, b
+    return 2 * nbytes / (ms * 1e-3) / 1e9
+
+
 def cpu_baseline(inp, w, budget_s=20.0):
     """The fp64 oracle on the same workload: whole batch rows, as many as fit in
     about budget_s seconds (all of them when the estimate allows)."""
@@ -248,6 +294,14 @@ def main():
                       "in_dtype": w.dtype, "out_dtype": "f32", "disc": w.disc,
                       "plan_workspace_bytes": nb},
            "roofline": roof}
+    # the same call with the caches flushed before each run, and the copy bandwidth
+    cold_med, cold_min, ctrl_med = time_flushed(step, torch)
+    sgbs = stream_gbs(torch)
+    roof["cold"] = {"median_ms": round(cold_med, 4), "min_ms": round(cold_min, 4),
+                    "control_median_ms": round(ctrl_med, 4), "flush_bytes": 512 << 20,
+                    "runs": 20}
+    roof["hbm"]["stream_gbs"] = round(sgbs, 1)
+    roof["hbm"]["frac_of_stream"] = round(hbm_gbs / sgbs, 4)
     del d, y, ws
     torch.cuda.empty_cache()
 
