@@ -187,9 +187,32 @@ def cpu_baseline(inp, w, budget_s=20.0):
         rows = int(max(1, min(w.B, budget_s / max(dt1, 1e-3))))
         dt = run(rows) if rows > 1 else dt1
         elems, what = rows * w.L * w.D * w.N, "batch rows 0..%d of %d (all channels)" % (rows - 1, w.B)
-    return {"value": elems / dt, "unit": "elements/s", "cores": threads, "kind": "oracle",
-            "sample": "%s, full L=%d, N=%d, %s: %.2f s of fp64 C (OpenMP over channels)" % (
-                what, w.L, w.N, w.disc, dt)}
+    res = {"value": elems / dt, "unit": "elements/s", "cores": threads, "kind": "oracle",
+           "sample": "%s, full L=%d, N=%d, %s: %.2f s of fp64 C (OpenMP over channels)" % (
+               what, w.L, w.N, w.disc, dt)}
+    # the same code on one thread, over a smaller sample (1024 channels of batch row 0)
+    nch = min(w.D, 1024)
+    sl = (slice(0, 1), slice(None), slice(0, nch))
+    t0 = time.perf_counter()
+    oracle.fwd(inp.u[sl], inp.delta[sl], inp.A[:nch], inp.B[:1], inp.C[:1], D=inp.D[:nch],
+               delta_bias=inp.delta_bias[:nch], z=None if inp.z is None else inp.z[sl],
+               disc=w.disc, nthreads=1)
+    dt1 = time.perf_counter() - t0
+    res["single_thread"] = {"value": w.L * nch * w.N / dt1, "unit": "elements/s",
+                            "sample": "batch row 0, channels 0..%d, full L=%d: %.2f s" % (
+                                nch - 1, w.L, dt1)}
+    res["cpu_model"] = cpu_model()
+    return res
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def copy_calibration(torch, nbytes=1 << 30, reps=3):
