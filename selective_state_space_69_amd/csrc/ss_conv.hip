@@ -30,6 +30,29 @@ __device__ __forceinline__ void load_vec(const T* p, float (&v)[VEC]) {
     v[0] = to_f32(*p);
   }
 }
+// raw (undecoded) VEC channels of one row, and their decoding
+template <typename T, int VEC>
+struct RawV {
+  using type = typename Raw4<T>::type;
+};
+template <typename T>
+struct RawV<T, 1> {
+  using type = T;
+};
+template <typename T, int VEC>
+__device__ __forceinline__ typename RawV<T, VEC>::type load_raw_vec(const T* p) {
+  if constexpr (VEC == 4) return *reinterpret_cast<const typename Raw4<T>::type*>(p);
+  else return *p;
+}
+template <typename T, int VEC>
+__device__ __forceinline__ void unpack_raw_vec(typename RawV<T, VEC>::type r, float (&v)[VEC]) {
+  if constexpr (VEC == 4) {
+    const float4 f = unpack4(r);
+    v[0] = f.x; v[1] = f.y; v[2] = f.z; v[3] = f.w;
+  } else {
+    v[0] = to_f32(r);
+  }
+}
 __device__ __forceinline__ void load_f32(const float* p, float (&v)[4]) {
   const float4 f = *reinterpret_cast<const float4*>(p);
   v[0] = f.x; v[1] = f.y; v[2] = f.z; v[3] = f.w;
@@ -111,23 +134,43 @@ __global__ __launch_bounds__(kThreads) void conv_fwd_kernel(ConvParams p) {
 #pragma unroll
       for (int j = 0; j < VEC; ++j) win[k][j] = 0.0f;
   }
-  // unrolled so that several rows' loads are in flight at once
-#pragma unroll 8
-  for (int64_t t = t0; t < t1; ++t) {
-    load_vec<In, VEC>(x + t * p.D, win[K - 1]);
-    float o[VEC];
+  // the segment in blocks of kPf steps; the raw rows of the next block are
+  // fetched while the current one is computed, so loads stay in flight
+  constexpr int kPf = 8;
+  using R = typename RawV<In, VEC>::type;
+  R buf[2][kPf];
+  auto fetch = [&](R (&dst)[kPf], int64_t tb) {
 #pragma unroll
-    for (int j = 0; j < VEC; ++j) {
-      float s = bias[j];
-#pragma unroll
-      for (int k = 0; k < K; ++k) s = __builtin_fmaf(w[k][j], win[k][j], s);
-      o[j] = SILU ? s * sigmoid(s) : s;
+    for (int i = 0; i < kPf; ++i) {
+      const int64_t t = tb + i < t1 ? tb + i : t1 - 1;
+      dst[i] = load_raw_vec<In, VEC>(x + t * p.D);
     }
-    store_vec<Out, VEC>(u + t * p.D, o);
+  };
+  fetch(buf[0], t0);
 #pragma unroll
-    for (int k = 0; k < K - 1; ++k)
+  for (int blk = 0; blk < kSeg / kPf; ++blk) {
+    const int64_t tb = t0 + int64_t(blk) * kPf;
+    if (tb >= t1) break;                            // uniform: the segment's end
+    if (blk + 1 < kSeg / kPf && tb + kPf < t1) fetch(buf[(blk + 1) & 1], tb + kPf);
 #pragma unroll
-      for (int j = 0; j < VEC; ++j) win[k][j] = win[k + 1][j];
+    for (int i = 0; i < kPf; ++i) {
+      const int64_t t = tb + i;
+      if (t >= t1) break;
+      unpack_raw_vec<In, VEC>(buf[blk & 1][i], win[K - 1]);
+      float o[VEC];
+#pragma unroll
+      for (int j = 0; j < VEC; ++j) {
+        float s = bias[j];
+#pragma unroll
+        for (int k = 0; k < K; ++k) s = __builtin_fmaf(w[k][j], win[k][j], s);
+        o[j] = SILU ? s * sigmoid(s) : s;
+      }
+      store_vec<Out, VEC>(u + t * p.D, o);
+#pragma unroll
+      for (int k = 0; k < K - 1; ++k)
+#pragma unroll
+        for (int j = 0; j < VEC; ++j) win[k][j] = win[k + 1][j];
+    }
   }
 }
 
