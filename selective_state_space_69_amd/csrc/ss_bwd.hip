@@ -47,9 +47,13 @@ struct BwdParams {
   const float* Dskip;
   const float* bias;
   const float* h0;
-  float* hstart;         // (B, nc, N, D): start state of chunk c (c >= 1)
+  // (B, nc, N, D): chunk c's zero-start end state from the summary pass (c <= nc - 2),
+  // then, after the forward carry walk, the start state of chunk c (c >= 1)
+  float* hstart;
   float* dsum;           // (B, nc, D): sum of dt * log2 e over chunk c (c <= nc - 2)
-  float* lam;            // (B, nc, N, D): adjoint carry entering chunk c from its end
+  // (B, nc, N, D): chunk c's local adjoint from the summary pass (c >= 1), then,
+  // after the reverse carry walk, the adjoint entering chunk c from its end
+  float* lam;
   float* du;
   float* ddelta;
   float* dz;
@@ -62,11 +66,6 @@ struct BwdParams {
   int64_t L, D;
   int32_t N, ndblk, nchunks;
 };
-
-template <typename In>
-__device__ __forceinline__ float ld(const void* base, int64_t i) {
-  return to_f32(static_cast<const In*>(base)[i]);
-}
 
 // (delta + bias) log2 e -> dt log2 e
 template <bool SOFTPLUS>
