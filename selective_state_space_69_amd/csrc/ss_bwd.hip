@@ -221,14 +221,13 @@ __device__ __forceinline__ void bwd_chunk(const BwdParams& p, float* lds, int64_
   const int64_t row0 = b * p.L;
   const int64_t ibase = row0 * D + dc;          // element (b, t = 0, d)
 
-  float A[kNS], iA[kNS], zm[kNS];
+  float A[kNS], iA[kNS];
 #pragma unroll
   for (int j = 0; j < kNS; ++j) {
     const int n = n0 + j;
     const float a = n < N ? p.A[dc * N + n] : -1.0f;
     A[j] = a;
     iA[j] = a == 0.0f ? 0.0f : 1.0f / a;
-    zm[j] = a == 0.0f ? 1.0f : 0.0f;
   }
   const float Dd = p.Dskip ? p.Dskip[dc] : 0.0f;
   const float bias2 = (p.bias ? p.bias[dc] : 0.0f) * kLog2e;
@@ -286,8 +285,8 @@ __device__ __forceinline__ void bwd_chunk(const BwdParams& p, float* lds, int64_
         if (DISC == kEuler) {
           bu = dtu * Bv[j];
         } else {
-          float coef = __builtin_fmaf(a, iA[j], -iA[j]);
-          if (SAFE) coef = __builtin_fmaf(dl * kLn2, zm[j], coef);
+          const float coef = SAFE ? zoh_coef_guarded(a, iA[j], dl * kLn2, dl * A[j])
+                                  : __builtin_fmaf(a, iA[j], -iA[j]);
           bu = coef * (Bv[j] * uf);
         }
         h[j] = __builtin_fmaf(a, h[j], bu);
@@ -340,7 +339,8 @@ __device__ __forceinline__ void bwd_chunk(const BwdParams& p, float* lds, int64_
       uf[k] = actU[kk * kWave + lane];
       const float4 B4 = row_of(kk, 0), C4 = row_of(kk, 1);
       const float Bv[kNS] = {B4.x, B4.y, B4.z, B4.w}, Cv[kNS] = {C4.x, C4.y, C4.z, C4.w};
-      const float dtu = dl[k] * kLn2 * uf[k];
+      const float dtu0 = dl[k] * kLn2;            // dt
+      const float dtu = dtu0 * uf[k];
       float y0 = 0.0f;
 #pragma unroll
       for (int j = 0; j < kNS; ++j) {
@@ -349,8 +349,8 @@ __device__ __forceinline__ void bwd_chunk(const BwdParams& p, float* lds, int64_
         if (DISC == kEuler) {
           bu = dtu * Bv[j];
         } else {
-          float coef = __builtin_fmaf(a, iA[j], -iA[j]);
-          if (SAFE) coef = __builtin_fmaf(dl[k] * kLn2, zm[j], coef);
+          const float coef = SAFE ? zoh_coef_guarded(a, iA[j], dtu0, dl[k] * A[j])
+                                  : __builtin_fmaf(a, iA[j], -iA[j]);
           bu = coef * (Bv[j] * uf[k]);
         }
         h[j] = __builtin_fmaf(a, h[j], bu);
@@ -370,7 +370,8 @@ __device__ __forceinline__ void bwd_chunk(const BwdParams& p, float* lds, int64_
     //   du = sum_n lam coef B
     //   d(dt) = sum_n nu h_{t-1} A + u sum_n (lam B [Euler] | nu B [ZOH])
     //   dA += nu h_{t-1} dt  (+ lam B u d coef / dA for ZOH, with
-    //         d coef / dA = (dt A_bar - coef) / A; the 1 / A is applied once per chunk)
+    //         d coef / dA = (dt A_bar - coef) / A; the 1 / A is applied once per
+    //         chunk; the guarded path takes its series where |dt A| < kZohSeries)
     float dup[kKB], ddp[kKB];
 #pragma unroll
     for (int k = kKB - 1; k >= 0; --k) {
@@ -393,16 +394,24 @@ __device__ __forceinline__ void bwd_chunk(const BwdParams& p, float* lds, int64_
           red[k * kNS + j] = lam * udt;                   // dB
           sLB = __builtin_fmaf(lam, Bv[j], sLB);
         } else {
-          float coef = __builtin_fmaf(a, iA[j], -iA[j]);
-          if (SAFE) coef = __builtin_fmaf(dtn, zm[j], coef);
+          const float x2 = dl[k] * A[j];         // dt A log2 e
+          const float coef = SAFE ? zoh_coef_guarded(a, iA[j], dtn, x2)
+                                  : __builtin_fmaf(a, iA[j], -iA[j]);
           const float cl = lam * coef;
           const float db = cl * uf[k];
           red[k * kNS + j] = db;                          // dB
           sdu = __builtin_fmaf(cl, Bv[j], sdu);
           sLB = __builtin_fmaf(nu[j], Bv[j], sLB);
-          dAc[j] = __builtin_fmaf(Bv[j], __builtin_fmaf(udt, nu[j], -db), dAc[j]);
-          // A == 0: coef = dt and d coef / dA = dt^2 / 2
-          if (SAFE) dA[j] = __builtin_fmaf(lam * zm[j], Bv[j] * (0.5f * udt * dtn), dA[j]);
+          const float dac = Bv[j] * __builtin_fmaf(udt, nu[j], -db);
+          if (SAFE) {
+            // near dt A = 0 the quotient form cancels: the series of d coef / dA
+            const bool ser = __builtin_unpredictable(__builtin_fabsf(x2) < kZohSeries * kLog2e);
+            dA[j] = __builtin_fmaf(ser ? lam * Bv[j] * uf[k] : 0.0f,
+                                   zoh_dcoef_series(dtn, x2 * kLn2), dA[j]);
+            dAc[j] += ser ? 0.0f : dac;
+          } else {
+            dAc[j] += dac;
+          }
         }
       }
       dup[k] = DISC == kEuler ? dtn * sLB : sdu;
@@ -493,14 +502,15 @@ __global__ __launch_bounds__(kWave * kNW, DISC == kEuler ? 3 : 2) void bwd_kerne
   bid /= p.ndblk;
   const int chunk = int(bid % p.nchunks);
   const int64_t b = bid / p.nchunks;
-  // exact ZOH with some A == 0 in the block takes the guarded path (all waves agree)
-  bool zero = false;
+  // exact ZOH with a slowly decaying state (|A| < kWeakA, A == 0 included) in
+  // the block takes the guarded path (all waves agree)
+  bool weak = false;
   if (DISC == kZoh) {
     const int64_t d = int64_t(dblk) * kWave + lane;
     const int64_t dc = d < p.D ? d : p.D - 1;
-    for (int n = 0; n < p.N; ++n) zero |= p.A[dc * p.N + n] == 0.0f;
+    for (int n = 0; n < p.N; ++n) weak |= __builtin_fabsf(p.A[dc * p.N + n]) < kWeakA;
   }
-  if (DISC == kZoh && __syncthreads_or(zero))
+  if (DISC == kZoh && __syncthreads_or(weak))
     bwd_chunk<In, DISC, HAS_Z, SOFTPLUS, true>(p, lds, b, dblk, chunk, wave, lane);
   else
     bwd_chunk<In, DISC, HAS_Z, SOFTPLUS, false>(p, lds, b, dblk, chunk, wave, lane);
@@ -530,14 +540,13 @@ __device__ __forceinline__ void summary_chunk(const BwdParams& p, float* lds, in
   const float bias2 = (p.bias ? p.bias[dc] : 0.0f) * kLog2e;
   stage_chunk<In, HAS_Z, SOFTPLUS>(p, lds, row0 * D + dc, row0, t0, t1, wave, lane, bias2,
                                    active ? 1.0f : 0.0f);
-  float A[kNS], iA[kNS], zm[kNS];
+  float A[kNS], iA[kNS];
 #pragma unroll
   for (int j = 0; j < kNS; ++j) {
     const int n = n0 + j;
     const float a = n < N ? p.A[dc * N + n] : -1.0f;
     A[j] = a;
     iA[j] = a == 0.0f ? 0.0f : 1.0f / a;
-    zm[j] = a == 0.0f ? 1.0f : 0.0f;
   }
   __syncthreads();
   const float* actDl = lds;
@@ -568,8 +577,8 @@ __device__ __forceinline__ void summary_chunk(const BwdParams& p, float* lds, in
       if (DISC == kEuler) {
         bu = dtu * Bv[j];
       } else {
-        float coef = __builtin_fmaf(a, iA[j], -iA[j]);
-        if (SAFE) coef = __builtin_fmaf(dl * kLn2, zm[j], coef);
+        const float coef = SAFE ? zoh_coef_guarded(a, iA[j], dl * kLn2, dl * A[j])
+                                : __builtin_fmaf(a, iA[j], -iA[j]);
         bu = coef * (Bv[j] * uf);
       }
       h[j] = __builtin_fmaf(a, h[j], bu);
@@ -605,13 +614,13 @@ __global__ __launch_bounds__(kWave * kNW, 5) void summary_kernel(BwdParams p) {
   bid /= p.ndblk;
   const int chunk = int(bid % p.nchunks);
   const int64_t b = bid / p.nchunks;
-  bool zero = false;
+  bool weak = false;   // as in bwd_kernel
   if (DISC == kZoh) {
     const int64_t d = int64_t(dblk) * kWave + lane;
     const int64_t dc = d < p.D ? d : p.D - 1;
-    for (int n = 0; n < p.N; ++n) zero |= p.A[dc * p.N + n] == 0.0f;
+    for (int n = 0; n < p.N; ++n) weak |= __builtin_fabsf(p.A[dc * p.N + n]) < kWeakA;
   }
-  if (DISC == kZoh && __syncthreads_or(zero))
+  if (DISC == kZoh && __syncthreads_or(weak))
     summary_chunk<In, DISC, HAS_Z, SOFTPLUS, true>(p, lds, b, dblk, chunk, wave, lane);
   else
     summary_chunk<In, DISC, HAS_Z, SOFTPLUS, false>(p, lds, b, dblk, chunk, wave, lane);

@@ -5,7 +5,7 @@
 // compare complex with real decay ("Mamba: S4 epic upgrade", ablation on A).
 // Per channel (b, d) and complex state n, with the real scan's step size:
 //     abar  = exp(dt a)                          a = A[d, n] complex
-//     bcoef = (abar - 1) / a   (exact ZOH; dt when a == 0 or in Euler mode)
+//     bcoef = (abar - 1) / a   (exact ZOH, a series near dt a = 0; dt in Euler mode)
 //     h_n   = abar h_n + bcoef B_n u             B_n, C_n complex (per b, t)
 //     y     = 2 Re(sum_n C_n h_n) + D u          each state stands for itself and
 //                                                its conjugate
@@ -110,7 +110,8 @@ struct Pair<uint16_t> {
 };
 
 template <typename In, typename Out, int DISC, bool HAS_Z, bool SOFTPLUS>
-__global__ __launch_bounds__(kWave * kCWaves) void fwd_complex_kernel(CParams p) {
+// five waves per SIMD (five workgroups per CU at the 2.8B width): at most 96 VGPRs
+__global__ __launch_bounds__(kWave * kCWaves, 5) void fwd_complex_kernel(CParams p) {
   const int tid = int(threadIdx.x);
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int lane = tid % kWave;
@@ -125,9 +126,9 @@ __global__ __launch_bounds__(kWave * kCWaves) void fwd_complex_kernel(CParams p)
   const int64_t L = p.L, D = p.D;
 
   // per-state constants: modulus rate, phase rate (revolutions per dt log2 e),
-  // 1 / a, and a == 0 (where the ZOH coefficient is dt)
-  float ar[kSPL], aw[kSPL], iar[kSPL], iai[kSPL], hr[kSPL], hi[kSPL];
-  bool zm[kSPL];
+  // a itself and 1 / a (0 when a == 0)
+  float ar[kSPL], aw[kSPL], ai[kSPL], iar[kSPL], iai[kSPL], hr[kSPL], hi[kSPL];
+  bool weak = false;
 #pragma unroll
   for (int j = 0; j < kSPL; ++j) {
     const int n = kSPL * q + j;
@@ -137,11 +138,12 @@ __global__ __launch_bounds__(kWave * kCWaves) void fwd_complex_kernel(CParams p)
       im = p.A[(dc * N + n) * 2 + 1];
     }
     ar[j] = re;
+    ai[j] = im;
     aw[j] = im * (kLn2 * kInv2Pi);
     const float m2 = re * re + im * im;
-    zm[j] = m2 == 0.0f;
-    iar[j] = zm[j] ? 0.0f : re / m2;
-    iai[j] = zm[j] ? 0.0f : -im / m2;
+    weak |= m2 < kWeakA * kWeakA;
+    iar[j] = m2 == 0.0f ? 0.0f : re / m2;
+    iai[j] = m2 == 0.0f ? 0.0f : -im / m2;
     hr[j] = 0.0f;
     hi[j] = 0.0f;
     if (p.h0 && n < N) {
@@ -149,6 +151,8 @@ __global__ __launch_bounds__(kWave * kCWaves) void fwd_complex_kernel(CParams p)
       hi[j] = p.h0[((b * D + dc) * N + n) * 2 + 1];
     }
   }
+  // exact ZOH: the guarded coefficient where some state of the wave has |a| < kWeakA
+  const bool guard = __any(weak);
   const float Dd = p.Dskip ? p.Dskip[dc] : 0.0f;
   const float bias2 = (p.bias ? p.bias[dc] : 0.0f) * kLog2e;
 
@@ -192,8 +196,11 @@ __global__ __launch_bounds__(kWave * kCWaves) void fwd_complex_kernel(CParams p)
     act[S][q][chan] = make_float2(dl, u_own[S]);
   };
 
-  auto block = [&](auto S_, int64_t t0) {
+  // G: the wave holds a slowly decaying state (guarded coefficient); a
+  // template parameter so that the fast loop has no branch inside
+  auto block = [&](auto S_, auto G_, int64_t t0) {
     constexpr int S = decltype(S_)::value;
+    constexpr bool G = decltype(G_)::value;
     if (t0 + kCBlk < L) fetch(std::integral_constant<int, S ^ 1>{}, t0 + kCBlk);
     float part[kCBlk];                                     // Re sum_n C h, per step
 #pragma unroll
@@ -212,11 +219,26 @@ __global__ __launch_bounds__(kWave * kCWaves) void fwd_complex_kernel(CParams p)
         const float ph = __builtin_amdgcn_fractf(dl * aw[j]);         // arg abar / 2 pi
         const float abr = e * __builtin_amdgcn_cosf(ph);
         const float abi = e * __builtin_amdgcn_sinf(ph);
-        float cr = dt, ci = 0.0f;                                     // Euler / a == 0
-        if (DISC == SS_ZOH && !zm[j]) {
+        float cr = dt, ci = 0.0f;                                     // Euler
+        if (DISC == SS_ZOH) {
           const float mr = abr - 1.0f;                                // (abar - 1) / a
           cr = mr * iar[j] - abi * iai[j];
           ci = __builtin_fmaf(mr, iai[j], abi * iar[j]);
+          if (G) {
+            // a slowly decaying state in the wave: near x = dt a = 0 the
+            // quotient cancels, so take dt (1 + x/2 + x^2/6 + x^3/24) there
+            const float xr = dt * ar[j], xi = dt * ai[j];
+            float pr = __builtin_fmaf(xr, 1.0f / 24.0f, 1.0f / 6.0f), pi = xi * (1.0f / 24.0f);
+            float tr = __builtin_fmaf(pr, xr, __builtin_fmaf(-pi, xi, 0.5f));
+            pi = __builtin_fmaf(pr, xi, pi * xr);
+            pr = tr;
+            tr = __builtin_fmaf(pr, xr, __builtin_fmaf(-pi, xi, 1.0f));
+            pi = __builtin_fmaf(pr, xi, pi * xr);
+            const bool ser =
+                __builtin_unpredictable(__builtin_fmaf(xr, xr, xi * xi) < kZohSeries * kZohSeries);
+            cr = ser ? dt * tr : cr;
+            ci = ser ? dt * pi : ci;
+          }
         }
         const float bur = Br[j] * uk, bui = Bi[j] * uk;
         const float qr = cr * bur - ci * bui, qi = __builtin_fmaf(cr, bui, ci * bur);
@@ -243,10 +265,14 @@ __global__ __launch_bounds__(kWave * kCWaves) void fwd_complex_kernel(CParams p)
   fetch(std::integral_constant<int, 0>{}, 0);
   stage(std::integral_constant<int, 0>{}, 0);
   __syncthreads();
-  for (int64_t t0 = 0; t0 < L; t0 += 2 * kCBlk) {
-    block(std::integral_constant<int, 0>{}, t0);
-    if (t0 + kCBlk < L) block(std::integral_constant<int, 1>{}, t0 + kCBlk);
-  }
+  auto walk = [&](auto G_) {
+    for (int64_t t0 = 0; t0 < L; t0 += 2 * kCBlk) {
+      block(std::integral_constant<int, 0>{}, G_, t0);
+      if (t0 + kCBlk < L) block(std::integral_constant<int, 1>{}, G_, t0 + kCBlk);
+    }
+  };
+  if (DISC == SS_ZOH && guard) walk(std::true_type{});
+  else walk(std::false_type{});
   if (p.h_last && active) {
 #pragma unroll
     for (int j = 0; j < kSPL; ++j) {

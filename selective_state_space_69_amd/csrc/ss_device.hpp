@@ -91,6 +91,32 @@ __device__ __forceinline__ float softplus_log2(float x2) {
   return __builtin_fmaxf(x2, 0.0f) + hw_log2(u1) * (e * hw_rcp(dm));
 }
 
+// Exact-ZOH input coefficient coef = (exp(x) - 1) / A with x = dt A ("Mamba: S4
+// epic upgrade", S4 intro: zero-order hold).  Formed as (Abar - 1) / A from the
+// rounded Abar it carries an absolute error of about 2^-24 / |A|, harmless for
+// |A| >= kWeakA but not below: states that decay that slowly take the guarded
+// path, where |x| < kZohSeries uses the series dt (1 + x/2 + x^2/6 + x^3/24)
+// (truncation < x^4 / 120 relative) and larger |x| the quotient (relative error
+// about 2^-24 / |x| < 1.2e-6).  A == 0 falls in the series (coef = dt).  The
+// series is evaluated in x2 = x log2 e, the exponential's own argument.
+constexpr float kWeakA = 0.25f;
+constexpr float kZohSeries = 0.05f;
+// x2 = x log2 e (the argument the exponential already takes), dt = x2 ln2 / A
+__device__ __forceinline__ float zoh_coef_guarded(float abar, float iA, float dt, float x2) {
+  constexpr float l1 = kLn2 / 2.0f, l2 = kLn2 * kLn2 / 6.0f, l3 = kLn2 * kLn2 * kLn2 / 24.0f;
+  const float ser = dt * __builtin_fmaf(x2, __builtin_fmaf(x2, __builtin_fmaf(x2, l3, l2), l1), 1.0f);
+  const float quot = __builtin_fmaf(abar, iA, -iA);
+  // a select, not a branch: the choice varies from lane to lane and step to step
+  return __builtin_unpredictable(__builtin_fabsf(x2) < kZohSeries * kLog2e) ? ser : quot;
+}
+// d coef / dA for |x| < kZohSeries: dt^2 (1/2 + x/3 + x^2/8 + x^3/30), the series
+// of (x e^x - e^x + 1) / x^2 (truncation < x^4 / 144)
+__device__ __forceinline__ float zoh_dcoef_series(float dt, float x) {
+  return dt * dt *
+         __builtin_fmaf(x, __builtin_fmaf(x, __builtin_fmaf(x, 1.0f / 30.0f, 0.125f), 1.0f / 3.0f),
+                        0.5f);
+}
+
 // silu(z) = z * sigmoid(z) = z / (1 + 2^(-z log2 e)); saturates cleanly at +-inf.
 __device__ __forceinline__ float silu(float z) {
   return z * hw_rcp(1.0f + hw_exp2(-z * kLog2e));

@@ -43,7 +43,7 @@ template <typename In, typename Out, int DISC, bool HAS_Z, bool SOFTPLUS, bool S
 struct HalfScan {
   using Raw2 = typename std::conditional<sizeof(In) == 2, uint32_t, uint2>::type;
   const FwdParams& p;
-  float A[2], iA[2], zm[2];
+  float A[2], iA[2];
   float h[2];
   float Dd, bias2;
   float dsum;
@@ -181,12 +181,15 @@ struct HalfScan {
         h[0] = __builtin_fmaf(a0, h[0], dtu * r.x);
         h[1] = __builtin_fmaf(a1, h[1], dtu * r.y);
       } else {
-        float q0 = __builtin_fmaf(a0, iA[0], -iA[0]);             // (A_bar - 1) / A
-        float q1 = __builtin_fmaf(a1, iA[1], -iA[1]);
+        float q0, q1;                                              // (A_bar - 1) / A
         if (SAFE) {
-          const float dt = d2 * kLn2;                              // dt where A == 0
-          q0 = __builtin_fmaf(dt, zm[0], q0);
-          q1 = __builtin_fmaf(dt, zm[1], q1);
+          // some |A| < kWeakA in the wave: the series near dt A = 0
+          const float dt = d2 * kLn2;
+          q0 = zoh_coef_guarded(a0, iA[0], dt, d2 * A[0]);
+          q1 = zoh_coef_guarded(a1, iA[1], dt, d2 * A[1]);
+        } else {
+          q0 = __builtin_fmaf(a0, iA[0], -iA[0]);
+          q1 = __builtin_fmaf(a1, iA[1], -iA[1]);
         }
         h[0] = __builtin_fmaf(a0, h[0], q0 * (r.x * uk));
         h[1] = __builtin_fmaf(a1, h[1], q1 * (r.y * uk));
@@ -263,11 +266,11 @@ __global__ __launch_bounds__(kWave * kWaves, 5) void fwd_hw_kernel(FwdParams p) 
   const int64_t base = b * p.L * p.D + (REV ? (p.L - 1) * p.D : 0) + int64_t(dblk) * kCh;
 
   float Av[2];
-  bool zero = false;
+  bool weak = false;
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     Av[j] = n0 + j < N ? p.A[dc * N + n0 + j] : -1.0f;   // unused states: inert
-    zero |= (Av[j] == 0.0f);
+    weak |= __builtin_fabsf(Av[j]) < kWeakA;
   }
   float hs[2];
 #pragma unroll
@@ -283,7 +286,6 @@ __global__ __launch_bounds__(kWave * kWaves, 5) void fwd_hw_kernel(FwdParams p) 
     for (int j = 0; j < 2; ++j) {
       sc.A[j] = Av[j];
       sc.iA[j] = Av[j] == 0.0f ? 0.0f : 1.0f / Av[j];
-      sc.zm[j] = Av[j] == 0.0f ? 1.0f : 0.0f;
       sc.h[j] = hs[j];
     }
     sc.Dd = p.Dskip ? p.Dskip[dc] : 0.0f;
@@ -320,9 +322,10 @@ __global__ __launch_bounds__(kWave * kWaves, 5) void fwd_hw_kernel(FwdParams p) 
     hs[0] = sc.h[0];
     hs[1] = sc.h[1];
   };
-  // exact ZOH needs the dt * B fallback only where some A entry is exactly 0
-  // (decided per wave; every wave still passes the same barriers)
-  if (DISC == kZoh && __any(zero)) {
+  // exact ZOH takes the guarded coefficient only where some state decays slowly
+  // (|A| < kWeakA, A == 0 included; decided per wave, every wave still passes
+  // the same barriers)
+  if (DISC == kZoh && __any(weak)) {
     HalfScan<In, Out, DISC, HAS_Z, SOFTPLUS, SUMMARY, true, REV> sc{p};
     go(sc);
   } else {

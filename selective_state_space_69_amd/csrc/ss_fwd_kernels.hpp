@@ -40,7 +40,6 @@ template <int NS>
 struct Chan {
   float A[NS];    // diagonal A[d, n]; unused states get -1 (inert: B = C = 0)
   float iA[NS];   // 1 / A (0 where A == 0)
-  float zm[NS];   // 1 where A == 0 (exact ZOH falls back to dt * B there)
 };
 
 // LDS per workgroup: B/C row staging, per wave 2 buffers x 8 steps x 2*NS floats
@@ -253,8 +252,9 @@ struct Scan {
 #pragma unroll
         for (int n = 0; n < NS; ++n) {
           const float a = hw_exp2(d2 * ch.A[n]);                  // A_bar = exp(dt A)
-          float coef = __builtin_fmaf(a, ch.iA[n], -ch.iA[n]);    // (A_bar - 1) / A
-          if (SAFE) coef = __builtin_fmaf(dt, ch.zm[n], coef);    // dt where A == 0
+          // (A_bar - 1) / A; the guarded form where some |A| < kWeakA
+          const float coef = SAFE ? zoh_coef_guarded(a, ch.iA[n], dt, d2 * ch.A[n])
+                                  : __builtin_fmaf(a, ch.iA[n], -ch.iA[n]);
           h[n] = __builtin_fmaf(a, h[n], coef * (Bv[n] * uk));
           if (!SUMMARY) {
             if (kTwo && (n & 1)) acc1 = __builtin_fmaf(Cv[n], h[n], acc1);
@@ -354,15 +354,14 @@ __global__ __launch_bounds__(kWave * NSPLIT, kMinWaves<NSPLIT>) void fwd_kernel(
   const int N = p.N;
 
   Chan<NS> ch;
-  bool zero = false;
+  bool weak = false;
 #pragma unroll
   for (int j = 0; j < NS; ++j) {
     const int n = n0 + j;
     const float a = n < N ? p.A[dc * N + n] : -1.0f;
     ch.A[j] = a;
     ch.iA[j] = a == 0.0f ? 0.0f : 1.0f / a;
-    ch.zm[j] = a == 0.0f ? 1.0f : 0.0f;
-    zero |= (a == 0.0f);
+    weak |= __builtin_fabsf(a) < kWeakA;
   }
 
   float h[NS];
@@ -408,9 +407,10 @@ __global__ __launch_bounds__(kWave * NSPLIT, kMinWaves<NSPLIT>) void fwd_kernel(
     return sc.dsum;
   };
   float dsum;
-  // exact ZOH needs the dt * B fallback only where some A entry is exactly 0
-  // (decided per wave; every wave still passes the same barriers)
-  if (DISC == kZoh && __any(zero)) {
+  // exact ZOH takes the guarded coefficient only where some state decays slowly
+  // (|A| < kWeakA, A == 0 included; decided per wave, every wave still passes
+  // the same barriers)
+  if (DISC == kZoh && __any(weak)) {
     Scan<In, Out, DISC, HAS_Z, SOFTPLUS, SUMMARY, true, NSPLIT, REV> sc{p, ch, h};
     dsum = setup(sc);
   } else {

@@ -74,8 +74,8 @@ __global__ __launch_bounds__(256) void step_kernel(StepParams p) {
     const float a = Av[j];
     const float abar = hw_exp2(dl * a);
     float coef;
-    if (p.disc == SS_EULER || a == 0.0f) coef = dt;
-    else coef = __builtin_fmaf(abar, 1.0f / a, -1.0f / a);
+    if (p.disc == SS_EULER) coef = dt;
+    else coef = zoh_coef_guarded(abar, a == 0.0f ? 0.0f : 1.0f / a, dt, dl * a);
     hv[j] = __builtin_fmaf(abar, hv[j], coef * (Bv[j] * uf));
     acc = __builtin_fmaf(Cv[j], hv[j], acc);
   }

@@ -102,6 +102,8 @@ def make_A(D: int, N: int, mode: str = "s4d_real", rng: np.random.Generator | No
     s4d_real : A[d, n] = -(n + 1)
     random   : A = -exp(N(0, 1))      (no integer structure)
     mixed    : random, with a few exact zeros and small positive entries
+    weak     : random, with about half the entries slowly decaying (|A| log-uniform
+               in [1e-4, 1e-2]), an exact zero and a tiny positive entry
     """
     if mode == "s4d_real":
         return np.tile(-np.arange(1, N + 1, dtype=np.float32), (D, 1))
@@ -113,6 +115,14 @@ def make_A(D: int, N: int, mode: str = "s4d_real", rng: np.random.Generator | No
             A[1, N - 1] = 0.0
         if D > 2:
             A[2, 0] = np.float32(0.05)   # mildly unstable entry, still finite over short L
+    elif mode == "weak":
+        slow = rng.random((D, N)) < 0.5
+        A = np.where(slow, -(10.0 ** rng.uniform(-4.0, -2.0, (D, N))), A).astype(np.float32)
+        A[0, 0] = 0.0
+        if D > 1:
+            A[1, N - 1] = np.float32(1e-3)
+    elif mode != "random":
+        raise ValueError(mode)
     return A
 
 
@@ -213,7 +223,9 @@ def make_A_complex(D: int, N: int, mode: str = "s4d_lin", rng: np.random.Generat
     """Complex diagonal A as (D, N, 2) float32 (re, im) pairs.
     s4d_lin : A[d, n] = -1/2 + i pi n   (the S4D-Lin initialisation)
     random  : re = -exp(N(0, 1)), im = pi * N(0, 2)
-    mixed   : random, with an exact zero and a purely imaginary entry"""
+    mixed   : random, with an exact zero and a purely imaginary entry
+    weak    : random, with about half the entries of modulus log-uniform in
+              [1e-4, 1e-2] (random phase) and an exact zero"""
     if mode == "s4d_lin":
         re = np.full((D, N), -0.5)
         im = np.tile(np.pi * np.arange(N), (D, 1))
@@ -225,6 +237,15 @@ def make_A_complex(D: int, N: int, mode: str = "s4d_lin", rng: np.random.Generat
             re[0, 0] = im[0, 0] = 0.0
             if D > 1:
                 re[1, N - 1] = 0.0
+        elif mode == "weak":
+            slow = rng.random((D, N)) < 0.5
+            mod = 10.0 ** rng.uniform(-4.0, -2.0, (D, N))
+            ang = rng.uniform(0.5 * np.pi, 1.5 * np.pi, (D, N))   # Re a <= 0
+            re = np.where(slow, mod * np.cos(ang), re)
+            im = np.where(slow, mod * np.sin(ang), im)
+            re[0, 0] = im[0, 0] = 0.0
+        elif mode != "random":
+            raise ValueError(mode)
     return np.stack([re, im], axis=-1).astype(np.float32)
 
 

@@ -32,6 +32,7 @@ CASES = [
     (2, 150, 150, 16, "zoh", "mixed", "f32"), (2, 150, 150, 16, "euler", "random", "f32"),
     (1, 300, 64, 5, "zoh", "random", "f32"), (2, 203, 100, 16, "zoh", "random", "bf16"),
     (1, 77, 40, 7, "euler", "mixed", "bf16"), (2, 9, 70, 16, "zoh", "s4d_real", "f32"),
+    (2, 120, 70, 16, "zoh", "weak", "f32"),
 ]
 
 

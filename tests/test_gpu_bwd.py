@@ -61,6 +61,11 @@ CASES = [
     (2, 130, 66, 5, "zoh", True, True, True, True, True, "random"),
     (1, 129, 64, 8, "euler", True, True, True, True, True, "random"),
     (2, 1, 64, 16, "zoh", True, True, True, True, True, "random"),
+    # slowly decaying states (|A| down to 1e-4): exact ZOH's guarded coefficient
+    # and the series of its derivative
+    (2, 200, 70, 16, "zoh", True, True, True, True, True, "weak"),
+    (1, 333, 64, 13, "zoh", True, True, True, True, False, "weak"),
+    (2, 130, 66, 16, "euler", True, True, True, True, True, "weak"),
 ]
 
 

@@ -41,6 +41,8 @@ CASES = [
     (2, 9, 64, 16, "euler", "s4d_lin", "bf16", False),
     (1, 200, 40, 1, "zoh", "random", "f32", True),
     (2, 1, 30, 16, "zoh", "s4d_lin", "f32", True),
+    (2, 100, 40, 16, "zoh", "weak", "f32", True),
+    (1, 64, 33, 9, "euler", "weak", "f32", False),
 ]
 
 

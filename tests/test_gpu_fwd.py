@@ -71,6 +71,9 @@ SPLIT_CASES = [
     (2, 150, 150, 16, "zoh", "mixed", "f32"), (2, 150, 150, 16, "euler", "random", "f32"),
     (1, 300, 64, 5, "zoh", "random", "f32"), (3, 61, 130, 16, "zoh", "s4d_real", "f32"),
     (2, 203, 100, 16, "zoh", "random", "bf16"), (1, 77, 40, 7, "euler", "mixed", "bf16"),
+    # slowly decaying states (|A| down to 1e-4): exact ZOH's guarded coefficient
+    (2, 150, 150, 16, "zoh", "weak", "f32"), (1, 203, 100, 13, "zoh", "weak", "bf16"),
+    (2, 77, 70, 16, "euler", "weak", "f32"),
 ]
 
 
@@ -207,9 +210,10 @@ def test_fwd_full_size_sampled(oracle, name):
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("disc", ["zoh", "euler"])
 @pytest.mark.parametrize("N", [16, 5, 13])
-def test_step_parity(oracle, dtype, disc, N):
-    log("step case", dtype, disc, N)
-    inp = synth.make_inputs(3, 1, 200, N, seed=9, dtype=dtype, with_h0=True, a_mode="mixed")
+@pytest.mark.parametrize("amode", ["mixed", "weak"])
+def test_step_parity(oracle, dtype, disc, N, amode):
+    log("step case", dtype, disc, N, amode)
+    inp = synth.make_inputs(3, 1, 200, N, seed=9, dtype=dtype, with_h0=True, a_mode=amode)
     d = upload(inp)
     h = d["h0"].clone()
     y = B.scan_step(h, d["u"][:, 0].contiguous(), d["delta"][:, 0].contiguous(), d["A"],
