@@ -190,8 +190,8 @@ def cpu_baseline(inp, w, budget_s=20.0):
     res = {"value": elems / dt, "unit": "elements/s", "cores": threads, "kind": "oracle",
            "sample": "%s, full L=%d, N=%d, %s: %.2f s of fp64 C (OpenMP over channels)" % (
                what, w.L, w.N, w.disc, dt)}
-    # the same code on one thread, over a smaller sample (1024 channels of batch row 0)
-    nch = min(w.D, 1024)
+    # the same code on one thread, over a smaller sample (4096 channels of batch row 0)
+    nch = min(w.D, 4096)
     sl = (slice(0, 1), slice(None), slice(0, nch))
     t0 = time.perf_counter()
     oracle.fwd(inp.u[sl], inp.delta[sl], inp.A[:nch], inp.B[:1], inp.C[:1], D=inp.D[:nch],
