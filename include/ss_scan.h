@@ -14,6 +14,9 @@
  *     decay  abar_n = exp(dt * A[d,n])
  *     input  bbar_n = (exp(dt*A[d,n]) - 1) / A[d,n] * B[b,t,n]   exact zero-order hold,
  *                     dt * B[b,t,n] when A[d,n] == 0 or in Euler mode
+ *                     (computed as (abar - 1) / A from the rounded abar, relative error
+ *                     about 2^-24 / |dt A|, where every |A| of a wave is >= 0.25; otherwise
+ *                     dt (1 + x/2 + x^2/6 + x^3/24), x = dt A, wherever |x| < 0.05)
  *            (ZOH and its first-order form: "Mamba explained", hackbyte.io,
  *             discretization section; "A Survey of Mamba" summary, csdn, SSM section)
  *     state  h_n    = abar_n * h_n + bbar_n * u[b,t,d]
@@ -39,7 +42,8 @@
  *     produced without a GPU.  No exception crosses the ABI.  The library never
  *     allocates device memory: scratch comes from the caller's workspace.
  *   - NaN / Inf inputs propagate unchecked.
- *   - The forward and step are deterministic (bitwise repeatable).
+ *   - The forward, backward and step are deterministic (bitwise repeatable): the
+ *     backward's reductions add their partial sums in a fixed order, without atomics.
  */
 #ifndef SS_SCAN_H
 #define SS_SCAN_H
