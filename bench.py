@@ -249,7 +249,7 @@ def main():
     WARM["min_s"] = args.min_warmup_s
     if args.gpus != 1:
         print("bench.py measures one GPU only: the selective scan needs no communication "
-              "(every (b, d) channel is independent) and this build has no multi-GPU path; "
+              "(every (b, d) channel is independent) and the library has no multi-GPU path; "
               "run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
