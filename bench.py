@@ -31,6 +31,10 @@ VALU_PEAK_TSLOT = SIMD_LANES * CLOCK_HZ / 1e12   # 39.32 T lane-slots/s (non-pac
 # minimal VALU issue slots per scanned element (b, t, d, n): one v_exp_f32 (2 slots,
 # half rate on gfx950) + 4 (Euler) or 6 (exact ZOH) single-slot vector ops
 SLOTS_PER_ELEM = {"euler": 6.0, "zoh": 8.0}
+# complex state (exact ZOH): v_exp_f32, v_sin_f32, v_cos_f32 (2 slots each) and 22
+# single-slot ops (dt a_re, dt a_im, fract, |abar| (cos, sin), (abar - 1) / a, B u,
+# bcoef B u, abar h + ., Re(C h))
+COMPLEX_SLOTS = 28.0
 
 
 # sources the forward half-wave kernel (the benchmark's dominant kernel) and its
@@ -488,7 +492,9 @@ def time_bidir(torch, Bnd, synth, steps, warm):
     for key, f, mult in (("bidir_2p8b:fwd+rev_acc", both, 2), ("bidir_2p8b:rev", lambda: rev(0), 1)):
         total, per, mn, _ = time_calls(f, steps, warm, torch)
         out[key] = {"ms": round(per, 4), "ms_min": round(mn, 4),
-                    "elements_per_s": mult * w.elements / (per * 1e-3)}
+                    "elements_per_s": mult * w.elements / (per * 1e-3),
+                    "alu_frac": round(SLOTS_PER_ELEM[w.disc] * mult * w.elements /
+                                      (per * 1e-3) / 1e12 / VALU_PEAK_TSLOT, 4)}
     del d, y, ws, inp
     torch.cuda.empty_cache()
     return out
@@ -509,7 +515,9 @@ def time_complex(torch, Bnd, synth, steps, warm):
     total, per, mn, _ = time_calls(f, steps, warm, torch)
     el = Bt * L * D * N
     out = {"complex_2p8b_s4dlin": {"ms": round(per, 4), "ms_min": round(mn, 4),
-                                   "elements_per_s": el / (per * 1e-3)}}
+                                   "elements_per_s": el / (per * 1e-3),
+                                   "alu_frac": round(COMPLEX_SLOTS * el / (per * 1e-3) / 1e12 /
+                                                     VALU_PEAK_TSLOT, 4)}}
     del u, dl, Bm, Cm, z, y
     torch.cuda.empty_cache()
     return out
