@@ -214,13 +214,18 @@ def cpu_baseline(inp, w, budget_s=20.0):
 def cpu_rows(oracle, threads):
     """The oracle beside the other rows: each on a bounded sample drawn with the
     row's own recipe (same L, N and distributions, fewer batch rows, channels or
-    heads), reported in the row's unit."""
+    heads), repeated for at least 0.5 s, reported in the row's unit."""
     import numpy as np
 
-    def timed(run):
-        t0 = time.perf_counter()
-        run()
-        return time.perf_counter() - t0
+    def timed(run, min_s=0.5):
+        """seconds per call, the call repeated until min_s has passed"""
+        n, t0 = 0, time.perf_counter()
+        while True:
+            run()
+            n += 1
+            el = time.perf_counter() - t0
+            if el >= min_s:
+                return el / n
 
     out = {}
     # backward, Mamba-130M recipe: batch row 0, 192 channels (one thread: the oracle's
@@ -232,7 +237,7 @@ def cpu_rows(oracle, threads):
         dt = timed(lambda: oracle.bwd(inp.u, inp.delta, inp.A, inp.B, inp.C, D=inp.D,
                                       delta_bias=inp.delta_bias, z=inp.z, g=inp.dy, disc=disc))
         out["bwd_130m:" + disc] = {"value": w.L * nch * w.N / dt, "unit": "elements/s",
-                                   "threads": 1, "sample": "1 x %d x %d, N=%d: %.2f s" % (
+                                   "threads": 1, "sample": "1 x %d x %d, N=%d: %.3f s per call" % (
                                        w.L, nch, w.N, dt)}
     # decode step at B=8, D=5120, N=16 (one thread)
     st = synth_mod().make_inputs(8, 1, 5120, 16, 9, "bf16", with_h0=True)
@@ -248,10 +253,10 @@ def cpu_rows(oracle, threads):
     g = rng.standard_normal((1, 2048, 1024)).astype(np.float32)
     dt = timed(lambda: oracle.conv1d_fwd(x, cw, cb))
     out["conv1d_fwd_b8_l2048_d5120"] = {"value": x.size / dt, "unit": "elements/s (b, t, d)",
-                                        "threads": 1, "sample": "1 x 2048 x 1024: %.2f s" % dt}
+                                        "threads": 1, "sample": "1 x 2048 x 1024: %.3f s per call" % dt}
     dt = timed(lambda: oracle.conv1d_bwd(x, cw, g, cb))
     out["conv1d_bwd_b8_l2048_d5120"] = {"value": x.size / dt, "unit": "elements/s (b, t, d)",
-                                        "threads": 1, "sample": "1 x 2048 x 1024: %.2f s" % dt}
+                                        "threads": 1, "sample": "1 x 2048 x 1024: %.3f s per call" % dt}
     # SSD layer, its workload recipe: one batch row, all heads
     sw = synth_mod().SSD_WORKLOAD
     si = synth_mod().make_ssd_inputs(1, sw["L"], sw["H"], sw["P"], sw["N"], 1, sw["seed"])
@@ -259,13 +264,13 @@ def cpu_rows(oracle, threads):
                                       nthreads=threads))
     out["ssd_bf16_b8_l2048_h80_p64_n64_g1"] = {
         "value": sw["L"] / dt, "unit": "tokens/s", "threads": threads,
-        "sample": "1 x %d tokens, %d heads: %.2f s" % (sw["L"], sw["H"], dt)}
+        "sample": "1 x %d tokens, %d heads: %.3f s per call" % (sw["L"], sw["H"], dt)}
     # complex A, S4D-Lin recipe: batch row 0, 2048 channels, full L, N=16
     ci = synth_mod().make_complex_inputs(1, 2048, 2048, 16, seed=1002, dtype="bf16")
     dt = timed(lambda: oracle.fwd_complex(ci.u, ci.delta, ci.A, ci.B, ci.C, D=ci.D,
                                           delta_bias=ci.delta_bias, z=ci.z, nthreads=threads))
     out["complex_2p8b_s4dlin"] = {"value": 2048 * 2048 * 16 / dt, "unit": "elements/s",
-                                  "threads": threads, "sample": "1 x 2048 x 2048: %.2f s" % dt}
+                                  "threads": threads, "sample": "1 x 2048 x 2048: %.3f s per call" % dt}
     return out
 
 
