@@ -382,17 +382,21 @@ int oracle_conv1d_step(int64_t Bt, int64_t D, int64_t K, int silu, double* state
  *   y_t  = H_t^T C_t + D_h x_t                       (P)
  * x, y: (Bt, L, Hh, P); dt: (Bt, L, Hh); A, D, dt_bias: (Hh);
  * Bm, Cm: (Bt, L, G, N), head h uses group h / (Hh / G).
+ * h0 (state before the first step, zero when NULL) and h_last (state after the
+ * last step, written when not NULL): (Bt, Hh, N, P).
  */
 int oracle_ssd_fwd(int64_t Bt, int64_t L, int64_t Hh, int64_t P, int64_t N, int64_t G,
                    int softplus, const double* x, const double* dt_raw, const double* A,
                    const double* Bm, const double* Cm, const double* Dh, const double* dt_bias,
-                   double* y, int nthreads) {
+                   const double* h0, double* y, double* h_last, int nthreads) {
   if (Bt < 0 || L < 0 || Hh < 1 || P < 1 || N < 1 || G < 1 || Hh % G) return -1;
   const int64_t hpg = Hh / G;
 #pragma omp parallel for collapse(2) schedule(dynamic) num_threads(nthreads > 0 ? nthreads : 1)
   for (int64_t b = 0; b < Bt; ++b) {
     for (int64_t h = 0; h < Hh; ++h) {
       double* H = (double*)calloc((size_t)(N * P), sizeof(double));
+      if (h0)
+        for (int64_t k = 0; k < N * P; ++k) H[k] = h0[(b * Hh + h) * N * P + k];
       const int64_t g = h / hpg;
       for (int64_t t = 0; t < L; ++t) {
         double dt = step_size(dt_raw[(b * L + t) * Hh + h], dt_bias ? dt_bias[h] : 0.0, softplus);
@@ -410,6 +414,8 @@ int oracle_ssd_fwd(int64_t Bt, int64_t L, int64_t Hh, int64_t P, int64_t N, int6
           yt[p] = s + (Dh ? Dh[h] : 0.0) * xt[p];
         }
       }
+      if (h_last)
+        for (int64_t k = 0; k < N * P; ++k) h_last[(b * Hh + h) * N * P + k] = H[k];
       free(H);
     }
   }

@@ -63,7 +63,7 @@ def _load():
         lib.oracle_conv1d_bwd.restype = I
         lib.oracle_conv1d_step.argtypes = [I64, I64, I64, I] + [P] * 5
         lib.oracle_conv1d_step.restype = I
-        lib.oracle_ssd_fwd.argtypes = [I64] * 6 + [I] + [P] * 8 + [I]
+        lib.oracle_ssd_fwd.argtypes = [I64] * 6 + [I] + [P] * 10 + [I]
         lib.oracle_ssd_fwd.restype = I
         lib.oracle_fwd_complex.argtypes = [I64, I64, I64, I64, I, I] + [P] * 11 + [I]
         lib.oracle_fwd_complex.restype = I
@@ -251,17 +251,23 @@ def conv1d_step(state, x, w, bias=None, silu=True):
 
 
 # ---------------------------------------------------------------- SSD (Mamba-2)
-def ssd_fwd(x, dt, A, B, C, D=None, dt_bias=None, softplus=True, nthreads=None):
+def ssd_fwd(x, dt, A, B, C, D=None, dt_bias=None, softplus=True, nthreads=None, h0=None,
+            return_last=False):
     """Sequential SSD layer: x (Bt, L, H, P), dt (Bt, L, H), A (H,), B and C
-    (Bt, L, G, N), D and dt_bias (H,).  Returns y (Bt, L, H, P) float64."""
+    (Bt, L, G, N), D and dt_bias (H,), h0 (Bt, H, N, P) or None.  Returns y
+    (Bt, L, H, P) float64, and the state after the last step (Bt, H, N, P) when
+    return_last."""
     x = _f64(x); dt = _f64(dt); A = _f64(A); B = _f64(B); C = _f64(C)
     D = None if D is None else _f64(D)
     dt_bias = None if dt_bias is None else _f64(dt_bias)
+    h0 = None if h0 is None else _f64(h0)
     Bt, L, H, P = x.shape
     G, N = B.shape[2], B.shape[3]
     y = np.empty((Bt, L, H, P))
+    hl = np.empty((Bt, H, N, P)) if return_last else None
     th = nthreads if nthreads else min(16, os.cpu_count() or 1)
     rc = _load().oracle_ssd_fwd(Bt, L, H, P, N, G, int(bool(softplus)), _ptr(x), _ptr(dt),
-                                _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(dt_bias), _ptr(y), th)
+                                _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(dt_bias), _ptr(h0),
+                                _ptr(y), _ptr(hl), th)
     assert rc == 0
-    return y
+    return (y, hl) if return_last else y

@@ -63,3 +63,41 @@ def test_ssd_zero_step_keeps_skip_only(oracle):
     x, dt, A, B, C, D, _ = _inputs(Bt, L, H, P, N, 1, seed=2)
     y = oracle.ssd_fwd(x, np.full_like(dt, -60.0), A, B, C, D=D, dt_bias=None)
     assert np.max(np.abs(y - D[None, None, :, None] * x)) <= 1e-20
+
+
+def test_ssd_state_in_and_out_closed_form(oracle):
+    """With a start state H0 the output gains C_t . (prod_{s<=t} a_s) H0 and the
+    final state is (prod_t a_t) H0 + sum_t (prod_{s>t} a_s) dt_t B_t x_t^T, both
+    written here as numpy products over the whole sequence."""
+    Bt, L, H, P, N, G = 2, 17, 3, 5, 4, 1
+    x, dt, A, B, C, D, bias = _inputs(Bt, L, H, P, N, G, seed=21)
+    rng = np.random.default_rng(22)
+    h0 = rng.standard_normal((Bt, H, N, P))
+    y, hl = oracle.ssd_fwd(x, dt, A, B, C, D=D, dt_bias=bias, h0=h0, return_last=True)
+    y0 = oracle.ssd_fwd(x, dt, A, B, C, D=D, dt_bias=bias)
+    for b in range(Bt):
+        for h in range(H):
+            d = _softplus(dt[b, :, h] + bias[h])
+            la = np.cumsum(d * A[h])                      # log prod_{s<=t} a_s
+            # the start state's share of y_t
+            extra = np.exp(la)[:, None] * (C[b, :, 0] @ h0[b, h])      # (L, P)
+            assert np.max(np.abs(y[b, :, h] - y0[b, :, h] - extra)) <= 1e-10 * (
+                1 + np.max(np.abs(extra)))
+            w = np.exp(la[-1] - la) * d                   # prod_{s>t} a_s * dt_t
+            ref = np.exp(la[-1]) * h0[b, h] + (B[b, :, 0] * w[:, None]).T @ x[b, :, h]
+            assert np.max(np.abs(hl[b, h] - ref)) <= 1e-10 * (1 + np.max(np.abs(ref)))
+
+
+def test_ssd_split_sequence(oracle):
+    """Running [0, L1) and then [L1, L) from the state the first part leaves equals
+    one run over [0, L) (outputs and final state)."""
+    Bt, L, H, P, N, G = 2, 29, 4, 3, 5, 2
+    x, dt, A, B, C, D, bias = _inputs(Bt, L, H, P, N, G, seed=23)
+    y, hl = oracle.ssd_fwd(x, dt, A, B, C, D=D, dt_bias=bias, return_last=True)
+    L1 = 11
+    ya, ha = oracle.ssd_fwd(x[:, :L1], dt[:, :L1], A, B[:, :L1], C[:, :L1], D=D, dt_bias=bias,
+                            return_last=True)
+    yb, hb = oracle.ssd_fwd(x[:, L1:], dt[:, L1:], A, B[:, L1:], C[:, L1:], D=D, dt_bias=bias,
+                            h0=ha, return_last=True)
+    assert np.max(np.abs(np.concatenate([ya, yb], axis=1) - y)) <= 1e-12 * (1 + np.max(np.abs(y)))
+    assert np.max(np.abs(hb - hl)) <= 1e-12 * (1 + np.max(np.abs(hl)))
