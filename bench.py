@@ -518,9 +518,64 @@ def time_ssd(torch, Bnd, synth, steps, warm):
             "hbm_frac": round(alg / (per * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
             "tflops": round(flops / (per * 1e-3) / 1e12, 1), "algorithmic_bytes": alg}
         del y
-    del x, dt, Bm, Cm
+    # from a start state, keeping the final state, in place (a prefill that
+    # continues a sequence): the state is read and written once more
+    h = torch.zeros((Bt, H, N, P), dtype=f32, device="cuda")
+    y = torch.empty(x.shape, dtype=f32, device="cuda")
+    desc = Bnd.make_ssd_desc(Bt, L, H, P, N, G, Bnd.SS_BF16, Bnd.SS_F32, True)
+    f = lambda: Bnd.ss_ssd_fwd_state(desc, x, dt, A, Bm, Cm, Dh, bias, h, y, h)  # noqa
+    total, per, mn, _ = time_calls(f, steps, warm, torch)
+    alg = toks * H * P * (2 + 4) + toks * H * 2 + 2 * toks * G * N * 2 + 3 * H * 4
+    alg += 2 * Bt * H * N * P * 4
+    out["%s:y_f32_state_in_out" % w["name"]] = {
+        "ms": round(per, 4), "ms_min": round(mn, 4), "tokens_per_s": toks / (per * 1e-3),
+        "hbm_gbs": round(alg / (per * 1e-3) / 1e9, 1),
+        "hbm_frac": round(alg / (per * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "tflops": round(flops / (per * 1e-3) / 1e12, 1), "algorithmic_bytes": alg}
+    del x, dt, Bm, Cm, h, y
     torch.cuda.empty_cache()
+    out.update(time_ssd_step(torch, Bnd, synth))
     return out
+
+
+def time_ssd_step(torch, Bnd, synth):
+    """SSD decode step: 256 rows x 80 heads of 64 channels, 64 states; the
+    state (256, 80, 64, 64) fp32 is 336 MB, more than the last-level cache, and
+    is read and written once per step.  100 steps captured in one graph."""
+    Bt, H, P, N, G = 256, 80, 64, 64, 1
+    inp = synth.make_ssd_inputs(Bt, 1, H, P, N, G, seed=2002)
+    bf, f32 = torch.bfloat16, torch.float32
+    dev = lambda a, t: torch.from_numpy(a).to("cuda").to(t).contiguous()  # noqa
+    x, dt, Bm, Cm = (dev(a[:, 0], bf) for a in (inp.x, inp.dt, inp.B, inp.C))
+    A, Dh, bias = (dev(a, f32) for a in (inp.A, inp.D, inp.dt_bias))
+    h = torch.zeros((Bt, H, N, P), dtype=f32, device="cuda")
+    y = torch.empty((Bt, H, P), dtype=f32, device="cuda")
+    desc = Bnd.make_ssd_desc(Bt, 1, H, P, N, G, Bnd.SS_BF16, Bnd.SS_F32, True)
+
+    def steps(k):
+        for _ in range(k):
+            rc = Bnd.ss_ssd_step(desc, h, x, dt, A, Bm, Cm, Dh, bias, y)
+            if rc != 0:
+                raise RuntimeError(Bnd.ss_scan_strerror(rc))
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        steps(3)
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        steps(100)
+    total, per, mn, _ = time_calls(g.replay, 10, 2, torch)
+    us = per * 10   # 100 steps per replay
+    alg = 2 * Bt * H * N * P * 4 + Bt * H * P * (2 + 4) + Bt * H * 2 + 2 * Bt * G * N * 2 + 3 * H * 4
+    del g, h, x, dt, Bm, Cm, y
+    torch.cuda.empty_cache()
+    return {"ssd_step_b256_h80_p64_n64_g1": {
+        "us_per_step": round(us, 3), "algorithmic_bytes": alg,
+        "hbm_gbs": round(alg / (us * 1e-6) / 1e9, 1),
+        "hbm_frac": round(alg / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+        "how": "100 steps captured in one graph, 10 replays"}}
 
 
 def time_bwd(torch, Bnd, synth, steps, warm):

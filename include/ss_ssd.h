@@ -50,11 +50,42 @@ typedef struct ss_ssd_desc {
 
 /*
  * SSD forward.  x, dt, A, Bm, Cm, y required; D and dt_bias optional (NULL = 0).
- * y must not alias an input.
+ * y must not alias an input.  The state starts at zero.
  */
 int ss_ssd_fwd(const ss_ssd_desc_t* desc, const void* x, const void* dt, const float* A,
                const void* Bm, const void* Cm, const float* D, const float* dt_bias, void* y,
                void* stream);
+
+/*
+ * SSD forward from a given state, keeping the state after the last step, so
+ * that a sequence may be processed in pieces (prefill) and continued by
+ * ss_ssd_step: the recurrence above with H_0 = h0 instead of zero, and
+ * h_last = H_L.
+ *   h0     : (B, H, N, P) float32, the state before step 1; NULL = zero.
+ *   h_last : (B, H, N, P) float32 output; NULL = not stored.  It may be the
+ *            same buffer as h0 (the state is then advanced in place), and must
+ *            not alias any other argument.
+ * Element [b][h][n][p] of a state is H[n][p] of head h of batch row b.
+ * Other arguments, validation and status codes as ss_ssd_fwd.
+ */
+int ss_ssd_fwd_state(const ss_ssd_desc_t* desc, const void* x, const void* dt, const float* A,
+                     const void* Bm, const void* Cm, const float* D, const float* dt_bias,
+                     const float* h0, void* y, float* h_last, void* stream);
+
+/*
+ * One SSD step (decoding): desc->seqlen is not read.
+ *   h      : (B, H, N, P) float32, state in / out, advanced in place;
+ *   x      : (B, H, P) in_dtype;  dt : (B, H) in_dtype;
+ *   Bm, Cm : (B, G, N) in_dtype;  A, D, dt_bias : (H) float32 (D, dt_bias
+ *            optional);  y : (B, H, P) out_dtype.
+ * Computes H <- a H + dt B x^T and y = H^T C + D x with dt and a as in the
+ * recurrence above.  y and h must not alias any other argument.  Device
+ * pointers, 16-byte aligned; asynchronous on `stream`; no allocation;
+ * deterministic.
+ */
+int ss_ssd_step(const ss_ssd_desc_t* desc, float* h, const void* x, const void* dt,
+                const float* A, const void* Bm, const void* Cm, const float* D,
+                const float* dt_bias, void* y, void* stream);
 
 #ifdef __cplusplus
 }

@@ -3,11 +3,12 @@ include/ss_conv.h and include/ss_ssd.h).
 
 The functions named like the C entry points (ss_scan_fwd, ss_scan_fwd_dir,
 ss_scan_fwd_complex, ss_scan_bwd, ss_scan_step, ss_scan_workspace_bytes, ss_scan_strerror, ss_scan_version,
-ss_conv1d_fwd, ss_conv1d_bwd, ss_conv1d_step, ss_conv1d_workspace_bytes, ss_ssd_fwd) only
+ss_conv1d_fwd, ss_conv1d_bwd, ss_conv1d_step, ss_conv1d_workspace_bytes, ss_ssd_fwd,
+ss_ssd_fwd_state, ss_ssd_step) only
 marshal arguments: torch tensors become device pointers, None becomes NULL and
 the stream defaults to torch's current HIP stream.  Every step runs in the HIP
 kernels; there is no fallback.  The convenience wrappers scan_fwd, scan_bwd,
-scan_bidir, scan_fwd_complex, scan_step, conv1d_fwd, conv1d_bwd, conv1d_step and ssd_fwd additionally allocate
+scan_bidir, scan_fwd_complex, scan_step, conv1d_fwd, conv1d_bwd, conv1d_step, ssd_fwd and ssd_step additionally allocate
 outputs and workspace with torch.
 """
 from __future__ import annotations
@@ -93,6 +94,10 @@ def load_library():
         lib.ss_conv1d_step.restype = I
         lib.ss_ssd_fwd.argtypes = [ctypes.POINTER(ss_ssd_desc_t)] + [P] * 8 + [P]
         lib.ss_ssd_fwd.restype = I
+        lib.ss_ssd_fwd_state.argtypes = [ctypes.POINTER(ss_ssd_desc_t)] + [P] * 10 + [P]
+        lib.ss_ssd_fwd_state.restype = I
+        lib.ss_ssd_step.argtypes = [ctypes.POINTER(ss_ssd_desc_t)] + [P] * 9 + [P]
+        lib.ss_ssd_step.restype = I
         lib.ss_scan_strerror.argtypes = [I]
         lib.ss_scan_strerror.restype = ctypes.c_char_p
         lib.ss_scan_version.argtypes = []
@@ -208,6 +213,17 @@ def make_ssd_desc(batch, seqlen, nheads, headdim, dstate, ngroups=1, in_dtype=SS
 def ss_ssd_fwd(desc, x, dt, A, Bm, Cm, D, dt_bias, y, stream=None) -> int:
     return load_library().ss_ssd_fwd(ctypes.byref(desc), _p(x), _p(dt), _p(A), _p(Bm), _p(Cm),
                                       _p(D), _p(dt_bias), _p(y), _stream(stream))
+
+
+def ss_ssd_fwd_state(desc, x, dt, A, Bm, Cm, D, dt_bias, h0, y, h_last, stream=None) -> int:
+    return load_library().ss_ssd_fwd_state(ctypes.byref(desc), _p(x), _p(dt), _p(A), _p(Bm),
+                                            _p(Cm), _p(D), _p(dt_bias), _p(h0), _p(y),
+                                            _p(h_last), _stream(stream))
+
+
+def ss_ssd_step(desc, h, x, dt, A, Bm, Cm, D, dt_bias, y, stream=None) -> int:
+    return load_library().ss_ssd_step(ctypes.byref(desc), _p(h), _p(x), _p(dt), _p(A), _p(Bm),
+                                       _p(Cm), _p(D), _p(dt_bias), _p(y), _stream(stream))
 
 
 def _check(rc, where):
@@ -344,12 +360,32 @@ def conv1d_step(state, x, w, bias=None, silu=True, out_dtype=torch.float32, stre
 
 
 def ssd_fwd(x, dt, A, B, C, D=None, dt_bias=None, softplus=True, out_dtype=torch.float32,
-            stream=None):
+            stream=None, h0=None, return_last=False):
     """SSD (Mamba-2) layer forward: x (Bt, L, H, P), dt (Bt, L, H), B and C
-    (Bt, L, G, N) in bf16; A, D, dt_bias (H,) fp32.  Returns y (Bt, L, H, P)."""
+    (Bt, L, G, N) in bf16; A, D, dt_bias (H,) fp32; optional start state h0
+    (Bt, H, N, P) fp32.  Returns y (Bt, L, H, P), and with return_last the
+    state after the last step as well."""
     Bt, L, H, P = x.shape
     G, N = B.shape[2], B.shape[3]
     desc = make_ssd_desc(Bt, L, H, P, N, G, _DTYPE[x.dtype], _DTYPE[out_dtype], softplus)
     y = torch.empty(x.shape, dtype=out_dtype, device=x.device)
-    _check(ss_ssd_fwd(desc, x, dt, A, B, C, D, dt_bias, y, stream), "ss_ssd_fwd")
+    if h0 is None and not return_last:
+        _check(ss_ssd_fwd(desc, x, dt, A, B, C, D, dt_bias, y, stream), "ss_ssd_fwd")
+        return y
+    h_last = (torch.empty((Bt, H, N, P), dtype=torch.float32, device=x.device)
+              if return_last else None)
+    _check(ss_ssd_fwd_state(desc, x, dt, A, B, C, D, dt_bias, h0, y, h_last, stream),
+           "ss_ssd_fwd_state")
+    return (y, h_last) if return_last else y
+
+
+def ssd_step(h, x, dt, A, B, C, D=None, dt_bias=None, softplus=True, out_dtype=torch.float32,
+             stream=None):
+    """One SSD decode step: h (Bt, H, N, P) fp32 updated in place; x (Bt, H, P),
+    dt (Bt, H), B and C (Bt, G, N) bf16.  Returns y (Bt, H, P)."""
+    Bt, H, P = x.shape
+    G, N = B.shape[1], B.shape[2]
+    desc = make_ssd_desc(Bt, 1, H, P, N, G, _DTYPE[x.dtype], _DTYPE[out_dtype], softplus)
+    y = torch.empty(x.shape, dtype=out_dtype, device=x.device)
+    _check(ss_ssd_step(desc, h, x, dt, A, B, C, D, dt_bias, y, stream), "ss_ssd_step")
     return y

@@ -170,15 +170,18 @@ int check_conv(const ss_conv_desc_t* d, bool need_len) {
   return SS_OK;
 }
 
-// SSD descriptions: positive sizes, heads divisible into groups, 32-bit grid.
-int check_ssd(const ss_ssd_desc_t* d) {
+// SSD descriptions: positive sizes, heads divisible into groups, 32-bit grid
+// (seqlen checked only where the call reads it).
+int check_ssd(const ss_ssd_desc_t* d, bool need_len = true) {
   if (!d || d->reserved != 0) return SS_ERR_INVALID_ARG;
-  if (d->batch < 1 || d->seqlen < 1 || d->nheads < 1 || d->headdim < 1 || d->dstate < 1 ||
+  if (d->batch < 1 || (need_len && d->seqlen < 1) || d->nheads < 1 || d->headdim < 1 ||
+      d->dstate < 1 ||
       d->ngroups < 1 || d->nheads % d->ngroups != 0)
     return SS_ERR_INVALID_ARG;
   const int64_t lim = int64_t(1) << 40;
-  if (d->batch > lim || d->seqlen > lim || d->nheads > lim || d->ngroups > lim ||
-      d->batch > (int64_t(INT32_MAX) / d->nheads) || d->batch * d->seqlen > lim / d->nheads)
+  const int64_t L = need_len ? d->seqlen : 1;
+  if (d->batch > lim || L > lim || d->nheads > lim || d->ngroups > lim ||
+      d->batch > (int64_t(INT32_MAX) / d->nheads) || d->batch * L > lim / d->nheads)
     return SS_ERR_INVALID_ARG;
   if (d->headdim != 64 || d->dstate != 64) return SS_ERR_UNSUPPORTED;
   if (d->in_dtype != SS_BF16 || !valid_dtype(d->out_dtype)) return SS_ERR_UNSUPPORTED;
@@ -367,17 +370,49 @@ int ss_conv1d_step(const ss_conv_desc_t* desc, float* state, const void* x, cons
   return launch_conv_step(*desc, state, x, w, bias, u, stream) == 0 ? SS_OK : SS_ERR_HIP;
 }
 
-int ss_ssd_fwd(const ss_ssd_desc_t* desc, const void* x, const void* dt, const float* A,
-               const void* Bm, const void* Cm, const float* D, const float* dt_bias, void* y,
-               void* stream) {
+int ss_ssd_fwd_state(const ss_ssd_desc_t* desc, const void* x, const void* dt, const float* A,
+                     const void* Bm, const void* Cm, const float* D, const float* dt_bias,
+                     const float* h0, void* y, float* h_last, void* stream) {
   int rc = check_ssd(desc);
   if (rc != SS_OK) return rc;
   if (!x || !dt || !A || !Bm || !Cm || !y) return SS_ERR_INVALID_ARG;
   if (y == x || y == dt || y == Bm || y == Cm) return SS_ERR_INVALID_ARG;
-  const void* ptrs[] = {x, dt, A, Bm, Cm, D, dt_bias, y};
+  if (h0 && (static_cast<const void*>(h0) == y)) return SS_ERR_INVALID_ARG;
+  if (h_last) {
+    const void* hl = h_last;
+    if (hl == x || hl == dt || hl == Bm || hl == Cm || hl == y || h_last == A || h_last == D ||
+        h_last == dt_bias)
+      return SS_ERR_INVALID_ARG;
+  }
+  const void* ptrs[] = {x, dt, A, Bm, Cm, D, dt_bias, h0, y, h_last};
   for (const void* p : ptrs)
     if (p && !aligned(p, kPtrAlign)) return SS_ERR_INVALID_ARG;
-  return launch_ssd_fwd(*desc, x, dt, A, Bm, Cm, D, dt_bias, y, stream) == 0 ? SS_OK : SS_ERR_HIP;
+  return launch_ssd_fwd(*desc, x, dt, A, Bm, Cm, D, dt_bias, h0, y, h_last, stream) == 0
+             ? SS_OK
+             : SS_ERR_HIP;
+}
+
+int ss_ssd_fwd(const ss_ssd_desc_t* desc, const void* x, const void* dt, const float* A,
+               const void* Bm, const void* Cm, const float* D, const float* dt_bias, void* y,
+               void* stream) {
+  return ss_ssd_fwd_state(desc, x, dt, A, Bm, Cm, D, dt_bias, nullptr, y, nullptr, stream);
+}
+
+int ss_ssd_step(const ss_ssd_desc_t* desc, float* h, const void* x, const void* dt,
+                const float* A, const void* Bm, const void* Cm, const float* D,
+                const float* dt_bias, void* y, void* stream) {
+  int rc = check_ssd(desc, false);
+  if (rc != SS_OK) return rc;
+  if (!h || !x || !dt || !A || !Bm || !Cm || !y) return SS_ERR_INVALID_ARG;
+  const void* hv = h;
+  if (y == x || y == dt || y == Bm || y == Cm || y == hv) return SS_ERR_INVALID_ARG;
+  if (hv == x || hv == dt || hv == Bm || hv == Cm || h == A || h == D || h == dt_bias)
+    return SS_ERR_INVALID_ARG;
+  const void* ptrs[] = {h, x, dt, A, Bm, Cm, D, dt_bias, y};
+  for (const void* p : ptrs)
+    if (p && !aligned(p, kPtrAlign)) return SS_ERR_INVALID_ARG;
+  return launch_ssd_step(*desc, h, x, dt, A, Bm, Cm, D, dt_bias, y, stream) == 0 ? SS_OK
+                                                                                  : SS_ERR_HIP;
 }
 
 }  // extern "C"

@@ -35,6 +35,10 @@
 // (from the G^T tiles) and for H alike, and the LDS operands are read in the
 // same order.
 //
+// The state may start from a given H (else zero) and its value after the last
+// step may be stored; both in the accumulator's own layout, straight from and
+// to global memory, once per workgroup.
+//
 // Per chunk: the next chunk's x, B, C rows are fetched into registers (buffer
 // loads; rows past the end read as zero) while this one is computed, then
 // written to LDS as B and C rows and as B^T and x^T (4 x 4 transposes in
@@ -149,6 +153,8 @@ struct SsdArgs {
   const float* D;          // (H) or null
   const float* dt_bias;    // (H) or null
   void* y;                 // (B, L, H, P)
+  const float* h0;         // (B, H, N, P) state before the first step, or null (zero)
+  float* h_last;           // (B, H, N, P) state after the last step, or null
   int64_t L;
   int H, G;
 };
@@ -168,7 +174,9 @@ __device__ __forceinline__ void store_y4<uint16_t>(Rsrc r, uint32_t voff, f32x4 
   __builtin_amdgcn_raw_buffer_store_b64(p, r, voff, 0, 0);
 }
 
-template <typename Out, bool SOFTPLUS>
+// STATE: a start state is read (zero where h0 is null) and the final state is
+// stored where h_last is not null.
+template <typename Out, bool SOFTPLUS, bool STATE>
 __global__ __launch_bounds__(kThreads, 3) void ssd_fwd_kernel(SsdArgs a) {
   __shared__ __align__(16) char sm[kSmemBytes];
   const int tid = int(threadIdx.x);
@@ -248,13 +256,29 @@ __global__ __launch_bounds__(kThreads, 3) void ssd_fwd_kernel(SsdArgs a) {
 
   // state H[n][p]: tile ni holds rows 16 ni + 4g + r, column 16 w + c16
   f32x4 hacc[4];
+  if constexpr (STATE) {
+    // element (n, p) of this head's state: (b H + h) N P + n P + p; a null h0
+    // gets a buffer of no records, whose loads return zero
+    const Rsrc rh = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float*>(a.h0) + (b * a.H + h) * int64_t(kDim * kDim), short(0),
+        a.h0 ? 0x7fffffff : 0, 0x00020000);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) hacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        hacc[i][r] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+            rh, uint32_t((16 * i + 4 * g + r) * kDim + 16 * w + c16) * 4u, 0, 0));
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) hacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
 
-  // One chunk, from register set sg.  The first chunk is peeled off the loop
-  // below: every path into the loop head then has the previous chunk's output
-  // stores issued after its prefetch loads, so the wait at the head covers the
-  // loads only.
+  // One chunk, from register set sg.  Without a start state the first chunk
+  // is peeled off the loop below: every path into the loop head then has the
+  // previous chunk's output stores issued after its prefetch loads, so the
+  // wait at the head covers the loads only.  With a start state the peeled
+  // copy (whose state is no longer known to be zero) would not fit the
+  // register budget, and the loop runs from the first chunk.
   auto chunk = [&](int c, Stage& sg) __attribute__((always_inline)) {
     const int64_t t0 = int64_t(c) * kQ;
     const int64_t rows = L - t0;
@@ -482,25 +506,166 @@ __global__ __launch_bounds__(kThreads, 3) void ssd_fwd_kernel(SsdArgs a) {
     }
   };
   load_chunk(0, st0);
-  chunk(0, st0);
-  for (int c = 1; c < nc; ++c) chunk(c, st0);
+  if constexpr (STATE) {
+    for (int c = 0; c < nc; ++c) chunk(c, st0);
+  } else {
+    chunk(0, st0);
+    for (int c = 1; c < nc; ++c) chunk(c, st0);
+  }
+  if (STATE && a.h_last) {
+    // lane index and its parts formed afresh: nothing of the prologue's
+    // addressing stays live through the chunk loop
+    const int ln = int(__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)));
+    const uint32_t col = uint32_t(16 * w + (ln & 15)), row = uint32_t(4 * (ln >> 4));
+    const Rsrc rh = make_rsrc(a.h_last + (b * a.H + h) * int64_t(kDim * kDim));
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(hacc[i][r]), rh,
+                                              ((row + 16 * i + r) * kDim + col) * 4u, 0, 0);
+  }
+}
+
+// One step of the recurrence on the state of one (batch row, head):
+//     H <- exp(dt A) H + dt B x^T,   y = H^T C + D x
+// 256 threads; thread (wave w, lane l) owns columns p = 4 (l & 15) .. +3 of
+// rows n = 4 w + (l >> 4) + 16 k, k = 0..3, so every state row is read and
+// written as 16-byte pieces, a wave's four rows of one k being 1 KB in a row.
+// C^T H is summed over a wave's rows with lane exchanges and over the four
+// waves in LDS, in a fixed order.  The step sizes, decay and B weight are
+// formed as in the chunked kernel above, so a step continues its state.
+struct SsdStepArgs {
+  float* h;                // (B, H, N, P) fp32, in place
+  const uint16_t* x;       // (B, H, P) bf16
+  const uint16_t* dt;      // (B, H) bf16
+  const float* A;          // (H)
+  const uint16_t* Bm;      // (B, G, N) bf16
+  const uint16_t* Cm;      // (B, G, N) bf16
+  const float* D;          // (H) or null
+  const float* dt_bias;    // (H) or null
+  void* y;                 // (B, H, P)
+  int H, G;
+};
+
+template <typename Out>
+__device__ __forceinline__ void store_y4_ptr(Out* p, float4 v);
+template <>
+__device__ __forceinline__ void store_y4_ptr<float>(float* p, float4 v) {
+  *reinterpret_cast<float4*>(p) = v;
+}
+template <>
+__device__ __forceinline__ void store_y4_ptr<uint16_t>(uint16_t* p, float4 v) {
+  *reinterpret_cast<uint2*>(p) = make_uint2(pack_bf16(v.x, v.y), pack_bf16(v.z, v.w));
+}
+
+template <typename Out, bool SOFTPLUS>
+__global__ __launch_bounds__(kThreads) void ssd_step_kernel(SsdStepArgs a) {
+  __shared__ float4 part[kNW][16];
+  const int tid = int(threadIdx.x);
+  const int w = tid / kWave, lane = tid % kWave;
+  const int q = lane & 15, r = 4 * w + (lane >> 4);
+  const int h = int(blockIdx.x % unsigned(a.H));
+  const int64_t b = int64_t(blockIdx.x / unsigned(a.H));
+  const int grp = h / (a.H / a.G);
+  const int64_t bh = b * a.H + h;
+
+  const float v = to_f32<uint16_t>(a.dt[bh]) + (a.dt_bias ? a.dt_bias[h] : 0.0f);
+  float dt2;   // dt * log2(e)
+  if constexpr (SOFTPLUS) dt2 = softplus_log2(v * kLog2e);
+  else dt2 = v * kLog2e;
+  const float decay = hw_exp2(dt2 * a.A[h]);
+  const float dtn = dt2 * kLn2;
+  const float4 xv = unpack4(*reinterpret_cast<const uint2*>(a.x + bh * kDim + 4 * q));
+  const uint16_t* Bg = a.Bm + (b * a.G + grp) * kDim;
+  const uint16_t* Cg = a.Cm + (b * a.G + grp) * kDim;
+  float* hp = a.h + bh * (kDim * kDim) + 4 * q;
+
+  float4 hv[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) hv[k] = *reinterpret_cast<const float4*>(hp + (r + 16 * k) * kDim);
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int n = r + 16 * k;
+    const float bw = dtn * to_f32<uint16_t>(Bg[n]), cn = to_f32<uint16_t>(Cg[n]);
+    float4 s = hv[k];
+    s.x = fmaf(decay, s.x, bw * xv.x);
+    s.y = fmaf(decay, s.y, bw * xv.y);
+    s.z = fmaf(decay, s.z, bw * xv.z);
+    s.w = fmaf(decay, s.w, bw * xv.w);
+    *reinterpret_cast<float4*>(hp + n * kDim) = s;
+    acc.x = fmaf(cn, s.x, acc.x);
+    acc.y = fmaf(cn, s.y, acc.y);
+    acc.z = fmaf(cn, s.z, acc.z);
+    acc.w = fmaf(cn, s.w, acc.w);
+  }
+#pragma unroll
+  for (int m = 16; m < kWave; m *= 2) {
+    acc.x += __shfl_xor(acc.x, m);
+    acc.y += __shfl_xor(acc.y, m);
+    acc.z += __shfl_xor(acc.z, m);
+    acc.w += __shfl_xor(acc.w, m);
+  }
+  if (lane < 16) part[w][q] = acc;
+  __syncthreads();
+  if (tid < 16) {
+    float4 s = part[0][tid];
+#pragma unroll
+    for (int i = 1; i < kNW; ++i) {
+      const float4 o = part[i][tid];
+      s.x += o.x; s.y += o.y; s.z += o.z; s.w += o.w;
+    }
+    if (a.D) {
+      const float Dh = a.D[h];
+      const float4 xq = unpack4(*reinterpret_cast<const uint2*>(a.x + bh * kDim + 4 * tid));
+      s.x = fmaf(Dh, xq.x, s.x);
+      s.y = fmaf(Dh, xq.y, s.y);
+      s.z = fmaf(Dh, xq.z, s.z);
+      s.w = fmaf(Dh, xq.w, s.w);
+    }
+    store_y4_ptr<Out>(static_cast<Out*>(a.y) + bh * kDim + 4 * tid, s);
+  }
 }
 
 }  // namespace
 
-int launch_ssd_fwd(const ss_ssd_desc_t& d, const void* x, const void* dt, const float* A,
-                   const void* Bm, const void* Cm, const float* D, const float* dt_bias, void* y,
-                   void* stream) {
-  SsdArgs a{static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(dt), A,
-            static_cast<const uint16_t*>(Bm), static_cast<const uint16_t*>(Cm), D, dt_bias, y,
-            d.seqlen, int(d.nheads), int(d.ngroups)};
+int launch_ssd_step(const ss_ssd_desc_t& d, float* h, const void* x, const void* dt,
+                    const float* A, const void* Bm, const void* Cm, const float* D,
+                    const float* dt_bias, void* y, void* stream) {
+  SsdStepArgs a{h, static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(dt), A,
+                static_cast<const uint16_t*>(Bm), static_cast<const uint16_t*>(Cm), D, dt_bias, y,
+                int(d.nheads), int(d.ngroups)};
   hipStream_t st = static_cast<hipStream_t>(stream);
   const dim3 grid(unsigned(d.batch * d.nheads)), block(kThreads);
   const bool f32 = d.out_dtype == SS_F32, sp = d.dt_softplus != 0;
-  if (f32 && sp) hipLaunchKernelGGL((ssd_fwd_kernel<float, true>), grid, block, 0, st, a);
-  else if (f32) hipLaunchKernelGGL((ssd_fwd_kernel<float, false>), grid, block, 0, st, a);
-  else if (sp) hipLaunchKernelGGL((ssd_fwd_kernel<uint16_t, true>), grid, block, 0, st, a);
-  else hipLaunchKernelGGL((ssd_fwd_kernel<uint16_t, false>), grid, block, 0, st, a);
+  if (f32 && sp) hipLaunchKernelGGL((ssd_step_kernel<float, true>), grid, block, 0, st, a);
+  else if (f32) hipLaunchKernelGGL((ssd_step_kernel<float, false>), grid, block, 0, st, a);
+  else if (sp) hipLaunchKernelGGL((ssd_step_kernel<uint16_t, true>), grid, block, 0, st, a);
+  else hipLaunchKernelGGL((ssd_step_kernel<uint16_t, false>), grid, block, 0, st, a);
+  return int(hipGetLastError());
+}
+
+int launch_ssd_fwd(const ss_ssd_desc_t& d, const void* x, const void* dt, const float* A,
+                   const void* Bm, const void* Cm, const float* D, const float* dt_bias,
+                   const float* h0, void* y, float* h_last, void* stream) {
+  SsdArgs a{static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(dt), A,
+            static_cast<const uint16_t*>(Bm), static_cast<const uint16_t*>(Cm), D, dt_bias, y,
+            h0, h_last, d.seqlen, int(d.nheads), int(d.ngroups)};
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const dim3 grid(unsigned(d.batch * d.nheads)), block(kThreads);
+  const bool f32 = d.out_dtype == SS_F32, sp = d.dt_softplus != 0;
+  if (h0 || h_last) {
+    if (f32 && sp) hipLaunchKernelGGL((ssd_fwd_kernel<float, true, true>), grid, block, 0, st, a);
+    else if (f32) hipLaunchKernelGGL((ssd_fwd_kernel<float, false, true>), grid, block, 0, st, a);
+    else if (sp) hipLaunchKernelGGL((ssd_fwd_kernel<uint16_t, true, true>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((ssd_fwd_kernel<uint16_t, false, true>), grid, block, 0, st, a);
+  } else {
+    if (f32 && sp) hipLaunchKernelGGL((ssd_fwd_kernel<float, true, false>), grid, block, 0, st, a);
+    else if (f32) hipLaunchKernelGGL((ssd_fwd_kernel<float, false, false>), grid, block, 0, st, a);
+    else if (sp) hipLaunchKernelGGL((ssd_fwd_kernel<uint16_t, true, false>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((ssd_fwd_kernel<uint16_t, false, false>), grid, block, 0, st, a);
+  }
   return int(hipGetLastError());
 }
 

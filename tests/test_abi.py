@@ -35,7 +35,8 @@ def test_header_declares_entry_points():
     names = declared_functions()
     for n in ("ss_scan_fwd", "ss_scan_bwd", "ss_scan_step", "ss_scan_workspace_bytes",
               "ss_scan_strerror", "ss_scan_version", "ss_conv1d_fwd", "ss_conv1d_bwd",
-              "ss_conv1d_step", "ss_conv1d_workspace_bytes", "ss_ssd_fwd", "ss_scan_fwd_dir", "ss_scan_fwd_complex"):
+              "ss_conv1d_step", "ss_conv1d_workspace_bytes", "ss_ssd_fwd", "ss_ssd_fwd_state",
+              "ss_ssd_step", "ss_scan_fwd_dir", "ss_scan_fwd_complex"):
         assert n in names
 
 
@@ -203,6 +204,64 @@ def test_ssd_validation(lib):
     assert ssd(ok, D=FAKE + 2) == B.SS_ERR_INVALID_ARG           # misaligned
     assert ssd(ok, y=FAKE + 20488) == B.SS_ERR_INVALID_ARG
     assert B.load_library().ss_ssd_fwd(None, *([None] * 8), None) == B.SS_ERR_INVALID_ARG
+
+
+def ssd_state(desc, **kw):
+    P = FAKE
+    args = dict(x=P, dt=P + 4096, A=P + 8192, Bm=P + 12288, Cm=P + 16384, D=None, dt_bias=None,
+                h0=P + 24576, y=P + 20480, h_last=P + 28672)
+    args.update(kw)
+    return B.ss_ssd_fwd_state(desc, args["x"], args["dt"], args["A"], args["Bm"], args["Cm"],
+                              args["D"], args["dt_bias"], args["h0"], args["y"], args["h_last"],
+                              stream=0)
+
+
+def test_ssd_state_validation(lib):
+    # the description and the plain forward's pointer rules are shared
+    for bad in (sdesc(seqlen=0), sdesc(ngroups=3)):
+        assert ssd_state(bad) == B.SS_ERR_INVALID_ARG
+    assert ssd_state(sdesc(headdim=32)) == B.SS_ERR_UNSUPPORTED
+    ok = sdesc()
+    for name in ("x", "dt", "A", "Bm", "Cm", "y"):
+        assert ssd_state(ok, **{name: None}) == B.SS_ERR_INVALID_ARG, name
+    # the states are optional
+    for name in ("h0", "h_last"):
+        assert ssd_state(ok, **{name: FAKE + 4}) == B.SS_ERR_INVALID_ARG, name   # misaligned
+    # h_last may be h0 but no other argument; h0 may not be y
+    for other in ("x", "dt", "A", "Bm", "Cm", "y"):
+        target = {"x": FAKE, "dt": FAKE + 4096, "A": FAKE + 8192, "Bm": FAKE + 12288,
+                  "Cm": FAKE + 16384, "y": FAKE + 20480}[other]
+        assert ssd_state(ok, h_last=target) == B.SS_ERR_INVALID_ARG, other
+    assert ssd_state(ok, D=FAKE + 32768, h_last=FAKE + 32768) == B.SS_ERR_INVALID_ARG
+    assert ssd_state(ok, h0=FAKE + 20480) == B.SS_ERR_INVALID_ARG
+    assert B.load_library().ss_ssd_fwd_state(None, *([None] * 10), None) == B.SS_ERR_INVALID_ARG
+
+
+def ssd_step(desc, **kw):
+    P = FAKE
+    args = dict(h=P + 24576, x=P, dt=P + 4096, A=P + 8192, Bm=P + 12288, Cm=P + 16384, D=None,
+                dt_bias=None, y=P + 20480)
+    args.update(kw)
+    return B.ss_ssd_step(desc, args["h"], args["x"], args["dt"], args["A"], args["Bm"],
+                         args["Cm"], args["D"], args["dt_bias"], args["y"], stream=0)
+
+
+def test_ssd_step_validation(lib):
+    for bad in (sdesc(batch=0), sdesc(nheads=0), sdesc(ngroups=3), sdesc(batch=1 << 30)):
+        assert ssd_step(bad) == B.SS_ERR_INVALID_ARG
+    d = sdesc()
+    d.reserved = 1
+    assert ssd_step(d) == B.SS_ERR_INVALID_ARG
+    for uns in (sdesc(headdim=32), sdesc(dstate=16), sdesc(in_dtype=B.SS_F32)):
+        assert ssd_step(uns) == B.SS_ERR_UNSUPPORTED
+    ok = sdesc()
+    for name in ("h", "x", "dt", "A", "Bm", "Cm", "y"):
+        assert ssd_step(ok, **{name: None}) == B.SS_ERR_INVALID_ARG, name
+    assert ssd_step(ok, y=FAKE) == B.SS_ERR_INVALID_ARG            # y aliases x
+    assert ssd_step(ok, y=FAKE + 24576) == B.SS_ERR_INVALID_ARG    # y aliases h
+    assert ssd_step(ok, h=FAKE + 8192) == B.SS_ERR_INVALID_ARG     # h aliases A
+    assert ssd_step(ok, dt_bias=FAKE + 8) == B.SS_ERR_INVALID_ARG  # misaligned
+    assert B.load_library().ss_ssd_step(None, *([None] * 9), None) == B.SS_ERR_INVALID_ARG
 
 
 def test_fwd_dir_validation(lib):

@@ -104,3 +104,167 @@ def test_ssd_deterministic():
     y1 = _run(inp)
     y2 = _run(inp)
     assert np.array_equal(y1, y2)
+
+
+# ---------------------------------------------------------------- start state, final state, step
+def _state(Bt, H, seed, scale=1.0):
+    rng = np.random.default_rng(seed)
+    return rng.standard_normal((Bt, H, 64, 64), dtype=np.float32) * np.float32(scale)
+
+
+def _inputs_dev(inp):
+    bf, f32 = torch.bfloat16, torch.float32
+    return dict(x=_dev(inp.x, bf), dt=_dev(inp.dt, bf), A=_dev(inp.A, f32), B=_dev(inp.B, bf),
+                C=_dev(inp.C, bf), D=_dev(inp.D, f32), dt_bias=_dev(inp.dt_bias, f32))
+
+
+def _np(t):
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+STATE_CASES = [
+    # (Bt, L, H, G, seed)
+    (1, 64, 2, 1, 31),      # one full chunk
+    (2, 200, 4, 2, 32),     # ragged tail
+    (1, 1, 3, 1, 33),       # a single step
+    (2, 129, 2, 2, 34),     # two chunks and one step
+]
+
+
+@pytest.mark.parametrize("case", STATE_CASES, ids=lambda c: "b%d_l%d_h%d_g%d" % c[:4])
+def test_ssd_state_in_out(oracle, case):
+    """ss_ssd_fwd_state from a random start state: y and the final state
+    against the oracle on the same bits (state bound as y's)."""
+    Bt, L, H, G, seed = case
+    log("ssd state case", case)
+    inp = make_ssd_inputs(Bt, L, H, 64, 64, G, seed)
+    h0 = _state(Bt, H, seed + 100)
+    d = _inputs_dev(inp)
+    y, hl = B.ssd_fwd(d["x"], d["dt"], d["A"], d["B"], d["C"], D=d["D"], dt_bias=d["dt_bias"],
+                      h0=_dev(h0, torch.float32), return_last=True)
+    torch.cuda.synchronize()
+    ref, ref_h = oracle.ssd_fwd(inp.x, inp.dt, inp.A, inp.B, inp.C, D=inp.D, dt_bias=inp.dt_bias,
+                                h0=h0, return_last=True)
+    _check(_np(y), ref, "ssd state y %s" % (case,))
+    _check(_np(hl), ref_h, "ssd state h_last %s" % (case,))
+
+
+def test_ssd_state_none_matches_plain():
+    """No start state and no final state: the same bits as ss_ssd_fwd; with
+    return_last alone, y is unchanged."""
+    inp = make_ssd_inputs(2, 150, 3, 64, 64, 1, 35)
+    d = _inputs_dev(inp)
+    y0 = B.ssd_fwd(d["x"], d["dt"], d["A"], d["B"], d["C"], D=d["D"], dt_bias=d["dt_bias"])
+    y1, _ = B.ssd_fwd(d["x"], d["dt"], d["A"], d["B"], d["C"], D=d["D"], dt_bias=d["dt_bias"],
+                      return_last=True)
+    torch.cuda.synchronize()
+    assert torch.equal(y0, y1)
+
+
+def test_ssd_prefill_in_pieces(oracle):
+    """A sequence cut into pieces (64-aligned and not), the state advanced in
+    place from piece to piece (h0 and h_last one buffer), equals the oracle's
+    single pass."""
+    Bt, L, H, G, seed = 2, 300, 2, 1, 36
+    log("ssd pieces", (Bt, L, H, G, seed))
+    inp = make_ssd_inputs(Bt, L, H, 64, 64, G, seed)
+    d = _inputs_dev(inp)
+    h = torch.zeros((Bt, H, 64, 64), dtype=torch.float32, device="cuda")
+    ys = []
+    cuts = [0, 64, 101, 230, 300]
+    for t0, t1 in zip(cuts[:-1], cuts[1:]):
+        sl = lambda t: t[:, t0:t1].contiguous()
+        desc = B.make_ssd_desc(Bt, t1 - t0, H, 64, 64, G, B.SS_BF16, B.SS_F32, True)
+        y = torch.empty((Bt, t1 - t0, H, 64), dtype=torch.float32, device="cuda")
+        rc = B.ss_ssd_fwd_state(desc, sl(d["x"]), sl(d["dt"]), d["A"], sl(d["B"]), sl(d["C"]),
+                                d["D"], d["dt_bias"], h, y, h)
+        assert rc == B.SS_OK
+        ys.append(y)
+    torch.cuda.synchronize()
+    y = _np(torch.cat(ys, dim=1))
+    ref, ref_h = oracle.ssd_fwd(inp.x, inp.dt, inp.A, inp.B, inp.C, D=inp.D, dt_bias=inp.dt_bias,
+                                return_last=True)
+    _check(y, ref, "ssd pieces y")
+    _check(_np(h), ref_h, "ssd pieces state")
+
+
+STEP_CASES = [
+    # (Bt, H, G, seed, options)
+    (1, 1, 1, 41, {}),
+    (3, 8, 2, 42, {}),
+    (2, 6, 3, 43, {"with_D": False, "with_bias": False}),
+    (4, 4, 1, 44, {"softplus": False, "with_bias": False}),
+    (2, 4, 1, 45, {"bf16_out": True}),
+]
+
+
+@pytest.mark.parametrize("case", STEP_CASES, ids=lambda c: "b%d_h%d_g%d_s%d" % c[:4])
+def test_ssd_step_parity(oracle, case):
+    """ss_ssd_step on a random state against the oracle's layer over one step
+    from that state."""
+    Bt, H, G, seed, opt = case
+    opt = dict(opt)
+    softplus = opt.pop("softplus", True)
+    bf16_out = opt.pop("bf16_out", False)
+    log("ssd step case", case)
+    inp = make_ssd_inputs(Bt, 1, H, 64, 64, G, seed, **opt)
+    if not softplus:
+        inp.dt = np.abs(inp.dt) * np.float32(0.5)
+    h0 = _state(Bt, H, seed + 100)
+    d = _inputs_dev(inp)
+    h = _dev(h0, torch.float32)
+    y = B.ssd_step(h, d["x"][:, 0].contiguous(), d["dt"][:, 0].contiguous(), d["A"],
+                   d["B"][:, 0].contiguous(), d["C"][:, 0].contiguous(), D=d["D"],
+                   dt_bias=d["dt_bias"], softplus=softplus,
+                   out_dtype=torch.bfloat16 if bf16_out else torch.float32)
+    torch.cuda.synchronize()
+    ref, ref_h = oracle.ssd_fwd(inp.x, inp.dt, inp.A, inp.B, inp.C, D=inp.D, dt_bias=inp.dt_bias,
+                                softplus=softplus, h0=h0, return_last=True)
+    _check(_np(y), ref[:, 0], "ssd step y %s" % (case[:4],), bf16_out)
+    _check(_np(h), ref_h, "ssd step state %s" % (case[:4],))
+
+
+def test_ssd_step_continues_prefill(oracle):
+    """Prefill 100 steps with the chunked kernel, keep the state, decode 5 more
+    steps one at a time: y of every step and the final state against the
+    oracle's single pass over all 105."""
+    Bt, L, H, G, seed, k = 2, 105, 4, 2, 46, 5
+    log("ssd prefill + decode", (Bt, L, H, G, seed, k))
+    inp = make_ssd_inputs(Bt, L, H, 64, 64, G, seed)
+    d = _inputs_dev(inp)
+    pre = slice(0, L - k)
+    y_pre, h = B.ssd_fwd(*(d[n][:, pre].contiguous() for n in ("x", "dt")), d["A"],
+                         *(d[n][:, pre].contiguous() for n in ("B", "C")), D=d["D"],
+                         dt_bias=d["dt_bias"], return_last=True)
+    ys = [y_pre]
+    for t in range(L - k, L):
+        ys.append(B.ssd_step(h, d["x"][:, t].contiguous(), d["dt"][:, t].contiguous(), d["A"],
+                             d["B"][:, t].contiguous(), d["C"][:, t].contiguous(), D=d["D"],
+                             dt_bias=d["dt_bias"])[:, None])
+    torch.cuda.synchronize()
+    ref, ref_h = oracle.ssd_fwd(inp.x, inp.dt, inp.A, inp.B, inp.C, D=inp.D, dt_bias=inp.dt_bias,
+                                return_last=True)
+    _check(_np(torch.cat(ys, dim=1)), ref, "ssd prefill + decode y")
+    _check(_np(h), ref_h, "ssd prefill + decode state")
+
+
+def test_ssd_step_full_size(oracle):
+    """A decode batch at the layer's width (256 rows x 80 heads) in the launch
+    configuration of the step leg of the benchmark; the oracle checks four
+    heads of every row."""
+    Bt, H = 256, 80
+    log("ssd step full size", (Bt, H))
+    inp = make_ssd_inputs(Bt, 1, H, 64, 64, 1, 47)
+    h0 = _state(Bt, H, 147)
+    d = _inputs_dev(inp)
+    h = _dev(h0, torch.float32)
+    y = B.ssd_step(h, d["x"][:, 0].contiguous(), d["dt"][:, 0].contiguous(), d["A"],
+                   d["B"][:, 0].contiguous(), d["C"][:, 0].contiguous(), D=d["D"],
+                   dt_bias=d["dt_bias"])
+    torch.cuda.synchronize()
+    heads = [0, 9, 40, 79]
+    ref, ref_h = oracle.ssd_fwd(inp.x[:, :, heads], inp.dt[:, :, heads], inp.A[heads], inp.B,
+                                inp.C, D=inp.D[heads], dt_bias=inp.dt_bias[heads],
+                                h0=h0[:, heads], return_last=True)
+    _check(_np(y)[:, heads], ref[:, 0], "ssd step full size y")
+    _check(_np(h)[:, heads], ref_h, "ssd step full size state")
