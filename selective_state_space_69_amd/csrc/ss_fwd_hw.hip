@@ -14,10 +14,10 @@
 // workgroups for 256 compute units (two or three per unit, so the slowest
 // units do 20% more than the mean); here 1280 workgroups give exactly five per
 // unit and five waves per SIMD, which also hides more latency.  The work per
-// (b, t, d, n) element is unchanged: one v_exp_f32 and 6 (exact ZOH) or 4
-// (Euler) other vector ops ("A Visual Guide to Mamba" summary, Hardware-aware
-// Algorithm: discretisation, scan and C contraction fused, nothing of size
-// (B, L, D, N) in memory).
+// (b, t, d, n) element: one v_exp_f32 and 4 (Euler) or 5.5 (exact ZOH, with the
+// scaled states below; 6 in the guarded path) other vector ops ("A Visual
+// Guide to Mamba" summary, Hardware-aware Algorithm: discretisation, scan and C
+// contraction fused, nothing of size (B, L, D, N) in memory).
 #include "ss_fwd_common.hpp"
 
 namespace ss {
@@ -42,8 +42,17 @@ template <typename In, typename Out, int DISC, bool HAS_Z, bool SOFTPLUS, bool S
           bool REV>
 struct HalfScan {
   using Raw2 = typename std::conditional<sizeof(In) == 2, uint32_t, uint2>::type;
+  // Exact ZOH outside the guarded path keeps the lane's two states scaled by
+  // A[0]: s = A[0] h.  State 0 then advances as s <- a (s + B u) - B u, one
+  // operation fewer than a h + ((a - 1) / A) B u, state 1 as
+  // s <- a s + (a - 1) (A[0] / A[1]) B u; the partial C s carries the factor
+  // A[0], which the summing lane removes with the 1 / A[0] of the slot that
+  // wrote it (an fma in place of the add).
+  static constexpr bool kScaled = DISC == kZoh && !SAFE;
   const FwdParams& p;
   float A[2], iA[2];
+  float rA1;             // A[0] / A[1] (scaled form)
+  float mo[kOwners];     // per owner slot: 1 / A[0] of the slot's lane if scaled, else 1
   float h[2];
   float Dd, bias2;
   float dsum;
@@ -180,22 +189,23 @@ struct HalfScan {
         const float dtu = d2 * (kLn2 * uk);                       // dt * u
         h[0] = __builtin_fmaf(a0, h[0], dtu * r.x);
         h[1] = __builtin_fmaf(a1, h[1], dtu * r.y);
+      } else if (kScaled) {
+        // scaled states (s = A[0] h)
+        const float bu0 = r.x * uk, bu1 = r.y * uk;
+        const float q1 = __builtin_fmaf(a1, rA1, -rA1);           // (A_bar - 1) A[0] / A[1]
+        h[0] = __builtin_fmaf(a0, h[0] + bu0, -bu0);
+        h[1] = __builtin_fmaf(a1, h[1], q1 * bu1);
       } else {
-        float q0, q1;                                              // (A_bar - 1) / A
-        if (SAFE) {
-          // some |A| < kWeakA in the wave: the series near dt A = 0
-          const float dt = d2 * kLn2;
-          q0 = zoh_coef_guarded(a0, iA[0], dt, d2 * A[0]);
-          q1 = zoh_coef_guarded(a1, iA[1], dt, d2 * A[1]);
-        } else {
-          q0 = __builtin_fmaf(a0, iA[0], -iA[0]);
-          q1 = __builtin_fmaf(a1, iA[1], -iA[1]);
-        }
+        // guarded path (some |A| < kWeakA in the wave): (A_bar - 1) / A with
+        // the series near dt A = 0
+        const float dt = d2 * kLn2;
+        const float q0 = zoh_coef_guarded(a0, iA[0], dt, d2 * A[0]);
+        const float q1 = zoh_coef_guarded(a1, iA[1], dt, d2 * A[1]);
         h[0] = __builtin_fmaf(a0, h[0], q0 * (r.x * uk));
         h[1] = __builtin_fmaf(a1, h[1], q1 * (r.y * uk));
       }
       if (SUMMARY) dsum += d2;
-      else parts[k * kCh] = __builtin_fmaf(r.w, h[1], r.z * h[0]);   // partial C h
+      else parts[k * kCh] = __builtin_fmaf(r.w, h[1], r.z * h[0]);   // partial C h (x A[0] if scaled)
     }
     // activations, step sizes and rows of block t + 8 (slot S^1)
     activations<S ^ 1, GUARD>(t + kBlk);
@@ -205,7 +215,11 @@ struct HalfScan {
     // output of the owned step: the eight owners' partials, skip, gate, store
     float yv = 0.0f;
 #pragma unroll
-    for (int w = 0; w < kOwners; ++w) yv += part[S * kPartF + w * kPartRow + o * kCh + c];
+    for (int w = 0; w < kOwners; ++w) {
+      const float pw = part[S * kPartF + w * kPartRow + o * kCh + c];
+      if (DISC == kZoh) yv = __builtin_fmaf(mo[w], pw, yv);
+      else yv += pw;
+    }
     yv = __builtin_fmaf(Dd, us, yv);                                 // + D skip
     if (HAS_Z) yv *= g;                                              // silu(z) gate
     if (!GUARD || t + o < t1) {
@@ -317,10 +331,23 @@ __global__ __launch_bounds__(kWave * kWaves, 5) void fwd_hw_kernel(FwdParams p) 
     sc.stage = lds + 2 * kActF;
     sc.part = sc.stage + 2 * kStageF;
     sc.stage_w = sc.stage + (fo * kBlk + sc.k_row) * 4;
+    constexpr bool scaled = std::decay_t<decltype(sc)>::kScaled;
+    if (scaled) {
+      sc.rA1 = Av[0] * sc.iA[1];
+      sc.h[0] *= Av[0];
+      sc.h[1] *= Av[0];
+    }
+    if (DISC == kZoh && !SUMMARY) {
+      // owner multipliers through the (not yet used) partial-sum buffer
+      sc.part[o * kPartRow + c] = scaled ? sc.iA[0] : 1.0f;
+      __syncthreads();
+#pragma unroll
+      for (int w = 0; w < kOwners; ++w) sc.mo[w] = sc.part[w * kPartRow + c];
+    }
     sc.run(t0);
     dsum = sc.dsum;
-    hs[0] = sc.h[0];
-    hs[1] = sc.h[1];
+    hs[0] = scaled ? sc.h[0] * sc.iA[0] : sc.h[0];
+    hs[1] = scaled ? sc.h[1] * sc.iA[0] : sc.h[1];
   };
   // exact ZOH takes the guarded coefficient only where some state decays slowly
   // (|A| < kWeakA, A == 0 included; decided per wave, every wave still passes
