@@ -5,8 +5,10 @@
 // exchanged through LDS once per block), with a different lane mapping: a
 // workgroup covers 32 channels and all 16 states with 4 waves; lane l of wave
 // w serves channel l % 32 and the two states n = 2o, 2o + 1 of its owner slot
-// o = 2w + l / 32.  Each lane owns one step of every block (step o): it computes
-// that step's softplus and gate, sums the eight owners' partials and stores y.
+// o = 2w + l / 32.  Each lane owns one step of every block (step o): it loads
+// that step's delta, z and u, computes its softplus and gate, publishes the
+// step size and u (fp32) to the other lanes of its channel through LDS, and
+// later sums the eight owners' partials and stores y.
 //
 // Why: with two states per lane a problem has twice as many workgroups and
 // four times as many waves as with 64 channels and four states per lane.  On
@@ -27,12 +29,12 @@ constexpr int kCh = 32;        // channels per workgroup
 constexpr int kOwners = 8;     // 4 waves x 2 halves, each with 2 states
 constexpr int kWaves = 4;
 // LDS (floats), all double-buffered by block parity:
-//   act   [2][8 steps][32 ch]                step sizes (log2 units)
+//   act   [2][8 steps][32 ch] x 2            step size (log2 units) and u
 //   stage [2][8 owners][8 steps][4]          B[2o], B[2o+1], C[2o], C[2o+1]
 //   part  [2][8 owners][8 steps + 1][32 ch]  partial sums of C h (the padding
 //                                            row puts the two halves of a wave
 //                                            on different banks)
-constexpr int kActF = kBlk * kCh;
+constexpr int kActF = kBlk * kCh * 2;
 constexpr int kStageF = kOwners * kBlk * 4;
 constexpr int kPartRow = (kBlk + 1) * kCh;
 constexpr int kPartF = kOwners * kPartRow;
@@ -78,36 +80,27 @@ struct HalfScan {
   float* part;
   float* stage_w;        // where this lane writes its staged pair (buffer 0)
   // two-deep prefetch ring, slot = block parity (as in ss_fwd.hip)
-  In ur[2][kBlk];
   In dr[2], zr[2], uo[2];
   Raw2 rb[2], rc[2];     // B and C pairs of the lane's fetch slot
   float dl_own, g_own, u_own;
 
-  // prefetch of block t into ring slot S: u of every step, delta, z and u of
-  // the owned step, this lane's B/C pair.  The u loads can be issued one step
-  // at a time (load_u) so that each reuses the register its predecessor in
-  // the slot has just released.
+  // prefetch of block t into ring slot S: delta, z and u of the owned step,
+  // this lane's B/C pair.  Every lane reads u of the other steps from LDS,
+  // where the step's owner publishes it (in fp32) with the step size.
   template <typename T>
   __device__ __forceinline__ Rsrc at(const T* base, int32_t t) const {
     return make_rsrc(base + int64_t(td.blk(t)) * td.ts);
   }
-  __device__ __forceinline__ Rsrc u_rsrc(int32_t t) const { return at(ub, t); }
   template <int S>
-  __device__ __forceinline__ void load_u(const Rsrc& ru, int k, int32_t lim, bool clamp) {
-    int32_t tt = k;
-    if (clamp) tt = tt < lim ? tt : lim;
-    ur[S][k] = buf_load<In>(ru, vin, td.pos(tt) * rowb_in);
-  }
-  template <int S>
-  __device__ __forceinline__ void load_rest(int32_t t, bool clamp) {
-    const Rsrc ru = u_rsrc(t), rd = at(db, t);
+  __device__ __forceinline__ void load_ring(int32_t t, bool clamp) {
+    const Rsrc ru = at(ub, t), rd = at(db, t);
     const Rsrc rz = at(HAS_Z ? zb : ub, t);
     const int32_t lim = tlast - t;
     uint32_t vo = vown;
     if (clamp) vo = vin + td.pos(o < lim ? o : lim) * rowb_in;
     dr[S] = buf_load<In>(rd, vo, 0);
     if (HAS_Z && !SUMMARY) zr[S] = buf_load<In>(rz, vo, 0);
-    if (!SUMMARY) uo[S] = buf_load<In>(ru, vo, 0);
+    uo[S] = buf_load<In>(ru, vo, 0);
     // B/C pair: step k_row of the block, states 2 * (owner) .. + 1
     const int64_t rw = td.row(bidx, p.L, t);
     const Rsrc rB = make_rsrc(brb + rw * kMaxState);
@@ -117,13 +110,6 @@ struct HalfScan {
                     td.pos(k_row < lim ? k_row : lim) * uint32_t(kMaxState * sizeof(In));
     rb[S] = load_pair(rB, vr);
     if (!SUMMARY) rc[S] = load_pair(rC, vr);
-  }
-  template <int S>
-  __device__ __forceinline__ void load_ring(int32_t t, bool clamp) {
-    const Rsrc ru = u_rsrc(t);
-#pragma unroll
-    for (int k = 0; k < kBlk; ++k) load_u<S>(ru, k, tlast - t, clamp);
-    load_rest<S>(t, clamp);
   }
   __device__ __forceinline__ Raw2 load_pair(Rsrc r, uint32_t vo) {
     if constexpr (sizeof(In) == 2) {
@@ -147,11 +133,12 @@ struct HalfScan {
     if (GUARD && t + o >= t1) x2 = SOFTPLUS ? -__builtin_inff() : 0.0f;
     dl_own = SOFTPLUS ? softplus_log2(x2) : x2;                 // dt * log2 e
     if (HAS_Z && !SUMMARY) g_own = silu(to_f32(zr[S]));
-    if (!SUMMARY) u_own = to_f32(uo[S]);
+    u_own = to_f32(uo[S]);
+    if (GUARD && t + o >= t1) u_own = 0.0f;                     // padded step: inert
   }
   template <int S>
   __device__ __forceinline__ void publish() {
-    act[S * kActF + o * kCh + c] = dl_own;
+    reinterpret_cast<float2*>(act + S * kActF)[o * kCh + c] = make_float2(dl_own, u_own);
     const float2 b2 = unpack_pair(rb[S]);
     const float2 c2 = SUMMARY ? make_float2(0.0f, 0.0f) : unpack_pair(rc[S]);
     *reinterpret_cast<float4*>(stage_w + S * kStageF) = make_float4(b2.x, b2.y, c2.x, c2.y);
@@ -159,31 +146,28 @@ struct HalfScan {
 
   // One block of 8 steps at t, parity S.  On entry the LDS buffer S holds the
   // block's step sizes and rows (behind a barrier) and the owned-step
-  // activations are computed; ring slot S holds the block's u.
+  // activations are computed.
   template <bool GUARD, int S>
   __device__ __forceinline__ void block(int32_t t) {
     const float g = g_own, us = u_own;
-    // prefetch block t + 16 into slot S: owned-step inputs and rows now, u of
-    // step k right after step k has consumed its slot entry
+    // prefetch block t + 16 into slot S: owned-step inputs and rows
     const int32_t tn0 = t + 2 * kBlk;
     const int32_t tn = tn0 < tlast ? tn0 : tlast;
-    load_rest<S>(tn, GUARD);
-    const Rsrc ru = u_rsrc(tn);
+    load_ring<S>(tn, GUARD);
     const float4* rows = reinterpret_cast<const float4*>(stage + S * kStageF + o * kBlk * 4);
-    const float* dls = act + S * kActF + c;
+    const float2* dls = reinterpret_cast<const float2*>(act + S * kActF) + c;   // (dt log2 e, u)
     float* parts = part + S * kPartF + o * kPartRow + c;
     float4 rn = rows[0];
-    float dn = dls[0];
+    float2 dn = dls[0];
 #pragma unroll
     for (int k = 0; k < kBlk; ++k) {
       const float4 r = rn;                         // B[2o], B[2o+1], C[2o], C[2o+1]
-      const float d2 = dn;                         // dt * log2 e
+      const float d2 = dn.x;                       // dt * log2 e
+      const float uk = dn.y;
       if (k + 1 < kBlk) {
         rn = rows[k + 1];
         dn = dls[(k + 1) * kCh];
       }
-      const float uk = to_f32(ur[S][k]);
-      load_u<S>(ru, k, tlast - tn, GUARD);
       const float a0 = hw_exp2(d2 * A[0]), a1 = hw_exp2(d2 * A[1]);   // A_bar = exp(dt A)
       if (DISC == kEuler) {
         const float dtu = d2 * (kLn2 * uk);                       // dt * u
