@@ -44,14 +44,14 @@ struct Chan {
 
 // LDS per workgroup: B/C row staging, per wave 2 buffers x 8 steps x 2*NS floats
 // (= 512 floats for the whole group); with NSPLIT > 1 also the shared step
-// sizes, [2 buffers][8 steps][64 lanes], and the partial outputs, [2 buffers]
-// [NSPLIT waves][8 steps][64 lanes].  Lane is the fastest index, so the 32-bit
-// accesses of a wave hit consecutive banks.
+// sizes and u, [2 buffers][8 steps][64 lanes][2], and the partial outputs,
+// [2 buffers][NSPLIT waves][8 steps][64 lanes].  Lane is the fastest index, so
+// the accesses of a wave hit consecutive banks.
 template <int NSPLIT>
 struct Lds {
   static constexpr int kNS = kMaxState / NSPLIT;
   static constexpr int kStage = 2 * kPrefetch * 2 * kNS;                 // floats per wave
-  static constexpr int kAct = NSPLIT > 1 ? 2 * kWave * kPrefetch : 0;
+  static constexpr int kAct = NSPLIT > 1 ? 2 * kWave * kPrefetch * 2 : 0;
   static constexpr int kPart = NSPLIT > 1 ? 2 * NSPLIT * kWave * kPrefetch : 0;
   static constexpr int kFloats = NSPLIT * kStage + kAct + kPart;
 };
@@ -79,14 +79,17 @@ struct Scan {
   uint32_t rowb_in, rowb_out;
   int32_t t1, tlast;
   float* stage;          // this wave's row staging buffer (2 x 8 x 2*NS floats)
-  float* act;            // shared step sizes (NSPLIT > 1)
+  float* act;            // shared step sizes and u (NSPLIT > 1)
   float* part;           // partial outputs (NSPLIT > 1)
   uint32_t lane;
   int wave, n0;          // wave index in the group, first state of this wave
   // Two-deep prefetch ring, slot = block parity: while block t runs, slot
   // (t / 8) & 1 receives block t + 16 and the other slot holds block t + 8.  A
-  // load thus has a whole block of compute before its value is needed.
-  In ur[2][kPrefetch];                  // u of every step
+  // load thus has a whole block of compute before its value is needed.  With
+  // one wave it holds u of every step; with several, each step's owner loads
+  // its u and publishes it (fp32) with the step size, so no wave loads and
+  // widens the u of the others' steps.
+  In ur[2][kPrefetch];                  // u of every step (NSPLIT == 1)
   In dr[2][OWN], zr[2][OWN], uo[2][OWN];   // delta, z, u of the owned steps
   typename Raw4<In>::type rowq[2];      // this lane's 16 (fp32) or 8 (bf16) bytes of rows
   float dl_own[OWN], g_own[OWN], u_own[OWN];   // step size, gate and u of the owned steps
@@ -120,16 +123,16 @@ struct Scan {
       const uint32_t so = td.pos(tt) * rowb_in;
       dr[S][i] = buf_load<In>(rd, vin, so);
       if (HAS_Z && !SUMMARY) zr[S][i] = buf_load<In>(rz, vin, so);
-      // a second read of u for the owned steps: the ring cannot be indexed by
-      // the (runtime) wave number without leaving registers
-      if (!SUMMARY && NSPLIT > 1) uo[S][i] = buf_load<In>(ru, vin, so);
+      if (NSPLIT > 1) uo[S][i] = buf_load<In>(ru, vin, so);
     }
   }
   template <int S>
   __device__ __forceinline__ void load_ring(int32_t t, bool clamp) {
-    const Rsrc ru = u_rsrc(t);
+    if constexpr (NSPLIT == 1) {
+      const Rsrc ru = u_rsrc(t);
 #pragma unroll
-    for (int k = 0; k < kPrefetch; ++k) load_u<S>(ru, k, tlast - t, clamp);
+      for (int k = 0; k < kPrefetch; ++k) load_u<S>(ru, k, tlast - t, clamp);
+    }
     load_owned<S>(t, clamp);
   }
 
@@ -140,17 +143,21 @@ struct Scan {
 #pragma unroll
     for (int i = 0; i < OWN; ++i) {
       float x2 = __builtin_fmaf(to_f32(dr[S][i]), kLog2e, bias2);  // (delta + bias) log2 e
-      if (t + owned(i) >= t1) x2 = SOFTPLUS ? -__builtin_inff() : 0.0f;
+      const bool pad = t + owned(i) >= t1;
+      if (pad) x2 = SOFTPLUS ? -__builtin_inff() : 0.0f;
       dl_own[i] = SOFTPLUS ? softplus_log2(x2) : x2;               // dt * log2 e
       if (HAS_Z && !SUMMARY) g_own[i] = silu(to_f32(zr[S][i]));
-      if (!SUMMARY) u_own[i] = to_f32(NSPLIT > 1 ? uo[S][i] : ur[S][i]);
+      if constexpr (NSPLIT > 1) u_own[i] = pad ? 0.0f : to_f32(uo[S][i]);   // padded: inert
+      else if (!SUMMARY) u_own[i] = to_f32(ur[S][i]);
     }
   }
   template <int S>
   __device__ __forceinline__ void publish() {
     if (NSPLIT == 1) return;
 #pragma unroll
-    for (int i = 0; i < OWN; ++i) act[(S * kPrefetch + owned(i)) * kWave + lane] = dl_own[i];
+    for (int i = 0; i < OWN; ++i)
+      reinterpret_cast<float2*>(act)[(S * kPrefetch + owned(i)) * kWave + lane] =
+          make_float2(dl_own[i], u_own[i]);
   }
 
   // Rows of block [t, t + 8): per step, NS values of B then NS of C (this wave's
@@ -205,35 +212,38 @@ struct Scan {
       g[i] = g_own[i];
       us[i] = u_own[i];
     }
-    // prefetch block t + 16 into slot S: owned-step inputs and rows now, the u
-    // of step k right after step k has read its slot entry
+    // prefetch block t + 16 into slot S: owned-step inputs and rows now, with
+    // one wave the u of step k right after step k has read its slot entry
     const int32_t tn0 = t + 2 * kPrefetch;
     const int32_t tn = tn0 < tlast ? tn0 : tlast;
     load_owned<S>(tn, GUARD);
     fetch_rows<S>(tn);
     const Rsrc ru = u_rsrc(tn);
     const Rsrc ry = at(yb, t);
-    const float* dls = act + S * kPrefetch * kWave + lane;
+    const float2* dls = reinterpret_cast<const float2*>(act) + S * kPrefetch * kWave + lane;
     float* parts = part + (S * NSPLIT + wave) * kPrefetch * kWave + lane;
     // the recurrence, one step at a time (rows and step sizes read one step ahead)
     float Bn[NS], Cn[NS];
     read_rows<S>(0, Bn, Cn);
-    float dn;
-    if constexpr (NSPLIT == 1) dn = dl_own[0];
+    float2 dn;   // (dt log2 e, u) of the next step
+    if constexpr (NSPLIT == 1) dn = make_float2(dl_own[0], 0.0f);
     else dn = dls[0];
 #pragma unroll
     for (int k = 0; k < kPrefetch; ++k) {
       float Bv[NS], Cv[NS];
 #pragma unroll
       for (int n = 0; n < NS; ++n) { Bv[n] = Bn[n]; Cv[n] = Cn[n]; }
-      const float d2 = dn;
+      const float d2 = dn.x;
+      float uk = dn.y;
       if (k + 1 < kPrefetch) {
         read_rows<S>(k + 1, Bn, Cn);
-        if constexpr (NSPLIT == 1) dn = dl_own[k + 1];
+        if constexpr (NSPLIT == 1) dn = make_float2(dl_own[k + 1], 0.0f);
         else dn = dls[(k + 1) * kWave];
       }
-      const float uk = to_f32(ur[S][k]);
-      load_u<S>(ru, k, tlast - tn, GUARD);
+      if constexpr (NSPLIT == 1) {
+        uk = to_f32(ur[S][k]);
+        load_u<S>(ru, k, tlast - tn, GUARD);
+      }
       float acc0 = 0.0f, acc1 = 0.0f;   // two chains when a wave holds many states
       constexpr bool kTwo = NS > 4;
       if (DISC == kEuler) {
