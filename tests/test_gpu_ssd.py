@@ -123,30 +123,38 @@ def _np(t):
 
 
 STATE_CASES = [
-    # (Bt, L, H, G, seed)
-    (1, 64, 2, 1, 31),      # one full chunk
-    (2, 200, 4, 2, 32),     # ragged tail
-    (1, 1, 3, 1, 33),       # a single step
-    (2, 129, 2, 2, 34),     # two chunks and one step
+    # (Bt, L, H, G, seed, options)
+    (1, 64, 2, 1, 31, {}),       # one full chunk
+    (2, 200, 4, 2, 32, {}),      # ragged tail
+    (1, 1, 3, 1, 33, {}),        # a single step
+    (2, 129, 2, 2, 34, {}),      # two chunks and one step
+    (1, 150, 2, 1, 37, {"softplus": False, "with_bias": False}),
+    (2, 100, 2, 1, 38, {"bf16_out": True}),
 ]
 
 
-@pytest.mark.parametrize("case", STATE_CASES, ids=lambda c: "b%d_l%d_h%d_g%d" % c[:4])
+@pytest.mark.parametrize("case", STATE_CASES, ids=lambda c: "b%d_l%d_h%d_g%d_s%d" % c[:5])
 def test_ssd_state_in_out(oracle, case):
     """ss_ssd_fwd_state from a random start state: y and the final state
     against the oracle on the same bits (state bound as y's)."""
-    Bt, L, H, G, seed = case
+    Bt, L, H, G, seed, opt = case
+    opt = dict(opt)
+    softplus = opt.pop("softplus", True)
+    bf16_out = opt.pop("bf16_out", False)
     log("ssd state case", case)
-    inp = make_ssd_inputs(Bt, L, H, 64, 64, G, seed)
+    inp = make_ssd_inputs(Bt, L, H, 64, 64, G, seed, **opt)
+    if not softplus:
+        inp.dt = np.abs(inp.dt) * np.float32(0.5)
     h0 = _state(Bt, H, seed + 100)
     d = _inputs_dev(inp)
     y, hl = B.ssd_fwd(d["x"], d["dt"], d["A"], d["B"], d["C"], D=d["D"], dt_bias=d["dt_bias"],
+                      softplus=softplus, out_dtype=torch.bfloat16 if bf16_out else torch.float32,
                       h0=_dev(h0, torch.float32), return_last=True)
     torch.cuda.synchronize()
     ref, ref_h = oracle.ssd_fwd(inp.x, inp.dt, inp.A, inp.B, inp.C, D=inp.D, dt_bias=inp.dt_bias,
-                                h0=h0, return_last=True)
-    _check(_np(y), ref, "ssd state y %s" % (case,))
-    _check(_np(hl), ref_h, "ssd state h_last %s" % (case,))
+                                softplus=softplus, h0=h0, return_last=True)
+    _check(_np(y), ref, "ssd state y %s" % (case[:5],), bf16_out)
+    _check(_np(hl), ref_h, "ssd state h_last %s" % (case[:5],))
 
 
 def test_ssd_state_none_matches_plain():
