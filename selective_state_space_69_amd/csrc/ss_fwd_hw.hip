@@ -138,7 +138,9 @@ struct HalfScan {
   }
   template <int S>
   __device__ __forceinline__ void publish() {
-    reinterpret_cast<float2*>(act + S * kActF)[o * kCh + c] = make_float2(dl_own, u_own);
+    // Euler uses u only as dt u = (dt log2 e) (u ln 2): the ln 2 is applied here, once per step
+    reinterpret_cast<float2*>(act + S * kActF)[o * kCh + c] =
+        make_float2(dl_own, DISC == kEuler ? u_own * kLn2 : u_own);
     const float2 b2 = unpack_pair(rb[S]);
     const float2 c2 = SUMMARY ? make_float2(0.0f, 0.0f) : unpack_pair(rc[S]);
     *reinterpret_cast<float4*>(stage_w + S * kStageF) = make_float4(b2.x, b2.y, c2.x, c2.y);
@@ -163,14 +165,14 @@ struct HalfScan {
     for (int k = 0; k < kBlk; ++k) {
       const float4 r = rn;                         // B[2o], B[2o+1], C[2o], C[2o+1]
       const float d2 = dn.x;                       // dt * log2 e
-      const float uk = dn.y;
+      const float uk = dn.y;                       // u (Euler: u ln 2)
       if (k + 1 < kBlk) {
         rn = rows[k + 1];
         dn = dls[(k + 1) * kCh];
       }
       const float a0 = hw_exp2(d2 * A[0]), a1 = hw_exp2(d2 * A[1]);   // A_bar = exp(dt A)
       if (DISC == kEuler) {
-        const float dtu = d2 * (kLn2 * uk);                       // dt * u
+        const float dtu = d2 * uk;                                // dt * u
         h[0] = __builtin_fmaf(a0, h[0], dtu * r.x);
         h[1] = __builtin_fmaf(a1, h[1], dtu * r.y);
       } else if (kScaled) {
