@@ -104,6 +104,8 @@ def make_A(D: int, N: int, mode: str = "s4d_real", rng: np.random.Generator | No
     mixed    : random, with a few exact zeros and small positive entries
     weak     : random, with about half the entries slowly decaying (|A| log-uniform
                in [1e-4, 1e-2]), an exact zero and a tiny positive entry
+    grow     : every |A| >= 0.25, about a quarter of the entries positive in
+               [0.25, 1] (growing states; for short sequences)
     """
     if mode == "s4d_real":
         return np.tile(-np.arange(1, N + 1, dtype=np.float32), (D, 1))
@@ -121,6 +123,10 @@ def make_A(D: int, N: int, mode: str = "s4d_real", rng: np.random.Generator | No
         A[0, 0] = 0.0
         if D > 1:
             A[1, N - 1] = np.float32(1e-3)
+    elif mode == "grow":
+        A = (A - np.float32(0.25)).astype(np.float32)
+        pos = rng.random((D, N)) < 0.25
+        A = np.where(pos, rng.uniform(0.25, 1.0, (D, N)), A).astype(np.float32)
     elif mode != "random":
         raise ValueError(mode)
     return A

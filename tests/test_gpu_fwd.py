@@ -74,6 +74,8 @@ SPLIT_CASES = [
     # slowly decaying states (|A| down to 1e-4): exact ZOH's guarded coefficient
     (2, 150, 150, 16, "zoh", "weak", "f32"), (1, 203, 100, 13, "zoh", "weak", "bf16"),
     (2, 77, 70, 16, "euler", "weak", "f32"),
+    # every |A| >= 0.25 with positive entries: the scaled exact-ZOH states with A[0] > 0
+    (2, 61, 150, 16, "zoh", "grow", "f32"), (1, 77, 100, 16, "zoh", "grow", "bf16"),
 ]
 
 
