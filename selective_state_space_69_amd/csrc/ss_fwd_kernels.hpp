@@ -157,7 +157,7 @@ struct Scan {
 #pragma unroll
     for (int i = 0; i < OWN; ++i)
       reinterpret_cast<float2*>(act)[(S * kPrefetch + owned(i)) * kWave + lane] =
-          make_float2(dl_own[i], u_own[i]);
+          make_float2(dl_own[i], DISC == kEuler ? u_own[i] * kLn2 : u_own[i]);   // Euler: u ln 2
   }
 
   // Rows of block [t, t + 8): per step, NS values of B then NS of C (this wave's
@@ -247,7 +247,7 @@ struct Scan {
       float acc0 = 0.0f, acc1 = 0.0f;   // two chains when a wave holds many states
       constexpr bool kTwo = NS > 4;
       if (DISC == kEuler) {
-        const float dtu = d2 * (kLn2 * uk);                       // dt * u
+        const float dtu = NSPLIT > 1 ? d2 * uk : d2 * (kLn2 * uk);   // dt * u (shared u: u ln 2)
 #pragma unroll
         for (int n = 0; n < NS; ++n) {
           const float a = hw_exp2(d2 * ch.A[n]);                  // A_bar = exp(dt A)
