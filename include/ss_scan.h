@@ -167,6 +167,23 @@ int ss_scan_fwd_complex(const ss_desc_t* desc,
                         void* y, float* h_last, void* stream);
 
 /*
+ * One recurrent step with complex diagonal A (decoding), the single-token form
+ * of ss_scan_fwd_complex: desc->seqlen is not read; desc->dstate = N <= 16
+ * complex states.
+ *   h      : (B, D, N, 2) float32 (re, im), state in / out, advanced in place
+ *   u, delta, z : (B, D) in_dtype (z optional);  A : (D, N, 2) float32
+ *   Bm, Cm : (B, N, 2) in_dtype;  D_skip, delta_bias : (D) float32, optional
+ *   y      : (B, D) out_dtype, 2 Re(sum_n C_n h_n) + D u, gated by silu(z)
+ * The discretisation and its guarded series near dt A = 0 are those of
+ * ss_scan_fwd_complex, so a step continues a scan's h_last.  y must not alias
+ * an input.  Device pointers, 16-byte aligned; asynchronous on `stream`; no
+ * allocation; deterministic.
+ */
+int ss_scan_step_complex(const ss_desc_t* desc, float* h, const void* u, const void* delta,
+                         const float* A, const void* Bm, const void* Cm, const float* D_skip,
+                         const float* delta_bias, const void* z, void* y, void* stream);
+
+/*
  * Backward of ss_scan_fwd with recomputation: the states are rebuilt from the
  * inputs (chunk start states in the workspace, the rest on chip), never read
  * from a stored (B,L,D,N) tensor ("A Visual Guide to Mamba" summary,

@@ -2,13 +2,13 @@
 include/ss_conv.h and include/ss_ssd.h).
 
 The functions named like the C entry points (ss_scan_fwd, ss_scan_fwd_dir,
-ss_scan_fwd_complex, ss_scan_bwd, ss_scan_step, ss_scan_workspace_bytes, ss_scan_strerror, ss_scan_version,
+ss_scan_fwd_complex, ss_scan_bwd, ss_scan_step, ss_scan_step_complex, ss_scan_workspace_bytes, ss_scan_strerror, ss_scan_version,
 ss_conv1d_fwd, ss_conv1d_bwd, ss_conv1d_step, ss_conv1d_workspace_bytes, ss_ssd_fwd,
 ss_ssd_fwd_state, ss_ssd_step) only
 marshal arguments: torch tensors become device pointers, None becomes NULL and
 the stream defaults to torch's current HIP stream.  Every step runs in the HIP
 kernels; there is no fallback.  The convenience wrappers scan_fwd, scan_bwd,
-scan_bidir, scan_fwd_complex, scan_step, conv1d_fwd, conv1d_bwd, conv1d_step, ssd_fwd and ssd_step additionally allocate
+scan_bidir, scan_fwd_complex, scan_step, scan_step_complex, conv1d_fwd, conv1d_bwd, conv1d_step, ssd_fwd and ssd_step additionally allocate
 outputs and workspace with torch.
 """
 from __future__ import annotations
@@ -83,6 +83,8 @@ def load_library():
         lib.ss_scan_bwd.restype = I
         lib.ss_scan_step.argtypes = [D] + [P] * 10 + [P]
         lib.ss_scan_step.restype = I
+        lib.ss_scan_step_complex.argtypes = [D] + [P] * 10 + [P]
+        lib.ss_scan_step_complex.restype = I
         C = ctypes.POINTER(ss_conv_desc_t)
         lib.ss_conv1d_workspace_bytes.argtypes = [C]
         lib.ss_conv1d_workspace_bytes.restype = SZ
@@ -176,6 +178,13 @@ def ss_scan_step(desc, h, u, delta, A, Bm, Cm, D_skip, delta_bias, z, y, stream=
     return load_library().ss_scan_step(ctypes.byref(desc), _p(h), _p(u), _p(delta), _p(A), _p(Bm),
                                        _p(Cm), _p(D_skip), _p(delta_bias), _p(z), _p(y),
                                        _stream(stream))
+
+
+def ss_scan_step_complex(desc, h, u, delta, A, Bm, Cm, D_skip, delta_bias, z, y,
+                         stream=None) -> int:
+    return load_library().ss_scan_step_complex(ctypes.byref(desc), _p(h), _p(u), _p(delta),
+                                               _p(A), _p(Bm), _p(Cm), _p(D_skip),
+                                               _p(delta_bias), _p(z), _p(y), _stream(stream))
 
 
 def make_conv_desc(batch, seqlen, dim, width, in_dtype=SS_F32, out_dtype=SS_F32, silu=True):
@@ -322,6 +331,19 @@ def scan_step(h, u, delta, A, B, C, D=None, delta_bias=None, z=None, disc="zoh",
                      softplus)
     y = torch.empty(u.shape, dtype=out_dtype, device=u.device)
     _check(ss_scan_step(desc, h, u, delta, A, B, C, D, delta_bias, z, y, stream), "ss_scan_step")
+    return y
+
+
+def scan_step_complex(h, u, delta, A, B, C, D=None, delta_bias=None, z=None, disc="zoh",
+                      softplus=True, out_dtype=torch.float32, stream=None):
+    """One step with complex A: h (B,D,N,2) fp32 updated in place, A (D,N,2),
+    B and C (B,N,2); returns y (B,D)."""
+    Bt, Dd = u.shape
+    desc = make_desc(Bt, 1, Dd, A.shape[1], _DTYPE[u.dtype], _DTYPE[out_dtype], _DISC[disc],
+                     softplus)
+    y = torch.empty(u.shape, dtype=out_dtype, device=u.device)
+    _check(ss_scan_step_complex(desc, h, u, delta, A, B, C, D, delta_bias, z, y, stream),
+           "ss_scan_step_complex")
     return y
 
 

@@ -324,6 +324,22 @@ int ss_scan_step(const ss_desc_t* desc, float* h, const void* u, const void* del
   return launch_step(*desc, a, stream) == 0 ? SS_OK : SS_ERR_HIP;
 }
 
+int ss_scan_step_complex(const ss_desc_t* desc, float* h, const void* u, const void* delta,
+                         const float* A, const void* Bm, const void* Cm, const float* D_skip,
+                         const float* delta_bias, const void* z, void* y, void* stream) {
+  int rc = check_desc(desc, false);
+  if (rc != SS_OK) return rc;
+  if (!h || !u || !delta || !A || !Bm || !Cm || !y) return SS_ERR_INVALID_ARG;
+  if (desc->batch * desc->dim > (int64_t(1) << 33)) return SS_ERR_INVALID_ARG;   // 32-bit grid
+  const void* hv = h;
+  if (y == hv || y == u || y == delta || y == Bm || y == Cm || y == z) return SS_ERR_INVALID_ARG;
+  const void* ptrs[] = {h, u, delta, A, Bm, Cm, D_skip, delta_bias, z, y};
+  for (const void* p : ptrs)
+    if (p && !aligned(p, kPtrAlign)) return SS_ERR_INVALID_ARG;
+  StepArgs a{h, u, delta, A, Bm, Cm, D_skip, delta_bias, z, y};
+  return launch_step_complex(*desc, a, stream) == 0 ? SS_OK : SS_ERR_HIP;
+}
+
 size_t ss_conv1d_workspace_bytes(const ss_conv_desc_t* desc) {
   if (check_conv(desc, true) != SS_OK) return 0;
   return plan_conv(*desc).bytes;

@@ -305,7 +305,109 @@ hipError_t dispatch_disc(const CParams& p, int disc, bool has_z, bool sp, dim3 g
                         : dispatch_flags<In, Out, SS_EULER>(p, has_z, sp, grid, st);
 }
 
+// One recurrent step with complex A (decoding): h (B, D, N, 2) in place, y (B, D).
+// kLPC lanes per (b, d), lane q holding states n = kSPL q + j as in the scan,
+// with the same per-state arithmetic (modulus and phase of A_bar, the ZOH
+// coefficient with its series near dt a = 0), so a step continues a scan.  The
+// lanes' partial sums of Re C h meet by butterflies in a fixed order.
+template <typename In, typename Out, int DISC, bool HAS_Z, bool SOFTPLUS>
+__global__ __launch_bounds__(256) void step_complex_kernel(StepArgs a, int64_t BD, int64_t D, int N) {
+  const int64_t gid = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int q = int(gid % kLPC);
+  const int64_t ch = gid / kLPC;
+  const bool live = ch < BD;
+  const int64_t chc = live ? ch : BD - 1;                 // idle lanes still join the butterflies
+  const int64_t b = chc / D, d = chc % D;
+  const float x2 = __builtin_fmaf(to_f32(static_cast<const In*>(a.delta)[chc]), kLog2e,
+                                  (a.bias ? a.bias[d] : 0.0f) * kLog2e);
+  const float dl = SOFTPLUS ? softplus_log2(x2) : x2;     // dt log2 e
+  const float dt = dl * kLn2;
+  const float uk = to_f32(static_cast<const In*>(a.u)[chc]);
+  float acc = 0.0f;
+#pragma unroll
+  for (int j = 0; j < kSPL; ++j) {
+    const int n = kSPL * q + j;
+    if (n >= N) continue;
+    const float ar = a.A[(d * N + n) * 2], ai = a.A[(d * N + n) * 2 + 1];
+    const float m2 = ar * ar + ai * ai;
+    const float iar = m2 == 0.0f ? 0.0f : ar / m2, iai = m2 == 0.0f ? 0.0f : -ai / m2;
+    const float e = hw_exp2(dl * ar);
+    const float ph = __builtin_amdgcn_fractf(dl * (ai * (kLn2 * kInv2Pi)));
+    const float abr = e * __builtin_amdgcn_cosf(ph), abi = e * __builtin_amdgcn_sinf(ph);
+    float cr = dt, ci = 0.0f;                                     // Euler
+    if (DISC == SS_ZOH) {
+      const float mr = abr - 1.0f;
+      cr = mr * iar - abi * iai;
+      ci = __builtin_fmaf(mr, iai, abi * iar);
+      const float xr = dt * ar, xi = dt * ai;
+      float pr = __builtin_fmaf(xr, 1.0f / 24.0f, 1.0f / 6.0f), pi = xi * (1.0f / 24.0f);
+      float tr = __builtin_fmaf(pr, xr, __builtin_fmaf(-pi, xi, 0.5f));
+      pi = __builtin_fmaf(pr, xi, pi * xr);
+      pr = tr;
+      tr = __builtin_fmaf(pr, xr, __builtin_fmaf(-pi, xi, 1.0f));
+      pi = __builtin_fmaf(pr, xi, pi * xr);
+      const bool ser =
+          __builtin_unpredictable(__builtin_fmaf(xr, xr, xi * xi) < kZohSeries * kZohSeries);
+      cr = ser ? dt * tr : cr;
+      ci = ser ? dt * pi : ci;
+    }
+    const typename Pair<In>::raw rb = Pair<In>::load(static_cast<const In*>(a.Bm) + (b * N + n) * 2);
+    const typename Pair<In>::raw rc = Pair<In>::load(static_cast<const In*>(a.Cm) + (b * N + n) * 2);
+    const float2 Bv = Pair<In>::f32(rb), Cv = Pair<In>::f32(rc);
+    const float bur = Bv.x * uk, bui = Bv.y * uk;
+    const float qr = cr * bur - ci * bui, qi = __builtin_fmaf(cr, bui, ci * bur);
+    float* hp = a.h + (chc * N + n) * 2;
+    const float hr = hp[0], hi = hp[1];
+    const float nr = __builtin_fmaf(abr, hr, __builtin_fmaf(-abi, hi, qr));
+    const float ni = __builtin_fmaf(abr, hi, __builtin_fmaf(abi, hr, qi));
+    if (live) {
+      hp[0] = nr;
+      hp[1] = ni;
+    }
+    acc = __builtin_fmaf(Cv.x, nr, __builtin_fmaf(-Cv.y, ni, acc));
+  }
+#pragma unroll
+  for (int m = 1; m < kLPC; m *= 2) acc += __shfl_xor(acc, m);
+  if (q == 0 && live) {
+    float y = __builtin_fmaf(a.Dskip ? a.Dskip[d] : 0.0f, uk, 2.0f * acc);   // conjugate pairs
+    if (HAS_Z) y *= silu(to_f32(static_cast<const In*>(a.z)[chc]));
+    store_out<Out>(static_cast<Out*>(a.y) + chc, y);
+  }
+}
+
+template <typename In, typename Out, int DISC>
+hipError_t step_flags(const StepArgs& s, int64_t BD, int64_t D, int N, bool has_z, bool sp,
+                      hipStream_t st) {
+  const dim3 grid(unsigned((BD * kLPC + 255) / 256)), block(256);
+  if (has_z) {
+    if (sp) hipLaunchKernelGGL((step_complex_kernel<In, Out, DISC, true, true>), grid, block, 0, st, s, BD, D, N);
+    else hipLaunchKernelGGL((step_complex_kernel<In, Out, DISC, true, false>), grid, block, 0, st, s, BD, D, N);
+  } else {
+    if (sp) hipLaunchKernelGGL((step_complex_kernel<In, Out, DISC, false, true>), grid, block, 0, st, s, BD, D, N);
+    else hipLaunchKernelGGL((step_complex_kernel<In, Out, DISC, false, false>), grid, block, 0, st, s, BD, D, N);
+  }
+  return hipGetLastError();
+}
+
+template <typename In, typename Out>
+hipError_t step_disc(const StepArgs& s, const ss_desc_t& d, hipStream_t st) {
+  const int64_t BD = d.batch * d.dim;
+  const bool has_z = s.z != nullptr, sp = d.delta_softplus != 0;
+  return d.disc == SS_ZOH ? step_flags<In, Out, SS_ZOH>(s, BD, d.dim, int(d.dstate), has_z, sp, st)
+                          : step_flags<In, Out, SS_EULER>(s, BD, d.dim, int(d.dstate), has_z, sp, st);
+}
+
 }  // namespace
+
+int launch_step_complex(const ss_desc_t& d, const StepArgs& s, void* stream) {
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (d.in_dtype == SS_BF16)
+    e = d.out_dtype == SS_F32 ? step_disc<uint16_t, float>(s, d, st) : step_disc<uint16_t, uint16_t>(s, d, st);
+  else
+    e = d.out_dtype == SS_F32 ? step_disc<float, float>(s, d, st) : step_disc<float, uint16_t>(s, d, st);
+  return int(e);
+}
 
 int launch_fwd_complex(const ss_desc_t& d, const void* u, const void* delta, const float* A,
                        const void* Bm, const void* Cm, const float* Dskip, const float* bias,

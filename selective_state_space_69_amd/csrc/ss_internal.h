@@ -155,6 +155,8 @@ int launch_step(const ss_desc_t& d, const StepArgs& a, void* stream);
 int launch_fwd_complex(const ss_desc_t& d, const void* u, const void* delta, const float* A,
                        const void* Bm, const void* Cm, const float* Dskip, const float* bias,
                        const void* z, const float* h0, void* y, float* h_last, void* stream);
+// Complex-A decode step (ss_complex.hip): h (B,D,N,2) in place, A (D,N,2), B, C (B,N,2).
+int launch_step_complex(const ss_desc_t& d, const StepArgs& a, void* stream);
 // SSD (Mamba-2) forward (ss_ssd.hip): one workgroup per (batch row, head);
 // h0 / h_last (B, H, N, P) may be null and may be the same buffer.
 int launch_ssd_fwd(const ss_ssd_desc_t& d, const void* x, const void* dt, const float* A,

@@ -36,7 +36,7 @@ def test_header_declares_entry_points():
     for n in ("ss_scan_fwd", "ss_scan_bwd", "ss_scan_step", "ss_scan_workspace_bytes",
               "ss_scan_strerror", "ss_scan_version", "ss_conv1d_fwd", "ss_conv1d_bwd",
               "ss_conv1d_step", "ss_conv1d_workspace_bytes", "ss_ssd_fwd", "ss_ssd_fwd_state",
-              "ss_ssd_step", "ss_scan_fwd_dir", "ss_scan_fwd_complex"):
+              "ss_ssd_step", "ss_scan_fwd_dir", "ss_scan_fwd_complex", "ss_scan_step_complex"):
         assert n in names
 
 
@@ -284,3 +284,19 @@ def test_fwd_complex_validation(lib):
     assert B.ss_scan_fwd_complex(ok, *args(u=None), stream=0) == B.SS_ERR_INVALID_ARG
     assert B.ss_scan_fwd_complex(ok, *args(A=P + 4), stream=0) == B.SS_ERR_INVALID_ARG
     assert B.ss_scan_fwd_complex(ok, *args(h0=P + 8192, hl=P + 8192), stream=0) == B.SS_ERR_INVALID_ARG
+
+
+def test_step_complex_validation(lib):
+    P = FAKE
+    d = B.make_desc(2, 1, 64, 16, B.SS_BF16, B.SS_F32)
+    call = lambda desc, **kw: B.ss_scan_step_complex(  # noqa: E731
+        desc, kw.get("h", P + 8192), kw.get("u", P), kw.get("delta", P + 256), kw.get("A", P + 512),
+        kw.get("Bm", P + 1024), kw.get("Cm", P + 1536), None, None, kw.get("z", None),
+        kw.get("y", P + 4096), stream=0)
+    for name in ("h", "u", "delta", "A", "Bm", "Cm", "y"):
+        assert call(d, **{name: None}) == B.SS_ERR_INVALID_ARG, name
+    assert call(d, y=P) == B.SS_ERR_INVALID_ARG                   # y aliases u
+    assert call(d, y=P + 8192) == B.SS_ERR_INVALID_ARG            # y aliases h
+    assert call(d, A=P + 516) == B.SS_ERR_INVALID_ARG             # misaligned
+    assert call(B.make_desc(2, 1, 64, 17, B.SS_BF16, B.SS_F32)) == B.SS_ERR_INVALID_ARG   # N > 16
+    assert B.load_library().ss_scan_step_complex(None, *([None] * 10), None) == B.SS_ERR_INVALID_ARG

@@ -112,3 +112,57 @@ def test_complex_deterministic():
     y2 = _gpu(d, "zoh", last=False)
     torch.cuda.synchronize()
     assert torch.equal(y1, y2)
+
+
+# ---------------------------------------------------------------- decode step
+STEP_CASES = [
+    # (B, D, N, disc, a_mode, dtype)
+    (3, 100, 16, "zoh", "s4d_lin", "f32"),
+    (2, 70, 5, "zoh", "mixed", "f32"),
+    (2, 64, 16, "euler", "random", "bf16"),
+    (1, 33, 9, "zoh", "weak", "bf16"),
+]
+
+
+@pytest.mark.parametrize("case", STEP_CASES, ids=lambda c: "b%d_d%d_n%d_%s_%s_%s" % c)
+def test_complex_step_parity(oracle, case):
+    """ss_scan_step_complex from a random state against the oracle's complex
+    scan over one step from that state: y and the new state."""
+    Bt, D, N, disc, amode, dt = case
+    log("complex step case", case)
+    inp = synth.make_complex_inputs(Bt, 1, D, N, seed=3200 + STEP_CASES.index(case), dtype=dt,
+                                    a_mode=amode, with_h0=True)
+    d = _up(inp)
+    h = d["h0"].clone()
+    y = B.scan_step_complex(h, d["u"][:, 0].contiguous(), d["delta"][:, 0].contiguous(), d["A"],
+                            d["B"][:, 0].contiguous(), d["C"][:, 0].contiguous(), D=d["D"],
+                            delta_bias=d["delta_bias"], z=d["z"][:, 0].contiguous(), disc=disc)
+    torch.cuda.synchronize()
+    ref, href = _ref(oracle, inp, disc)
+    check_f32(y.cpu().numpy(), ref[:, 0], "complex step y")
+    hc = h.cpu().numpy().astype(np.float64)
+    check_f32(hc[..., 0], href.real, "complex step h re")
+    check_f32(hc[..., 1], href.imag, "complex step h im")
+
+
+def test_complex_step_continues_scan(oracle):
+    """A scan over 60 steps keeping h_last, then 4 decode steps: y of every
+    step and the final state against the oracle's scan over all 64."""
+    Bt, L, D, N, k = 2, 64, 96, 16, 4
+    inp = synth.make_complex_inputs(Bt, L, D, N, seed=3250, dtype="bf16", with_h0=True)
+    d = _up(inp)
+    pre = {n: (d[n][:, :L - k].contiguous() if n in ("u", "delta", "B", "C", "z") else d[n])
+           for n in d}
+    y0, h = _gpu(pre, "zoh")
+    ys = [y0]
+    for t in range(L - k, L):
+        ys.append(B.scan_step_complex(h, d["u"][:, t].contiguous(), d["delta"][:, t].contiguous(),
+                                      d["A"], d["B"][:, t].contiguous(), d["C"][:, t].contiguous(),
+                                      D=d["D"], delta_bias=d["delta_bias"],
+                                      z=d["z"][:, t].contiguous())[:, None])
+    torch.cuda.synchronize()
+    ref, href = _ref(oracle, inp, "zoh")
+    check_f32(torch.cat(ys, dim=1).cpu().numpy(), ref, "complex scan + steps y")
+    hc = h.cpu().numpy().astype(np.float64)
+    check_f32(hc[..., 0], href.real, "complex scan + steps h re")
+    check_f32(hc[..., 1], href.imag, "complex scan + steps h im")
