@@ -168,6 +168,43 @@ def make_inputs(B: int, L: int, D: int, N: int, seed: int, dtype: str = "f32",
                             a_mode=a_mode))
 
 
+def make_lti_inputs(B: int, L: int, D: int, N: int, seed: int, dtype: str = "f32",
+                    dt_range=(1e-4, 1e-3), a_range=(0.25, 1.0), a_log: bool = False) -> Inputs:
+    """A time-invariant problem with one-signed input, the hardest case for
+    fp32 state: per channel a constant step (raw delta = 0, the bias the
+    inverse softplus of a step log-uniform in dt_range), B and C rows constant
+    over time (one N(0,1) row per batch row), u = 0.25 + |N(0, 1)| (never
+    negative, so rounding errors do not average out), A = -U(a_range) (or
+    log-uniform in a_range when a_log), D_skip ~ U(0.5, 1.5), no gate.
+    Order of draws: u, B row, C row, U for the step, A, D_skip."""
+    rng = np.random.default_rng(seed)
+    f32 = np.float32
+    u = (0.25 + np.abs(rng.standard_normal((B, L, D)))).astype(f32)
+    Brow = rng.standard_normal((B, 1, N)).astype(f32)
+    Crow = rng.standard_normal((B, 1, N)).astype(f32)
+    U = rng.random(D)
+    lo, hi = a_range
+    if a_log:
+        A = -np.exp(rng.uniform(math.log(lo), math.log(hi), (D, N)))
+    else:
+        A = -rng.uniform(lo, hi, (D, N))
+    A = A.astype(f32)
+    dskip = (0.5 + rng.random(D)).astype(f32)
+    dlo, dhi = dt_range
+    dt = np.exp(math.log(dlo) + U * (math.log(dhi) - math.log(dlo)))
+    bias = (dt + np.log(-np.expm1(-dt))).astype(f32)
+    Bm = np.ascontiguousarray(np.broadcast_to(Brow, (B, L, N)))
+    Cm = np.ascontiguousarray(np.broadcast_to(Crow, (B, L, N)))
+    delta = np.zeros((B, L, D), dtype=f32)
+    if dtype == "bf16":
+        u, Bm, Cm = (round_to_bf16(x) for x in (u, Bm, Cm))
+    elif dtype != "f32":
+        raise ValueError(dtype)
+    return Inputs(u=u, delta=delta, A=A, B=Bm, C=Cm, D=dskip, delta_bias=bias, z=None,
+                  dtype=dtype, meta=dict(B=B, L=L, D=D, N=N, seed=seed, dt_range=tuple(dt_range),
+                                         a_range=tuple(a_range), lti=True))
+
+
 def make_workload(name: str, with_dy: bool | None = None) -> Inputs:
     w = WORKLOADS[name]
     if with_dy is None:

@@ -103,6 +103,24 @@ def test_bwd_many_chunks(oracle, disc):
     log("  worst rel err", {k: "%.2e" % v for k, v in worst.items()})
 
 
+@pytest.mark.parametrize("disc", ["zoh", "euler"])
+@pytest.mark.parametrize("amode", ["random", "weak", "s4d_real"])
+def test_bwd_long_small_steps(oracle, disc, amode):
+    """10,250 fp32 steps with steps of 1e-4 to 1e-2 (long memory), random, weak
+    and S4D-real A: the exact-ZOH derivative of the input coefficient w.r.t. A
+    cancels strongly where |dt A| is small."""
+    seed = 3200 + ["random", "weak", "s4d_real"].index(amode)
+    inp = synth.make_inputs(1, 10250, 64, 16, seed=seed, dtype="f32", with_dy=True,
+                            with_h0=True, a_mode=amode, dt_range=(1e-4, 1e-2))
+    d = upload(inp)
+    log("bwd long small steps", disc, amode)
+    g = run_gpu(d, disc)
+    torch.cuda.synchronize()
+    ref = run_oracle(oracle, inp, disc)
+    worst = compare(g, ref, what="long small steps %s %s" % (disc, amode))
+    log("  worst rel err", {k: "%.2e" % v for k, v in worst.items()})
+
+
 def test_bwd_deterministic():
     inp = synth.make_inputs(2, 300, 200, 16, seed=31, dtype="bf16", with_dy=True)
     d = upload(inp)

@@ -6,7 +6,7 @@ import torch
 
 from selective_state_space_69_amd import binding as B
 from selective_state_space_69_amd import synth
-from gpu_util import TOL_BF16, check_f32, check_rel_max, log, sample_channels
+from gpu_util import TOL_BF16, check_f32, check_rel_max, log, oracle_threads
 
 pytestmark = pytest.mark.gpu
 
@@ -83,25 +83,17 @@ def test_complex_bf16_output(oracle):
     assert np.all(np.abs(got - ref) <= bound), float((np.abs(got - ref) / bound).max())
 
 
-def test_complex_full_size_sampled(oracle):
+def test_complex_full_size(oracle):
     """Mamba-2.8B-shaped layer (B=8, L=2048, D=5120, N=16, bf16) with the S4D-Lin
-    A; sampled channels against the oracle."""
+    A; every element of y against the oracle."""
     Bt, L, D, N = 8, 2048, 5120, 16
     log("complex full size")
     inp = synth.make_complex_inputs(Bt, L, D, N, seed=3120, dtype="bf16")
     y = _gpu(_up(inp), "zoh", last=False)
     torch.cuda.synchronize()
-    assert bool(torch.isfinite(y).all())
-    chans = sample_channels(Bt, D, 16, seed=5)
-    refs = []
-    for b, dd in chans:
-        sl = (slice(b, b + 1), slice(None), slice(dd, dd + 1))
-        r, _ = oracle.fwd_complex(inp.u[sl], inp.delta[sl], inp.A[dd:dd + 1], inp.B[b:b + 1],
-                                  inp.C[b:b + 1], D=inp.D[dd:dd + 1],
-                                  delta_bias=inp.delta_bias[dd:dd + 1], z=inp.z[sl])
-        refs.append(r[0, :, 0])
-    got = np.stack([y[b, :, dd].cpu().numpy() for b, dd in chans])
-    r = check_rel_max(got, np.stack(refs), TOL_BF16, "complex full size")
+    ref, _ = oracle.fwd_complex(inp.u, inp.delta, inp.A, inp.B, inp.C, D=inp.D,
+                                delta_bias=inp.delta_bias, z=inp.z, nthreads=oracle_threads())
+    r = check_rel_max(y.cpu().numpy(), ref, TOL_BF16, "complex full size")
     log("  max err / max|ref| =", r)
 
 

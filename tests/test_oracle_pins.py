@@ -415,3 +415,32 @@ def test_step_bias_recipe(oracle):
     assert dt.min() >= 1e-3 * (1 - 1e-5) and dt.max() <= 1e-1 * (1 + 1e-5)
     hist, _ = np.histogram(np.log(dt), bins=4, range=(math.log(1e-3), math.log(1e-1)))
     assert hist.min() > 0.2 * len(dt)
+
+
+@pytest.mark.parametrize("disc", ["zoh", "euler"])
+def test_backward_dot_product_full_shape(oracle, disc):
+    """P-DOT at the full backward shape (B=8, L=2048, D=1536, N=16: the
+    Mamba-130M layer, on that workload's own bf16-valued inputs and upstream
+    gradient): <g, J v> from two fp64 forwards equals <J^T g, v> from the
+    oracle's backward, for one random direction v in every input at once."""
+    inp = make_inputs(8, 2048, 1536, 16, seed=1004, dtype="bf16", with_dy=True)
+    p = {k: getattr(inp, k) for k in GRAD_INPUTS if getattr(inp, k) is not None}
+    g = inp.dy
+    th = os.cpu_count() or 1
+    grads = oracle.bwd(p["u"], p["delta"], p["A"], p["B"], p["C"], D=p["D"],
+                       delta_bias=p["delta_bias"], z=p["z"], g=g, disc=disc)
+    rng = np.random.default_rng(1005)
+    v = {k: rng.standard_normal(x.shape) for k, x in p.items()}
+    rhs = sum(float(np.sum(grads[GRAD_KEYS[k]] * v[k])) for k in p)
+
+    def loss(sign, eps):
+        q = {k: x + sign * eps * v[k] for k, x in p.items()}
+        out, _ = oracle.fwd(q["u"], q["delta"], q["A"], q["B"], q["C"], D=q["D"],
+                            delta_bias=q["delta_bias"], z=q["z"], disc=disc, nthreads=th)
+        return float(np.sum(g * out))
+
+    eps = 1e-6
+    lhs = (loss(1, eps) - loss(-1, eps)) / (2 * eps)
+    # fp64 cancellation in the difference of two sums of 2.5e7 terms of size ~1:
+    # about 1e-16 * sqrt(2.5e7) * |loss| / eps, far below 1e-7 of |rhs|
+    assert abs(lhs - rhs) <= 1e-7 * max(1.0, abs(rhs)), (lhs, rhs)
