@@ -8,7 +8,10 @@
 // Guide to Mamba" summary, The Scan Operation: segments combined associatively;
 // "A Survey of Mamba" summary, hardware-aware computation: parallel scan), so
 // the start states of all chunks are an inclusive scan of the maps applied to
-// the initial state.
+// the initial state.  The decay is carried as e = a - 1 (precise_expm1): a
+// chunk that barely decays its state keeps it for many chunks, and a rounded
+// near 1 would compound its rounding over all of them.  In that form the
+// composition is (e1, s1) then (e2, s2) = (e1 + e2 + e1 e2, s1 + e2 s1 + s2).
 //
 // Two kernels, chosen by the number of chunks:
 //  - few chunks (< 256): one lane per (b, n, d) walks the chunks in order.
@@ -47,23 +50,23 @@ __device__ __forceinline__ float dpp_or(float old, float src) {
                                                     ROW_MASK, 0xf, false));
 }
 
-// (a, s) of a lane becomes the composition of the maps of lanes 0..lane (lane 0
-// first).  Lanes without a predecessor at a step receive the identity (1, 0).
+// (e, s) of a lane becomes the composition of the maps of lanes 0..lane (lane 0
+// first).  Lanes without a predecessor at a step receive the identity (0, 0).
 template <int CTRL, int ROW_MASK>
-__device__ __forceinline__ void scan_step(float& a, float& s) {
-  const float ap = dpp_or<CTRL, ROW_MASK>(1.0f, a);
+__device__ __forceinline__ void scan_step(float& e, float& s) {
+  const float ep = dpp_or<CTRL, ROW_MASK>(0.0f, e);
   const float sp = dpp_or<CTRL, ROW_MASK>(0.0f, s);
-  s = __builtin_fmaf(a, sp, s);      // earlier (ap, sp) then (a, s)
-  a = ap * a;
+  s = __builtin_fmaf(e, sp, s) + sp;      // earlier (ep, sp) then (e, s)
+  e = __builtin_fmaf(e, ep, e) + ep;
 }
 
-__device__ __forceinline__ void wave_scan(float& a, float& s) {
-  scan_step<kRowShr + 1, 0xf>(a, s);
-  scan_step<kRowShr + 2, 0xf>(a, s);
-  scan_step<kRowShr + 4, 0xf>(a, s);
-  scan_step<kRowShr + 8, 0xf>(a, s);
-  scan_step<kRowBcast15, 0xa>(a, s);
-  scan_step<kRowBcast31, 0xc>(a, s);
+__device__ __forceinline__ void wave_scan(float& e, float& s) {
+  scan_step<kRowShr + 1, 0xf>(e, s);
+  scan_step<kRowShr + 2, 0xf>(e, s);
+  scan_step<kRowShr + 4, 0xf>(e, s);
+  scan_step<kRowShr + 8, 0xf>(e, s);
+  scan_step<kRowBcast15, 0xa>(e, s);
+  scan_step<kRowBcast31, 0xc>(e, s);
 }
 
 // Forward (REVERSE = false): states[b][c] holds chunk c's zero-start end state
@@ -80,7 +83,7 @@ __global__ __launch_bounds__(kWave * kWaves) void chunk_carry_kernel(float* __re
                                                                    const float* __restrict__ h0,
                                                                    int64_t D, int N, int nc,
                                                                    int ndblk) {
-  __shared__ float ta[kTile][kPad], ts[kTile][kPad];
+  __shared__ float ta[kTile][kPad], ts[kTile][kPad];   // decays e = a - 1, states
   __shared__ float lastv[2][kCh];   // a tile's last result, stored after the next tile's
                                     // loads (double-buffered by tile parity)
   const int wave = __builtin_amdgcn_readfirstlane(int(threadIdx.x) / kWave);
@@ -117,15 +120,15 @@ __global__ __launch_bounds__(kWave * kWaves) void chunk_carry_kernel(float* __re
 #pragma unroll
     for (int i = 0; i < kTile / kRows; ++i) {
       const int jl = i * kRows + trow, j = j0 + jl;
-      float a = 1.0f, s = 0.0f;
+      float e = 0.0f, s = 0.0f;
       if (j < npairs) {
         const int c = REVERSE ? nc - 1 - j : j;
         s = st[int64_t(c) * sstride];
         // the last chunk's step sum is never formed: its map multiplies a zero
         // adjoint, so any finite decay will do
-        a = (REVERSE && j == 0) ? 1.0f : hw_exp2(An * ds[int64_t(c) * D]);
+        e = (REVERSE && j == 0) ? 0.0f : precise_expm1(An * ds[int64_t(c) * D]);
       }
-      ta[jl][tch] = a;
+      ta[jl][tch] = e;
       ts[jl][tch] = s;
     }
     __syncthreads();
@@ -133,9 +136,9 @@ __global__ __launch_bounds__(kWave * kWaves) void chunk_carry_kernel(float* __re
 #pragma unroll
     for (int i = 0; i < kChPerWave; ++i) {
       const int ch = wave * kChPerWave + i;
-      float a = ta[lane][ch], s = ts[lane][ch];
-      wave_scan(a, s);
-      const float h = __builtin_fmaf(a, carry[i], s);   // state after pair j0 + lane
+      float e = ta[lane][ch], s = ts[lane][ch];
+      wave_scan(e, s);
+      const float h = carry[i] + __builtin_fmaf(e, carry[i], s);   // state after pair j0 + lane
       ts[lane][ch] = h;
       carry[i] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(h), kTile - 1));
     }
@@ -193,7 +196,7 @@ __global__ __launch_bounds__(256) void chunk_walk_kernel(float* __restrict__ sta
         const int c = c0 + g;
         if (c >= nc - 1) break;
         if (c >= 1) st[int64_t(c) * sstride] = h;
-        h = __builtin_fmaf(hw_exp2(An * dv[g]), h, sv[g]);
+        h += __builtin_fmaf(precise_expm1(An * dv[g]), h, sv[g]);
       }
     }
     st[int64_t(nc - 1) * sstride] = h;
@@ -213,7 +216,7 @@ __global__ __launch_bounds__(256) void chunk_walk_kernel(float* __restrict__ sta
         const int c = c0 - g;
         if (c < 1) break;
         st[int64_t(c) * sstride] = h;
-        h = __builtin_fmaf(hw_exp2(An * dv[g]), h, sv[g]);
+        h += __builtin_fmaf(precise_expm1(An * dv[g]), h, sv[g]);
       }
     }
     st[0] = h;

@@ -83,12 +83,19 @@ template <> __device__ __forceinline__ void buf_store<uint16_t>(Rsrc r, uint32_t
 // Step size in log2 units: softplus(x) * log2(e) = log2(1 + 2^x2) with
 // x2 = x * log2(e), written as max(x2, 0) + log2(1 + 2^-|x2|).  The log of
 // 1 + e is corrected for the rounding of 1 + e (log1p by the Goldberg/Kahan
-// trick log(u) * e / (u - 1)), so small steps keep full relative accuracy.
+// trick log(u) * e / (u - 1)).  Where 1 + e rounds to 1 (e < 2^-24, x below
+// about -16.6) that trick yields 0; there log2(1 + e) = e log2(e) (1 - e/2) to
+// fp32 accuracy.  That expression is a lower bound of log2(1 + e) for every
+// e >= 0 (alternating series), and the Goldberg value is accurate wherever it
+// is not 0, so the larger of the two is right everywhere: small steps keep
+// full relative accuracy down to the smallest normal e, with no select.
 __device__ __forceinline__ float softplus_log2(float x2) {
   const float e = hw_exp2(-__builtin_fabsf(x2));
   const float u1 = 1.0f + e;
   const float dm = __builtin_fmaxf(u1 - 1.0f, 0x1p-100f);
-  return __builtin_fmaxf(x2, 0.0f) + hw_log2(u1) * (e * hw_rcp(dm));
+  const float lo = (e * kLog2e) * __builtin_fmaf(e, -0.5f, 1.0f);
+  const float l1p = __builtin_fmaxf(hw_log2(u1) * (e * hw_rcp(dm)), lo);
+  return __builtin_fmaxf(x2, 0.0f) + l1p;
 }
 
 // Exact-ZOH input coefficient coef = (exp(x) - 1) / A with x = dt A ("Mamba: S4
@@ -109,6 +116,43 @@ __device__ __forceinline__ float zoh_coef_guarded(float abar, float iA, float dt
   // a select, not a branch: the choice varies from lane to lane and step to step
   return __builtin_unpredictable(__builtin_fabsf(x2) < kZohSeries * kLog2e) ? ser : quot;
 }
+// Precise decay.  A state that a step barely decays (|x| = |dt A| small) is
+// remembered for about 1/|x| steps, and A_bar = exp(x) rounded to fp32 is off
+// by up to an ulp near 1 (~6e-8 absolute): that error compounds over the
+// memory to about 6e-8/|x| of the state, which for a constant step and input
+// of one sign leaves the fp32 bound at |x| ~ 1e-4.  The precise form carries
+// the decay as E = exp(x) - 1 instead, h <- h + (E h + coef B u), with E from
+// the series x (1 + x/2 + x^2/6 + x^3/24) where |x| < kZohSeries (truncation
+// below x^4 / 120 relative) and exp2 - 1 elsewhere (there the memory is under
+// 20 steps); the exact-ZOH input coefficient coef = E / A comes from the same
+// series as dt (1 + x/2 + ...), so A == 0 gives coef = dt.  Everything is in
+// the exponential's own argument y2 = x log2 e = d2 A, d2 = dt log2 e:
+// exp(x) - 1 = y2 Q(y2) and coef = d2 Q(y2) with Q(y2) = ln2 P(y2 ln2).
+constexpr float kSeries2 = kZohSeries * kLog2e;
+__device__ __forceinline__ float expm1_factor(float y2) {
+  constexpr float q0 = kLn2, q1 = kLn2 * kLn2 / 2.0f, q2 = kLn2 * kLn2 * kLn2 / 6.0f,
+                  q3 = kLn2 * kLn2 * kLn2 * kLn2 / 24.0f;
+  return __builtin_fmaf(y2, __builtin_fmaf(y2, __builtin_fmaf(y2, q3, q2), q1), q0);
+}
+// E = exp(x) - 1 for y2 = x log2 e, to full relative accuracy
+__device__ __forceinline__ float precise_expm1(float y2) {
+  const float a = hw_exp2(y2);
+  const float ser = y2 * expm1_factor(y2);
+  // a select, not a branch: the choice varies from lane to lane and step to step
+  return __builtin_unpredictable(__builtin_fabsf(y2) < kSeries2) ? ser : a - 1.0f;
+}
+// E (returned) and, for exact ZOH, coef = E / A (with iA = 1 / A, 0 for A == 0)
+template <bool ZOH>
+__device__ __forceinline__ float precise_decay(float d2, float A, float iA, float& coef) {
+  const float y2 = d2 * A;
+  const float a = hw_exp2(y2);
+  const float q = expm1_factor(y2);
+  const bool small = __builtin_unpredictable(__builtin_fabsf(y2) < kSeries2);
+  const float e = small ? y2 * q : a - 1.0f;
+  if (ZOH) coef = small ? d2 * q : e * iA;
+  return e;
+}
+
 // d coef / dA for |x| < kZohSeries: dt^2 (1/2 + x/3 + x^2/8 + x^3/30), the series
 // of (x e^x - e^x + 1) / x^2 (truncation < x^4 / 144)
 __device__ __forceinline__ float zoh_dcoef_series(float dt, float x) {

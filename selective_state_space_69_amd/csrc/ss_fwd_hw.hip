@@ -17,7 +17,7 @@
 // units do 20% more than the mean); here 1280 workgroups give exactly five per
 // unit and five waves per SIMD, which also hides more latency.  The work per
 // (b, t, d, n) element: one v_exp_f32 and 4 (Euler) or 5.5 (exact ZOH, with the
-// scaled states below; 6 in the guarded path) other vector ops ("A Visual
+// scaled states below) other vector ops; about 14 in the precise path ("A Visual
 // Guide to Mamba" summary, Hardware-aware Algorithm: discretisation, scan and C
 // contraction fused, nothing of size (B, L, D, N) in memory).
 #include "ss_fwd_common.hpp"
@@ -40,17 +40,19 @@ constexpr int kPartRow = (kBlk + 1) * kCh;
 constexpr int kPartF = kOwners * kPartRow;
 constexpr int kLdsF = 2 * (kActF + kStageF + kPartF);
 
-template <typename In, typename Out, int DISC, bool HAS_Z, bool SOFTPLUS, bool SUMMARY, bool SAFE,
-          bool REV>
+template <typename In, typename Out, int DISC, bool HAS_Z, bool SOFTPLUS, bool SUMMARY,
+          bool PRECISE, bool REV>
 struct HalfScan {
   using Raw2 = typename std::conditional<sizeof(In) == 2, uint32_t, uint2>::type;
-  // Exact ZOH outside the guarded path keeps the lane's two states scaled by
+  // Exact ZOH outside the precise path keeps the lane's two states scaled by
   // A[0]: s = A[0] h.  State 0 then advances as s <- a (s + B u) - B u, one
   // operation fewer than a h + ((a - 1) / A) B u, state 1 as
   // s <- a s + (a - 1) (A[0] / A[1]) B u; the partial C s carries the factor
   // A[0], which the summing lane removes with the 1 / A[0] of the slot that
-  // wrote it (an fma in place of the add).
-  static constexpr bool kScaled = DISC == kZoh && !SAFE;
+  // wrote it (an fma in place of the add).  The precise path (fp32 inputs, or
+  // a slowly decaying state in the wave) keeps plain states and the decay as
+  // E = A_bar - 1 (precise_decay).
+  static constexpr bool kScaled = DISC == kZoh && !PRECISE;
   const FwdParams& p;
   float A[2], iA[2];
   float rA1;             // A[0] / A[1] (scaled form)
@@ -170,25 +172,28 @@ struct HalfScan {
         rn = rows[k + 1];
         dn = dls[(k + 1) * kCh];
       }
-      const float a0 = hw_exp2(d2 * A[0]), a1 = hw_exp2(d2 * A[1]);   // A_bar = exp(dt A)
-      if (DISC == kEuler) {
-        const float dtu = d2 * uk;                                // dt * u
-        h[0] = __builtin_fmaf(a0, h[0], dtu * r.x);
-        h[1] = __builtin_fmaf(a1, h[1], dtu * r.y);
-      } else if (kScaled) {
-        // scaled states (s = A[0] h)
-        const float bu0 = r.x * uk, bu1 = r.y * uk;
-        const float q1 = __builtin_fmaf(a1, rA1, -rA1);           // (A_bar - 1) A[0] / A[1]
-        h[0] = __builtin_fmaf(a0, h[0] + bu0, -bu0);
-        h[1] = __builtin_fmaf(a1, h[1], q1 * bu1);
+      if (PRECISE) {
+        // h <- h + (E h + coef B u), E = A_bar - 1 and coef to full relative accuracy
+        float q0 = 0.0f, q1 = 0.0f;
+        const float e0 = precise_decay<DISC == kZoh>(d2, A[0], iA[0], q0);
+        const float e1 = precise_decay<DISC == kZoh>(d2, A[1], iA[1], q1);
+        const float in0 = DISC == kEuler ? (d2 * uk) * r.x : q0 * (r.x * uk);   // Euler: dt u B
+        const float in1 = DISC == kEuler ? (d2 * uk) * r.y : q1 * (r.y * uk);
+        h[0] += __builtin_fmaf(e0, h[0], in0);
+        h[1] += __builtin_fmaf(e1, h[1], in1);
       } else {
-        // guarded path (some |A| < kWeakA in the wave): (A_bar - 1) / A with
-        // the series near dt A = 0
-        const float dt = d2 * kLn2;
-        const float q0 = zoh_coef_guarded(a0, iA[0], dt, d2 * A[0]);
-        const float q1 = zoh_coef_guarded(a1, iA[1], dt, d2 * A[1]);
-        h[0] = __builtin_fmaf(a0, h[0], q0 * (r.x * uk));
-        h[1] = __builtin_fmaf(a1, h[1], q1 * (r.y * uk));
+        const float a0 = hw_exp2(d2 * A[0]), a1 = hw_exp2(d2 * A[1]);   // A_bar = exp(dt A)
+        if (DISC == kEuler) {
+          const float dtu = d2 * uk;                                // dt * u
+          h[0] = __builtin_fmaf(a0, h[0], dtu * r.x);
+          h[1] = __builtin_fmaf(a1, h[1], dtu * r.y);
+        } else {
+          // scaled states (s = A[0] h)
+          const float bu0 = r.x * uk, bu1 = r.y * uk;
+          const float q1 = __builtin_fmaf(a1, rA1, -rA1);           // (A_bar - 1) A[0] / A[1]
+          h[0] = __builtin_fmaf(a0, h[0] + bu0, -bu0);
+          h[1] = __builtin_fmaf(a1, h[1], q1 * bu1);
+        }
       }
       if (SUMMARY) dsum += d2;
       else parts[k * kCh] = __builtin_fmaf(r.w, h[1], r.z * h[0]);   // partial C h (x A[0] if scaled)
@@ -325,7 +330,7 @@ __global__ __launch_bounds__(kWave * kWaves, 5) void fwd_hw_kernel(FwdParams p) 
     }
     if (DISC == kZoh && !SUMMARY) {
       // owner multipliers through the (not yet used) partial-sum buffer
-      sc.part[o * kPartRow + c] = scaled ? sc.iA[0] : 1.0f;
+      sc.part[o * kPartRow + c] = scaled ? sc.iA[0] : 1.0f;   // 1 in a precise wave
       __syncthreads();
 #pragma unroll
       for (int w = 0; w < kOwners; ++w) sc.mo[w] = sc.part[w * kPartRow + c];
@@ -335,10 +340,16 @@ __global__ __launch_bounds__(kWave * kWaves, 5) void fwd_hw_kernel(FwdParams p) 
     hs[0] = scaled ? sc.h[0] * sc.iA[0] : sc.h[0];
     hs[1] = scaled ? sc.h[1] * sc.iA[0] : sc.h[1];
   };
-  // exact ZOH takes the guarded coefficient only where some state decays slowly
-  // (|A| < kWeakA, A == 0 included; decided per wave, every wave still passes
-  // the same barriers)
-  if (DISC == kZoh && __any(weak)) {
+  // The precise path: always for fp32 inputs (their bound is elementwise), and
+  // for bf16 inputs where some state of the wave decays slowly (|A| < kWeakA,
+  // A == 0 included; decided per wave, every wave still passes the same
+  // barriers).  bf16 waves whose states all have |A| >= kWeakA run the fast
+  // path: their memory is at most 4 / dt steps, and the decay's rounding stays
+  // far inside the bf16 bound.
+  if constexpr (std::is_same<In, float>::value) {
+    HalfScan<In, Out, DISC, HAS_Z, SOFTPLUS, SUMMARY, true, REV> sc{p};
+    go(sc);
+  } else if (__any(weak)) {
     HalfScan<In, Out, DISC, HAS_Z, SOFTPLUS, SUMMARY, true, REV> sc{p};
     go(sc);
   } else {

@@ -9,7 +9,8 @@
 // Selection), so it is the same for the whole wave: the rows are staged through
 // LDS a block of 8 steps at a time and read back with broadcast loads.  Per
 // element (b, t, d, n) the work is one v_exp_f32 and 4 (Euler) or 6 (exact ZOH)
-// vector ops; the discretised A_bar, B_bar and the states never touch memory
+// vector ops (about 14 with the precise decay of fp32 inputs and slowly
+// decaying states); the discretised A_bar, B_bar and the states never touch memory
 // ("A Visual Guide to Mamba" summary, Hardware-aware Algorithm: discretisation,
 // scan and the C contraction fused in one kernel).  With NSPLIT > 1 the waves'
 // partial sums over n of C h are added through LDS once per 8-step block; the
@@ -59,8 +60,8 @@ struct Lds {
 // Step ownership inside a block of 8 steps: step k belongs to wave k % NSPLIT,
 // which alone computes its softplus step size (shared with the other waves
 // through LDS), its gate, and its final output.
-template <typename In, typename Out, int DISC, bool HAS_Z, bool SOFTPLUS, bool SUMMARY, bool SAFE,
-          int NSPLIT, bool REV>
+template <typename In, typename Out, int DISC, bool HAS_Z, bool SOFTPLUS, bool SUMMARY,
+          bool PRECISE, int NSPLIT, bool REV>
 struct Scan {
   static constexpr int NS = kMaxState / NSPLIT;
   static constexpr int OWN = kPrefetch / NSPLIT;   // steps owned per block
@@ -250,22 +251,32 @@ struct Scan {
         const float dtu = NSPLIT > 1 ? d2 * uk : d2 * (kLn2 * uk);   // dt * u (shared u: u ln 2)
 #pragma unroll
         for (int n = 0; n < NS; ++n) {
-          const float a = hw_exp2(d2 * ch.A[n]);                  // A_bar = exp(dt A)
-          h[n] = __builtin_fmaf(a, h[n], dtu * Bv[n]);            // + dt B u
+          if (PRECISE) {
+            float unused;
+            const float e = precise_decay<false>(d2, ch.A[n], ch.iA[n], unused);   // A_bar - 1
+            h[n] += __builtin_fmaf(e, h[n], dtu * Bv[n]);
+          } else {
+            const float a = hw_exp2(d2 * ch.A[n]);                // A_bar = exp(dt A)
+            h[n] = __builtin_fmaf(a, h[n], dtu * Bv[n]);          // + dt B u
+          }
           if (!SUMMARY) {
             if (kTwo && (n & 1)) acc1 = __builtin_fmaf(Cv[n], h[n], acc1);
             else acc0 = __builtin_fmaf(Cv[n], h[n], acc0);
           }
         }
       } else {
-        const float dt = SAFE ? d2 * kLn2 : 0.0f;
 #pragma unroll
         for (int n = 0; n < NS; ++n) {
-          const float a = hw_exp2(d2 * ch.A[n]);                  // A_bar = exp(dt A)
-          // (A_bar - 1) / A; the guarded form where some |A| < kWeakA
-          const float coef = SAFE ? zoh_coef_guarded(a, ch.iA[n], dt, d2 * ch.A[n])
-                                  : __builtin_fmaf(a, ch.iA[n], -ch.iA[n]);
-          h[n] = __builtin_fmaf(a, h[n], coef * (Bv[n] * uk));
+          if (PRECISE) {
+            // h <- h + (E h + coef B u): E = A_bar - 1, coef = E / A, full relative accuracy
+            float coef;
+            const float e = precise_decay<true>(d2, ch.A[n], ch.iA[n], coef);
+            h[n] += __builtin_fmaf(e, h[n], coef * (Bv[n] * uk));
+          } else {
+            const float a = hw_exp2(d2 * ch.A[n]);                // A_bar = exp(dt A)
+            const float coef = __builtin_fmaf(a, ch.iA[n], -ch.iA[n]);   // (A_bar - 1) / A
+            h[n] = __builtin_fmaf(a, h[n], coef * (Bv[n] * uk));
+          }
           if (!SUMMARY) {
             if (kTwo && (n & 1)) acc1 = __builtin_fmaf(Cv[n], h[n], acc1);
             else acc0 = __builtin_fmaf(Cv[n], h[n], acc0);
@@ -417,10 +428,14 @@ __global__ __launch_bounds__(kWave * NSPLIT, kMinWaves<NSPLIT>) void fwd_kernel(
     return sc.dsum;
   };
   float dsum;
-  // exact ZOH takes the guarded coefficient only where some state decays slowly
+  // The precise decay (precise_decay): always for fp32 inputs, whose bound is
+  // elementwise; for bf16 inputs where some state of the wave decays slowly
   // (|A| < kWeakA, A == 0 included; decided per wave, every wave still passes
-  // the same barriers)
-  if (DISC == kZoh && __any(weak)) {
+  // the same barriers).  Other bf16 waves run the fast path.
+  if constexpr (std::is_same<In, float>::value) {
+    Scan<In, Out, DISC, HAS_Z, SOFTPLUS, SUMMARY, true, NSPLIT, REV> sc{p, ch, h};
+    dsum = setup(sc);
+  } else if (__any(weak)) {
     Scan<In, Out, DISC, HAS_Z, SOFTPLUS, SUMMARY, true, NSPLIT, REV> sc{p, ch, h};
     dsum = setup(sc);
   } else {

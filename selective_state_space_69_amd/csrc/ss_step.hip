@@ -68,15 +68,17 @@ __global__ __launch_bounds__(256) void step_kernel(StepParams p) {
       Cv[j] = in ? to_f32(Cp[j]) : 0.0f;
     }
   }
+  // the precise decay (the step is bound by the state's traffic, so its few
+  // extra operations are free): h <- h + (E h + coef B u), E = A_bar - 1, so a
+  // long decode loop does not compound the rounding of A_bar near 1
   float acc = 0.0f;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const float a = Av[j];
-    const float abar = hw_exp2(dl * a);
     float coef;
+    const float e = precise_decay<true>(dl, a, a == 0.0f ? 0.0f : 1.0f / a, coef);
     if (p.disc == SS_EULER) coef = dt;
-    else coef = zoh_coef_guarded(abar, a == 0.0f ? 0.0f : 1.0f / a, dt, dl * a);
-    hv[j] = __builtin_fmaf(abar, hv[j], coef * (Bv[j] * uf));
+    hv[j] += __builtin_fmaf(e, hv[j], coef * (Bv[j] * uf));
     acc = __builtin_fmaf(Cv[j], hv[j], acc);
   }
   // sum over the quad (lanes 4k .. 4k+3 hold one (b, d))
