@@ -38,9 +38,12 @@
  *     else.  bf16 values are raw IEEE bfloat16 bit patterns (uint16).
  *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = the null
  *     stream).  Kernel faults surface at the next synchronisation.
- *   - All validation happens before any HIP call, so every error code can be
- *     produced without a GPU.  No exception crosses the ABI.  The library never
- *     allocates device memory: scratch comes from the caller's workspace.
+ *   - Argument validation happens before any HIP call, so every validation
+ *     error can be produced without a GPU.  After it, each entry point checks
+ *     that the current device is a gfx950 (SS_ERR_UNSUPPORTED otherwise; the
+ *     answer is cached per device, see ss_scan_arch_supported) and launches.
+ *     No exception crosses the ABI.  The library never allocates device
+ *     memory: scratch comes from the caller's workspace.
  *   - NaN / Inf inputs propagate unchecked.
  *   - The forward, backward and step are deterministic (bitwise repeatable): the
  *     backward's reductions add their partial sums in a fixed order, without atomics.
@@ -58,7 +61,8 @@ extern "C" {
 /* Status codes. */
 #define SS_OK 0
 #define SS_ERR_INVALID_ARG (-1)  /* NULL required pointer, size out of range, aliasing */
-#define SS_ERR_UNSUPPORTED (-2)  /* dtype / discretisation / flag combination not provided */
+#define SS_ERR_UNSUPPORTED (-2)  /* dtype / discretisation / flag combination not provided,
+                                    or the current device is not a gfx950 */
 #define SS_ERR_WORKSPACE (-3)    /* workspace NULL or smaller than ss_scan_workspace_bytes */
 #define SS_ERR_HIP (-4)          /* a HIP launch reported an error */
 
@@ -210,15 +214,27 @@ int ss_scan_bwd(const ss_desc_t* desc,
 /*
  * One recurrent (inference) step for every (b, d): the state h (B,D,N) fp32 is
  * read and overwritten in place; u, delta, z, y are (B,D); Bm, Cm are (B,N).
- * desc->seqlen is ignored.  Optional pointers as in ss_scan_fwd.  The state is
- * O(1) per token, unlike a growing attention cache ("Mamba explained",
- * hackbyte.io, quadratic-bottleneck section).
+ * desc->seqlen is ignored.  Optional pointers as in ss_scan_fwd.  y must not
+ * alias h, u, delta, Bm, Cm or z (SS_ERR_INVALID_ARG): it is written while other
+ * lanes still read them.  batch * dim <= 2^33.  The state is O(1) per token,
+ * unlike a growing attention cache ("Mamba explained", hackbyte.io,
+ * quadratic-bottleneck section).
  */
 int ss_scan_step(const ss_desc_t* desc, float* h,
                  const void* u, const void* delta, const float* A,
                  const void* Bm, const void* Cm,
                  const float* D_skip, const float* delta_bias, const void* z,
                  void* y, void* stream);
+
+/*
+ * Whether the library's kernels run on a device of this architecture:
+ * arch_name is a HIP gcnArchName such as "gfx950:sramecc+:xnack-".  Returns
+ * SS_OK for "gfx950" (with or without ":feature" suffixes), SS_ERR_UNSUPPORTED
+ * for any other name, SS_ERR_INVALID_ARG for NULL.  Pure host function (no
+ * HIP call); every launching entry point applies it to the current device
+ * after its argument checks.
+ */
+int ss_scan_arch_supported(const char* arch_name);
 
 /* Static, human-readable text for a status code. */
 const char* ss_scan_strerror(int status);

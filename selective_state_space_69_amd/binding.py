@@ -104,6 +104,8 @@ def load_library():
         lib.ss_scan_strerror.restype = ctypes.c_char_p
         lib.ss_scan_version.argtypes = []
         lib.ss_scan_version.restype = I
+        lib.ss_scan_arch_supported.argtypes = [ctypes.c_char_p]
+        lib.ss_scan_arch_supported.restype = I
         _lib = lib
     return _lib
 
@@ -133,6 +135,11 @@ def _stream(stream):
 # ---------------------------------------------------------------- C-named entry points
 def ss_scan_version() -> int:
     return load_library().ss_scan_version()
+
+
+def ss_scan_arch_supported(arch_name) -> int:
+    return load_library().ss_scan_arch_supported(
+        None if arch_name is None else arch_name.encode())
 
 
 def ss_scan_strerror(status: int) -> str:

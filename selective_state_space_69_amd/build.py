@@ -23,7 +23,8 @@ BUILD = os.path.join(PKG, "_build")
 # slowest translation units first, so that the parallel build finishes sooner
 SOURCES = ["ss_fwd_bf16_f32.hip", "ss_fwd_bf16_bf16.hip", "ss_fwd_f32_f32.hip",
            "ss_fwd_f32_bf16.hip", "ss_fwd_hw.hip", "ss_bwd.hip", "ss_ssd.hip", "ss_conv.hip",
-           "ss_complex.hip", "ss_step.hip", "ss_carry.hip", "ss_fwd.hip", "ss_api.cpp"]
+           "ss_complex.hip", "ss_step.hip", "ss_carry.hip", "ss_fwd.hip", "ss_runtime.hip",
+           "ss_api.cpp"]
 ARCH = os.environ.get("SS_SCAN_ARCH", "gfx950")
 FLAGS = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=" + ARCH, "-I" + INCLUDE, "-I" + CSRC,
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

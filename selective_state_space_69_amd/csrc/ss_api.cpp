@@ -1,6 +1,8 @@
 // C-ABI entry points of libssscan: argument validation, time planning and
-// workspace layout.  Everything here is plain host logic that runs before any
-// HIP call, so every status code can be produced (and tested) without a GPU.
+// workspace layout.  Validation is plain host logic that runs before any HIP
+// call, so every validation status can be produced (and tested) without a GPU;
+// only then does an entry point ask whether the current device is a gfx950
+// (check_device, cached per device) and launch.
 #include <climits>
 #include <cstdint>
 #include <cstdlib>
@@ -209,11 +211,20 @@ extern "C" {
 
 int ss_scan_version(void) { return 10000; }
 
+int ss_scan_arch_supported(const char* arch_name) {
+  if (!arch_name) return SS_ERR_INVALID_ARG;
+  // "gfx950" alone or followed by target features ("gfx950:sramecc+:xnack-")
+  static const char kArch[] = "gfx950";
+  if (std::strncmp(arch_name, kArch, sizeof(kArch) - 1) != 0) return SS_ERR_UNSUPPORTED;
+  const char next = arch_name[sizeof(kArch) - 1];
+  return (next == '\0' || next == ':') ? SS_OK : SS_ERR_UNSUPPORTED;
+}
+
 const char* ss_scan_strerror(int status) {
   switch (status) {
     case SS_OK: return "ok";
     case SS_ERR_INVALID_ARG: return "invalid argument (null required pointer, size out of range, misaligned pointer or aliasing)";
-    case SS_ERR_UNSUPPORTED: return "unsupported dtype, discretisation or option combination";
+    case SS_ERR_UNSUPPORTED: return "unsupported dtype, discretisation or option combination, or the current device is not a gfx950";
     case SS_ERR_WORKSPACE: return "workspace missing or smaller than ss_scan_workspace_bytes()";
     case SS_ERR_HIP: return "HIP kernel launch failed";
     default: return "unknown status";
@@ -264,6 +275,7 @@ int ss_scan_fwd_dir(const ss_desc_t* desc, int direction, int accumulate, const 
     a.hend = reinterpret_cast<float*>(ws + plan.off_hend);
     a.dsum = reinterpret_cast<float*>(ws + plan.off_dsum);
   }
+  if ((rc = check_device()) != SS_OK) return rc;
   return launch_fwd(*desc, plan, a, stream) == 0 ? SS_OK : SS_ERR_HIP;
 }
 
@@ -279,6 +291,7 @@ int ss_scan_fwd_complex(const ss_desc_t* desc, const void* u, const void* delta,
   const void* ptrs[] = {u, delta, Bm, Cm, z, A, D_skip, delta_bias, h0, h_last, y};
   for (const void* p : ptrs)
     if (p && !aligned(p, kPtrAlign)) return SS_ERR_INVALID_ARG;
+  if ((rc = check_device()) != SS_OK) return rc;
   return launch_fwd_complex(*desc, u, delta, A, Bm, Cm, D_skip, delta_bias, z, h0, y, h_last,
                             stream) == 0
              ? SS_OK
@@ -308,6 +321,7 @@ int ss_scan_bwd(const ss_desc_t* desc, const void* u, const void* delta, const f
   BwdArgs a{u, delta, A, Bm, Cm, D_skip, delta_bias, z, h0, dy,
             static_cast<float*>(du), static_cast<float*>(ddelta), dA, dB, dC, dD_skip,
             ddelta_bias, static_cast<float*>(dz), dh0, static_cast<char*>(workspace)};
+  if ((rc = check_device()) != SS_OK) return rc;
   return launch_bwd(*desc, plan, a, stream) == 0 ? SS_OK : SS_ERR_HIP;
 }
 
@@ -317,10 +331,15 @@ int ss_scan_step(const ss_desc_t* desc, float* h, const void* u, const void* del
   int rc = check_desc(desc, false);
   if (rc != SS_OK) return rc;
   if (!h || !u || !delta || !A || !Bm || !Cm || !y) return SS_ERR_INVALID_ARG;
+  if (desc->batch * desc->dim > (int64_t(1) << 33)) return SS_ERR_INVALID_ARG;   // 32-bit grid
+  // y is written while other lanes still read the state and the inputs
+  const void* hv = h;
+  if (y == hv || y == u || y == delta || y == Bm || y == Cm || y == z) return SS_ERR_INVALID_ARG;
   const void* ptrs[] = {h, u, delta, A, Bm, Cm, D_skip, delta_bias, z, y};
   for (const void* p : ptrs)
     if (p && !aligned(p, kPtrAlign)) return SS_ERR_INVALID_ARG;
   StepArgs a{h, u, delta, A, Bm, Cm, D_skip, delta_bias, z, y};
+  if ((rc = check_device()) != SS_OK) return rc;
   return launch_step(*desc, a, stream) == 0 ? SS_OK : SS_ERR_HIP;
 }
 
@@ -337,6 +356,7 @@ int ss_scan_step_complex(const ss_desc_t* desc, float* h, const void* u, const v
   for (const void* p : ptrs)
     if (p && !aligned(p, kPtrAlign)) return SS_ERR_INVALID_ARG;
   StepArgs a{h, u, delta, A, Bm, Cm, D_skip, delta_bias, z, y};
+  if ((rc = check_device()) != SS_OK) return rc;
   return launch_step_complex(*desc, a, stream) == 0 ? SS_OK : SS_ERR_HIP;
 }
 
@@ -353,6 +373,7 @@ int ss_conv1d_fwd(const ss_conv_desc_t* desc, const void* x, const float* w, con
   const void* ptrs[] = {x, w, bias, u};
   for (const void* p : ptrs)
     if (p && !aligned(p, kPtrAlign)) return SS_ERR_INVALID_ARG;
+  if ((rc = check_device()) != SS_OK) return rc;
   return launch_conv_fwd(*desc, plan_conv(*desc), x, w, bias, u, stream) == 0 ? SS_OK : SS_ERR_HIP;
 }
 
@@ -369,6 +390,7 @@ int ss_conv1d_bwd(const ss_conv_desc_t* desc, const void* x, const float* w, con
     if (p && !aligned(p, kPtrAlign)) return SS_ERR_INVALID_ARG;
   const ConvPlan plan = plan_conv(*desc);
   if (!workspace || ws_bytes < plan.bytes || !aligned(workspace, kAlign)) return SS_ERR_WORKSPACE;
+  if ((rc = check_device()) != SS_OK) return rc;
   return launch_conv_bwd(*desc, plan, x, w, bias, du, dx, dw, dbias,
                          static_cast<char*>(workspace), stream) == 0
              ? SS_OK
@@ -383,6 +405,7 @@ int ss_conv1d_step(const ss_conv_desc_t* desc, float* state, const void* x, cons
   const void* ptrs[] = {state, x, w, bias, u};
   for (const void* p : ptrs)
     if (p && !aligned(p, kPtrAlign)) return SS_ERR_INVALID_ARG;
+  if ((rc = check_device()) != SS_OK) return rc;
   return launch_conv_step(*desc, state, x, w, bias, u, stream) == 0 ? SS_OK : SS_ERR_HIP;
 }
 
@@ -403,6 +426,7 @@ int ss_ssd_fwd_state(const ss_ssd_desc_t* desc, const void* x, const void* dt, c
   const void* ptrs[] = {x, dt, A, Bm, Cm, D, dt_bias, h0, y, h_last};
   for (const void* p : ptrs)
     if (p && !aligned(p, kPtrAlign)) return SS_ERR_INVALID_ARG;
+  if ((rc = check_device()) != SS_OK) return rc;
   return launch_ssd_fwd(*desc, x, dt, A, Bm, Cm, D, dt_bias, h0, y, h_last, stream) == 0
              ? SS_OK
              : SS_ERR_HIP;
@@ -427,6 +451,7 @@ int ss_ssd_step(const ss_ssd_desc_t* desc, float* h, const void* x, const void* 
   const void* ptrs[] = {h, x, dt, A, Bm, Cm, D, dt_bias, y};
   for (const void* p : ptrs)
     if (p && !aligned(p, kPtrAlign)) return SS_ERR_INVALID_ARG;
+  if ((rc = check_device()) != SS_OK) return rc;
   return launch_ssd_step(*desc, h, x, dt, A, Bm, Cm, D, dt_bias, y, stream) == 0 ? SS_OK
                                                                                   : SS_ERR_HIP;
 }

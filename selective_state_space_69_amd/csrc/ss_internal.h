@@ -57,6 +57,11 @@ struct BwdPlan {
          off_pC = 0, off_pA = 0, off_pD = 0, off_pbias = 0, bytes = 0;
 };
 
+// SS_OK when the current device is a gfx950, SS_ERR_UNSUPPORTED for another
+// architecture, SS_ERR_HIP when no device can be queried (ss_runtime.hip; the
+// answer is cached per device).
+int check_device();
+
 TimePlan plan_time(const ss_desc_t& d);
 FwdPlan plan_fwd(const ss_desc_t& d);
 BwdPlan plan_bwd(const ss_desc_t& d);

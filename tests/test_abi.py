@@ -36,7 +36,8 @@ def test_header_declares_entry_points():
     for n in ("ss_scan_fwd", "ss_scan_bwd", "ss_scan_step", "ss_scan_workspace_bytes",
               "ss_scan_strerror", "ss_scan_version", "ss_conv1d_fwd", "ss_conv1d_bwd",
               "ss_conv1d_step", "ss_conv1d_workspace_bytes", "ss_ssd_fwd", "ss_ssd_fwd_state",
-              "ss_ssd_step", "ss_scan_fwd_dir", "ss_scan_fwd_complex", "ss_scan_step_complex"):
+              "ss_ssd_step", "ss_scan_fwd_dir", "ss_scan_fwd_complex", "ss_scan_step_complex",
+              "ss_scan_arch_supported"):
         assert n in names
 
 
@@ -300,3 +301,33 @@ def test_step_complex_validation(lib):
     assert call(d, A=P + 516) == B.SS_ERR_INVALID_ARG             # misaligned
     assert call(B.make_desc(2, 1, 64, 17, B.SS_BF16, B.SS_F32)) == B.SS_ERR_INVALID_ARG   # N > 16
     assert B.load_library().ss_scan_step_complex(None, *([None] * 10), None) == B.SS_ERR_INVALID_ARG
+
+
+def test_step_validation_aliasing_and_grid(lib):
+    """y of the decode step must not alias the state or an input (it is written
+    while other lanes still read them); batch * dim is bounded by the grid."""
+    P = FAKE
+    d = B.make_desc(2, 1, 64, 16, B.SS_BF16, B.SS_F32)
+    call = lambda desc, **kw: B.ss_scan_step(  # noqa: E731
+        desc, kw.get("h", P + 8192), kw.get("u", P), kw.get("delta", P + 256), kw.get("A", P + 512),
+        kw.get("Bm", P + 1024), kw.get("Cm", P + 1536), None, None, kw.get("z", P + 2048),
+        kw.get("y", P + 4096), stream=0)
+    for name in ("h", "u", "delta", "A", "Bm", "Cm", "y"):
+        assert call(d, **{name: None}) == B.SS_ERR_INVALID_ARG, name
+    for alias in (P + 8192, P, P + 256, P + 1024, P + 1536, P + 2048):   # h, u, delta, B, C, z
+        assert call(d, y=alias) == B.SS_ERR_INVALID_ARG, alias
+    assert call(d, Cm=P + 1540) == B.SS_ERR_INVALID_ARG                 # misaligned
+    huge = B.make_desc(1 << 20, 1, 1 << 14, 16, B.SS_BF16, B.SS_F32)    # 2^34 channels
+    assert call(huge) == B.SS_ERR_INVALID_ARG
+
+
+def test_arch_supported(lib):
+    """Only gfx950 devices run the kernels: the name check every launching entry
+    point applies to the current device."""
+    for name in ("gfx950", "gfx950:sramecc+:xnack-", "gfx950:xnack+"):
+        assert B.ss_scan_arch_supported(name) == B.SS_OK, name
+    for name in ("gfx942", "gfx942:sramecc+:xnack-", "gfx90a", "gfx9500", "gfx95", "", "sm_90",
+                 "gfx1100", " gfx950"):
+        assert B.ss_scan_arch_supported(name) == B.SS_ERR_UNSUPPORTED, name
+    assert B.ss_scan_arch_supported(None) == B.SS_ERR_INVALID_ARG
+    assert "gfx950" in B.ss_scan_strerror(B.SS_ERR_UNSUPPORTED)
