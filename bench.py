@@ -166,10 +166,13 @@ def cpu_baseline(inp, w, budget_s=20.0):
     about budget_s seconds (all of them when the estimate allows)."""
     from oracle import oracle
     try:
-        threads = len(os.sched_getaffinity(0))
+        affinity = len(os.sched_getaffinity(0))
     except AttributeError:
-        threads = os.cpu_count() or 1
-    threads = max(1, min(16, threads))
+        affinity = os.cpu_count() or 1
+    # the host's CPU share for one GPU (OMP_NUM_THREADS on the GPU hosts), at
+    # most the cores this process may run on
+    share = int(os.environ.get("OMP_NUM_THREADS", "16") or 16)
+    threads = max(1, min(share, affinity))
 
     def run(rows):
         sl = slice(0, rows)
@@ -207,6 +210,7 @@ def cpu_baseline(inp, w, budget_s=20.0):
                             "sample": "batch row 0, channels 0..%d, full L=%d: %.2f s" % (
                                 nch - 1, w.L, dt1)}
     res["cpu_model"] = cpu_model()
+    res["host_cpus"] = {"nproc": os.cpu_count(), "affinity": affinity, "omp_share": share}
     res["other_rows"] = cpu_rows(oracle, threads)
     return res
 
@@ -377,14 +381,19 @@ def main():
     alg = algorithmic_bytes(w, 2 if w.dtype == "bf16" else 4, 4)
     hbm_gbs = alg / (per_ms * 1e-3) / 1e9
     slots = SLOTS_PER_ELEM[w.disc] * elems / (per_ms * 1e-3) / 1e12
-    roof = {"bound": "alu", "achieved": round(slots, 3), "peak": round(VALU_PEAK_TSLOT, 3),
-            "unit": "Tslot/s", "frac": round(slots / VALU_PEAK_TSLOT, 4),
-            "traffic": load_traffic(w.name),
+    # The roofline is HBM bandwidth: algorithmic bytes (each input read once,
+    # y written once) over the mean per-call time, against the 8 TB/s peak.  The
+    # VALU lane-slot figure beside it is a model (minimal vector issue slots per
+    # element at the published clock), not a measured peak.
+    roof = {"bound": "hbm", "achieved": round(hbm_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(hbm_gbs / HBM_PEAK_GBS, 4), "traffic": load_traffic(w.name),
+            "algorithmic_bytes": alg,
             "kernel_ms": round(per_ms, 4), "kernel_ms_min": round(min_ms, 4),
-            "work_per_element": "%s: %d VALU lane-slots (1 v_exp_f32 = 2 slots)" % (
-                w.disc, SLOTS_PER_ELEM[w.disc]),
-            "hbm": {"achieved": round(hbm_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                    "frac": round(hbm_gbs / HBM_PEAK_GBS, 4), "algorithmic_bytes": alg}}
+            "alu_model": {"achieved": round(slots, 3), "peak": round(VALU_PEAK_TSLOT, 3),
+                          "unit": "Tslot/s", "frac": round(slots / VALU_PEAK_TSLOT, 4),
+                          "work_per_element": "%s: %d VALU lane-slots (model: 1 v_exp_f32 = 2 "
+                                              "slots), 256 CUs x 64 lanes x 2.4 GHz" % (
+                                                  w.disc, SLOTS_PER_ELEM[w.disc])}}
     res = {"metric": "selective-scan elements (B*L*D*N)/s, 1 GPU", "value": value,
            "unit": "elements/s", "n_gpus": 1, "steps": args.steps, "warmup": warm_calls,
            "warmup_requested": args.warmup, "warmup_min_s": WARM["min_s"],
@@ -401,8 +410,8 @@ def main():
         roof["cold"] = {"median_ms": round(cold_med, 4), "min_ms": round(cold_min, 4),
                         "control_median_ms": round(ctrl_med, 4), "flush_bytes": 512 << 20,
                         "runs": 20}
-        roof["hbm"]["stream_gbs"] = round(sgbs, 1)
-        roof["hbm"]["frac_of_stream"] = round(hbm_gbs / sgbs, 4)
+        roof["stream_gbs"] = round(sgbs, 1)
+        roof["frac_of_stream"] = round(hbm_gbs / sgbs, 4)
     del d, y, ws
     torch.cuda.empty_cache()
 
@@ -436,7 +445,8 @@ def extras(torch, Bnd, synth, args):
         alg = algorithmic_bytes(w)
         out[name] = {"ms": round(per, 4), "elements_per_s": w.elements / (per * 1e-3),
                      "hbm_gbs": round(alg / (per * 1e-3) / 1e9, 1),
-                     "alu_frac": round(SLOTS_PER_ELEM[disc] * w.elements / (per * 1e-3) / 1e12
+                     "hbm_frac": round(alg / (per * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                     "alu_model_frac": round(SLOTS_PER_ELEM[disc] * w.elements / (per * 1e-3) / 1e12
                                        / VALU_PEAK_TSLOT, 4),
                      "chunks": "workspace %d B" % nb}
         del d, y, ws, inp
@@ -617,7 +627,7 @@ def time_bidir(torch, Bnd, synth, steps, warm):
         total, per, mn, _ = time_calls(f, steps, warm, torch)
         out[key] = {"ms": round(per, 4), "ms_min": round(mn, 4),
                     "elements_per_s": mult * w.elements / (per * 1e-3),
-                    "alu_frac": round(SLOTS_PER_ELEM[w.disc] * mult * w.elements /
+                    "alu_model_frac": round(SLOTS_PER_ELEM[w.disc] * mult * w.elements /
                                       (per * 1e-3) / 1e12 / VALU_PEAK_TSLOT, 4)}
     del d, y, ws, inp
     torch.cuda.empty_cache()
@@ -640,7 +650,7 @@ def time_complex(torch, Bnd, synth, steps, warm):
     el = Bt * L * D * N
     out = {"complex_2p8b_s4dlin": {"ms": round(per, 4), "ms_min": round(mn, 4),
                                    "elements_per_s": el / (per * 1e-3),
-                                   "alu_frac": round(COMPLEX_SLOTS * el / (per * 1e-3) / 1e12 /
+                                   "alu_model_frac": round(COMPLEX_SLOTS * el / (per * 1e-3) / 1e12 /
                                                      VALU_PEAK_TSLOT, 4)}}
     # the decode step on a (B, D, N, 2) state, 100 steps captured in one graph
     h = torch.zeros((Bt, D, N, 2), dtype=f32, device="cuda")
