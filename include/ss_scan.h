@@ -65,6 +65,8 @@ extern "C" {
                                     or the current device is not a gfx950 */
 #define SS_ERR_WORKSPACE (-3)    /* workspace NULL or smaller than ss_scan_workspace_bytes */
 #define SS_ERR_HIP (-4)          /* a HIP launch reported an error */
+#define SS_ERR_SCRATCH_LIMIT (-5) /* ss_scan_fwd_noalloc: the plan needs more scratch than
+                                     SS_SCAN_STATIC_SCRATCH_BYTES */
 
 typedef enum { SS_F32 = 0, SS_BF16 = 1 } ss_dtype_t;
 typedef enum { SS_ZOH = 0, SS_EULER = 1 } ss_disc_t;
@@ -114,6 +116,35 @@ int ss_scan_fwd(const ss_desc_t* desc,
                 const float* h0,
                 void* y, float* h_last,
                 void* workspace, size_t ws_bytes, void* stream);
+
+/* Bytes of the static scratch array ss_scan_fwd_noalloc uses on each GPU. */
+#define SS_SCAN_STATIC_SCRATCH_BYTES (32u << 20)
+
+/*
+ * ss_scan_fwd without a workspace argument, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc.  The scratch a plan needs (chunk start states and
+ * step sums, padded B/C rows; ss_scan_workspace_bytes(desc, SS_OP_FWD) bytes,
+ * at most about 9 MB for chunk carries at any shape) comes from a static
+ * device array of SS_SCAN_STATIC_SCRATCH_BYTES (32 MiB) that each GPU the
+ * library runs on holds from load until the process ends.  The call makes no
+ * allocation of any kind.
+ *   Arguments, results and other status codes: exactly ss_scan_fwd (the same
+ *   kernels and plan, so the output is bitwise that of ss_scan_fwd).
+ *   Returns SS_ERR_SCRATCH_LIMIT, before any HIP call, when the plan needs
+ *   more than SS_SCAN_STATIC_SCRATCH_BYTES (e.g. dstate < 16 with a very long
+ *   batch * seqlen, whose padded rows scale with it); use ss_scan_fwd then.
+ * All calls on one GPU share its array, which keeps the last call's contents
+ * (every value a call reads from it, that call has written first): calls that
+ * overlap on one GPU (different streams, or threads without ordering) race.
+ * Serialise them on one stream or with events.
+ */
+int ss_scan_fwd_noalloc(const ss_desc_t* desc,
+                        const void* u, const void* delta, const float* A,
+                        const void* Bm, const void* Cm,
+                        const float* D_skip, const float* delta_bias, const void* z,
+                        const float* h0,
+                        void* y, float* h_last, void* stream);
 
 /* Time directions of ss_scan_fwd_dir. */
 #define SS_DIR_FORWARD 0

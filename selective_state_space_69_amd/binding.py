@@ -1,7 +1,7 @@
 """Thin ctypes binding of libssscan.so (C ABI declared in include/ss_scan.h,
 include/ss_conv.h and include/ss_ssd.h).
 
-The functions named like the C entry points (ss_scan_fwd, ss_scan_fwd_dir,
+The functions named like the C entry points (ss_scan_fwd, ss_scan_fwd_noalloc, ss_scan_fwd_dir,
 ss_scan_fwd_complex, ss_scan_bwd, ss_scan_step, ss_scan_step_complex, ss_scan_workspace_bytes, ss_scan_strerror, ss_scan_version,
 ss_conv1d_fwd, ss_conv1d_bwd, ss_conv1d_step, ss_conv1d_workspace_bytes, ss_ssd_fwd,
 ss_ssd_fwd_state, ss_ssd_step) only
@@ -22,6 +22,8 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libssscan.so")
 
 SS_OK, SS_ERR_INVALID_ARG, SS_ERR_UNSUPPORTED, SS_ERR_WORKSPACE, SS_ERR_HIP = 0, -1, -2, -3, -4
+SS_ERR_SCRATCH_LIMIT = -5
+SS_SCAN_STATIC_SCRATCH_BYTES = 32 << 20
 SS_F32, SS_BF16 = 0, 1
 SS_ZOH, SS_EULER = 0, 1
 SS_OP_FWD, SS_OP_BWD = 0, 1
@@ -75,6 +77,8 @@ def load_library():
         lib.ss_scan_workspace_bytes.restype = SZ
         lib.ss_scan_fwd.argtypes = [D] + [P] * 11 + [P, SZ, P]
         lib.ss_scan_fwd.restype = I
+        lib.ss_scan_fwd_noalloc.argtypes = [D] + [P] * 11 + [P]
+        lib.ss_scan_fwd_noalloc.restype = I
         lib.ss_scan_fwd_dir.argtypes = [D, I, I] + [P] * 11 + [P, SZ, P]
         lib.ss_scan_fwd_dir.restype = I
         lib.ss_scan_fwd_complex.argtypes = [D] + [P] * 11 + [P]
@@ -155,6 +159,13 @@ def ss_scan_fwd(desc, u, delta, A, Bm, Cm, D_skip, delta_bias, z, h0, y, h_last,
     return load_library().ss_scan_fwd(ctypes.byref(desc), _p(u), _p(delta), _p(A), _p(Bm), _p(Cm),
                                       _p(D_skip), _p(delta_bias), _p(z), _p(h0), _p(y), _p(h_last),
                                       _p(workspace), int(ws_bytes), _stream(stream))
+
+
+def ss_scan_fwd_noalloc(desc, u, delta, A, Bm, Cm, D_skip, delta_bias, z, h0, y, h_last,
+                        stream=None) -> int:
+    return load_library().ss_scan_fwd_noalloc(ctypes.byref(desc), _p(u), _p(delta), _p(A), _p(Bm),
+                                              _p(Cm), _p(D_skip), _p(delta_bias), _p(z), _p(h0),
+                                              _p(y), _p(h_last), _stream(stream))
 
 
 def ss_scan_fwd_dir(desc, direction, accumulate, u, delta, A, Bm, Cm, D_skip, delta_bias, z, h0,

@@ -207,6 +207,51 @@ ConvPlan plan_conv(const ss_conv_desc_t& d) {
 
 using namespace ss;
 
+namespace {
+
+// The forward in either direction.  static_ws: the scratch is the library's
+// static array (ss_scan_fwd_noalloc) instead of the caller's workspace.
+int fwd_call(const ss_desc_t* desc, int direction, int accumulate, const void* u,
+             const void* delta, const float* A, const void* Bm, const void* Cm,
+             const float* D_skip, const float* delta_bias, const void* z, const float* h0,
+             void* y, float* h_last, void* workspace, size_t ws_bytes, bool static_ws,
+             void* stream) {
+  int rc = check_desc(desc, true);
+  if (rc != SS_OK) return rc;
+  if (direction != SS_DIR_FORWARD && direction != SS_DIR_REVERSE) return SS_ERR_INVALID_ARG;
+  if (!u || !delta || !A || !Bm || !Cm || !y) return SS_ERR_INVALID_ARG;
+  if (h_last && h0 && static_cast<const void*>(h_last) == static_cast<const void*>(h0))
+    return SS_ERR_INVALID_ARG;
+  const void* ptrs[] = {u, delta, Bm, Cm, z, A, D_skip, delta_bias, h0, h_last, y};
+  for (const void* p : ptrs)
+    if (p && !aligned(p, kPtrAlign)) return SS_ERR_INVALID_ARG;
+  const FwdPlan plan = plan_fwd(*desc);
+  if (static_ws) {
+    if (plan.bytes > kStaticScratchBytes) return SS_ERR_SCRATCH_LIMIT;
+  } else if (plan.bytes > 0 &&
+             (!workspace || ws_bytes < plan.bytes || !aligned(workspace, kAlign))) {
+    return SS_ERR_WORKSPACE;
+  }
+  if ((rc = check_device()) != SS_OK) return rc;
+  if (static_ws && plan.bytes > 0 && (rc = static_scratch(&workspace)) != SS_OK) return rc;
+  FwdArgs a{u, delta, A, Bm, Cm, D_skip, delta_bias, z, h0, y, h_last,
+            nullptr, nullptr, nullptr, nullptr};
+  a.rev = direction == SS_DIR_REVERSE;
+  a.acc = accumulate != 0;
+  char* ws = static_cast<char*>(workspace);
+  if (plan.packed_rows) {
+    a.Brow = ws + plan.off_brow;
+    a.Crow = ws + plan.off_crow;
+  }
+  if (plan.tp.nchunks > 1) {
+    a.hend = reinterpret_cast<float*>(ws + plan.off_hend);
+    a.dsum = reinterpret_cast<float*>(ws + plan.off_dsum);
+  }
+  return launch_fwd(*desc, plan, a, stream) == 0 ? SS_OK : SS_ERR_HIP;
+}
+
+}  // namespace
+
 extern "C" {
 
 int ss_scan_version(void) { return 10000; }
@@ -227,6 +272,7 @@ const char* ss_scan_strerror(int status) {
     case SS_ERR_UNSUPPORTED: return "unsupported dtype, discretisation or option combination, or the current device is not a gfx950";
     case SS_ERR_WORKSPACE: return "workspace missing or smaller than ss_scan_workspace_bytes()";
     case SS_ERR_HIP: return "HIP kernel launch failed";
+    case SS_ERR_SCRATCH_LIMIT: return "the plan needs more scratch than the static array of ss_scan_fwd_noalloc (SS_SCAN_STATIC_SCRATCH_BYTES); use ss_scan_fwd with a workspace";
     default: return "unknown status";
   }
 }
@@ -250,33 +296,16 @@ int ss_scan_fwd_dir(const ss_desc_t* desc, int direction, int accumulate, const 
                     const void* delta, const float* A, const void* Bm, const void* Cm,
                     const float* D_skip, const float* delta_bias, const void* z, const float* h0,
                     void* y, float* h_last, void* workspace, size_t ws_bytes, void* stream) {
-  int rc = check_desc(desc, true);
-  if (rc != SS_OK) return rc;
-  if (direction != SS_DIR_FORWARD && direction != SS_DIR_REVERSE) return SS_ERR_INVALID_ARG;
-  if (!u || !delta || !A || !Bm || !Cm || !y) return SS_ERR_INVALID_ARG;
-  if (h_last && h0 && static_cast<const void*>(h_last) == static_cast<const void*>(h0))
-    return SS_ERR_INVALID_ARG;
-  const void* ptrs[] = {u, delta, Bm, Cm, z, A, D_skip, delta_bias, h0, h_last, y};
-  for (const void* p : ptrs)
-    if (p && !aligned(p, kPtrAlign)) return SS_ERR_INVALID_ARG;
-  const FwdPlan plan = plan_fwd(*desc);
-  if (plan.bytes > 0 && (!workspace || ws_bytes < plan.bytes || !aligned(workspace, kAlign)))
-    return SS_ERR_WORKSPACE;
-  FwdArgs a{u, delta, A, Bm, Cm, D_skip, delta_bias, z, h0, y, h_last,
-            nullptr, nullptr, nullptr, nullptr};
-  a.rev = direction == SS_DIR_REVERSE;
-  a.acc = accumulate != 0;
-  char* ws = static_cast<char*>(workspace);
-  if (plan.packed_rows) {
-    a.Brow = ws + plan.off_brow;
-    a.Crow = ws + plan.off_crow;
-  }
-  if (plan.tp.nchunks > 1) {
-    a.hend = reinterpret_cast<float*>(ws + plan.off_hend);
-    a.dsum = reinterpret_cast<float*>(ws + plan.off_dsum);
-  }
-  if ((rc = check_device()) != SS_OK) return rc;
-  return launch_fwd(*desc, plan, a, stream) == 0 ? SS_OK : SS_ERR_HIP;
+  return fwd_call(desc, direction, accumulate, u, delta, A, Bm, Cm, D_skip, delta_bias, z, h0, y,
+                  h_last, workspace, ws_bytes, false, stream);
+}
+
+int ss_scan_fwd_noalloc(const ss_desc_t* desc, const void* u, const void* delta, const float* A,
+                        const void* Bm, const void* Cm, const float* D_skip,
+                        const float* delta_bias, const void* z, const float* h0, void* y,
+                        float* h_last, void* stream) {
+  return fwd_call(desc, SS_DIR_FORWARD, 0, u, delta, A, Bm, Cm, D_skip, delta_bias, z, h0, y,
+                  h_last, nullptr, 0, true, stream);
 }
 
 int ss_scan_fwd_complex(const ss_desc_t* desc, const void* u, const void* delta, const float* A,

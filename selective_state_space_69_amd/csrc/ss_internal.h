@@ -62,6 +62,12 @@ struct BwdPlan {
 // answer is cached per device).
 int check_device();
 
+// Size of the static scratch array of ss_scan_fwd_noalloc (ss_runtime.hip).
+constexpr size_t kStaticScratchBytes = size_t(SS_SCAN_STATIC_SCRATCH_BYTES);
+// This GPU's copy of that array (its device address, looked up once per
+// device with the device current): SS_OK, SS_ERR_HIP or SS_ERR_UNSUPPORTED.
+int static_scratch(void** out);
+
 TimePlan plan_time(const ss_desc_t& d);
 FwdPlan plan_fwd(const ss_desc_t& d);
 BwdPlan plan_bwd(const ss_desc_t& d);

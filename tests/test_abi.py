@@ -37,7 +37,7 @@ def test_header_declares_entry_points():
               "ss_scan_strerror", "ss_scan_version", "ss_conv1d_fwd", "ss_conv1d_bwd",
               "ss_conv1d_step", "ss_conv1d_workspace_bytes", "ss_ssd_fwd", "ss_ssd_fwd_state",
               "ss_ssd_step", "ss_scan_fwd_dir", "ss_scan_fwd_complex", "ss_scan_step_complex",
-              "ss_scan_arch_supported"):
+              "ss_scan_arch_supported", "ss_scan_fwd_noalloc"):
         assert n in names
 
 
@@ -331,3 +331,27 @@ def test_arch_supported(lib):
         assert B.ss_scan_arch_supported(name) == B.SS_ERR_UNSUPPORTED, name
     assert B.ss_scan_arch_supported(None) == B.SS_ERR_INVALID_ARG
     assert "gfx950" in B.ss_scan_strerror(B.SS_ERR_UNSUPPORTED)
+
+
+def test_noalloc_validation_and_scratch_limit(lib):
+    """ss_scan_fwd_noalloc validates like ss_scan_fwd and refuses, before any
+    HIP call, a plan that needs more scratch than its static array."""
+    P = FAKE
+    args = lambda **kw: [kw.get(k, v) for k, v in dict(u=P, delta=P + 256, A=P + 512, Bm=P + 1024,  # noqa
+                         Cm=P + 1536, D=None, bias=None, z=None, h0=None, y=P + 4096,
+                         hl=None).items()]
+    big = B.make_desc(1, 1 << 20, 256, 8, B.SS_BF16, B.SS_F32)     # padded rows: 72 MB
+    assert B.ss_scan_workspace_bytes(big, B.SS_OP_FWD) > B.SS_SCAN_STATIC_SCRATCH_BYTES
+    assert B.ss_scan_fwd_noalloc(big, *args(), stream=0) == B.SS_ERR_SCRATCH_LIMIT
+    assert "static" in B.ss_scan_strerror(B.SS_ERR_SCRATCH_LIMIT)
+    ok = B.make_desc(2, 64, 32, 16, B.SS_F32, B.SS_F32)
+    assert B.ss_scan_fwd_noalloc(ok, *args(u=None), stream=0) == B.SS_ERR_INVALID_ARG
+    assert B.ss_scan_fwd_noalloc(ok, *args(A=P + 516), stream=0) == B.SS_ERR_INVALID_ARG
+    assert B.ss_scan_fwd_noalloc(ok, *args(h0=P + 8192, hl=P + 8192), stream=0) == \
+        B.SS_ERR_INVALID_ARG
+    assert B.ss_scan_fwd_noalloc(B.make_desc(2, 64, 32, 17), *args(), stream=0) == \
+        B.SS_ERR_INVALID_ARG
+    # the binding's size constant is the header's
+    text = open(os.path.join(INCLUDE, "ss_scan.h")).read()
+    m = re.search(r"#define SS_SCAN_STATIC_SCRATCH_BYTES \((\d+)u << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == B.SS_SCAN_STATIC_SCRATCH_BYTES
