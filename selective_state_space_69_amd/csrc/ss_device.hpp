@@ -41,6 +41,16 @@ template <> __device__ __forceinline__ void buf_store<float>(Rsrc r, uint32_t vo
   __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, voff, soff, 0);
 }
 
+// Workgroups are handed to the 8 XCDs round-robin (workgroup i to XCD i % 8),
+// and each XCD has its own L2.  This bijection on [0, G) gives each XCD a
+// contiguous range of logical workgroup indices, so neighbours that share
+// input lines (adjacent channel groups, the heads of one batch row) meet in
+// one L2 instead of being fetched by every XCD.
+__device__ __forceinline__ int64_t xcd_contiguous(int64_t i, int64_t G) {
+  const int64_t xi = i % 8, q8 = G / 8, r8 = G % 8;
+  return xi * q8 + (xi < r8 ? xi : r8) + i / 8;
+}
+
 // Element types: fp32, or bf16 carried as its raw uint16 bit pattern.
 template <typename T> __device__ __forceinline__ float to_f32(T x);
 template <> __device__ __forceinline__ float to_f32<float>(float x) { return x; }
@@ -81,21 +91,21 @@ template <> __device__ __forceinline__ void buf_store<uint16_t>(Rsrc r, uint32_t
 }
 
 // Step size in log2 units: softplus(x) * log2(e) = log2(1 + 2^x2) with
-// x2 = x * log2(e), written as max(x2, 0) + log2(1 + 2^-|x2|).  The log of
-// 1 + e is corrected for the rounding of 1 + e (log1p by the Goldberg/Kahan
-// trick log(u) * e / (u - 1)).  Where 1 + e rounds to 1 (e < 2^-24, x below
-// about -16.6) that trick yields 0; there log2(1 + e) = e log2(e) (1 - e/2) to
-// fp32 accuracy.  That expression is a lower bound of log2(1 + e) for every
-// e >= 0 (alternating series), and the Goldberg value is accurate wherever it
-// is not 0, so the larger of the two is right everywhere: small steps keep
-// full relative accuracy down to the smallest normal e, with no select.
+// x2 = x * log2(e), written as max(x2, 0) + log2(1 + e), e = 2^-|x2| in (0, 1].
+// log1p without cancellation: u1 = fl(1 + e) and r = e - (u1 - 1) give
+// 1 + e = u1 + r exactly (Fast2Sum, 1 >= e), so
+// log2(1 + e) = log2(u1) + log2(1 + r / u1) = log2(u1) + r log2(e) / u1 to
+// within (r / u1)^2 < 2^-48.  The correction needs 1/u1 only roughly: it is
+// exact where it matters (u1 == 1, e < 2^-24, where the whole answer is
+// r log2 e = e log2 e) and below 2^-24 of the result elsewhere, so 1/u1 is
+// replaced by 2 - u1 (relative error (u1 - 1)^2 / u1).  Small steps keep full
+// relative accuracy down to the smallest normal e.
 __device__ __forceinline__ float softplus_log2(float x2) {
   const float e = hw_exp2(-__builtin_fabsf(x2));
   const float u1 = 1.0f + e;
-  const float dm = __builtin_fmaxf(u1 - 1.0f, 0x1p-100f);
-  const float lo = (e * kLog2e) * __builtin_fmaf(e, -0.5f, 1.0f);
-  const float l1p = __builtin_fmaxf(hw_log2(u1) * (e * hw_rcp(dm)), lo);
-  return __builtin_fmaxf(x2, 0.0f) + l1p;
+  const float r = e - (u1 - 1.0f);                               // exact rounding error of u1
+  const float k = __builtin_fmaf(-u1, kLog2e, 2.0f * kLog2e);    // log2(e) (2 - u1)
+  return __builtin_fmaxf(x2, 0.0f) + __builtin_fmaf(r, k, hw_log2(u1));
 }
 
 // Exact-ZOH input coefficient coef = (exp(x) - 1) / A with x = dt A ("Mamba: S4

@@ -248,12 +248,10 @@ __global__ __launch_bounds__(kWave * kWaves, 5) void fwd_hw_kernel(FwdParams p) 
   const int o = 2 * wave + half;
   const uint32_t c = uint32_t(lane % kCh);
   const int n0 = 2 * o;
-  // Workgroups are handed to the 8 XCDs round-robin (id i -> XCD i % 8).  Two
-  // neighbouring 32-channel groups share every 128-byte line of u, delta and
-  // z, so give each XCD a contiguous range of groups: then both halves of a
-  // line are fetched through the same L2.  The remap is a bijection on the grid.
-  const int64_t G = gridDim.x, xi = blockIdx.x % 8, q8 = G / 8, r8 = G % 8;
-  int64_t bid = xi * q8 + (xi < r8 ? xi : r8) + blockIdx.x / 8;
+  // Two neighbouring 32-channel groups share every 128-byte line of u, delta
+  // and z: with each XCD on a contiguous range of groups both halves of a line
+  // are fetched through the same L2.
+  int64_t bid = xcd_contiguous(blockIdx.x, gridDim.x);
   const int dblk = int(bid % p.ndblk);
   bid /= p.ndblk;
   const int chunk = int(bid % p.grid_chunks);

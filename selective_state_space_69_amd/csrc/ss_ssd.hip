@@ -183,8 +183,11 @@ __global__ __launch_bounds__(kThreads, 3) void ssd_fwd_kernel(SsdArgs a) {
   const int w = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int lane = tid % kWave;
   const int c16 = lane & 15, g = lane >> 4;
-  const int h = int(blockIdx.x % unsigned(a.H));
-  const int64_t b = int64_t(blockIdx.x / unsigned(a.H));
+  // the heads of one batch row read the same B and C rows: with each XCD on a
+  // contiguous range of (b, h) those rows are fetched once per batch row
+  const int64_t bid = xcd_contiguous(blockIdx.x, gridDim.x);
+  const int h = int(bid % a.H);
+  const int64_t b = bid / a.H;
   const int grp = h / (a.H / a.G);
   const int64_t L = a.L;
   const int nc = int((L + kQ - 1) / kQ);
