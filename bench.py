@@ -652,6 +652,34 @@ def time_complex(torch, Bnd, synth, steps, warm):
                                    "elements_per_s": el / (per * 1e-3),
                                    "alu_model_frac": round(COMPLEX_SLOTS * el / (per * 1e-3) / 1e12 /
                                                      VALU_PEAK_TSLOT, 4)}}
+    # the same shape with fp32 inputs: every wave on the precise step
+    fu, fdl, fB, fC, fz = (cv(a, f32) for a in (inp.u, inp.delta, inp.B, inp.C, inp.z))
+    fdesc = Bnd.make_desc(Bt, L, D, N, Bnd.SS_F32, Bnd.SS_F32, Bnd.SS_ZOH, True)
+    f = lambda: Bnd.ss_scan_fwd_complex(fdesc, fu, fdl, A, fB, fC, Dk, bias, fz, None, y, None)  # noqa
+    total, per, mn, _ = time_calls(f, steps, warm, torch)
+    out["complex_2p8b_s4dlin_f32in"] = {"ms": round(per, 4), "ms_min": round(mn, 4),
+                                        "elements_per_s": el / (per * 1e-3),
+                                        "path": "precise step (fp32 inputs)"}
+    del fu, fdl, fB, fC, fz
+    torch.cuda.empty_cache()
+    # the million-step shape (B=1, L=2^20, D=256): the chunked complex plan
+    li = synth.make_complex_inputs(1, 1 << 20, 256, N, seed=1003, dtype="bf16",
+                                   dt_range=(1e-4, 1e-2))
+    lu, ldl, lB, lC, lz = (cv(a, bf) for a in (li.u, li.delta, li.B, li.C, li.z))
+    lA, lD, lbias = (cv(a, f32) for a in (li.A, li.D, li.delta_bias))
+    ly = torch.empty((1, 1 << 20, 256), dtype=f32, device="cuda")
+    ldesc = Bnd.make_desc(1, 1 << 20, 256, N, Bnd.SS_BF16, Bnd.SS_F32, Bnd.SS_ZOH, True)
+    lnb = Bnd.ss_scan_workspace_bytes(ldesc, Bnd.SS_OP_FWD_COMPLEX)
+    lws = Bnd.workspace(lnb, "cuda")
+    f = lambda: Bnd.ss_scan_fwd_complex_ws(ldesc, lu, ldl, lA, lB, lC, lD, lbias, lz, None, ly,  # noqa
+                                           None, lws, lnb)
+    total, per, mn, _ = time_calls(f, max(3, steps // 2), warm, torch)
+    lel = (1 << 20) * 256 * N
+    out["complex_long_b1_l1048576_d256_s4dlin"] = {
+        "ms": round(per, 4), "ms_min": round(mn, 4), "elements_per_s": lel / (per * 1e-3),
+        "chunks": "workspace %d B" % lnb}
+    del lu, ldl, lB, lC, lz, ly, lws, li
+    torch.cuda.empty_cache()
     # the decode step on a (B, D, N, 2) state, 100 steps captured in one graph
     h = torch.zeros((Bt, D, N, 2), dtype=f32, device="cuda")
     u1, dl1, z1 = (t[:, 0].contiguous() for t in (u, dl, z))

@@ -86,10 +86,12 @@ typedef struct ss_desc {
 /* Operations for ss_scan_workspace_bytes. */
 #define SS_OP_FWD 0
 #define SS_OP_BWD 1
+#define SS_OP_FWD_COMPLEX 2   /* ss_scan_fwd_complex_ws */
 
 /*
- * Bytes of device workspace that ss_scan_fwd (op = SS_OP_FWD) or ss_scan_bwd
- * (op = SS_OP_BWD) needs for this description (0 when none).  The size depends
+ * Bytes of device workspace that ss_scan_fwd (op = SS_OP_FWD), ss_scan_bwd
+ * (op = SS_OP_BWD) or ss_scan_fwd_complex_ws (op = SS_OP_FWD_COMPLEX) needs for
+ * this description (0 when none).  The size depends
  * only on the description (and the SS_SCAN_CHUNK tuning variable, if set).
  * Returns 0 for an invalid description.  Workspace contents are scratch: they
  * need not be initialised and are clobbered.
@@ -192,7 +194,9 @@ int ss_scan_fwd_dir(const ss_desc_t* desc, int direction, int accumulate,
  *     A : (D, N, 2) float32;  Bm, Cm : (B, L, N, 2) in in_dtype;
  *     h0, h_last : (B, D, N, 2) float32.
  * Everything else as ss_scan_fwd.  dstate = N complex states (1..16).  No
- * workspace: one workgroup walks the whole sequence of its 64 channels.
+ * workspace: one workgroup walks the whole sequence of its 32 channels, so a
+ * long sequence with few channels runs on few workgroups; use
+ * ss_scan_fwd_complex_ws there.
  */
 int ss_scan_fwd_complex(const ss_desc_t* desc,
                         const void* u, const void* delta, const float* A,
@@ -200,6 +204,28 @@ int ss_scan_fwd_complex(const ss_desc_t* desc,
                         const float* D_skip, const float* delta_bias, const void* z,
                         const float* h0,
                         void* y, float* h_last, void* stream);
+
+/*
+ * ss_scan_fwd_complex with a workspace of ss_scan_workspace_bytes(desc,
+ * SS_OP_FWD_COMPLEX) bytes (256-byte aligned), which lets long, narrow
+ * problems be cut into time chunks: a summary pass gives each chunk's end state
+ * from a zero start and its sum of step sizes, an in-order walk over the
+ * chunks turns them into start states (the chunk maps h -> abar_c h + s_c,
+ * abar_c = exp(a sum dt), composed associatively: "A Visual Guide to Mamba"
+ * summary, The Scan Operation), and the output pass runs every chunk from its
+ * true start.  The step sums are kept in fp64, since a chunk's rotation angle
+ * Im(a) sum dt can reach hundreds of radians.  With workspace == NULL and
+ * ws_bytes == 0 this is exactly ss_scan_fwd_complex (one pass).  Returns
+ * SS_ERR_WORKSPACE when a workspace is given but is too small or misaligned.
+ * Other arguments and status codes as ss_scan_fwd_complex.
+ */
+int ss_scan_fwd_complex_ws(const ss_desc_t* desc,
+                           const void* u, const void* delta, const float* A,
+                           const void* Bm, const void* Cm,
+                           const float* D_skip, const float* delta_bias, const void* z,
+                           const float* h0,
+                           void* y, float* h_last,
+                           void* workspace, size_t ws_bytes, void* stream);
 
 /*
  * One recurrent step with complex diagonal A (decoding), the single-token form

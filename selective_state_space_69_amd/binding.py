@@ -2,7 +2,7 @@
 include/ss_conv.h and include/ss_ssd.h).
 
 The functions named like the C entry points (ss_scan_fwd, ss_scan_fwd_noalloc, ss_scan_fwd_dir,
-ss_scan_fwd_complex, ss_scan_bwd, ss_scan_step, ss_scan_step_complex, ss_scan_workspace_bytes, ss_scan_strerror, ss_scan_version,
+ss_scan_fwd_complex, ss_scan_fwd_complex_ws, ss_scan_bwd, ss_scan_step, ss_scan_step_complex, ss_scan_workspace_bytes, ss_scan_strerror, ss_scan_version,
 ss_conv1d_fwd, ss_conv1d_bwd, ss_conv1d_step, ss_conv1d_workspace_bytes, ss_ssd_fwd,
 ss_ssd_fwd_state, ss_ssd_step) only
 marshal arguments: torch tensors become device pointers, None becomes NULL and
@@ -26,7 +26,7 @@ SS_ERR_SCRATCH_LIMIT = -5
 SS_SCAN_STATIC_SCRATCH_BYTES = 32 << 20
 SS_F32, SS_BF16 = 0, 1
 SS_ZOH, SS_EULER = 0, 1
-SS_OP_FWD, SS_OP_BWD = 0, 1
+SS_OP_FWD, SS_OP_BWD, SS_OP_FWD_COMPLEX = 0, 1, 2
 SS_DIR_FORWARD, SS_DIR_REVERSE = 0, 1
 
 _DTYPE = {torch.float32: SS_F32, torch.bfloat16: SS_BF16}
@@ -83,6 +83,8 @@ def load_library():
         lib.ss_scan_fwd_dir.restype = I
         lib.ss_scan_fwd_complex.argtypes = [D] + [P] * 11 + [P]
         lib.ss_scan_fwd_complex.restype = I
+        lib.ss_scan_fwd_complex_ws.argtypes = [D] + [P] * 11 + [P, SZ, P]
+        lib.ss_scan_fwd_complex_ws.restype = I
         lib.ss_scan_bwd.argtypes = [D] + [P] * 19 + [P, SZ, P]
         lib.ss_scan_bwd.restype = I
         lib.ss_scan_step.argtypes = [D] + [P] * 10 + [P]
@@ -181,6 +183,14 @@ def ss_scan_fwd_complex(desc, u, delta, A, Bm, Cm, D_skip, delta_bias, z, h0, y,
     return load_library().ss_scan_fwd_complex(ctypes.byref(desc), _p(u), _p(delta), _p(A), _p(Bm),
                                               _p(Cm), _p(D_skip), _p(delta_bias), _p(z), _p(h0),
                                               _p(y), _p(h_last), _stream(stream))
+
+
+def ss_scan_fwd_complex_ws(desc, u, delta, A, Bm, Cm, D_skip, delta_bias, z, h0, y, h_last,
+                           workspace, ws_bytes, stream=None) -> int:
+    return load_library().ss_scan_fwd_complex_ws(ctypes.byref(desc), _p(u), _p(delta), _p(A),
+                                                 _p(Bm), _p(Cm), _p(D_skip), _p(delta_bias), _p(z),
+                                                 _p(h0), _p(y), _p(h_last), _p(workspace),
+                                                 int(ws_bytes), _stream(stream))
 
 
 def ss_scan_bwd(desc, u, delta, A, Bm, Cm, D_skip, delta_bias, z, h0, dy, du, ddelta, dA, dB, dC,
@@ -295,15 +305,19 @@ def scan_fwd_complex(u, delta, A, B, C, D=None, delta_bias=None, z=None, h0=None
                      softplus=True, out_dtype=torch.float32, return_last_state=False,
                      stream=None):
     """Complex-A forward: A (D, N, 2) float32, B and C (B, L, N, 2) in u's dtype,
-    h0 (B, D, N, 2) float32 ((re, im) pairs).  Returns y (and h_last (B, D, N, 2))."""
+    h0 (B, D, N, 2) float32 ((re, im) pairs).  Returns y (and h_last (B, D, N, 2)).
+    Uses ss_scan_fwd_complex_ws with a torch workspace (time chunks where the
+    plan wants them)."""
     Bt, L, Dd = u.shape
     N = A.shape[1]
     desc = make_desc(Bt, L, Dd, N, _DTYPE[u.dtype], _DTYPE[out_dtype], _DISC[disc], softplus)
     y = torch.empty(u.shape, dtype=out_dtype, device=u.device)
     h_last = (torch.empty((Bt, Dd, N, 2), dtype=torch.float32, device=u.device)
               if return_last_state else None)
-    _check(ss_scan_fwd_complex(desc, u, delta, A, B, C, D, delta_bias, z, h0, y, h_last, stream),
-           "ss_scan_fwd_complex")
+    nb = ss_scan_workspace_bytes(desc, SS_OP_FWD_COMPLEX)
+    ws = workspace(nb, u.device)
+    _check(ss_scan_fwd_complex_ws(desc, u, delta, A, B, C, D, delta_bias, z, h0, y, h_last, ws,
+                                  nb, stream), "ss_scan_fwd_complex_ws")
     return (y, h_last) if return_last_state else y
 
 

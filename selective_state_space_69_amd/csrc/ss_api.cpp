@@ -156,6 +156,42 @@ BwdPlan plan_bwd(const ss_desc_t& d) {
   return p;
 }
 
+// Complex-A forward: 32-channel workgroups, five per compute unit when the
+// problem is wide enough (B * ceil(D / 32) >= 640 groups, or short sequences:
+// one pass); otherwise time chunks of >= 128 steps so that about 1280
+// workgroups run, at the cost of the summary pass (the real scan's plan, with
+// the complex kernel's group size).  SS_SCAN_CHUNK overrides the chunk length.
+CplxPlan plan_fwd_complex(const ss_desc_t& d, bool allow_chunks) {
+  CplxPlan p;
+  const int64_t L = d.seqlen;
+  const int64_t cols = d.batch * ((d.dim + 31) / 32);
+  constexpr int64_t kWide = 640, kWant = 1280, kMinChunk = 128;
+  int64_t chunk = L;
+  if (allow_chunks) {
+    const int64_t forced = env_int("SS_SCAN_CHUNK");
+    if (forced > 0) {
+      chunk = forced;
+    } else if (cols < kWide && L >= 2 * kMinChunk) {
+      const int64_t want = (kWant + cols - 1) / cols;
+      chunk = (L + want - 1) / want;
+      if (chunk < kMinChunk) chunk = kMinChunk;
+      chunk = (chunk + 15) / 16 * 16;
+    }
+  }
+  if (chunk > L) chunk = L;
+  p.chunk_len = chunk;
+  p.nchunks = (L + chunk - 1) / chunk;
+  if (p.nchunks > 1) {
+    const size_t B = size_t(d.batch), C = size_t(p.nchunks), D = size_t(d.dim),
+                 N = size_t(d.dstate);
+    size_t off = 0;
+    p.off_hend = off; off += align_up(B * C * N * D * 2 * sizeof(float));
+    p.off_dsum = off; off += align_up(B * C * D * sizeof(double));
+    p.bytes = off;
+  }
+  return p;
+}
+
 namespace {
 
 // Conv1d descriptions: positive sizes, width 1..4, 32-bit segment count.
@@ -281,6 +317,7 @@ size_t ss_scan_workspace_bytes(const ss_desc_t* desc, int op) {
   if (check_desc(desc, true) != SS_OK) return 0;
   if (op == SS_OP_FWD) return plan_fwd(*desc).bytes;
   if (op == SS_OP_BWD) return plan_bwd(*desc).bytes;
+  if (op == SS_OP_FWD_COMPLEX) return plan_fwd_complex(*desc, true).bytes;
   return 0;
 }
 
@@ -308,10 +345,10 @@ int ss_scan_fwd_noalloc(const ss_desc_t* desc, const void* u, const void* delta,
                   h_last, nullptr, 0, true, stream);
 }
 
-int ss_scan_fwd_complex(const ss_desc_t* desc, const void* u, const void* delta, const float* A,
-                        const void* Bm, const void* Cm, const float* D_skip,
-                        const float* delta_bias, const void* z, const float* h0, void* y,
-                        float* h_last, void* stream) {
+int ss_scan_fwd_complex_ws(const ss_desc_t* desc, const void* u, const void* delta,
+                           const float* A, const void* Bm, const void* Cm, const float* D_skip,
+                           const float* delta_bias, const void* z, const float* h0, void* y,
+                           float* h_last, void* workspace, size_t ws_bytes, void* stream) {
   int rc = check_desc(desc, true);
   if (rc != SS_OK) return rc;
   if (!u || !delta || !A || !Bm || !Cm || !y) return SS_ERR_INVALID_ARG;
@@ -320,11 +357,23 @@ int ss_scan_fwd_complex(const ss_desc_t* desc, const void* u, const void* delta,
   const void* ptrs[] = {u, delta, Bm, Cm, z, A, D_skip, delta_bias, h0, h_last, y};
   for (const void* p : ptrs)
     if (p && !aligned(p, kPtrAlign)) return SS_ERR_INVALID_ARG;
+  // the one-pass plan when the caller brings no workspace at all
+  const CplxPlan plan = plan_fwd_complex(*desc, workspace != nullptr || ws_bytes != 0);
+  if (plan.bytes > 0 && (!workspace || ws_bytes < plan.bytes || !aligned(workspace, kAlign)))
+    return SS_ERR_WORKSPACE;
   if ((rc = check_device()) != SS_OK) return rc;
-  return launch_fwd_complex(*desc, u, delta, A, Bm, Cm, D_skip, delta_bias, z, h0, y, h_last,
-                            stream) == 0
+  return launch_fwd_complex(*desc, plan, u, delta, A, Bm, Cm, D_skip, delta_bias, z, h0, y,
+                            h_last, static_cast<char*>(workspace), stream) == 0
              ? SS_OK
              : SS_ERR_HIP;
+}
+
+int ss_scan_fwd_complex(const ss_desc_t* desc, const void* u, const void* delta, const float* A,
+                        const void* Bm, const void* Cm, const float* D_skip,
+                        const float* delta_bias, const void* z, const float* h0, void* y,
+                        float* h_last, void* stream) {
+  return ss_scan_fwd_complex_ws(desc, u, delta, A, Bm, Cm, D_skip, delta_bias, z, h0, y, h_last,
+                                nullptr, 0, stream);
 }
 
 int ss_scan_bwd(const ss_desc_t* desc, const void* u, const void* delta, const float* A,

@@ -18,14 +18,35 @@
 // softplus and gate, publishes (dt, u) through LDS for the other lanes, and
 // stores its y.  The 8 per-step partial sums of C h a lane builds in a block
 // are reduce-scattered over the channel's 8 lanes (DPP half-row mirror, then
-// quad swaps), so lane q ends with the sum for its own step.  Each state and
-// step needs one v_exp_f32 (the modulus) and one v_sin_f32 / v_cos_f32 pair
-// (the phase, in revolutions, reduced to [0, 1) first).  B and C rows of a
+// quad swaps), so lane q ends with the sum for its own step.
+//
+// Two forms of the step.  The fast one forms abar from one v_exp_f32 (the
+// modulus) and one v_sin_f32 / v_cos_f32 pair (the phase, in revolutions).
+// Those hardware results are off by up to ~1.3e-7, and v_cos_f32 is biased
+// low by ~5e-8 near a zero phase; a state remembered for M steps at a nearly
+// constant step size compounds that bias to ~M * 5e-8 of its modulus, which
+// outgrows the fp32 bound once M reaches a few thousand steps.  The precise
+// form carries E = abar - 1 = e^x (cos th + i sin th) - 1 instead,
+// h <- h + (E h + bcoef B u), with e^x - 1 to full relative accuracy and sin,
+// cos and cos - 1 from polynomials (sincos_rev), and takes the ZOH coefficient
+// as E / a.  fp32 inputs always take it; bf16 waves take it when some state
+// decays slowly (|Re a| < kWeakA), the others keep the fast form, whose error
+// stays inside the bf16 bound.  B and C rows of a
 // block are staged in LDS as fp32 (re, im) pairs; the inputs of the next block
-// are fetched while the current one runs.  No time chunks: one workgroup walks
-// the whole sequence of its channels.  On the Mamba-2.8B width (B = 8,
+// are fetched while the current one runs.  On the Mamba-2.8B width (B = 8,
 // D = 5120) the grid is 1280 workgroups: five per compute unit, five waves per
-// SIMD.
+// SIMD, each walking the whole sequence of its channels.
+//
+// Long, narrow problems are cut into time chunks, as the real scan is: a
+// summary pass runs each chunk but the last from a zero state and keeps its end
+// state and its sum of step sizes; an in-order walk (one lane per (b, n, d))
+// turns those into each chunk's start state with the chunk maps
+// h -> abar_c h + s_c, abar_c = exp(a sum dt) ("A Visual Guide to Mamba"
+// summary, The Scan Operation: segments combined associatively); the output
+// pass then runs every chunk from its true start.  The step sums are kept in
+// fp64: a chunk's rotation angle Im(a) sum dt reaches hundreds of radians, and
+// an fp32 sum (relative error ~1e-6 over thousands of steps) would put ~1e-2 rad
+// of phase error into the carried state.
 #include <type_traits>
 
 #include "ss_device.hpp"
@@ -40,7 +61,8 @@ constexpr int kChPerWave = kWave / kLPC;
 constexpr int kCWaves = 4;
 constexpr int kChPerGroup = kChPerWave * kCWaves;
 constexpr int kMaxC = kSPL * kLPC;       // 16 complex states
-constexpr float kInv2Pi = 0.15915494309189535f;
+constexpr double kLn2Over2Pi = 0.69314718055994531 / 6.283185307179586;   // revolutions per log2 e
+constexpr double kLog2eD = 1.4426950408889634;
 static_assert(kLPC == kCBlk, "lane q of a channel owns step q of a block");
 
 struct CParams {
@@ -55,8 +77,13 @@ struct CParams {
   const float* h0;      // (B, D, N, 2)
   void* y;
   float* h_last;        // (B, D, N, 2)
+  // (B, nc, N, D) complex: chunk c's zero-start end state from the summary pass
+  // (c <= nc - 2), then the start state of chunk c (c >= 1)
+  float2* hend;
+  double* dsum;         // (B, nc, D): sum over chunk c of dt log2 e (c <= nc - 2)
   int64_t L, D;
-  int32_t N, ndblk;
+  int64_t chunk_len;
+  int32_t N, ndblk, nchunks, grid_chunks;
 };
 
 // x from the lane DPP control CTRL selects (every control used here has a
@@ -86,6 +113,78 @@ __device__ __forceinline__ float reduce_scatter8(const float (&v)[8], int q) {
   return dpp_pair<kDppQuadXor1>(e[0], e[1], (q & 1) != 0);
 }
 
+// sin(2 pi ph), cos(2 pi ph) and cos(2 pi ph) - 1 for a phase ph in
+// revolutions (|ph| < 2^22), each to about 2 ulp (cos - 1 relative to itself):
+// ph = k / 2 + r with k = rint(2 ph) and |r| <= 1/4 (exact in fp32), Taylor
+// polynomials of sin t (through t^13) and cos t - 1 (through t^12) at
+// t = 2 pi r, |t| <= pi / 2 (truncation below 7e-10 and 7e-9 relative), then
+// a sign flip for odd k.  2 pi enters as a two-term split, so t is rounded
+// once.
+__device__ __forceinline__ void sincos_rev(float ph, float& s, float& c, float& cm1) {
+  constexpr float kTwoPiHi = 6.28318548202514648f;        // fp32(2 pi)
+  constexpr float kTwoPiLo = -1.7484555314695172e-07f;    // 2 pi - kTwoPiHi
+  const float k = __builtin_rintf(2.0f * ph);
+  const float r = __builtin_fmaf(k, -0.5f, ph);
+  const float t = __builtin_fmaf(r, kTwoPiHi, r * kTwoPiLo);
+  const float t2 = t * t;
+  float ps = 1.0f / 6227020800.0f;                        // 1 / 13!
+  ps = __builtin_fmaf(ps, t2, -1.0f / 39916800.0f);
+  ps = __builtin_fmaf(ps, t2, 1.0f / 362880.0f);
+  ps = __builtin_fmaf(ps, t2, -1.0f / 5040.0f);
+  ps = __builtin_fmaf(ps, t2, 1.0f / 120.0f);
+  ps = __builtin_fmaf(ps, t2, -1.0f / 6.0f);
+  ps = __builtin_fmaf(ps, t2, 1.0f);
+  float pc = 1.0f / 479001600.0f;                         // 1 / 12!
+  pc = __builtin_fmaf(pc, t2, -1.0f / 3628800.0f);
+  pc = __builtin_fmaf(pc, t2, 1.0f / 40320.0f);
+  pc = __builtin_fmaf(pc, t2, -1.0f / 720.0f);
+  pc = __builtin_fmaf(pc, t2, 1.0f / 24.0f);
+  pc = __builtin_fmaf(pc, t2, -0.5f);
+  const float st = t * ps, cmt = t2 * pc;                 // sin t, cos t - 1
+  const bool odd = __builtin_amdgcn_fractf(0.5f * k) != 0.0f;
+  s = odd ? -st : st;
+  c = odd ? -1.0f - cmt : 1.0f + cmt;
+  cm1 = odd ? -2.0f - cmt : cmt;
+}
+
+// dt log2 e = softplus(delta + bias) log2 e (or (delta + bias) log2 e), with the
+// argument x2 = (delta + bias) log2 e carried as two terms.  Rounded to fp32
+// once, x2 (|x2| ~ 9 at dt ~ 1e-3, ulp ~ 1e-6) would put up to ~3e-7 of
+// relative error into dt, and the bias's share of that error repeats every
+// step; a complex state turns through Im(a) / |Re(a)| radians over its memory
+// (~75 for the S4D-Lin A), which multiplies a repeated error in dt.  Here
+// b2h + b2l = bias log2 e (formed in fp64), delta log2 e keeps its exact
+// product error, the two high parts meet in a TwoSum, and 2^-|x2| takes the
+// low part to first order (it is below 2^-20 of x2).  The rest is
+// softplus_log2's Fast2Sum form of log2(1 + e).
+__device__ __forceinline__ float step_log2(float delta, float b2h, float b2l, bool softplus) {
+  constexpr float kL2eHi = 1.44269502162933349609375f;    // fp32(log2 e)
+  constexpr float kL2eLo = 1.925963033500011e-08f;         // log2 e - kL2eHi
+  const float ph = delta * kL2eHi;
+  const float pl = __builtin_fmaf(delta, kL2eHi, -ph) + delta * kL2eLo;
+  const float sh = ph + b2h;                               // TwoSum: sh + sl = ph + b2h
+  const float bv = sh - ph;
+  const float sl = (ph - (sh - bv)) + (b2h - bv);
+  const float lo = sl + (pl + b2l);
+  if (!softplus) return sh + lo;
+  const bool pos = sh > 0.0f;
+  const float e0 = hw_exp2(-__builtin_fabsf(sh));
+  const float e = __builtin_fmaf(e0, (pos ? -lo : lo) * kLn2, e0);   // 2^-|sh + lo|
+  const float u1 = 1.0f + e;
+  const float r = e - (u1 - 1.0f);                         // exact rounding error of u1
+  const float k = __builtin_fmaf(-u1, kLog2e, 2.0f * kLog2e);
+  return __builtin_fmaxf(sh, 0.0f) + ((pos ? lo : 0.0f) + __builtin_fmaf(r, k, hw_log2(u1)));
+}
+
+// E = abar - 1 for abar = e^x (cos th + i sin th): y2 = x log2 e, ph = th / 2 pi
+__device__ __forceinline__ void cexpm1(float y2, float ph, float& er, float& ei) {
+  const float em1 = precise_expm1(y2);
+  float sn, cs, cm1;
+  sincos_rev(ph, sn, cs, cm1);
+  er = __builtin_fmaf(em1, cs, cm1);       // (e^x - 1) cos th + (cos th - 1)
+  ei = __builtin_fmaf(em1, sn, sn);        // e^x sin th
+}
+
 template <typename In>
 struct Pair;
 template <>
@@ -109,25 +208,35 @@ struct Pair<uint16_t> {
   }
 };
 
-template <typename In, typename Out, int DISC, bool HAS_Z, bool SOFTPLUS>
-// five waves per SIMD (five workgroups per CU at the 2.8B width): at most 96 VGPRs
-__global__ __launch_bounds__(kWave * kCWaves, 5) void fwd_complex_kernel(CParams p) {
+// SUMMARY: run chunk `chunk` from a zero state and keep its end state and step
+// sum (no output); otherwise run it from its start state and store y.
+template <typename In, typename Out, int DISC, bool HAS_Z, bool SOFTPLUS, bool SUMMARY>
+// five waves per SIMD (five workgroups per CU at the 2.8B width): at most 96
+// VGPRs; the summary pass, which also keeps an fp64 step sum, four (128 VGPRs)
+__global__ __launch_bounds__(kWave * kCWaves, SUMMARY ? 4 : 5) void fwd_complex_kernel(CParams p) {
   const int tid = int(threadIdx.x);
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int lane = tid % kWave;
   const int q = lane % kLPC, cl = lane / kLPC;
   const int chan = wave * kChPerWave + cl;                 // channel within the group
   const int dblk = int(blockIdx.x % unsigned(p.ndblk));
-  const int64_t b = int64_t(blockIdx.x / unsigned(p.ndblk));
+  const int64_t rest = int64_t(blockIdx.x / unsigned(p.ndblk));
+  const int chunk = int(rest % p.grid_chunks);
+  const int64_t b = rest / p.grid_chunks;
   const int64_t d = int64_t(dblk) * kChPerGroup + chan;
   const bool active = d < p.D;
   const int64_t dc = active ? d : p.D - 1;
   const int N = p.N;
   const int64_t L = p.L, D = p.D;
+  // this workgroup's steps [tb, te); "L" below bounds the loads and stores
+  const int64_t tb = int64_t(chunk) * p.chunk_len;
+  const int64_t te = tb + p.chunk_len < L ? tb + p.chunk_len : L;
 
-  // per-state constants: modulus rate, phase rate (revolutions per dt log2 e),
-  // a itself and 1 / a (0 when a == 0)
-  float ar[kSPL], aw[kSPL], ai[kSPL], iar[kSPL], iai[kSPL], hr[kSPL], hi[kSPL];
+  // per-state constants: modulus rate, phase rate (revolutions per dt log2 e,
+  // formed in fp64 and kept as aw + awl, so that the rate carries no rounding
+  // that would repeat every step), 1 / a (0 when a == 0) and z0 = [a == 0]
+  // (the ZOH coefficient is then dt)
+  float ar[kSPL], aw[kSPL], awl[kSPL], iar[kSPL], iai[kSPL], z0[kSPL], hr[kSPL], hi[kSPL];
   bool weak = false;
 #pragma unroll
   for (int j = 0; j < kSPL; ++j) {
@@ -138,23 +247,35 @@ __global__ __launch_bounds__(kWave * kCWaves, 5) void fwd_complex_kernel(CParams
       im = p.A[(dc * N + n) * 2 + 1];
     }
     ar[j] = re;
-    ai[j] = im;
-    aw[j] = im * (kLn2 * kInv2Pi);
+    const double awd = double(im) * kLn2Over2Pi;
+    aw[j] = float(awd);
+    awl[j] = float(awd - double(aw[j]));
     const float m2 = re * re + im * im;
-    weak |= m2 < kWeakA * kWeakA;
+    weak |= !(__builtin_fabsf(re) >= kWeakA);
     iar[j] = m2 == 0.0f ? 0.0f : re / m2;
     iai[j] = m2 == 0.0f ? 0.0f : -im / m2;
+    z0[j] = m2 == 0.0f ? 1.0f : 0.0f;
     hr[j] = 0.0f;
     hi[j] = 0.0f;
-    if (p.h0 && n < N) {
-      hr[j] = p.h0[((b * D + dc) * N + n) * 2];
-      hi[j] = p.h0[((b * D + dc) * N + n) * 2 + 1];
+    if (!SUMMARY && n < N) {
+      if (chunk == 0 && p.h0) {
+        hr[j] = p.h0[((b * D + dc) * N + n) * 2];
+        hi[j] = p.h0[((b * D + dc) * N + n) * 2 + 1];
+      } else if (chunk > 0) {
+        const float2 hs = p.hend[((b * p.nchunks + chunk) * N + n) * D + dc];
+        hr[j] = hs.x;
+        hi[j] = hs.y;
+      }
     }
   }
-  // exact ZOH: the guarded coefficient where some state of the wave has |a| < kWeakA
-  const bool guard = __any(weak);
+  double dsum = 0.0;
+  // the precise step for fp32 inputs and for waves holding a slowly decaying state
+  bool precise;
+  if constexpr (std::is_same<In, float>::value) precise = true;
+  else precise = __any(weak);
   const float Dd = p.Dskip ? p.Dskip[dc] : 0.0f;
-  const float bias2 = (p.bias ? p.bias[dc] : 0.0f) * kLog2e;
+  const double b2 = double(p.bias ? p.bias[dc] : 0.0f) * kLog2eD;   // bias log2 e, two terms
+  const float b2h = float(b2), b2l = float(b2 - double(b2h));
 
   // B and C rows of a block: [buffer][step][B | C][state] as (re, im); the
   // owned steps' (dt log2 e, u): [buffer][step][channel]
@@ -175,38 +296,48 @@ __global__ __launch_bounds__(kWave * kCWaves, 5) void fwd_complex_kernel(CParams
   // their step size and input are forced to 0 below)
   auto fetch = [&](auto S_, int64_t t0) {
     constexpr int S = decltype(S_)::value;
-    const int64_t t = t0 + q < L ? t0 + q : L - 1;
+    const int64_t t = t0 + q < te ? t0 + q : te - 1;
     ur[S] = ub[t * D];
     dr[S] = db[t * D];
-    if (HAS_Z) zr[S] = zb[t * D];
-    const int64_t tr = t0 + sk < L ? t0 + sk : L - 1;
+    if (HAS_Z && !SUMMARY) zr[S] = zb[t * D];
+    const int64_t tr = t0 + sk < te ? t0 + sk : te - 1;
     rw[S] = Pair<In>::load(rbase + ((b * L + tr) * N + (sn < N ? sn : 0)) * 2);
   };
   // the block's rows and this lane's owned-step values into buffer S
-  auto stage = [&](auto S_, int64_t t0) {
+  // P: the precise step, which also takes the step size from the two-term
+  // argument (the fast step's error budget does not need it)
+  auto stage = [&](auto S_, auto P_, int64_t t0) {
     constexpr int S = decltype(S_)::value;
+    constexpr bool P = decltype(P_)::value;
     float2 v = Pair<In>::f32(rw[S]);
-    if (sn >= N || t0 + sk >= L) v = make_float2(0.0f, 0.0f);
+    if (sn >= N || t0 + sk >= te) v = make_float2(0.0f, 0.0f);
     rows[S][sk][sw][sn] = v;
-    const bool valid = t0 + q < L;
-    const float x2 = __builtin_fmaf(to_f32(dr[S]), kLog2e, bias2);
-    const float dl = valid ? (SOFTPLUS ? softplus_log2(x2) : x2) : 0.0f;   // dt log2 e
+    const bool valid = t0 + q < te;
+    float dl;                                                         // dt log2 e
+    if (P) {
+      dl = step_log2(to_f32(dr[S]), b2h, b2l, SOFTPLUS);
+    } else {
+      const float x2 = __builtin_fmaf(to_f32(dr[S]), kLog2e, b2h);
+      dl = SOFTPLUS ? softplus_log2(x2) : x2;
+    }
+    dl = valid ? dl : 0.0f;
     u_own[S] = valid ? to_f32(ur[S]) : 0.0f;
-    g_own[S] = HAS_Z ? silu(to_f32(zr[S])) : 1.0f;
+    g_own[S] = HAS_Z && !SUMMARY ? silu(to_f32(zr[S])) : 1.0f;
     act[S][q][chan] = make_float2(dl, u_own[S]);
   };
 
-  // G: the wave holds a slowly decaying state (guarded coefficient); a
-  // template parameter so that the fast loop has no branch inside
-  auto block = [&](auto S_, auto G_, int64_t t0) {
+  // P: the precise step (a template parameter, so that neither loop branches)
+  auto block = [&](auto S_, auto P_, int64_t t0) {
     constexpr int S = decltype(S_)::value;
-    constexpr bool G = decltype(G_)::value;
-    if (t0 + kCBlk < L) fetch(std::integral_constant<int, S ^ 1>{}, t0 + kCBlk);
+    constexpr bool P = decltype(P_)::value;
+    if (t0 + kCBlk < te) fetch(std::integral_constant<int, S ^ 1>{}, t0 + kCBlk);
     float part[kCBlk];                                     // Re sum_n C h, per step
+    float bsum = 0.0f;                                     // the block's step sum
 #pragma unroll
     for (int k = 0; k < kCBlk; ++k) {
       const float2 du = act[S][k][chan];
       const float dl = du.x, uk = du.y;
+      if (SUMMARY) bsum += dl;
       const float dt = dl * kLn2;
       const float4 bq = *reinterpret_cast<const float4*>(&rows[S][k][0][kSPL * q]);
       const float4 cq = *reinterpret_cast<const float4*>(&rows[S][k][1][kSPL * q]);
@@ -215,65 +346,78 @@ __global__ __launch_bounds__(kWave * kCWaves, 5) void fwd_complex_kernel(CParams
       float acc = 0.0f;
 #pragma unroll
       for (int j = 0; j < kSPL; ++j) {
-        const float e = hw_exp2(dl * ar[j]);                          // |abar|
-        const float ph = __builtin_amdgcn_fractf(dl * aw[j]);         // arg abar / 2 pi
-        const float abr = e * __builtin_amdgcn_cosf(ph);
-        const float abi = e * __builtin_amdgcn_sinf(ph);
-        float cr = dt, ci = 0.0f;                                     // Euler
-        if (DISC == SS_ZOH) {
-          const float mr = abr - 1.0f;                                // (abar - 1) / a
-          cr = mr * iar[j] - abi * iai[j];
-          ci = __builtin_fmaf(mr, iai[j], abi * iar[j]);
-          if (G) {
-            // a slowly decaying state in the wave: near x = dt a = 0 the
-            // quotient cancels, so take dt (1 + x/2 + x^2/6 + x^3/24) there
-            const float xr = dt * ar[j], xi = dt * ai[j];
-            float pr = __builtin_fmaf(xr, 1.0f / 24.0f, 1.0f / 6.0f), pi = xi * (1.0f / 24.0f);
-            float tr = __builtin_fmaf(pr, xr, __builtin_fmaf(-pi, xi, 0.5f));
-            pi = __builtin_fmaf(pr, xi, pi * xr);
-            pr = tr;
-            tr = __builtin_fmaf(pr, xr, __builtin_fmaf(-pi, xi, 1.0f));
-            pi = __builtin_fmaf(pr, xi, pi * xr);
-            const bool ser =
-                __builtin_unpredictable(__builtin_fmaf(xr, xr, xi * xi) < kZohSeries * kZohSeries);
-            cr = ser ? dt * tr : cr;
-            ci = ser ? dt * pi : ci;
-          }
-        }
         const float bur = Br[j] * uk, bui = Bi[j] * uk;
-        const float qr = cr * bur - ci * bui, qi = __builtin_fmaf(cr, bui, ci * bur);
-        const float nr = __builtin_fmaf(abr, hr[j], __builtin_fmaf(-abi, hi[j], qr));
-        const float ni = __builtin_fmaf(abr, hi[j], __builtin_fmaf(abi, hr[j], qi));
+        float nr, ni;
+        if (P) {
+          float er, ei;                                               // abar - 1
+          cexpm1(dl * ar[j], __builtin_fmaf(dl, aw[j], dl * awl[j]), er, ei);
+          float cr = dt, ci = 0.0f;                                   // Euler
+          if (DISC == SS_ZOH) {                                       // E / a (dt if a == 0)
+            cr = __builtin_fmaf(er, iar[j], __builtin_fmaf(-ei, iai[j], dt * z0[j]));
+            ci = __builtin_fmaf(er, iai[j], ei * iar[j]);
+          }
+          const float qr = cr * bur - ci * bui, qi = __builtin_fmaf(cr, bui, ci * bur);
+          nr = hr[j] + __builtin_fmaf(er, hr[j], __builtin_fmaf(-ei, hi[j], qr));
+          ni = hi[j] + __builtin_fmaf(er, hi[j], __builtin_fmaf(ei, hr[j], qi));
+        } else {
+          const float e = hw_exp2(dl * ar[j]);                        // |abar|
+          const float ph = __builtin_amdgcn_fractf(dl * aw[j]);       // arg abar / 2 pi
+          const float abr = e * __builtin_amdgcn_cosf(ph);
+          const float abi = e * __builtin_amdgcn_sinf(ph);
+          float cr = dt, ci = 0.0f;                                   // Euler
+          if (DISC == SS_ZOH) {
+            const float mr = abr - 1.0f;                              // (abar - 1) / a
+            cr = mr * iar[j] - abi * iai[j];
+            ci = __builtin_fmaf(mr, iai[j], abi * iar[j]);
+          }
+          const float qr = cr * bur - ci * bui, qi = __builtin_fmaf(cr, bui, ci * bur);
+          nr = __builtin_fmaf(abr, hr[j], __builtin_fmaf(-abi, hi[j], qr));
+          ni = __builtin_fmaf(abr, hi[j], __builtin_fmaf(abi, hr[j], qi));
+        }
         hr[j] = nr;
         hi[j] = ni;
-        acc = __builtin_fmaf(Cr[j], nr, __builtin_fmaf(-Ci[j], ni, acc));
+        if (!SUMMARY) acc = __builtin_fmaf(Cr[j], nr, __builtin_fmaf(-Ci[j], ni, acc));
       }
       part[k] = acc;
     }
-    // y of the owned step: the channel's sum for step q, skip, gate
-    const float sum = reduce_scatter8(part, q);
-    float yv = __builtin_fmaf(2.0f, sum, Dd * u_own[S]);
-    if (HAS_Z) yv *= g_own[S];
-    if (t0 + q < L && active) store_out<Out>(yb + (t0 + q) * D, yv);
+    if (SUMMARY) dsum += double(bsum);   // 8 fp32 terms per block, fp64 across blocks
+    if (!SUMMARY) {
+      // y of the owned step: the channel's sum for step q, skip, gate
+      const float sum = reduce_scatter8(part, q);
+      float yv = __builtin_fmaf(2.0f, sum, Dd * u_own[S]);
+      if (HAS_Z) yv *= g_own[S];
+      if (t0 + q < te && active) store_out<Out>(yb + (t0 + q) * D, yv);
+    }
     // the next block's rows and owned-step values into the other buffers (last
     // read by the previous block, which every wave finished before the
     // barrier that ended it)
-    if (t0 + kCBlk < L) stage(std::integral_constant<int, S ^ 1>{}, t0 + kCBlk);
+    if (t0 + kCBlk < te) stage(std::integral_constant<int, S ^ 1>{}, P_, t0 + kCBlk);
     __syncthreads();
   };
 
-  fetch(std::integral_constant<int, 0>{}, 0);
-  stage(std::integral_constant<int, 0>{}, 0);
-  __syncthreads();
-  auto walk = [&](auto G_) {
-    for (int64_t t0 = 0; t0 < L; t0 += 2 * kCBlk) {
-      block(std::integral_constant<int, 0>{}, G_, t0);
-      if (t0 + kCBlk < L) block(std::integral_constant<int, 1>{}, G_, t0 + kCBlk);
+  auto walk = [&](auto P_) {
+    fetch(std::integral_constant<int, 0>{}, tb);
+    stage(std::integral_constant<int, 0>{}, P_, tb);
+    __syncthreads();
+    for (int64_t t0 = tb; t0 < te; t0 += 2 * kCBlk) {
+      block(std::integral_constant<int, 0>{}, P_, t0);
+      if (t0 + kCBlk < te) block(std::integral_constant<int, 1>{}, P_, t0 + kCBlk);
     }
   };
-  if (DISC == SS_ZOH && guard) walk(std::true_type{});
+  if (precise) walk(std::true_type{});
   else walk(std::false_type{});
-  if (p.h_last && active) {
+  if (SUMMARY) {
+    if (active) {
+#pragma unroll
+      for (int j = 0; j < kSPL; ++j) {
+        const int n = kSPL * q + j;
+        if (n < N) p.hend[((b * p.nchunks + chunk) * N + n) * D + d] = make_float2(hr[j], hi[j]);
+      }
+      if (q == 0) p.dsum[(b * p.nchunks + chunk) * D + d] = dsum;
+    }
+    return;
+  }
+  if (p.h_last && active && te == L) {
 #pragma unroll
     for (int j = 0; j < kSPL; ++j) {
       const int n = kSPL * q + j;
@@ -286,30 +430,91 @@ __global__ __launch_bounds__(kWave * kCWaves, 5) void fwd_complex_kernel(CParams
 }
 
 template <typename In, typename Out, int DISC>
-hipError_t dispatch_flags(const CParams& p, bool has_z, bool sp, dim3 grid, hipStream_t st) {
+hipError_t dispatch_flags(const CParams& p, bool has_z, bool sp, bool summary, dim3 grid,
+                          hipStream_t st) {
   const dim3 block(kWave * kCWaves);
+  if (summary) {
+    // no output, no gate: one instantiation per input type (the fp32-output one)
+    if constexpr (std::is_same<Out, float>::value) {
+      if (sp) hipLaunchKernelGGL((fwd_complex_kernel<In, Out, DISC, false, true, true>), grid, block, 0, st, p);
+      else hipLaunchKernelGGL((fwd_complex_kernel<In, Out, DISC, false, false, true>), grid, block, 0, st, p);
+      return hipGetLastError();
+    } else {
+      return hipErrorInvalidValue;
+    }
+  }
   if (has_z) {
-    if (sp) hipLaunchKernelGGL((fwd_complex_kernel<In, Out, DISC, true, true>), grid, block, 0, st, p);
-    else hipLaunchKernelGGL((fwd_complex_kernel<In, Out, DISC, true, false>), grid, block, 0, st, p);
+    if (sp) hipLaunchKernelGGL((fwd_complex_kernel<In, Out, DISC, true, true, false>), grid, block, 0, st, p);
+    else hipLaunchKernelGGL((fwd_complex_kernel<In, Out, DISC, true, false, false>), grid, block, 0, st, p);
   } else {
-    if (sp) hipLaunchKernelGGL((fwd_complex_kernel<In, Out, DISC, false, true>), grid, block, 0, st, p);
-    else hipLaunchKernelGGL((fwd_complex_kernel<In, Out, DISC, false, false>), grid, block, 0, st, p);
+    if (sp) hipLaunchKernelGGL((fwd_complex_kernel<In, Out, DISC, false, true, false>), grid, block, 0, st, p);
+    else hipLaunchKernelGGL((fwd_complex_kernel<In, Out, DISC, false, false, false>), grid, block, 0, st, p);
   }
   return hipGetLastError();
 }
 
 template <typename In, typename Out>
-hipError_t dispatch_disc(const CParams& p, int disc, bool has_z, bool sp, dim3 grid,
+hipError_t dispatch_disc(const CParams& p, int disc, bool has_z, bool sp, bool summary, dim3 grid,
                          hipStream_t st) {
-  return disc == SS_ZOH ? dispatch_flags<In, Out, SS_ZOH>(p, has_z, sp, grid, st)
-                        : dispatch_flags<In, Out, SS_EULER>(p, has_z, sp, grid, st);
+  return disc == SS_ZOH ? dispatch_flags<In, Out, SS_ZOH>(p, has_z, sp, summary, grid, st)
+                        : dispatch_flags<In, Out, SS_EULER>(p, has_z, sp, summary, grid, st);
+}
+
+hipError_t dispatch_types(const ss_desc_t& d, const CParams& p, bool summary, dim3 grid,
+                          hipStream_t st) {
+  const bool has_z = p.z != nullptr, sp = d.delta_softplus != 0;
+  if (d.in_dtype == SS_BF16)
+    return d.out_dtype == SS_F32 || summary
+               ? dispatch_disc<uint16_t, float>(p, d.disc, has_z, sp, summary, grid, st)
+               : dispatch_disc<uint16_t, uint16_t>(p, d.disc, has_z, sp, false, grid, st);
+  return d.out_dtype == SS_F32 || summary
+             ? dispatch_disc<float, float>(p, d.disc, has_z, sp, summary, grid, st)
+             : dispatch_disc<float, uint16_t>(p, d.disc, has_z, sp, false, grid, st);
+}
+
+// Chunk carries of the complex scan: one lane per (b, n, d) walks the chunks
+// in order.  Slot c of hend holds chunk c's zero-start end state s_c
+// (c <= nc - 2); afterwards slot c (c >= 1) holds chunk c's start state.  The
+// chunk map is h -> abar_c h + s_c with abar_c = exp(a sum dt), applied in the
+// precise form h + (E_c h + s_c), E_c = abar_c - 1; its phase Im(a) sum dt is
+// reduced to [-1/2, 1/2] revolutions in fp64 (the sum is fp64 too).
+__global__ __launch_bounds__(256) void complex_walk_kernel(float2* __restrict__ hend,
+                                                           const double* __restrict__ dsum,
+                                                           const float* __restrict__ A,
+                                                           const float* __restrict__ h0,
+                                                           int64_t B, int64_t D, int N, int nc) {
+  const int64_t gid = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (gid >= B * N * D) return;
+  const int64_t d = gid % D;
+  const int n = int((gid / D) % N);
+  const int64_t b = gid / (D * N);
+  const float ar = A[(d * N + n) * 2];
+  const double aw = double(A[(d * N + n) * 2 + 1]) * kLn2Over2Pi;
+  float hr = h0 ? h0[((b * D + d) * N + n) * 2] : 0.0f;
+  float hi = h0 ? h0[((b * D + d) * N + n) * 2 + 1] : 0.0f;
+  float2* st = hend + (b * nc) * int64_t(N) * D + int64_t(n) * D + d;
+  const int64_t sstride = int64_t(N) * D;
+  const double* ds = dsum + (b * nc) * D + d;
+  for (int c = 0; c < nc - 1; ++c) {
+    const float2 sc = st[c * sstride];
+    if (c >= 1) st[c * sstride] = make_float2(hr, hi);
+    const double dl = ds[int64_t(c) * D];                 // sum of dt log2 e over the chunk
+    const double rev = dl * aw;
+    float er, ei;                                         // abar_c - 1
+    cexpm1(float(dl) * ar, float(rev - __builtin_rint(rev)), er, ei);
+    const float nr = hr + __builtin_fmaf(er, hr, __builtin_fmaf(-ei, hi, sc.x));
+    const float ni = hi + __builtin_fmaf(er, hi, __builtin_fmaf(ei, hr, sc.y));
+    hr = nr;
+    hi = ni;
+  }
+  st[int64_t(nc - 1) * sstride] = make_float2(hr, hi);
 }
 
 // One recurrent step with complex A (decoding): h (B, D, N, 2) in place, y (B, D).
 // kLPC lanes per (b, d), lane q holding states n = kSPL q + j as in the scan,
-// with the same per-state arithmetic (modulus and phase of A_bar, the ZOH
-// coefficient with its series near dt a = 0), so a step continues a scan.  The
-// lanes' partial sums of Re C h meet by butterflies in a fixed order.
+// always in the scan's precise form (E = abar - 1, the ZOH coefficient E / a),
+// so a step continues a scan.  The lanes' partial sums of Re C h meet by
+// butterflies in a fixed order.
 template <typename In, typename Out, int DISC, bool HAS_Z, bool SOFTPLUS>
 __global__ __launch_bounds__(256) void step_complex_kernel(StepArgs a, int64_t BD, int64_t D, int N) {
   const int64_t gid = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
@@ -318,9 +523,9 @@ __global__ __launch_bounds__(256) void step_complex_kernel(StepArgs a, int64_t B
   const bool live = ch < BD;
   const int64_t chc = live ? ch : BD - 1;                 // idle lanes still join the butterflies
   const int64_t b = chc / D, d = chc % D;
-  const float x2 = __builtin_fmaf(to_f32(static_cast<const In*>(a.delta)[chc]), kLog2e,
-                                  (a.bias ? a.bias[d] : 0.0f) * kLog2e);
-  const float dl = SOFTPLUS ? softplus_log2(x2) : x2;     // dt log2 e
+  const double b2 = double(a.bias ? a.bias[d] : 0.0f) * kLog2eD;
+  const float b2h = float(b2), b2l = float(b2 - double(b2h));
+  const float dl = step_log2(to_f32(static_cast<const In*>(a.delta)[chc]), b2h, b2l, SOFTPLUS);
   const float dt = dl * kLn2;
   const float uk = to_f32(static_cast<const In*>(a.u)[chc]);
   float acc = 0.0f;
@@ -331,25 +536,14 @@ __global__ __launch_bounds__(256) void step_complex_kernel(StepArgs a, int64_t B
     const float ar = a.A[(d * N + n) * 2], ai = a.A[(d * N + n) * 2 + 1];
     const float m2 = ar * ar + ai * ai;
     const float iar = m2 == 0.0f ? 0.0f : ar / m2, iai = m2 == 0.0f ? 0.0f : -ai / m2;
-    const float e = hw_exp2(dl * ar);
-    const float ph = __builtin_amdgcn_fractf(dl * (ai * (kLn2 * kInv2Pi)));
-    const float abr = e * __builtin_amdgcn_cosf(ph), abi = e * __builtin_amdgcn_sinf(ph);
+    const double awd = double(ai) * kLn2Over2Pi;
+    const float aw = float(awd), awl = float(awd - double(aw));
+    float er, ei;                                                 // abar - 1
+    cexpm1(dl * ar, __builtin_fmaf(dl, aw, dl * awl), er, ei);
     float cr = dt, ci = 0.0f;                                     // Euler
-    if (DISC == SS_ZOH) {
-      const float mr = abr - 1.0f;
-      cr = mr * iar - abi * iai;
-      ci = __builtin_fmaf(mr, iai, abi * iar);
-      const float xr = dt * ar, xi = dt * ai;
-      float pr = __builtin_fmaf(xr, 1.0f / 24.0f, 1.0f / 6.0f), pi = xi * (1.0f / 24.0f);
-      float tr = __builtin_fmaf(pr, xr, __builtin_fmaf(-pi, xi, 0.5f));
-      pi = __builtin_fmaf(pr, xi, pi * xr);
-      pr = tr;
-      tr = __builtin_fmaf(pr, xr, __builtin_fmaf(-pi, xi, 1.0f));
-      pi = __builtin_fmaf(pr, xi, pi * xr);
-      const bool ser =
-          __builtin_unpredictable(__builtin_fmaf(xr, xr, xi * xi) < kZohSeries * kZohSeries);
-      cr = ser ? dt * tr : cr;
-      ci = ser ? dt * pi : ci;
+    if (DISC == SS_ZOH) {                                         // E / a (dt if a == 0)
+      cr = __builtin_fmaf(er, iar, __builtin_fmaf(-ei, iai, m2 == 0.0f ? dt : 0.0f));
+      ci = __builtin_fmaf(er, iai, ei * iar);
     }
     const typename Pair<In>::raw rb = Pair<In>::load(static_cast<const In*>(a.Bm) + (b * N + n) * 2);
     const typename Pair<In>::raw rc = Pair<In>::load(static_cast<const In*>(a.Cm) + (b * N + n) * 2);
@@ -358,8 +552,8 @@ __global__ __launch_bounds__(256) void step_complex_kernel(StepArgs a, int64_t B
     const float qr = cr * bur - ci * bui, qi = __builtin_fmaf(cr, bui, ci * bur);
     float* hp = a.h + (chc * N + n) * 2;
     const float hr = hp[0], hi = hp[1];
-    const float nr = __builtin_fmaf(abr, hr, __builtin_fmaf(-abi, hi, qr));
-    const float ni = __builtin_fmaf(abr, hi, __builtin_fmaf(abi, hr, qi));
+    const float nr = hr + __builtin_fmaf(er, hr, __builtin_fmaf(-ei, hi, qr));
+    const float ni = hi + __builtin_fmaf(er, hi, __builtin_fmaf(ei, hr, qi));
     if (live) {
       hp[0] = nr;
       hp[1] = ni;
@@ -409,22 +603,33 @@ int launch_step_complex(const ss_desc_t& d, const StepArgs& s, void* stream) {
   return int(e);
 }
 
-int launch_fwd_complex(const ss_desc_t& d, const void* u, const void* delta, const float* A,
-                       const void* Bm, const void* Cm, const float* Dskip, const float* bias,
-                       const void* z, const float* h0, void* y, float* h_last, void* stream) {
-  CParams p{u, delta, A, Bm, Cm, Dskip, bias, z, h0, y, h_last, d.seqlen, d.dim,
-            int32_t(d.dstate), int32_t((d.dim + kChPerGroup - 1) / kChPerGroup)};
-  const dim3 grid(unsigned(d.batch * p.ndblk));
+int launch_fwd_complex(const ss_desc_t& d, const CplxPlan& plan, const void* u, const void* delta,
+                       const float* A, const void* Bm, const void* Cm, const float* Dskip,
+                       const float* bias, const void* z, const float* h0, void* y, float* h_last,
+                       char* ws, void* stream) {
+  CParams p{};
+  p.u = u; p.delta = delta; p.A = A; p.Bm = Bm; p.Cm = Cm; p.Dskip = Dskip; p.bias = bias;
+  p.z = z; p.h0 = h0; p.y = y; p.h_last = h_last;
+  p.L = d.seqlen; p.D = d.dim; p.N = int32_t(d.dstate);
+  p.ndblk = int32_t((d.dim + kChPerGroup - 1) / kChPerGroup);
+  p.chunk_len = plan.chunk_len;
+  p.nchunks = int32_t(plan.nchunks);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  const bool has_z = z != nullptr, sp = d.delta_softplus != 0;
-  hipError_t e;
-  if (d.in_dtype == SS_BF16)
-    e = d.out_dtype == SS_F32 ? dispatch_disc<uint16_t, float>(p, d.disc, has_z, sp, grid, st)
-                              : dispatch_disc<uint16_t, uint16_t>(p, d.disc, has_z, sp, grid, st);
-  else
-    e = d.out_dtype == SS_F32 ? dispatch_disc<float, float>(p, d.disc, has_z, sp, grid, st)
-                              : dispatch_disc<float, uint16_t>(p, d.disc, has_z, sp, grid, st);
-  return int(e);
+  const int64_t cols = d.batch * p.ndblk;
+  if (plan.nchunks > 1) {
+    p.hend = reinterpret_cast<float2*>(ws + plan.off_hend);
+    p.dsum = reinterpret_cast<double*>(ws + plan.off_dsum);
+    p.grid_chunks = p.nchunks - 1;     // the last chunk's summary is never needed
+    hipError_t e = dispatch_types(d, p, true, dim3(unsigned(cols * p.grid_chunks)), st);
+    if (e != hipSuccess) return int(e);
+    const int64_t lanes = d.batch * d.dstate * d.dim;
+    hipLaunchKernelGGL(complex_walk_kernel, dim3(unsigned((lanes + 255) / 256)), dim3(256), 0, st,
+                       p.hend, p.dsum, A, h0, d.batch, d.dim, int(d.dstate), p.nchunks);
+    e = hipGetLastError();
+    if (e != hipSuccess) return int(e);
+  }
+  p.grid_chunks = p.nchunks;
+  return int(dispatch_types(d, p, false, dim3(unsigned(cols * p.grid_chunks)), st));
 }
 
 }  // namespace ss

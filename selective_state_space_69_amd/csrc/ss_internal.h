@@ -162,10 +162,22 @@ int launch_conv_step(const ss_conv_desc_t& d, float* state, const void* x, const
 int launch_chunk_carry(float* states, const float* dsum, const float* A, const float* h0,
                        int64_t batch, int64_t D, int N, int nc, bool reverse, void* stream);
 int launch_step(const ss_desc_t& d, const StepArgs& a, void* stream);
+// Complex-A forward plan: 32 channels per workgroup, time cut into nchunks
+// chunks of chunk_len steps (one when nchunks == 1).  Workspace (256-byte
+// aligned): hend (B, nchunks, N, D) complex fp32 pairs (chunk summaries, then
+// chunk start states) and dsum (B, nchunks, D) fp64 (sums of dt log2 e).
+struct CplxPlan {
+  int64_t chunk_len = 0;
+  int64_t nchunks = 1;
+  size_t off_hend = 0, off_dsum = 0, bytes = 0;
+};
+// allow_chunks = false: the one-pass plan (no workspace)
+CplxPlan plan_fwd_complex(const ss_desc_t& d, bool allow_chunks);
 // Complex-A forward (ss_complex.hip): A (D,N,2), B, C (B,L,N,2), h0 / h_last (B,D,N,2).
-int launch_fwd_complex(const ss_desc_t& d, const void* u, const void* delta, const float* A,
-                       const void* Bm, const void* Cm, const float* Dskip, const float* bias,
-                       const void* z, const float* h0, void* y, float* h_last, void* stream);
+int launch_fwd_complex(const ss_desc_t& d, const CplxPlan& plan, const void* u, const void* delta,
+                       const float* A, const void* Bm, const void* Cm, const float* Dskip,
+                       const float* bias, const void* z, const float* h0, void* y, float* h_last,
+                       char* ws, void* stream);
 // Complex-A decode step (ss_complex.hip): h (B,D,N,2) in place, A (D,N,2), B, C (B,N,2).
 int launch_step_complex(const ss_desc_t& d, const StepArgs& a, void* stream);
 // SSD (Mamba-2) forward (ss_ssd.hip): one workgroup per (batch row, head);

@@ -37,7 +37,7 @@ def test_header_declares_entry_points():
               "ss_scan_strerror", "ss_scan_version", "ss_conv1d_fwd", "ss_conv1d_bwd",
               "ss_conv1d_step", "ss_conv1d_workspace_bytes", "ss_ssd_fwd", "ss_ssd_fwd_state",
               "ss_ssd_step", "ss_scan_fwd_dir", "ss_scan_fwd_complex", "ss_scan_step_complex",
-              "ss_scan_arch_supported", "ss_scan_fwd_noalloc"):
+              "ss_scan_arch_supported", "ss_scan_fwd_noalloc", "ss_scan_fwd_complex_ws"):
         assert n in names
 
 
@@ -355,3 +355,23 @@ def test_noalloc_validation_and_scratch_limit(lib):
     text = open(os.path.join(INCLUDE, "ss_scan.h")).read()
     m = re.search(r"#define SS_SCAN_STATIC_SCRATCH_BYTES \((\d+)u << (\d+)\)", text)
     assert m and int(m.group(1)) << int(m.group(2)) == B.SS_SCAN_STATIC_SCRATCH_BYTES
+
+
+def test_complex_ws_plan_and_validation(lib):
+    """The chunked complex forward: long narrow problems get a workspace (chunk
+    start states as complex pairs, fp64 step sums), wide ones none; a given but
+    short workspace is refused before any HIP call."""
+    P = FAKE
+    narrow = B.make_desc(1, 1 << 20, 256, 16, B.SS_BF16, B.SS_F32)
+    nb = B.ss_scan_workspace_bytes(narrow, B.SS_OP_FWD_COMPLEX)
+    # about 1280 workgroups of 32 channels: 160 chunks, the last without a summary slot
+    assert nb > 0 and nb % 256 == 0
+    assert nb >= 160 * 16 * 256 * 8 + 160 * 256 * 8
+    assert B.ss_scan_workspace_bytes(B.make_desc(8, 2048, 5120, 16), B.SS_OP_FWD_COMPLEX) == 0
+    assert B.ss_scan_workspace_bytes(B.make_desc(1, 200, 64, 16), B.SS_OP_FWD_COMPLEX) == 0
+    args = [P, P + 256, P + 512, P + 1024, P + 1536, None, None, None, None, P + 4096, None]
+    assert B.ss_scan_fwd_complex_ws(narrow, *args, P + 8192, nb - 1, stream=0) == B.SS_ERR_WORKSPACE
+    assert B.ss_scan_fwd_complex_ws(narrow, *args, P + 8200, nb, stream=0) == B.SS_ERR_WORKSPACE
+    bad = list(args)
+    bad[0] = None
+    assert B.ss_scan_fwd_complex_ws(narrow, *bad, P + 8192, nb, stream=0) == B.SS_ERR_INVALID_ARG

@@ -97,6 +97,74 @@ def test_complex_full_size(oracle):
     log("  max err / max|ref| =", r)
 
 
+# (SS_SCAN_CHUNK): time chunks of the chunked complex plan, and one pass ("100000")
+CHUNKED = [
+    # (B, L, D, N, disc, a_mode, dtype, h0, chunk)
+    (2, 3000, 64, 16, "zoh", "s4d_lin", "f32", True, "256"),
+    (1, 3001, 40, 16, "zoh", "random", "f32", True, "128"),
+    (2, 2000, 70, 9, "euler", "random", "f32", False, "336"),
+    (1, 1500, 96, 16, "zoh", "mixed", "f32", True, "144"),
+    (2, 700, 40, 16, "zoh", "weak", "f32", True, "128"),
+    (2, 2500, 100, 13, "zoh", "random", "bf16", True, "256"),
+    (1, 3000, 64, 16, "zoh", "s4d_lin", "f32", True, "100000"),
+]
+
+
+@pytest.mark.parametrize("case", CHUNKED, ids=lambda c: "b%d_l%d_d%d_n%d_%s_%s_%s_h0%d_chunk%s" % c)
+def test_complex_chunked(oracle, monkeypatch, case):
+    """The chunked complex plan (summary pass, fp64 step sums, in-order carry
+    walk, output pass from each chunk's start state) against the oracle: y and
+    the state after the last step, ragged last chunks, with and without h0."""
+    Bt, L, D, N, disc, amode, dt, h0, chunk = case
+    log("complex chunked", case)
+    monkeypatch.setenv("SS_SCAN_CHUNK", chunk)
+    inp = synth.make_complex_inputs(Bt, L, D, N, seed=3300 + CHUNKED.index(case), dtype=dt,
+                                    a_mode=amode, with_h0=h0)
+    y, hl = _gpu(_up(inp), disc)
+    torch.cuda.synchronize()
+    ref, href = _ref(oracle, inp, disc)
+    w = check_f32(y.cpu().numpy(), ref, "y")
+    hg = hl.cpu().numpy().astype(np.float64)
+    check_f32(hg[..., 0], href.real, "h_last re")
+    check_f32(hg[..., 1], href.imag, "h_last im")
+    log("  worst err/bound", w)
+
+
+def test_complex_chunked_equals_one_pass(monkeypatch):
+    """Chunked and one-pass complex scans agree on fp32 inputs (the precise step
+    on both sides; chunk maps exp(a sum dt) instead of the product of per-step
+    factors: fp32 reassociation only)."""
+    inp = synth.make_complex_inputs(2, 2500, 64, 16, seed=3350, dtype="f32", a_mode="random",
+                                    with_h0=True)
+    d = _up(inp)
+    monkeypatch.setenv("SS_SCAN_CHUNK", "100000")
+    y1, h1 = _gpu(d, "zoh")
+    for chunk in ("128", "400", "1000"):
+        monkeypatch.setenv("SS_SCAN_CHUNK", chunk)
+        y2, h2 = _gpu(d, "zoh")
+        torch.cuda.synchronize()
+        assert float((y1 - y2).abs().max()) <= 1e-5 * float(y1.abs().max()), chunk
+        assert float((h1 - h2).abs().max()) <= 1e-5 * float(h1.abs().max()), chunk
+
+
+def test_complex_long_full_size(oracle):
+    """The million-step shape (B=1, L=2^20, D=256, N=16 complex, bf16, S4D-Lin A,
+    steps in [1e-4, 1e-2]) on the planner's chunked layout; every element of y
+    against the oracle (max|y - y_ref| <= 2e-3 max|y_ref|)."""
+    Bt, L, D, N = 1, 1 << 20, 256, 16
+    log("complex long full size")
+    inp = synth.make_complex_inputs(Bt, L, D, N, seed=3360, dtype="bf16", dt_range=(1e-4, 1e-2))
+    desc = B.make_desc(Bt, L, D, N, B.SS_BF16, B.SS_F32, B.SS_ZOH, True)
+    assert B.ss_scan_workspace_bytes(desc, B.SS_OP_FWD_COMPLEX) > 0, "expected a chunked plan"
+    y = _gpu(_up(inp), "zoh", last=False)
+    torch.cuda.synchronize()
+    log("  oracle on every channel")
+    ref, _ = oracle.fwd_complex(inp.u, inp.delta, inp.A, inp.B, inp.C, D=inp.D,
+                                delta_bias=inp.delta_bias, z=inp.z, nthreads=oracle_threads())
+    r = check_rel_max(y.cpu().numpy(), ref, TOL_BF16, "complex long")
+    log("  max err / max|ref| =", r)
+
+
 def test_complex_deterministic():
     inp = synth.make_complex_inputs(2, 300, 200, 16, seed=3130, dtype="bf16")
     d = _up(inp)
