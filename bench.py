@@ -39,8 +39,8 @@ COMPLEX_SLOTS = 28.0
 
 # sources the forward half-wave kernel (the benchmark's dominant kernel) and its
 # launch are built from: a change to any of them voids its stored traffic figure
-HEADLINE_SOURCES = ("ss_device.hpp", "ss_fwd_common.hpp", "ss_fwd_hw.hip", "ss_fwd.hip",
-                    "ss_internal.h")
+HEADLINE_SOURCES = ("ss_device.hpp", "ss_fwd_common.hpp", "ss_fwd_hw.hpp", "ss_fwd_hw.hip",
+                    "ss_fwd_hw_dispatch.inc", "ss_fwd.hip", "ss_internal.h")
 
 
 def kernel_source_hash():

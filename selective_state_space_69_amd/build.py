@@ -22,7 +22,7 @@ BUILD = os.path.join(PKG, "_build")
 
 # slowest translation units first, so that the parallel build finishes sooner
 SOURCES = ["ss_fwd_bf16_f32.hip", "ss_fwd_bf16_bf16.hip", "ss_fwd_f32_f32.hip",
-           "ss_fwd_f32_bf16.hip", "ss_fwd_hw.hip", "ss_bwd.hip", "ss_ssd.hip", "ss_conv.hip",
+           "ss_fwd_f32_bf16.hip", "ss_fwd_hw.hip", "ss_fwd_hw1.hip", "ss_bwd.hip", "ss_ssd.hip", "ss_conv.hip",
            "ss_complex.hip", "ss_step.hip", "ss_carry.hip", "ss_fwd.hip", "ss_runtime.hip",
            "ss_api.cpp"]
 ARCH = os.environ.get("SS_SCAN_ARCH", "gfx950")

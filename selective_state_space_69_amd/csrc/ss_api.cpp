@@ -53,7 +53,8 @@ int64_t env_int(const char* name) {
 // 4-6 FMA-class ops per element), and a SIMD running a single wave stalls on
 // transcendental and LDS latency, so the plan aims for several waves per SIMD
 // (the MI355X has 1024 SIMDs in 256 CUs) with the least redundant work.  With
-// cols = B * ceil(D / 64) channel blocks:
+// cols = B * ceil(D / 64) channel blocks (cols32, cols16: the same for 32 and
+// 16 channels):
 //  - cols >= 2048: one wave per block (16 states per lane), one pass;
 //  - cols >= 512: one pass, either 64-channel groups with the states split
 //    over 4 waves, or 32-channel groups with two states per lane (twice the
@@ -61,21 +62,33 @@ int64_t env_int(const char* name) {
 //    spreads the groups over the 256 CUs clearly more evenly: a CU holds at
 //    most 4 of the first kind at a time and 5 of the second, and the time is
 //    set by the most loaded CU (B = 8, D = 5120: 3 vs 2.5 groups' worth);
+//  - cols32 >= 512: one pass on 32-channel groups (two or more waves per
+//    SIMD; B = 8, D = 2560: 0.26 ms against 0.32 chunked);
+//  - cols16 >= 640: one pass on 16-channel groups with one state per lane
+//    (the same vector work per element, about twice the LDS traffic, three
+//    groups per CU; Mamba-130M, B = 8, D = 1536: 0.166 ms against 0.184
+//    chunked, 0.168 against 0.209 with exact ZOH);
 //  - fewer: 4 waves per 64-channel group and time cut into chunks of >= 128
 //    steps, about 8192 waves in all; a chunked forward costs about 1.8x the
 //    arithmetic (summary pass + output pass) but keeps every SIMD busy.
-// Measured on MI355X for the Mamba-130M/2.8B shapes and the 1M-step case.
-// SS_SCAN_NSPLIT (1, 2, 4, or 8 for the 32-channel kernel) and SS_SCAN_CHUNK
-// override the choice.
+// Measured on MI355X for the Mamba-130M/2.8B shapes, B = 2 at L = 8192, the
+// 1M-step case and a few widths between.  SS_SCAN_NSPLIT (1, 2, 4, 8 for the
+// 32-channel kernel, 16 for the 16-channel one) and SS_SCAN_CHUNK override
+// the choice.
 TimePlan plan_time(const ss_desc_t& d) {
   TimePlan tp;
   const int64_t L = d.seqlen;
   const int64_t cols = d.batch * ((d.dim + kWave - 1) / kWave);
   const int64_t cols32 = d.batch * ((d.dim + 31) / 32);
-  constexpr int64_t kWide = 2048, kMid = 512, kChunkWaves = 8192, kMinChunk = 128, kCUs = 256;
+  const int64_t cols16 = d.batch * ((d.dim + 15) / 16);
+  constexpr int64_t kWide = 2048, kMid = 512, kNarrow16 = 640, kChunkWaves = 8192,
+                    kMinChunk = 128, kCUs = 256;
   int nsplit = int(env_int("SS_SCAN_NSPLIT"));
-  const bool forced_split = nsplit == 1 || nsplit == 2 || nsplit == 4 || nsplit == kHalfWaveSplit;
+  const bool forced_split = nsplit == 1 || nsplit == 2 || nsplit == 4 || nsplit == kHalfWaveSplit ||
+                            nsplit == kOneStateSplit;
+  bool one_pass = false;
   if (!forced_split) {
+    one_pass = true;
     if (cols >= kWide) {
       nsplit = 1;
     } else if (cols >= kMid) {
@@ -83,16 +96,23 @@ TimePlan plan_time(const ss_desc_t& d) {
       const double t4 = double((cols + kCUs - 1) / kCUs);
       const double t8 = 0.5 * 1.05 * double((cols32 + kCUs - 1) / kCUs);
       nsplit = t8 < 0.9 * t4 ? kHalfWaveSplit : 4;
+    } else if (cols32 >= kMid) {
+      nsplit = kHalfWaveSplit;
+    } else if (cols16 >= kNarrow16) {
+      nsplit = kOneStateSplit;
     } else {
       nsplit = 4;
+      one_pass = false;
     }
   }
   int64_t chunk = env_int("SS_SCAN_CHUNK");
   if (chunk <= 0) {
-    if (cols >= kMid || L < 2 * kMinChunk) {
+    if (one_pass || cols >= kMid || L < 2 * kMinChunk) {
       chunk = L;
     } else {
-      const int64_t waves = nsplit == kHalfWaveSplit ? cols32 * 4 : cols * nsplit;
+      const int64_t waves = nsplit == kHalfWaveSplit   ? cols32 * 4
+                            : nsplit == kOneStateSplit ? cols16 * 4
+                                                       : cols * nsplit;
       const int64_t want = (kChunkWaves + waves - 1) / waves;
       chunk = (L + want - 1) / want;
       if (chunk < kMinChunk) chunk = kMinChunk;

@@ -50,7 +50,9 @@ FwdParams make_params(const ss_desc_t& d, const TimePlan& tp, const FwdArgs& a) 
   p.nchunks = int32_t(tp.nchunks);
   p.rev = a.rev ? 1 : 0;
   p.acc = a.acc ? 1 : 0;
-  const int64_t width = tp.nsplit == kHalfWaveSplit ? 32 : kWave;   // channels per workgroup
+  const int64_t width = tp.nsplit == kHalfWaveSplit   ? 32
+                        : tp.nsplit == kOneStateSplit ? 16
+                                                      : kWave;   // channels per workgroup
   p.ndblk = int32_t((d.dim + width - 1) / width);
   return p;
 }
@@ -79,9 +81,9 @@ int launch_fwd_carries(const ss_desc_t& d, const TimePlan& tp, const FwdArgs& a,
   FwdParams p = make_params(d, tp, a);
   const int64_t cols = d.batch * p.ndblk;
   p.grid_chunks = p.nchunks - 1;   // the last chunk's summary is never needed
-  hipError_t e = tp.nsplit == kHalfWaveSplit
-                     ? launch_fwd_hw(d, p, true, cols * p.grid_chunks, st)
-                     : dispatch(d, p, tp.nsplit, true, cols * p.grid_chunks, st);
+  hipError_t e = tp.nsplit == kHalfWaveSplit   ? launch_fwd_hw(d, p, true, cols * p.grid_chunks, st)
+                 : tp.nsplit == kOneStateSplit ? launch_fwd_hw1(d, p, true, cols * p.grid_chunks, st)
+                                               : dispatch(d, p, tp.nsplit, true, cols * p.grid_chunks, st);
   if (e != hipSuccess) return int(e);
   return launch_chunk_carry(a.hend, a.dsum, a.A, a.h0, d.batch, d.dim, int(d.dstate), p.nchunks,
                             false, stream);
@@ -105,6 +107,7 @@ int launch_fwd(const ss_desc_t& d, const FwdPlan& plan, const FwdArgs& args, voi
   p.grid_chunks = p.nchunks;
   const int64_t cols = d.batch * p.ndblk;
   if (plan.tp.nsplit == kHalfWaveSplit) return int(launch_fwd_hw(d, p, false, cols * p.grid_chunks, st));
+  if (plan.tp.nsplit == kOneStateSplit) return int(launch_fwd_hw1(d, p, false, cols * p.grid_chunks, st));
   return int(dispatch(d, p, plan.tp.nsplit, false, cols * p.grid_chunks, st));
 }
 

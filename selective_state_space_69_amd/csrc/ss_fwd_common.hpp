@@ -30,21 +30,21 @@ struct FwdParams {
   int32_t N, ndblk, nchunks, grid_chunks;
   // Time direction.  Logical step t of a batch row is physical step t
   // (forward) or L - 1 - t (reverse); the recurrence always runs over logical
-  // steps.  Buffer offsets cannot be negative, so in reverse a block of 8
+  // steps.  Buffer offsets cannot be negative, so in reverse a block of BLK
   // steps is addressed from its last logical step (its lowest address) and
-  // logical step t + k sits at position 7 - k.
+  // logical step t + k sits at position BLK - 1 - k.
   int32_t rev;
   int32_t acc;   // nonzero: y += result (the old y is read in the output type)
 };
 
-// Address helpers of the time direction (compile time; forward code is the
-// plain t * D addressing).
-template <bool REV>
+// Address helpers of the time direction for blocks of BLK steps (compile
+// time; forward code is the plain t * D addressing).
+template <bool REV, int BLK = kBlk>
 struct TimeDir {
   int64_t ts;     // elements from logical step t to t + 1 (+D or -D)
-  __device__ __forceinline__ int32_t blk(int32_t t) const { return REV ? t + (kBlk - 1) : t; }
+  __device__ __forceinline__ int32_t blk(int32_t t) const { return REV ? t + (BLK - 1) : t; }
   __device__ __forceinline__ uint32_t pos(int32_t k) const {
-    return uint32_t(REV ? (kBlk - 1) - k : k);
+    return uint32_t(REV ? (BLK - 1) - k : k);
   }
   // row index (b * L + physical step) of the block base of logical step t
   __device__ __forceinline__ int64_t row(int64_t b, int64_t L, int32_t t) const {
@@ -63,9 +63,13 @@ hipError_t fwd_dispatch_f32_f32(const FwdParams& p, int disc, int nsplit, bool h
 hipError_t fwd_dispatch_f32_bf16(const FwdParams& p, int disc, int nsplit, bool has_z,
                                  bool softplus, bool summary, int64_t nblocks, hipStream_t st);
 
-// Launch of the 32-channel kernel over B * ndblk * grid_chunks workgroups
-// (ndblk = ceil(D / 32)); summary = chunk summaries instead of outputs.
+// Launch of the 32-channel kernel (two states per lane) over
+// B * ndblk * grid_chunks workgroups (ndblk = ceil(D / 32)); summary = chunk
+// summaries instead of outputs.
 hipError_t launch_fwd_hw(const ss_desc_t& d, const FwdParams& p, bool summary, int64_t nblocks,
                          hipStream_t st);
+// The same with 16-channel workgroups, one state per lane (ndblk = ceil(D / 16)).
+hipError_t launch_fwd_hw1(const ss_desc_t& d, const FwdParams& p, bool summary, int64_t nblocks,
+                          hipStream_t st);
 
 }  // namespace ss

@@ -15,11 +15,14 @@ namespace ss {
 constexpr int kWave = 64;      // lanes per wavefront on CDNA
 constexpr int kMaxState = 16;  // states held per lane
 constexpr int kHalfWaveSplit = 8;
+constexpr int kOneStateSplit = 16;
 
 // How a forward (or the forward recompute inside the backward) is split.
 // nsplit : waves per (b, 64-channel block), each holding 16 / nsplit states;
 //          kHalfWaveSplit selects the 32-channel kernel (4 waves per
-//          (b, 32-channel block), two states per lane).
+//          (b, 32-channel block), two states per lane), kOneStateSplit the
+//          16-channel kernel (4 waves per (b, 16-channel block), one state per
+//          lane).
 // nchunks == 1: one sequential pass over time per workgroup.
 // nchunks  > 1: (1) chunk summaries, (2) carry scan over chunks, (3) output pass.
 struct TimePlan {

@@ -36,13 +36,14 @@ CASES = [
 ]
 
 
-@pytest.mark.parametrize("nsplit", ["1", "4", "8"])
+@pytest.mark.parametrize("nsplit", ["1", "4", "8", "16"])
 @pytest.mark.parametrize("chunk", ["0", "48"])
 @pytest.mark.parametrize("case", CASES, ids=lambda c: "b%d_l%d_d%d_n%d_%s_%s_%s" % c)
 def test_reverse_layouts(oracle, monkeypatch, nsplit, chunk, case):
-    """Reverse scan on the 32-channel layout ("8") and the 4-wave 64-channel
-    layout (which also serves plans that would use 1 or 2 waves forward), with
-    and without time chunks; y and the state after t = 0."""
+    """Reverse scan on the 32-channel layout ("8"), the 16-channel layout
+    ("16") and the 4-wave 64-channel layout (which also serves plans that would
+    use 1 or 2 waves forward), with and without time chunks; y and the state
+    after t = 0."""
     Bt, L, D, N, disc, amode, dt = case
     log("reverse case", nsplit, chunk, case)
     monkeypatch.setenv("SS_SCAN_NSPLIT", nsplit)
@@ -57,7 +58,7 @@ def test_reverse_layouts(oracle, monkeypatch, nsplit, chunk, case):
     check_f32(hl.cpu().numpy(), href, "h_last")
 
 
-@pytest.mark.parametrize("nsplit", ["4", "8"])
+@pytest.mark.parametrize("nsplit", ["4", "8", "16"])
 def test_bidirectional_sum(oracle, monkeypatch, nsplit):
     """Forward call, then reverse call with its own A, D and bias accumulating
     into y: equals the oracle's forward + reverse."""
@@ -101,7 +102,7 @@ def test_accumulate_bf16_output(oracle):
 
 @pytest.mark.parametrize("dt_range", [(1e-3, 1e-1), (1e-4, 1e-2)], ids=["dt1e-3", "dt1e-4"])
 @pytest.mark.parametrize("amode", ["s4d_real", "random", "weak"])
-@pytest.mark.parametrize("layout", [("16", "4"), ("40", "8"), ("100000", "8")],
+@pytest.mark.parametrize("layout", [("16", "4"), ("40", "8"), ("100000", "8"), ("100000", "16")],
                          ids=lambda v: "chunk%s_split%s" % v)
 def test_reverse_long_fp32(oracle, monkeypatch, layout, amode, dt_range):
     """10,250 fp32 steps in reverse time, with >= 256 chunks (the chunk carries

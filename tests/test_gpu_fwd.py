@@ -79,13 +79,14 @@ SPLIT_CASES = [
 ]
 
 
-@pytest.mark.parametrize("nsplit", ["1", "2", "4", "8"])
+@pytest.mark.parametrize("nsplit", ["1", "2", "4", "8", "16"])
 @pytest.mark.parametrize("chunk", ["0", "48"])
 @pytest.mark.parametrize("case", SPLIT_CASES, ids=lambda c: "b%d_l%d_d%d_n%d_%s_%s_%s" % c)
 def test_fwd_split_variants(oracle, monkeypatch, nsplit, chunk, case):
     """Every kernel layout (64-channel groups with 1, 2 or 4 waves over the
-    states; "8" = 32-channel groups, two states per lane), with and without
-    time chunks, against the oracle."""
+    states; "8" = 32-channel groups, two states per lane; "16" = 16-channel
+    groups, one state per lane), with and without time chunks, against the
+    oracle."""
     Bt, L, D, N, disc, amode, dt = case
     log("split case", nsplit, chunk, case)
     monkeypatch.setenv("SS_SCAN_NSPLIT", nsplit)
@@ -128,8 +129,9 @@ def test_chunked_equals_sequential(monkeypatch):
 
 
 # (SS_SCAN_CHUNK, SS_SCAN_NSPLIT): >= 256 chunks (lane-parallel carries) on the
-# 64-channel and 32-channel layouts, one pass on both, and the planner's choice
-LONG_LAYOUTS = [("16", "4"), ("40", "8"), ("100000", "8"), ("100000", "1"), ("0", "0")]
+# 64-, 32- and 16-channel layouts, one pass on each, and the planner's choice
+LONG_LAYOUTS = [("16", "4"), ("40", "8"), ("100000", "8"), ("100000", "1"), ("48", "16"),
+                ("100000", "16"), ("0", "0")]
 
 
 @pytest.mark.parametrize("dt_range", [(1e-3, 1e-1), (1e-4, 1e-2)], ids=["dt1e-3", "dt1e-4"])
@@ -157,7 +159,8 @@ def test_fwd_long_fp32(oracle, monkeypatch, layout, amode, dt_range):
 
 
 # (SS_SCAN_CHUNK, SS_SCAN_NSPLIT) for the time-invariant cases
-LTI_LAYOUTS = [("0", "8"), ("256", "8"), ("0", "1"), ("0", "2"), ("256", "4"), ("0", "0")]
+LTI_LAYOUTS = [("0", "8"), ("256", "8"), ("0", "1"), ("0", "2"), ("256", "4"), ("0", "16"),
+               ("256", "16"), ("0", "0")]
 
 
 @pytest.mark.parametrize("disc", ["zoh", "euler"])
@@ -202,7 +205,7 @@ def test_fwd_lti_one_signed_bf16(oracle, reverse):
     log("  max err / max|ref| =", r)
 
 
-@pytest.mark.parametrize("nsplit", ["8", "4", "1"])
+@pytest.mark.parametrize("nsplit", ["8", "4", "1", "16"])
 def test_fwd_tiny_steps_relative(oracle, monkeypatch, nsplit):
     """Steps of softplus(-20) ~ 2e-9 (and smaller): the state they build from
     a zero start keeps full relative accuracy (elementwise 1e-5 relative on
