@@ -64,10 +64,11 @@ int64_t env_int(const char* name) {
 //    set by the most loaded CU (B = 8, D = 5120: 3 vs 2.5 groups' worth);
 //  - cols32 >= 512: one pass on 32-channel groups (two or more waves per
 //    SIMD; B = 8, D = 2560: 0.26 ms against 0.32 chunked);
-//  - cols16 >= 640: one pass on 16-channel groups with one state per lane
-//    (the same vector work per element, about twice the LDS traffic, three
-//    groups per CU; Mamba-130M, B = 8, D = 1536: 0.166 ms against 0.184
-//    chunked, 0.168 against 0.209 with exact ZOH);
+//  - cols16 >= 384: one pass on 16-channel groups with one state per lane
+//    (the same vector work per element, 1.5x the LDS instructions, three
+//    groups per CU; Mamba-130M, B = 8, D = 1536: 0.142 ms against 0.180
+//    chunked, 0.141 against 0.204 with exact ZOH; B = 4: 0.107 against 0.111;
+//    at 192 groups, 0.090 against 0.068 chunked);
 //  - fewer: 4 waves per 64-channel group and time cut into chunks of >= 128
 //    steps, about 8192 waves in all; a chunked forward costs about 1.8x the
 //    arithmetic (summary pass + output pass) but keeps every SIMD busy.
@@ -81,7 +82,7 @@ TimePlan plan_time(const ss_desc_t& d) {
   const int64_t cols = d.batch * ((d.dim + kWave - 1) / kWave);
   const int64_t cols32 = d.batch * ((d.dim + 31) / 32);
   const int64_t cols16 = d.batch * ((d.dim + 15) / 16);
-  constexpr int64_t kWide = 2048, kMid = 512, kNarrow16 = 640, kChunkWaves = 8192,
+  constexpr int64_t kWide = 2048, kMid = 512, kNarrow16 = 384, kChunkWaves = 8192,
                     kMinChunk = 128, kCUs = 256;
   int nsplit = int(env_int("SS_SCAN_NSPLIT"));
   const bool forced_split = nsplit == 1 || nsplit == 2 || nsplit == 4 || nsplit == kHalfWaveSplit ||

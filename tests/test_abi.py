@@ -112,11 +112,12 @@ def test_plan_sizes(lib):
     # run in one pass on the one-state-per-lane layout
     assert B.ss_scan_workspace_bytes(desc(batch=8, seqlen=2048, dim=1536), B.SS_OP_FWD) == 0
     assert B.ss_scan_workspace_bytes(desc(batch=2, seqlen=8192, dim=5120), B.SS_OP_FWD) == 0
+    assert B.ss_scan_workspace_bytes(desc(batch=4, seqlen=2048, dim=1536), B.SS_OP_FWD) == 0
     # narrower ones are chunked: start states (B, chunks, N, D) + step sums (B, chunks, D)
-    n = B.ss_scan_workspace_bytes(desc(batch=4, seqlen=2048, dim=1536), B.SS_OP_FWD)
+    n = B.ss_scan_workspace_bytes(desc(batch=2, seqlen=2048, dim=1536), B.SS_OP_FWD)
     assert n > 0 and n % 256 == 0
-    chunks = n // (4 * 16 * 1536 * 4 + 4 * 1536 * 4)
-    assert n == chunks * (4 * 16 * 1536 * 4 + 4 * 1536 * 4) and chunks > 1
+    chunks = n // (2 * 16 * 1536 * 4 + 2 * 1536 * 4)
+    assert n == chunks * (2 * 16 * 1536 * 4 + 2 * 1536 * 4) and chunks > 1
     assert B.ss_scan_workspace_bytes(desc(batch=0), B.SS_OP_FWD) == 0
     assert B.ss_scan_workspace_bytes(desc(), 5) == 0
 
