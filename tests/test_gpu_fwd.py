@@ -228,7 +228,14 @@ def test_fwd_tiny_steps_relative(oracle, monkeypatch, nsplit):
     check_f32(y.cpu().numpy(), ref, "y")
 
 
-def test_fwd_deterministic():
+# "0": the planner's choice; the others force a layout (SS_SCAN_NSPLIT)
+LAYOUTS = ["0", "4", "8", "16"]
+
+
+@pytest.mark.parametrize("nsplit", LAYOUTS)
+def test_fwd_deterministic(monkeypatch, nsplit):
+    if nsplit != "0":
+        monkeypatch.setenv("SS_SCAN_NSPLIT", nsplit)
     inp = synth.make_inputs(4, 512, 320, 16, seed=6, dtype="bf16")
     d = upload(inp)
     y1 = gpu_fwd(d, "zoh")
@@ -237,8 +244,11 @@ def test_fwd_deterministic():
     assert torch.equal(y1, y2)
 
 
-def test_fwd_split_resume():
+@pytest.mark.parametrize("nsplit", LAYOUTS)
+def test_fwd_split_resume(monkeypatch, nsplit):
     """fwd(L1) -> h_last -> fwd(L2, h0 = h_last) equals fwd(L1 + L2)."""
+    if nsplit != "0":
+        monkeypatch.setenv("SS_SCAN_NSPLIT", nsplit)
     inp = synth.make_inputs(2, 300, 128, 16, seed=7, dtype="f32", with_h0=True, a_mode="random")
     d = upload(inp)
     y, h = gpu_fwd(d, "zoh", return_last_state=True)
@@ -254,7 +264,10 @@ def test_fwd_split_resume():
     assert float((h2 - h).abs().max()) <= 1e-5 * (1 + float(h.abs().max()))
 
 
-def test_fwd_bf16_output(oracle):
+@pytest.mark.parametrize("nsplit", LAYOUTS)
+def test_fwd_bf16_output(oracle, monkeypatch, nsplit):
+    if nsplit != "0":
+        monkeypatch.setenv("SS_SCAN_NSPLIT", nsplit)
     inp = synth.make_inputs(2, 200, 192, 16, seed=8, dtype="bf16")
     d = upload(inp)
     y = gpu_fwd(d, "zoh", out_dtype=torch.bfloat16)
