@@ -1,7 +1,8 @@
 // Forward selective scan, host side: the launch plan (row packing, chunk
 // summaries and carries, output pass) around the 64-channel kernels
 // (ss_fwd_kernels.hpp, instantiated in ss_fwd_<in>_<out>.hip) and the
-// 32-channel kernels (ss_fwd_hw.hip).
+// kernels with the states over the lanes (ss_fwd_hw.hpp: 32 channels in
+// ss_fwd_hw.hip, 16 in ss_fwd_hw1.hip).
 #include "ss_fwd_common.hpp"
 
 namespace ss {

@@ -1,6 +1,6 @@
-// Parameters shared by the two forward scan kernels (ss_fwd.hip: one wave per
-// 64 channels and a slice of the states; ss_fwd_hw.hip: 32 channels per wave
-// and two states per lane) and by their launchers.
+// Parameters shared by the forward scan kernels (ss_fwd_kernels.hpp: one wave
+// per 64 channels and a slice of the states; ss_fwd_hw.hpp: 32 or 16 channels
+// per workgroup with two states or one per lane) and by their launchers.
 #pragma once
 
 #include "ss_device.hpp"
