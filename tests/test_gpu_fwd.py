@@ -277,6 +277,36 @@ def test_fwd_bf16_output(oracle, monkeypatch, nsplit):
     check_rel_max(y.float().cpu().numpy(), ref, TOL_BF16 + 2.0 ** -8, "y bf16")
 
 
+# (B, L, D, N): a single step, one partial block, a block and a step, ragged D
+EDGE_SHAPES = [(1, 1, 1, 16), (2, 5, 17, 16), (1, 17, 16, 16), (2, 33, 33, 7)]
+
+
+@pytest.mark.parametrize("reverse", [False, True], ids=["fwd", "rev"])
+@pytest.mark.parametrize("chunk", ["0", "40", "7"])
+@pytest.mark.parametrize("nsplit", ["4", "8", "16"])
+@pytest.mark.parametrize("shape", EDGE_SHAPES, ids=lambda v: "b%d_l%d_d%d_n%d" % v)
+def test_fwd_layout_edges(oracle, monkeypatch, shape, nsplit, chunk, reverse):
+    """Edge shapes on every forced layout: L shorter than one block, chunk
+    lengths that are not a multiple of a block (7: more chunks than blocks),
+    D below one channel group, both time directions; fp32 at the elementwise
+    bound, y and the final state."""
+    Bt, L, D, N = shape
+    monkeypatch.setenv("SS_SCAN_NSPLIT", nsplit)
+    monkeypatch.setenv("SS_SCAN_CHUNK", chunk)
+    inp = synth.make_inputs(Bt, L, D, N, seed=4000 + EDGE_SHAPES.index(shape), dtype="f32",
+                            with_h0=True, a_mode="random")
+    d = upload(inp)
+    y, hl = B.scan_fwd(d["u"], d["delta"], d["A"], d["B"], d["C"], D=d["D"],
+                       delta_bias=d["delta_bias"], z=d["z"], h0=d["h0"], disc="zoh",
+                       return_last_state=True, reverse=reverse)
+    torch.cuda.synchronize()
+    fn = oracle.fwd_reverse if reverse else oracle.fwd
+    ref, href = fn(inp.u, inp.delta, inp.A, inp.B, inp.C, D=inp.D, delta_bias=inp.delta_bias,
+                   z=inp.z, h0=inp.h0, disc="zoh")
+    check_f32(y.cpu().numpy(), ref, "y")
+    check_f32(hl.cpu().numpy(), href, "h_last")
+
+
 # ------------------------------------------------------------------ full-size workloads
 # (workload, discretisation): every full-size forward workload in its own
 # discretisation, plus the Mamba-2.8B shape with Euler B_bar (also measured)
