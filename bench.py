@@ -18,6 +18,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -37,17 +38,27 @@ SLOTS_PER_ELEM = {"euler": 6.0, "zoh": 8.0}
 COMPLEX_SLOTS = 28.0
 
 
-# sources the forward half-wave kernel (the benchmark's dominant kernel) and its
-# launch are built from: a change to any of them voids its stored traffic figure
+# sources the benchmark's dominant kernel (the 32-channel forward) and its
+# launch are built from: a change to the code of any of them voids its stored
+# traffic figure (comments and layout do not count)
 HEADLINE_SOURCES = ("ss_device.hpp", "ss_fwd_common.hpp", "ss_fwd_hw.hpp", "ss_fwd_hw.hip",
                     "ss_fwd_hw_dispatch.inc", "ss_fwd.hip", "ss_internal.h")
+
+
+def _code_tokens(text):
+    """C++ source without comments, with runs of whitespace collapsed (string
+    literals in these files hold no comment markers)."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
 
 
 def kernel_source_hash():
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "selective_state_space_69_amd", "csrc")
     for f in HEADLINE_SOURCES:
-        h.update(open(os.path.join(csrc, f), "rb").read())
+        h.update(_code_tokens(open(os.path.join(csrc, f)).read()).encode())
+        h.update(b"\0")
     return h.hexdigest()[:16]
 
 

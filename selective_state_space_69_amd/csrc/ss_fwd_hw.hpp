@@ -1,9 +1,10 @@
 // Forward selective scan for gfx950 with the states of a channel spread over
 // the lanes: SPL (2 or 1) states per lane, 16 / SPL owner slots per channel.
 //
-// Same recurrence and block structure as ss_fwd.hip (a two-deep prefetch ring,
-// B/C rows staged in LDS, step sizes and partial sums of C h exchanged through
-// LDS once per block), with a different lane mapping: a workgroup of 4 waves
+// Same recurrence and block structure as the 64-channel kernel
+// (ss_fwd_kernels.hpp: a two-deep prefetch ring, B/C rows staged in LDS, step
+// sizes and partial sums of C h exchanged through LDS once per block), with a
+// different lane mapping: a workgroup of 4 waves
 // covers kCh = 256 SPL / 16 channels (32 or 16) and all 16 states; lane l of
 // wave w serves channel l % kCh and the SPL states n = SPL o .. SPL o + SPL - 1
 // of its owner slot o = (64 / kCh) w + l / kCh.  A block has one step per
@@ -113,7 +114,7 @@ struct HwScan {
   float* stage;
   float* part;
   float* stage_w;        // where this lane writes its staged values (buffer 0)
-  // two-deep prefetch ring, slot = block parity (as in ss_fwd.hip)
+  // two-deep prefetch ring, slot = block parity (as in ss_fwd_kernels.hpp)
   In dr[2], zr[2], uo[2];
   Raw rb[2], rc[2];      // B and C values of the lane's fetch slot
   float dl_own, g_own, u_own;
