@@ -32,6 +32,11 @@
  *       Bm, Cm, dB, dC                     : (B, L, N)
  *       A, dA : (D, N)   D_skip, delta_bias, dD_skip, ddelta_bias : (D)
  *       h0, h_last, dh0, step state h      : (B, D, N)
+ *     except that Bm and Cm may be read with a row stride (desc->bc_stride):
+ *     in the Mamba block B and C are column ranges of the input projection's
+ *     output (x_proj, (B, L, R + 2N): the low-rank step input, then B, then C;
+ *     Gu & Dao note, Mamba architecture; "Mamba: S4 epic upgrade",
+ *     parameter-efficient data dependence), and the scan reads them in place.
  *   - Pointers are DEVICE pointers owned by the caller, 16-byte aligned, and valid until
  *     the stream reaches the queued work.  Element types: in_dtype for u, delta,
  *     z, Bm, Cm and dy; out_dtype for y, du, ddelta and dz; float32 for everything
@@ -81,6 +86,13 @@ typedef struct ss_desc {
   int32_t out_dtype;      /* ss_dtype_t of y (fwd, step) and of du, ddelta, dz (bwd; must be SS_F32) */
   int32_t disc;           /* ss_disc_t: exact zero-order hold or Euler input coefficient */
   int32_t delta_softplus; /* nonzero: dt = softplus(delta + delta_bias); zero: dt = delta + delta_bias */
+  /* Elements from one (b, t) row of Bm and Cm to the next ((b) row for the
+   * step); 0 means dense (dstate).  Otherwise dstate <= bc_stride <= 2^20;
+   * Bm and Cm then need only be aligned to their element size (the forward and
+   * backward copy the rows into their workspace first, the step reads them
+   * element by element).  The complex-A entry points take 0 only.  The
+   * gradients dB, dC stay dense (B, L, N). */
+  int64_t bc_stride;
 } ss_desc_t;
 
 /* Operations for ss_scan_workspace_bytes. */
@@ -296,7 +308,8 @@ int ss_scan_arch_supported(const char* arch_name);
 /* Static, human-readable text for a status code. */
 const char* ss_scan_strerror(int status);
 
-/* Library ABI version (major * 10000 + minor * 100 + patch). */
+/* Library ABI version (major * 10000 + minor * 100 + patch).  2.0 added the
+ * trailing bc_stride field of ss_desc_t (the struct grew by 8 bytes). */
 int ss_scan_version(void);
 
 #ifdef __cplusplus

@@ -37,7 +37,7 @@ class ss_desc_t(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int64), ("seqlen", ctypes.c_int64), ("dim", ctypes.c_int64),
                 ("dstate", ctypes.c_int64), ("in_dtype", ctypes.c_int32),
                 ("out_dtype", ctypes.c_int32), ("disc", ctypes.c_int32),
-                ("delta_softplus", ctypes.c_int32)]
+                ("delta_softplus", ctypes.c_int32), ("bc_stride", ctypes.c_int64)]
 
 
 class ss_conv_desc_t(ctypes.Structure):
@@ -117,9 +117,9 @@ def load_library():
 
 
 def make_desc(batch, seqlen, dim, dstate, in_dtype=SS_BF16, out_dtype=SS_F32, disc=SS_ZOH,
-              delta_softplus=True) -> ss_desc_t:
+              delta_softplus=True, bc_stride=0) -> ss_desc_t:
     return ss_desc_t(int(batch), int(seqlen), int(dim), int(dstate), int(in_dtype),
-                     int(out_dtype), int(disc), int(bool(delta_softplus)))
+                     int(out_dtype), int(disc), int(bool(delta_softplus)), int(bc_stride))
 
 
 def _p(t):
@@ -268,10 +268,46 @@ def _check(rc, where):
         raise ScanError(rc, where)
 
 
-def _desc_from(u, A, disc, softplus, out_dtype):
+def _row_stride(t, name):
+    """Elements from one row of t to the next, over every leading axis flattened
+    ((B, L, N) -> B*L rows of N, (B, N) -> B rows); the last axis must be unit
+    stride."""
+    shape, stride = t.shape, t.stride()
+    if shape[-1] > 1 and stride[-1] != 1:
+        raise ValueError(f"{name}: the last axis must have unit stride")
+    S = None
+    step = None
+    for n, st in zip(reversed(shape[:-1]), reversed(stride[:-1])):
+        if n == 1:
+            continue
+        if S is None:
+            S, step = st, st * n
+        elif st != step:
+            raise ValueError(f"{name}: rows must be evenly spaced (one stride over all rows)")
+        else:
+            step = st * n
+    return shape[-1] if S is None else S
+
+
+def _bc_stride(B, C, N):
+    """ss_desc_t.bc_stride for B and C read in place: 0 for dense rows, else the
+    common row stride (e.g. B, C sliced from the input projection's output)."""
+    sb, sc = _row_stride(B, "B"), _row_stride(C, "C")
+    if sb != sc:
+        raise ValueError("B and C must share one row stride")
+    if sb < N:
+        raise ValueError("B, C rows overlap (row stride below dstate)")
+    # dense rows are read in place with 16-byte loads; a dense view at another
+    # offset goes through the strided path, which needs element alignment only
+    dense_ok = B.data_ptr() % 16 == 0 and C.data_ptr() % 16 == 0
+    return 0 if sb == N and dense_ok else sb
+
+
+def _desc_from(u, A, B, C, disc, softplus, out_dtype):
     Bt, L, D = u.shape
     N = A.shape[1]
-    return make_desc(Bt, L, D, N, _DTYPE[u.dtype], _DTYPE[out_dtype], _DISC[disc], softplus)
+    return make_desc(Bt, L, D, N, _DTYPE[u.dtype], _DTYPE[out_dtype], _DISC[disc], softplus,
+                     _bc_stride(B, C, N))
 
 
 def workspace(nbytes: int, device) -> torch.Tensor | None:
@@ -285,8 +321,10 @@ def scan_fwd(u, delta, A, B, C, D=None, delta_bias=None, z=None, h0=None, disc="
              ws=None, reverse=False, y=None):
     """Forward scan on device tensors; returns y (and h_last).  reverse=True runs
     the system from the last step to the first; passing y adds the result to it
-    (in place) instead of allocating a new output."""
-    desc = _desc_from(u, A, disc, softplus, out_dtype if y is None else y.dtype)
+    (in place) instead of allocating a new output.  B and C may be views with a
+    row stride (column ranges of one projection output); the other tensors are
+    dense."""
+    desc = _desc_from(u, A, B, C, disc, softplus, out_dtype if y is None else y.dtype)
     acc = y is not None
     if y is None:
         y = torch.empty(u.shape, dtype=out_dtype, device=u.device)
@@ -336,8 +374,9 @@ def scan_bidir(u, delta, A, B, C, D=None, delta_bias=None, z=None, disc="zoh", s
 
 def scan_bwd(u, delta, A, B, C, dy, D=None, delta_bias=None, z=None, h0=None, disc="zoh",
              softplus=True, want_dh0=False, stream=None):
-    """Backward scan; returns a dict of fp32 gradients."""
-    desc = _desc_from(u, A, disc, softplus, torch.float32)
+    """Backward scan; returns a dict of fp32 gradients (dB, dC dense even when B
+    and C are strided views)."""
+    desc = _desc_from(u, A, B, C, disc, softplus, torch.float32)
     dev = u.device
     f32 = dict(dtype=torch.float32, device=dev)
     g = {"du": torch.empty(u.shape, **f32), "ddelta": torch.empty(u.shape, **f32),
@@ -357,10 +396,11 @@ def scan_bwd(u, delta, A, B, C, dy, D=None, delta_bias=None, z=None, h0=None, di
 
 def scan_step(h, u, delta, A, B, C, D=None, delta_bias=None, z=None, disc="zoh", softplus=True,
               out_dtype=torch.float32, stream=None):
-    """One recurrent step; h (B,D,N) fp32 is updated in place; returns y (B,D)."""
+    """One recurrent step; h (B,D,N) fp32 is updated in place; returns y (B,D).
+    B and C (B,N) may be strided views, as in scan_fwd."""
     Bt, Dd = u.shape
     desc = make_desc(Bt, 1, Dd, A.shape[1], _DTYPE[u.dtype], _DTYPE[out_dtype], _DISC[disc],
-                     softplus)
+                     softplus, _bc_stride(B, C, A.shape[1]))
     y = torch.empty(u.shape, dtype=out_dtype, device=u.device)
     _check(ss_scan_step(desc, h, u, delta, A, B, C, D, delta_bias, z, y, stream), "ss_scan_step")
     return y

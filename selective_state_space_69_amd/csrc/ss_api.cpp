@@ -37,7 +37,19 @@ int check_desc(const ss_desc_t* d, bool need_len) {
   if (d->batch > lim / L || d->batch * L > lim / d->dim) return SS_ERR_INVALID_ARG;
   if (!valid_dtype(d->in_dtype) || !valid_dtype(d->out_dtype)) return SS_ERR_UNSUPPORTED;
   if (d->disc != SS_ZOH && d->disc != SS_EULER) return SS_ERR_UNSUPPORTED;
+  if (d->bc_stride != 0 && (d->bc_stride < d->dstate || d->bc_stride > (int64_t(1) << 20)))
+    return SS_ERR_INVALID_ARG;
   return SS_OK;
+}
+
+// Alignment asked of Bm and Cm: rows read in place take 16-byte loads, rows
+// with a stride are only read element by element (copied, or by the step).
+size_t bc_align(const ss_desc_t& d) {
+  return d.bc_stride == 0 ? kPtrAlign : (d.in_dtype == SS_BF16 ? 2 : 4);
+}
+
+bool bc_aligned(const ss_desc_t& d, const void* Bm, const void* Cm) {
+  return aligned(Bm, bc_align(d)) && aligned(Cm, bc_align(d));
 }
 
 int64_t env_int(const char* name) {
@@ -133,7 +145,7 @@ FwdPlan plan_fwd(const ss_desc_t& d) {
   const size_t B = size_t(d.batch), L = size_t(d.seqlen), C = size_t(p.tp.nchunks),
                D = size_t(d.dim), N = size_t(d.dstate);
   size_t off = 0;
-  p.packed_rows = d.dstate != kMaxState;
+  p.packed_rows = d.dstate != kMaxState || d.bc_stride != 0;
   const size_t es = d.in_dtype == SS_BF16 ? 2 : 4;
   if (p.packed_rows) {
     p.off_brow = off; off += align_up(B * L * kMaxState * es);
@@ -158,7 +170,7 @@ BwdPlan plan_bwd(const ss_desc_t& d) {
                D = size_t(d.dim), N = size_t(d.dstate);
   p.nblk = (d.dim + kWave - 1) / kWave;
   const size_t nb = size_t(p.nblk);
-  p.packed_rows = d.dstate != kMaxState;
+  p.packed_rows = d.dstate != kMaxState || d.bc_stride != 0;
   const size_t es = d.in_dtype == SS_BF16 ? 2 : 4;
   size_t off = 0;
   if (p.packed_rows) {
@@ -279,9 +291,10 @@ int fwd_call(const ss_desc_t* desc, int direction, int accumulate, const void* u
   if (!u || !delta || !A || !Bm || !Cm || !y) return SS_ERR_INVALID_ARG;
   if (h_last && h0 && static_cast<const void*>(h_last) == static_cast<const void*>(h0))
     return SS_ERR_INVALID_ARG;
-  const void* ptrs[] = {u, delta, Bm, Cm, z, A, D_skip, delta_bias, h0, h_last, y};
+  const void* ptrs[] = {u, delta, z, A, D_skip, delta_bias, h0, h_last, y};
   for (const void* p : ptrs)
     if (p && !aligned(p, kPtrAlign)) return SS_ERR_INVALID_ARG;
+  if (!bc_aligned(*desc, Bm, Cm)) return SS_ERR_INVALID_ARG;
   const FwdPlan plan = plan_fwd(*desc);
   if (static_ws) {
     if (plan.bytes > kStaticScratchBytes) return SS_ERR_SCRATCH_LIMIT;
@@ -311,7 +324,7 @@ int fwd_call(const ss_desc_t* desc, int direction, int accumulate, const void* u
 
 extern "C" {
 
-int ss_scan_version(void) { return 10000; }
+int ss_scan_version(void) { return 20000; }
 
 int ss_scan_arch_supported(const char* arch_name) {
   if (!arch_name) return SS_ERR_INVALID_ARG;
@@ -338,7 +351,7 @@ size_t ss_scan_workspace_bytes(const ss_desc_t* desc, int op) {
   if (check_desc(desc, true) != SS_OK) return 0;
   if (op == SS_OP_FWD) return plan_fwd(*desc).bytes;
   if (op == SS_OP_BWD) return plan_bwd(*desc).bytes;
-  if (op == SS_OP_FWD_COMPLEX) return plan_fwd_complex(*desc, true).bytes;
+  if (op == SS_OP_FWD_COMPLEX) return desc->bc_stride ? 0 : plan_fwd_complex(*desc, true).bytes;
   return 0;
 }
 
@@ -372,6 +385,7 @@ int ss_scan_fwd_complex_ws(const ss_desc_t* desc, const void* u, const void* del
                            float* h_last, void* workspace, size_t ws_bytes, void* stream) {
   int rc = check_desc(desc, true);
   if (rc != SS_OK) return rc;
+  if (desc->bc_stride != 0) return SS_ERR_UNSUPPORTED;
   if (!u || !delta || !A || !Bm || !Cm || !y) return SS_ERR_INVALID_ARG;
   if (h_last && h0 && static_cast<const void*>(h_last) == static_cast<const void*>(h0))
     return SS_ERR_INVALID_ARG;
@@ -410,10 +424,11 @@ int ss_scan_bwd(const ss_desc_t* desc, const void* u, const void* delta, const f
   if ((D_skip != nullptr) != (dD_skip != nullptr)) return SS_ERR_INVALID_ARG;
   if ((delta_bias != nullptr) != (ddelta_bias != nullptr)) return SS_ERR_INVALID_ARG;
   if ((z != nullptr) != (dz != nullptr)) return SS_ERR_INVALID_ARG;
-  const void* ptrs[] = {u, delta, Bm, Cm, z, dy, A, D_skip, delta_bias, h0, du, ddelta,
+  const void* ptrs[] = {u, delta, z, dy, A, D_skip, delta_bias, h0, du, ddelta,
                         dA, dB, dC, dD_skip, ddelta_bias, dz, dh0};
   for (const void* p : ptrs)
     if (p && !aligned(p, kPtrAlign)) return SS_ERR_INVALID_ARG;
+  if (!bc_aligned(*desc, Bm, Cm)) return SS_ERR_INVALID_ARG;
   const BwdPlan plan = plan_bwd(*desc);
   if (plan.bytes > 0 && (!workspace || ws_bytes < plan.bytes || !aligned(workspace, kAlign)))
     return SS_ERR_WORKSPACE;
@@ -434,9 +449,10 @@ int ss_scan_step(const ss_desc_t* desc, float* h, const void* u, const void* del
   // y is written while other lanes still read the state and the inputs
   const void* hv = h;
   if (y == hv || y == u || y == delta || y == Bm || y == Cm || y == z) return SS_ERR_INVALID_ARG;
-  const void* ptrs[] = {h, u, delta, A, Bm, Cm, D_skip, delta_bias, z, y};
+  const void* ptrs[] = {h, u, delta, A, D_skip, delta_bias, z, y};
   for (const void* p : ptrs)
     if (p && !aligned(p, kPtrAlign)) return SS_ERR_INVALID_ARG;
+  if (!bc_aligned(*desc, Bm, Cm)) return SS_ERR_INVALID_ARG;
   StepArgs a{h, u, delta, A, Bm, Cm, D_skip, delta_bias, z, y};
   if ((rc = check_device()) != SS_OK) return rc;
   return launch_step(*desc, a, stream) == 0 ? SS_OK : SS_ERR_HIP;
@@ -447,6 +463,7 @@ int ss_scan_step_complex(const ss_desc_t* desc, float* h, const void* u, const v
                          const float* delta_bias, const void* z, void* y, void* stream) {
   int rc = check_desc(desc, false);
   if (rc != SS_OK) return rc;
+  if (desc->bc_stride != 0) return SS_ERR_UNSUPPORTED;
   if (!h || !u || !delta || !A || !Bm || !Cm || !y) return SS_ERR_INVALID_ARG;
   if (desc->batch * desc->dim > (int64_t(1) << 33)) return SS_ERR_INVALID_ARG;   // 32-bit grid
   const void* hv = h;

@@ -9,18 +9,19 @@ namespace ss {
 namespace {
 
 // B and C rows padded to 16 entries per (b, t) (zero past N), in the input type:
-// the layout the scan kernels read.  Only needed when N < 16.
+// the layout the scan kernels read.  Needed when N < 16, and when the rows sit
+// S > N elements apart (column ranges of a wider projection output).
 template <typename In>
 __global__ __launch_bounds__(256) void pack_rows_kernel(const In* __restrict__ Bm,
                                                         const In* __restrict__ Cm,
                                                         In* __restrict__ Bp, In* __restrict__ Cp,
-                                                        int64_t rows, int N) {
+                                                        int64_t rows, int N, int64_t S) {
   const int64_t gid = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
   if (gid >= rows * kMaxState) return;
   const int64_t r = gid / kMaxState;
   const int n = int(gid % kMaxState);
-  Bp[gid] = n < N ? Bm[r * N + n] : In(0);
-  Cp[gid] = n < N ? Cm[r * N + n] : In(0);
+  Bp[gid] = n < N ? Bm[r * S + n] : In(0);
+  Cp[gid] = n < N ? Cm[r * S + n] : In(0);
 }
 
 hipError_t dispatch(const ss_desc_t& d, const FwdParams& p, int nsplit, bool summary,
@@ -65,15 +66,17 @@ int launch_pack_rows(const ss_desc_t& d, const void* Bm, const void* Cm, void* B
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int64_t rows = d.batch * d.seqlen;
   const unsigned nb = unsigned((rows * kMaxState + 255) / 256);
+  const int64_t S = d.bc_stride != 0 ? d.bc_stride : d.dstate;
   if (d.in_dtype == SS_BF16)
     hipLaunchKernelGGL(pack_rows_kernel<uint16_t>, dim3(nb), dim3(256), 0, st,
                        static_cast<const uint16_t*>(Bm), static_cast<const uint16_t*>(Cm),
                        static_cast<uint16_t*>(Brow), static_cast<uint16_t*>(Crow), rows,
-                       int(d.dstate));
+                       int(d.dstate), S);
   else
     hipLaunchKernelGGL(pack_rows_kernel<float>, dim3(nb), dim3(256), 0, st,
                        static_cast<const float*>(Bm), static_cast<const float*>(Cm),
-                       static_cast<float*>(Brow), static_cast<float*>(Crow), rows, int(d.dstate));
+                       static_cast<float*>(Brow), static_cast<float*>(Crow), rows, int(d.dstate),
+                       S);
   return int(hipGetLastError());
 }
 

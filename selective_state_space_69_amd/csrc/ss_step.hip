@@ -23,6 +23,7 @@ struct StepParams {
   const void* z;
   void* y;
   int64_t B, D;
+  int64_t S;   // elements from one batch row of Bm, Cm to the next
   int32_t N, disc, softplus;
 };
 
@@ -49,8 +50,8 @@ __global__ __launch_bounds__(256) void step_kernel(StepParams p) {
   const int n0 = q * 4;
   float* h = p.h + chc * N + n0;
   const float* Ap = p.A + d * N + n0;
-  const In* Bp = static_cast<const In*>(p.Bm) + b * N + n0;
-  const In* Cp = static_cast<const In*>(p.Cm) + b * N + n0;
+  const In* Bp = static_cast<const In*>(p.Bm) + b * p.S + n0;
+  const In* Cp = static_cast<const In*>(p.Cm) + b * p.S + n0;
   if constexpr (N16) {
     const float4 h4 = *reinterpret_cast<const float4*>(h), a4 = *reinterpret_cast<const float4*>(Ap);
     const float4 b4 = unpack4(load_raw4(Bp)), c4 = unpack4(load_raw4(Cp));
@@ -100,24 +101,28 @@ __global__ __launch_bounds__(256) void step_kernel(StepParams p) {
 
 }  // namespace
 
+// 16-byte vector loads only for dense 16-state rows (16-byte aligned by the
+// entry point's checks); rows with a stride are read element by element.
 template <typename In, typename Out>
-void launch_typed(const StepParams& p, dim3 grid, dim3 block, hipStream_t st) {
-  if (p.N == kMaxState) hipLaunchKernelGGL((step_kernel<In, Out, true>), grid, block, 0, st, p);
+void launch_typed(const StepParams& p, bool vec, dim3 grid, dim3 block, hipStream_t st) {
+  if (vec) hipLaunchKernelGGL((step_kernel<In, Out, true>), grid, block, 0, st, p);
   else hipLaunchKernelGGL((step_kernel<In, Out, false>), grid, block, 0, st, p);
 }
 
 int launch_step(const ss_desc_t& d, const StepArgs& a, void* stream) {
   StepParams p{a.h, a.u, a.delta, a.A, a.Bm, a.Cm, a.Dskip, a.bias, a.z, a.y,
-               d.batch, d.dim, int32_t(d.dstate), d.disc, d.delta_softplus};
+               d.batch, d.dim, d.bc_stride != 0 ? d.bc_stride : d.dstate,
+               int32_t(d.dstate), d.disc, d.delta_softplus};
   const int64_t total = d.batch * d.dim * kQuad;
   const dim3 grid(unsigned((total + 255) / 256)), block(256);
   hipStream_t st = static_cast<hipStream_t>(stream);
+  const bool vec = d.dstate == kMaxState && d.bc_stride == 0;
   if (d.in_dtype == SS_BF16) {
-    if (d.out_dtype == SS_F32) launch_typed<uint16_t, float>(p, grid, block, st);
-    else launch_typed<uint16_t, uint16_t>(p, grid, block, st);
+    if (d.out_dtype == SS_F32) launch_typed<uint16_t, float>(p, vec, grid, block, st);
+    else launch_typed<uint16_t, uint16_t>(p, vec, grid, block, st);
   } else {
-    if (d.out_dtype == SS_F32) launch_typed<float, float>(p, grid, block, st);
-    else launch_typed<float, uint16_t>(p, grid, block, st);
+    if (d.out_dtype == SS_F32) launch_typed<float, float>(p, vec, grid, block, st);
+    else launch_typed<float, uint16_t>(p, vec, grid, block, st);
   }
   return int(hipGetLastError());
 }
