@@ -159,16 +159,45 @@ constexpr int kRowF = kChunk * 2 * kMaxState;
 constexpr int kXchF = kNW * 3 * kKB * kWave;
 constexpr int kLdsFloats = 3 * kActF + kRowF + kXchF;
 
+// Buffer resources of the (B, L, D) tensors for one chunk and 64-channel group,
+// based at element (b, t0, first channel of the group): step k of the chunk and
+// lane l reach their element at soffset k * step bytes, voffset l * element
+// size.  Idle lanes (past D) carry an out-of-range voffset: their loads read 0
+// and their stores are dropped.  (k < 32 and D <= 2^24 keep every offset
+// inside 32 bits.)
+template <typename In>
+struct ChunkIO {
+  Rsrc dl, dy, z, u;         // inputs, In
+  Rsrc du, ddelta, dz;       // outputs, fp32
+  uint32_t vin, vout;        // lane offsets (bytes)
+  uint32_t sin, sout;        // bytes per step
+
+  __device__ __forceinline__ ChunkIO(const BwdParams& p, int64_t b, int32_t t0, int dblk,
+                                     uint32_t lane, bool active) {
+    const int64_t e0 = (b * p.L + t0) * p.D + int64_t(dblk) * kWave;
+    dl = make_rsrc(static_cast<const In*>(p.delta) + e0);
+    dy = make_rsrc(static_cast<const In*>(p.dy) + e0);
+    z = make_rsrc(p.z ? static_cast<const In*>(p.z) + e0 : static_cast<const In*>(p.dy) + e0);
+    u = make_rsrc(static_cast<const In*>(p.u) + e0);
+    du = make_rsrc(p.du + e0);
+    ddelta = make_rsrc(p.ddelta + e0);
+    dz = make_rsrc(p.dz ? p.dz + e0 : p.du + e0);
+    vin = active ? lane * uint32_t(sizeof(In)) : kOutOfRange;
+    vout = active ? lane * uint32_t(sizeof(float)) : kOutOfRange;
+    sin = uint32_t(p.D) * uint32_t(sizeof(In));
+    sout = uint32_t(p.D) * uint32_t(sizeof(float));
+  }
+};
+
 // Stages chunk [t0, t1) in LDS: per step and lane the step size dt log2 e, the
 // gated upstream gradient gy and the input u (all 0 past t1, gy and u 0 on idle
 // lanes), and the chunk's B/C rows.  Wave w prepares the steps k with
 // k % 4 == w; every load is issued before any is used.  The caller places the
 // barrier.
 template <typename In, bool HAS_Z, bool SOFTPLUS>
-__device__ __forceinline__ void stage_chunk(const BwdParams& p, float* lds, int64_t ibase,
+__device__ __forceinline__ void stage_chunk(const BwdParams& p, const ChunkIO<In>& io, float* lds,
                                             int64_t row0, int32_t t0, int32_t t1, int wave,
                                             uint32_t lane, float bias2, float amask) {
-  const int64_t D = p.D;
   float* actDl = lds;                            // [32 steps][64 lanes]
   float* actGy = lds + kActF;
   float* actU = lds + 2 * kActF;
@@ -177,11 +206,11 @@ __device__ __forceinline__ void stage_chunk(const BwdParams& p, float* lds, int6
 #pragma unroll
   for (int s = 0; s < kNB; ++s) {
     const int32_t t = t0 + s * kNW + wave;
-    const int64_t i = ibase + int64_t(t < t1 ? t : t1 - 1) * D;
-    rdl[s] = static_cast<const In*>(p.delta)[i];
-    rdy[s] = static_cast<const In*>(p.dy)[i];
-    if (HAS_Z) rz[s] = static_cast<const In*>(p.z)[i];
-    ru[s] = static_cast<const In*>(p.u)[i];
+    const uint32_t so = uint32_t((t < t1 ? t : t1 - 1) - t0) * io.sin;
+    rdl[s] = buf_load<In>(io.dl, io.vin, so);
+    rdy[s] = buf_load<In>(io.dy, io.vin, so);
+    if (HAS_Z) rz[s] = buf_load<In>(io.z, io.vin, so);
+    ru[s] = buf_load<In>(io.u, io.vin, so);
   }
   // 256 threads, 4 values each: step tid / 8, B (parts 0-3) or C (4-7)
   const int tid = wave * kWave + int(lane);
@@ -219,7 +248,7 @@ __device__ __forceinline__ void bwd_chunk(const BwdParams& p, float* lds, int64_
   const int32_t t0 = chunk * kChunk;
   const int32_t t1 = int32_t(t0 + kChunk < p.L ? t0 + kChunk : p.L);
   const int64_t row0 = b * p.L;
-  const int64_t ibase = row0 * D + dc;          // element (b, t = 0, d)
+  const ChunkIO<In> io(p, b, t0, dblk, lane, active);
 
   float A[kNS], iA[kNS];
 #pragma unroll
@@ -256,7 +285,7 @@ __device__ __forceinline__ void bwd_chunk(const BwdParams& p, float* lds, int64_
 #pragma unroll
     for (int j = 0; j < kNS; ++j) nu[j] = n0 + j < N ? ls[int64_t(n0 + j) * D] : 0.0f;
   }
-  stage_chunk<In, HAS_Z, SOFTPLUS>(p, lds, ibase, row0, t0, t1, wave, lane, bias2, amask);
+  stage_chunk<In, HAS_Z, SOFTPLUS>(p, io, lds, row0, t0, t1, wave, lane, bias2, amask);
   __syncthreads();
   // this wave's 4 states of the B (m = 0) or C (m = 1) row of step kk
   auto row_of = [&](int kk, int m) -> float4 {
@@ -264,8 +293,16 @@ __device__ __forceinline__ void bwd_chunk(const BwdParams& p, float* lds, int64_
   };
 
 
-  // ---- phase A2: forward over the chunk, one checkpoint per block
+  // ---- phase A2: forward over the chunk, one checkpoint per block.  Exact
+  //      ZOH off the guarded path (every |A| >= kWeakA) runs on scaled states
+  //      s = A h, as the forward does: s <- a (s + B u) - B u, one operation
+  //      fewer than a h + ((a - 1) / A) B u; the checkpoints hold s.
+  constexpr bool kScaledCk = DISC == kZoh && !SAFE;
   float ck[kNB][kNS];
+  if (kScaledCk) {
+#pragma unroll
+    for (int j = 0; j < kNS; ++j) h[j] *= A[j];
+  }
 #pragma unroll
   for (int jb = 0; jb < kNB; ++jb) {
 #pragma unroll
@@ -281,15 +318,15 @@ __device__ __forceinline__ void bwd_chunk(const BwdParams& p, float* lds, int64_
 #pragma unroll
       for (int j = 0; j < kNS; ++j) {
         const float a = hw_exp2(dl * A[j]);
-        float bu;
         if (DISC == kEuler) {
-          bu = dtu * Bv[j];
+          h[j] = __builtin_fmaf(a, h[j], dtu * Bv[j]);
+        } else if (kScaledCk) {
+          const float bu = Bv[j] * uf;
+          h[j] = __builtin_fmaf(a, h[j] + bu, -bu);
         } else {
-          const float coef = SAFE ? zoh_coef_guarded(a, iA[j], dl * kLn2, dl * A[j])
-                                  : __builtin_fmaf(a, iA[j], -iA[j]);
-          bu = coef * (Bv[j] * uf);
+          const float coef = zoh_coef_guarded(a, iA[j], dl * kLn2, dl * A[j]);
+          h[j] = __builtin_fmaf(a, h[j], coef * (Bv[j] * uf));
         }
-        h[j] = __builtin_fmaf(a, h[j], bu);
       }
     }
   }
@@ -303,12 +340,15 @@ __device__ __forceinline__ void bwd_chunk(const BwdParams& p, float* lds, int64_
   float dDacc = 0.0f, dbacc = 0.0f;
   // the value a lane holds after a reduce-scatter of [4 steps][4 states]: step
   // rk of the block, state n0 + rj; its rows of pB / pC for block 0
+  // (pB, pC rows of the chunk's first step, based at this group and wave's
+  // states; a lane that writes nothing gets an out-of-range offset)
   const int rk = int(lane >> 4), rj = int((lane >> 2) & 3u);
   const bool rwrite = (lane & 3u) == 0 && n0 + rj < N;
-  const int64_t roff = ((row0 + t0 + rk) * p.ndblk + dblk) * N + n0 + rj;
-  float* const pBl = p.pB + roff;
-  float* const pCl = p.pC + roff;
-  const int64_t rstep = int64_t(kKB) * p.ndblk * N;   // between blocks
+  const int64_t rbase = ((row0 + t0) * p.ndblk + dblk) * N + n0;
+  const Rsrc rpB = make_rsrc(p.pB + rbase), rpC = make_rsrc(p.pC + rbase);
+  const uint32_t rstep = uint32_t(p.ndblk) * uint32_t(N) * uint32_t(sizeof(float));   // per step
+  const uint32_t rvoff = rwrite ? uint32_t(rk) * rstep + uint32_t(rj) * uint32_t(sizeof(float))
+                                : kOutOfRange;
 
 #pragma unroll
   for (int jb = kNB - 1; jb >= 0; --jb) {
@@ -318,19 +358,25 @@ __device__ __forceinline__ void bwd_chunk(const BwdParams& p, float* lds, int64_
     In zo{}, go{}, dlo{};
     {
       const int32_t tw = t0 + jb * kKB + wave;
-      const int64_t iw = ibase + int64_t(tw < t1 ? tw : t1 - 1) * D;
+      const uint32_t so = uint32_t((tw < t1 ? tw : t1 - 1) - t0) * io.sin;
       if (HAS_Z) {
-        zo = static_cast<const In*>(p.z)[iw];
-        go = static_cast<const In*>(p.dy)[iw];
+        zo = buf_load<In>(io.z, io.vin, so);
+        go = buf_load<In>(io.dy, io.vin, so);
       }
-      if (SOFTPLUS) dlo = static_cast<const In*>(p.delta)[iw];
+      if (SOFTPLUS) dlo = buf_load<In>(io.dl, io.vin, so);
     }
     float uf[kKB], dl[kKB], gy[kKB], yp[kKB];
     float hs[kKB][kNS];
     float red[kKB * kNS];
-    // recompute the block; dC = gy h
+    // recompute the block from its checkpoint (scaled states: s runs as in the
+    // checkpoint pass, h = s / A); dC = gy h
+    float hb[kNS], sc[kNS];
 #pragma unroll
-    for (int j = 0; j < kNS; ++j) h[j] = ck[jb][j];
+    for (int j = 0; j < kNS; ++j) {
+      sc[j] = ck[jb][j];
+      hb[j] = kScaledCk ? sc[j] * iA[j] : sc[j];
+      h[j] = hb[j];
+    }
 #pragma unroll
     for (int k = 0; k < kKB; ++k) {
       const int kk = jb * kKB + k;
@@ -345,25 +391,27 @@ __device__ __forceinline__ void bwd_chunk(const BwdParams& p, float* lds, int64_
 #pragma unroll
       for (int j = 0; j < kNS; ++j) {
         const float a = hw_exp2(dl[k] * A[j]);
-        float bu;
         if (DISC == kEuler) {
-          bu = dtu * Bv[j];
+          h[j] = __builtin_fmaf(a, h[j], dtu * Bv[j]);
+        } else if (kScaledCk) {
+          const float bu = Bv[j] * uf[k];
+          sc[j] = __builtin_fmaf(a, sc[j] + bu, -bu);
+          h[j] = sc[j] * iA[j];
         } else {
-          const float coef = SAFE ? zoh_coef_guarded(a, iA[j], dtu0, dl[k] * A[j])
-                                  : __builtin_fmaf(a, iA[j], -iA[j]);
-          bu = coef * (Bv[j] * uf[k]);
+          const float coef = zoh_coef_guarded(a, iA[j], dtu0, dl[k] * A[j]);
+          h[j] = __builtin_fmaf(a, h[j], coef * (Bv[j] * uf[k]));
         }
-        h[j] = __builtin_fmaf(a, h[j], bu);
         hs[k][j] = h[j];
         y0 = __builtin_fmaf(Cv[j], h[j], y0);
         red[k * kNS + j] = gy[k] * h[j];                       // dC
       }
       yp[k] = y0;
     }
+    // a block's rows are 4 steps: the lane's step rk must lie before t1
+    const uint32_t rv = t0 + jb * kKB + rk < t1 ? rvoff : kOutOfRange;
     {
       const float r = reduce_scatter16(red, lane);
-      const int32_t t = t0 + jb * kKB + rk;
-      if (rwrite && t < t1) pCl[jb * rstep] = r;
+      buf_store<float>(rpC, rv, uint32_t(jb * kKB) * rstep, r);
     }
     // reverse sweep.  Per step, with lam = d loss / d h_t and nu = A_bar lam:
     //   dB = lam coef u (coef = dt for Euler, (A_bar - 1) / A for exact ZOH)
@@ -384,7 +432,7 @@ __device__ __forceinline__ void bwd_chunk(const BwdParams& p, float* lds, int64_
 #pragma unroll
       for (int j = 0; j < kNS; ++j) {
         const float a = hw_exp2(dl[k] * A[j]);     // same value as in the recompute
-        const float hp = k > 0 ? hs[k - 1][j] : ck[jb][j];
+        const float hp = k > 0 ? hs[k - 1][j] : hb[j];
         const float lam = __builtin_fmaf(gy[k], Cv[j], nu[j]);
         nu[j] = a * lam;
         const float nh = nu[j] * hp;
@@ -395,9 +443,9 @@ __device__ __forceinline__ void bwd_chunk(const BwdParams& p, float* lds, int64_
           sLB = __builtin_fmaf(lam, Bv[j], sLB);
         } else {
           const float x2 = dl[k] * A[j];         // dt A log2 e
-          const float coef = SAFE ? zoh_coef_guarded(a, iA[j], dtn, x2)
-                                  : __builtin_fmaf(a, iA[j], -iA[j]);
-          const float cl = lam * coef;
+          // lam coef: lam (a - 1) / A off the guarded path
+          const float cl = SAFE ? lam * zoh_coef_guarded(a, iA[j], dtn, x2)
+                                : __builtin_fmaf(a, lam, -lam) * iA[j];
           const float db = cl * uf[k];
           red[k * kNS + j] = db;                          // dB
           sdu = __builtin_fmaf(cl, Bv[j], sdu);
@@ -419,8 +467,7 @@ __device__ __forceinline__ void bwd_chunk(const BwdParams& p, float* lds, int64_
     }
     {
       const float r = reduce_scatter16(red, lane);
-      const int32_t t = t0 + jb * kKB + rk;
-      if (rwrite && t < t1) pBl[jb * rstep] = r;
+      buf_store<float>(rpB, rv, uint32_t(jb * kKB) * rstep, r);
     }
     // per-step partials of this wave -> LDS
 #pragma unroll
@@ -441,8 +488,8 @@ __device__ __forceinline__ void bwd_chunk(const BwdParams& p, float* lds, int64_
         sdd += xch[((w * 3 + 1) * kKB + k) * kWave + lane];
         sy += xch[((w * 3 + 2) * kKB + k) * kWave + lane];
       }
-      if (t < t1 && active) {
-        const int64_t i = ibase + int64_t(t) * D;
+      if (t < t1) {
+        const uint32_t so = uint32_t(t - t0) * io.sout;
         const int kk = jb * kKB + k;
         const float ui = actU[kk * kWave + lane], gyk = actGy[kk * kWave + lane];
         if (HAS_Z) {
@@ -450,12 +497,12 @@ __device__ __forceinline__ void bwd_chunk(const BwdParams& p, float* lds, int64_
           const float zf = to_f32(zo), g = to_f32(go);
           const float sz = sigmoid_log2(zf * kLog2e);
           const float y = __builtin_fmaf(Dd, ui, sy);
-          p.dz[i] = g * y * sz * __builtin_fmaf(zf, 1.0f - sz, 1.0f);
+          buf_store<float>(io.dz, io.vout, so, g * y * sz * __builtin_fmaf(zf, 1.0f - sz, 1.0f));
         }
-        p.du[i] = __builtin_fmaf(gyk, Dd, sdu);
+        buf_store<float>(io.du, io.vout, so, __builtin_fmaf(gyk, Dd, sdu));
         float ddv = sdd;                                 // d loss / d dt
         if (SOFTPLUS) ddv *= sigmoid_log2(__builtin_fmaf(to_f32(dlo), kLog2e, bias2));   // through softplus
-        p.ddelta[i] = ddv;
+        buf_store<float>(io.ddelta, io.vout, so, ddv);
         dDacc = __builtin_fmaf(gyk, ui, dDacc);
         dbacc += ddv;
       }
@@ -490,9 +537,11 @@ __device__ __forceinline__ void bwd_chunk(const BwdParams& p, float* lds, int64_
   }
 }
 
-// Euler: three waves per SIMD (at most 168 VGPRs); exact ZOH: two (256)
+// Three waves per SIMD (at most 168 VGPRs).  Exact ZOH's guarded path (a
+// workgroup holding a slowly decaying state) spills a few values to scratch at
+// this bound; the fast path does not.
 template <typename In, int DISC, bool HAS_Z, bool SOFTPLUS>
-__global__ __launch_bounds__(kWave * kNW, DISC == kEuler ? 3 : 2) void bwd_kernel(BwdParams p) {
+__global__ __launch_bounds__(kWave * kNW, 3) void bwd_kernel(BwdParams p) {
   __shared__ float4 lds4[kLdsFloats / 4];
   float* lds = reinterpret_cast<float*>(lds4);
   const int wave = __builtin_amdgcn_readfirstlane(int(threadIdx.x) / kWave);
@@ -538,7 +587,8 @@ __device__ __forceinline__ void summary_chunk(const BwdParams& p, float* lds, in
   const int32_t t1 = int32_t(t0 + kChunk < p.L ? t0 + kChunk : p.L);
   const int64_t row0 = b * p.L;
   const float bias2 = (p.bias ? p.bias[dc] : 0.0f) * kLog2e;
-  stage_chunk<In, HAS_Z, SOFTPLUS>(p, lds, row0 * D + dc, row0, t0, t1, wave, lane, bias2,
+  const ChunkIO<In> io(p, b, t0, dblk, lane, active);
+  stage_chunk<In, HAS_Z, SOFTPLUS>(p, io, lds, row0, t0, t1, wave, lane, bias2,
                                    active ? 1.0f : 0.0f);
   float A[kNS], iA[kNS];
 #pragma unroll
