@@ -611,7 +611,7 @@ __device__ __forceinline__ void summary_chunk(const BwdParams& p, float* lds, in
     R[j] = 0.0f;
   }
   float dsum = 0.0f;
-#pragma unroll 8
+#pragma unroll 4
   for (int k = 0; k < kChunk; ++k) {
     const float dl = actDl[k * kWave + lane];
     const float uf = actU[k * kWave + lane];
@@ -623,15 +623,16 @@ __device__ __forceinline__ void summary_chunk(const BwdParams& p, float* lds, in
 #pragma unroll
     for (int j = 0; j < kNS; ++j) {
       const float a = hw_exp2(dl * A[j]);
-      float bu;
       if (DISC == kEuler) {
-        bu = dtu * Bv[j];
+        h[j] = __builtin_fmaf(a, h[j], dtu * Bv[j]);
+      } else if (SAFE) {
+        const float coef = zoh_coef_guarded(a, iA[j], dl * kLn2, dl * A[j]);
+        h[j] = __builtin_fmaf(a, h[j], coef * (Bv[j] * uf));
       } else {
-        const float coef = SAFE ? zoh_coef_guarded(a, iA[j], dl * kLn2, dl * A[j])
-                                : __builtin_fmaf(a, iA[j], -iA[j]);
-        bu = coef * (Bv[j] * uf);
+        // scaled state s = A h, as in the main kernel's checkpoint pass
+        const float bu = Bv[j] * uf;
+        h[j] = __builtin_fmaf(a, h[j] + bu, -bu);
       }
-      h[j] = __builtin_fmaf(a, h[j], bu);
       P[j] *= a;
       R[j] = __builtin_fmaf(P[j], gy * Cv[j], R[j]);
     }
@@ -642,7 +643,7 @@ __device__ __forceinline__ void summary_chunk(const BwdParams& p, float* lds, in
   if (chunk <= p.nchunks - 2) {
 #pragma unroll
     for (int j = 0; j < kNS; ++j)
-      if (n0 + j < N) p.hstart[slot + int64_t(n0 + j) * D] = h[j];
+      if (n0 + j < N) p.hstart[slot + int64_t(n0 + j) * D] = DISC == kZoh && !SAFE ? h[j] * iA[j] : h[j];
     if (wave == 0) p.dsum[(b * p.nchunks + chunk) * D + d] = dsum;
   }
   if (chunk >= 1) {
