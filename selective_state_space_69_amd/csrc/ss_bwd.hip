@@ -21,8 +21,9 @@
 // and ddelta_bias per channel over the chunk, then over chunks and batch rows.
 // All partial sums are added in a fixed order: the backward is deterministic.
 // The chunk's inputs are all fetched at its start (one round trip to memory)
-// and kept in LDS (41 KB); the main kernel holds about 165 VGPRs for Euler (three
-// waves per SIMD) and 210 for exact ZOH (two).
+// and kept in LDS (41 KB); the main kernel holds at most 168 VGPRs (three waves
+// per SIMD): exact ZOH keeps scaled states s = A h off its guarded path, which
+// needs no cached coefficients.
 #include "ss_device.hpp"
 
 namespace ss {
