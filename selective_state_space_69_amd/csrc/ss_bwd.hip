@@ -151,6 +151,36 @@ __device__ __forceinline__ float reduce_scatter16(const float (&v)[16], uint32_t
   return d;
 }
 
+// 16 values per lane -> their sums over the wave's 64 lanes, through the wave's
+// own 3 KB of LDS, 8 values at a time: every lane writes its 8 values as rows
+// [value][lane] (rows padded to 68 floats), then lane l adds the 8 entries of
+// row l / 8 written by lanes 8 (l % 8) .. 8 (l % 8) + 7 (two 16-byte reads; the
+// 16 lanes of one read pass cover all 64 banks once) and the 8 lanes of a row
+// combine their sums with two quad butterflies and a half-row mirror.  After
+// half h, lanes 8i .. 8i+7 hold the sum of value 8h + i.  Every lane adds in the
+// same fixed order.  LDS requests of one wave are served in order, so the rows
+// a half reads are the ones it wrote, and the next half's writes land after
+// those reads; the wavefront-scope fences keep the compiler from reordering them.
+constexpr int kRedRow = kWave + 4;
+__device__ __forceinline__ void reduce_lds16(const float (&v)[16], float* xw, uint32_t lane,
+                                             float (&out)[2]) {
+  const int i = int(lane >> 3), q = int(lane & 7u);
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) xw[k * kRedRow + lane] = v[8 * h + k];
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    const float4 a = *reinterpret_cast<const float4*>(xw + i * kRedRow + 8 * q);
+    const float4 b = *reinterpret_cast<const float4*>(xw + i * kRedRow + 8 * q + 4);
+    float r = ((a.x + a.y) + (a.z + a.w)) + ((b.x + b.y) + (b.z + b.w));
+    r += dpp<kDppQuadXor1>(r);
+    r += dpp<kDppQuadXor2>(r);
+    r += dpp<kDppRowHalfMirror>(r);
+    out[h] = r;
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  }
+}
+
 // ---------------------------------------------------------------- main kernel
 // LDS (floats): step sizes, gated output gradients and inputs u
 // [32 steps][64 lanes], B/C rows [32 steps][B 16, C 16], per-step partials of
@@ -339,12 +369,20 @@ __device__ __forceinline__ void bwd_chunk(const BwdParams& p, float* lds, int64_
 #pragma unroll
   for (int j = 0; j < kNS; ++j) dA[j] = dAc[j] = 0.0f;
   float dDacc = 0.0f, dbacc = 0.0f;
-  // the value a lane holds after a reduce-scatter of [4 steps][4 states]: step
-  // rk of the block, state n0 + rj; its rows of pB / pC for block 0
-  // (pB, pC rows of the chunk's first step, based at this group and wave's
-  // states; a lane that writes nothing gets an out-of-range offset)
-  const int rk = int(lane >> 4), rj = int((lane >> 2) & 3u);
-  const bool rwrite = (lane & 3u) == 0 && n0 + rj < N;
+  // The sums over the 64 channels of a block's [4 steps][4 states] dB or dC
+  // values.  Exact ZOH takes them through LDS (reduce_lds16: after half h the
+  // first lane of each 8-lane row holds value 8h + lane / 8, i.e. step
+  // 2h + lane / 32 of the block, state n0 + (lane / 8) % 4); Euler, whose
+  // shorter sweep leaves less work to cover the LDS round trips, by the
+  // cross-lane reduce-scatter (the first lane of each quad holds value
+  // lane / 4: step lane / 16, state n0 + (lane / 4) % 4).  That lane stores it
+  // into the pB / pC rows (based at the chunk's first step, this group and this
+  // wave's states); the other lanes get an out-of-range offset.
+  constexpr bool kLdsRed = DISC == kZoh;
+  float* const xw = xch + wave * 3 * kKB * kWave;          // this wave's slice
+  const int rk = kLdsRed ? int(lane >> 5) : int(lane >> 4);
+  const int rj = kLdsRed ? int((lane >> 3) & 3u) : int((lane >> 2) & 3u);
+  const bool rwrite = (lane & (kLdsRed ? 7u : 3u)) == 0 && n0 + rj < N;
   const int64_t rbase = ((row0 + t0) * p.ndblk + dblk) * N + n0;
   const Rsrc rpB = make_rsrc(p.pB + rbase), rpC = make_rsrc(p.pC + rbase);
   const uint32_t rstep = uint32_t(p.ndblk) * uint32_t(N) * uint32_t(sizeof(float));   // per step
@@ -408,12 +446,22 @@ __device__ __forceinline__ void bwd_chunk(const BwdParams& p, float* lds, int64_
       }
       yp[k] = y0;
     }
-    // a block's rows are 4 steps: the lane's step rk must lie before t1
-    const uint32_t rv = t0 + jb * kKB + rk < t1 ? rvoff : kOutOfRange;
-    {
-      const float r = reduce_scatter16(red, lane);
-      buf_store<float>(rpC, rv, uint32_t(jb * kKB) * rstep, r);
-    }
+    // a block's rows are 4 steps: the lane's step (2h + rk in half h of the
+    // LDS form) must lie before t1
+    const uint32_t rv0 = t0 + jb * kKB + rk < t1 ? rvoff : kOutOfRange;
+    const uint32_t rv1 = kLdsRed && t0 + jb * kKB + 2 + rk < t1 ? rvoff + 2 * rstep : kOutOfRange;
+    auto reduce_store = [&](Rsrc rp) {
+      const uint32_t so = uint32_t(jb * kKB) * rstep;
+      if constexpr (kLdsRed) {
+        float r[2];
+        reduce_lds16(red, xw, lane, r);
+        buf_store<float>(rp, rv0, so, r[0]);
+        buf_store<float>(rp, rv1, so, r[1]);
+      } else {
+        buf_store<float>(rp, rv0, so, reduce_scatter16(red, lane));
+      }
+    };
+    reduce_store(rpC);
     // reverse sweep.  Per step, with lam = d loss / d h_t and nu = A_bar lam:
     //   dB = lam coef u (coef = dt for Euler, (A_bar - 1) / A for exact ZOH)
     //   du = sum_n lam coef B
@@ -466,10 +514,7 @@ __device__ __forceinline__ void bwd_chunk(const BwdParams& p, float* lds, int64_
       dup[k] = DISC == kEuler ? dtn * sLB : sdu;
       ddp[k] = __builtin_fmaf(uf[k], sLB, sdd);
     }
-    {
-      const float r = reduce_scatter16(red, lane);
-      buf_store<float>(rpB, rv, uint32_t(jb * kKB) * rstep, r);
-    }
+    reduce_store(rpB);
     // per-step partials of this wave -> LDS
 #pragma unroll
     for (int k = 0; k < kKB; ++k) {
