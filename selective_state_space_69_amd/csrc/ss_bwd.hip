@@ -16,9 +16,10 @@
 //     runs the chunk forward keeping one state checkpoint per 4-step block in
 //     registers, then walks the blocks backwards: recompute the block (A_bar
 //     and h kept in registers), reverse sweep, gradients.
-// Reductions: dB, dC over the 64 channels of a block by a cross-lane
-// reduce-scatter (permlane swaps and DPP), then over channel blocks; dA, dD_skip
-// and ddelta_bias per channel over the chunk, then over chunks and batch rows.
+// Reductions: dB, dC over the 64 channels of a block through LDS (exact ZOH) or
+// by a cross-lane reduce-scatter (permlane swaps and DPP; Euler), then over
+// channel blocks; dA, dD_skip and ddelta_bias per channel over the chunk, then
+// over chunks and batch rows.
 // All partial sums are added in a fixed order: the backward is deterministic.
 // The chunk's inputs are all fetched at its start (one round trip to memory)
 // and kept in LDS (41 KB); the main kernel holds at most 168 VGPRs (three waves
@@ -79,12 +80,11 @@ __device__ __forceinline__ float sigmoid_log2(float x2) {   // 1 / (1 + e^-x), x
 }
 
 // ---------------------------------------------------------------- reduce-scatter
-// 64 values per lane -> lane l holds the sum over the 64 lanes of value l.
-// Stages pair lanes at distance 32 and 16 (permlane swaps: the pair's two sums
-// come out of one swap + add), then 8 (row rotate), the mirror pairs inside
-// each 8-lane group, 2 and 1 (quad permutes).  After each stage a lane keeps
-// the half of its values selected by one bit of its lane id, so lane l ends
-// with value l.
+// Pairing stages of the cross-lane reduce-scatter below: lanes at distance 32
+// and 16 (permlane swaps: the pair's two sums come out of one swap + add),
+// then 8 (row rotate) and the mirror pairs inside each 8-lane group.  After
+// each stage a lane keeps the half of its values selected by one bit of its
+// lane id.
 __device__ __forceinline__ float swap_add32(float lo, float hi) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(lo), __float_as_uint(hi), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
@@ -111,28 +111,8 @@ constexpr int kDppRowHalfMirror = 0x141;
 constexpr int kDppQuadXor2 = 0x4e;   // quad_perm [2, 3, 0, 1]
 constexpr int kDppQuadXor1 = 0xb1;   // quad_perm [1, 0, 3, 2]
 
-__device__ __forceinline__ float reduce_scatter64(const float (&v)[64], uint32_t lane) {
-  float a[32];
-#pragma unroll
-  for (int i = 0; i < 32; ++i) a[i] = swap_add32(v[i], v[i + 32]);
-  float b[16];
-#pragma unroll
-  for (int i = 0; i < 16; ++i) b[i] = swap_add16(a[i], a[i + 16]);
-  float c[8];
-  const bool u3 = (lane >> 3) & 1u, u2 = (lane >> 2) & 1u, u1 = (lane >> 1) & 1u, u0 = lane & 1u;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) c[i] = dpp_pair<kDppRowRor8>(b[i], b[i + 8], u3);
-  float d[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) d[i] = dpp_pair<kDppRowHalfMirror>(c[i], c[i + 4], u2);
-  float e[2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i) e[i] = dpp_pair<kDppQuadXor2>(d[i], d[i + 2], u1);
-  return dpp_pair<kDppQuadXor1>(e[0], e[1], u0);
-}
-
 // 16 values per lane -> lanes 4i .. 4i+3 hold the sum over the 64 lanes of
-// value i: the same pairing stages down to one value per lane, then two
+// value i: the pairing stages down to one value per lane, then two
 // butterflies inside each quad.
 __device__ __forceinline__ float reduce_scatter16(const float (&v)[16], uint32_t lane) {
   float a[8];
