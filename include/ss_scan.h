@@ -37,7 +37,8 @@
  *     output (x_proj, (B, L, R + 2N): the low-rank step input, then B, then C;
  *     Gu & Dao note, Mamba architecture; "Mamba: S4 epic upgrade",
  *     parameter-efficient data dependence), and the scan reads them in place.
- *   - Pointers are DEVICE pointers owned by the caller, 16-byte aligned, and valid until
+ *   - Pointers are DEVICE pointers owned by the caller, 16-byte aligned (Bm and
+ *     Cm read with a row stride: aligned to their element size), and valid until
  *     the stream reaches the queued work.  Element types: in_dtype for u, delta,
  *     z, Bm, Cm and dy; out_dtype for y, du, ddelta and dz; float32 for everything
  *     else.  bf16 values are raw IEEE bfloat16 bit patterns (uint16).
@@ -282,7 +283,8 @@ int ss_scan_bwd(const ss_desc_t* desc,
 
 /*
  * One recurrent (inference) step for every (b, d): the state h (B,D,N) fp32 is
- * read and overwritten in place; u, delta, z, y are (B,D); Bm, Cm are (B,N).
+ * read and overwritten in place; u, delta, z, y are (B,D); Bm, Cm are (B,N)
+ * (rows desc->bc_stride elements apart when it is nonzero).
  * desc->seqlen is ignored.  Optional pointers as in ss_scan_fwd.  y must not
  * alias h, u, delta, Bm, Cm or z (SS_ERR_INVALID_ARG): it is written while other
  * lanes still read them.  batch * dim <= 2^33.  The state is O(1) per token,
