@@ -303,6 +303,14 @@ def _bc_stride(B, C, N):
     return 0 if sb == N and dense_ok else sb
 
 
+def _dense(**tensors):
+    """The library reads every tensor but strided B, C as dense rows: refuse
+    views with other strides instead of reading the wrong elements."""
+    for name, t in tensors.items():
+        if t is not None and not t.is_contiguous():
+            raise ValueError("%s must be contiguous (got strides %s)" % (name, tuple(t.stride())))
+
+
 def _desc_from(u, A, B, C, disc, softplus, out_dtype):
     Bt, L, D = u.shape
     N = A.shape[1]
@@ -324,6 +332,7 @@ def scan_fwd(u, delta, A, B, C, D=None, delta_bias=None, z=None, h0=None, disc="
     (in place) instead of allocating a new output.  B and C may be views with a
     row stride (column ranges of one projection output); the other tensors are
     dense."""
+    _dense(u=u, delta=delta, A=A, D=D, delta_bias=delta_bias, z=z, h0=h0, y=y)
     desc = _desc_from(u, A, B, C, disc, softplus, out_dtype if y is None else y.dtype)
     acc = y is not None
     if y is None:
@@ -346,6 +355,7 @@ def scan_fwd_complex(u, delta, A, B, C, D=None, delta_bias=None, z=None, h0=None
     h0 (B, D, N, 2) float32 ((re, im) pairs).  Returns y (and h_last (B, D, N, 2)).
     Uses ss_scan_fwd_complex_ws with a torch workspace (time chunks where the
     plan wants them)."""
+    _dense(u=u, delta=delta, A=A, B=B, C=C, D=D, delta_bias=delta_bias, z=z, h0=h0)
     Bt, L, Dd = u.shape
     N = A.shape[1]
     desc = make_desc(Bt, L, Dd, N, _DTYPE[u.dtype], _DTYPE[out_dtype], _DISC[disc], softplus)
@@ -376,6 +386,7 @@ def scan_bwd(u, delta, A, B, C, dy, D=None, delta_bias=None, z=None, h0=None, di
              softplus=True, want_dh0=False, stream=None):
     """Backward scan; returns a dict of fp32 gradients (dB, dC dense even when B
     and C are strided views)."""
+    _dense(u=u, delta=delta, A=A, D=D, delta_bias=delta_bias, z=z, h0=h0, dy=dy)
     desc = _desc_from(u, A, B, C, disc, softplus, torch.float32)
     dev = u.device
     f32 = dict(dtype=torch.float32, device=dev)
@@ -398,6 +409,7 @@ def scan_step(h, u, delta, A, B, C, D=None, delta_bias=None, z=None, disc="zoh",
               out_dtype=torch.float32, stream=None):
     """One recurrent step; h (B,D,N) fp32 is updated in place; returns y (B,D).
     B and C (B,N) may be strided views, as in scan_fwd."""
+    _dense(h=h, u=u, delta=delta, A=A, D=D, delta_bias=delta_bias, z=z)
     Bt, Dd = u.shape
     desc = make_desc(Bt, 1, Dd, A.shape[1], _DTYPE[u.dtype], _DTYPE[out_dtype], _DISC[disc],
                      softplus, _bc_stride(B, C, A.shape[1]))
@@ -410,6 +422,7 @@ def scan_step_complex(h, u, delta, A, B, C, D=None, delta_bias=None, z=None, dis
                       softplus=True, out_dtype=torch.float32, stream=None):
     """One step with complex A: h (B,D,N,2) fp32 updated in place, A (D,N,2),
     B and C (B,N,2); returns y (B,D)."""
+    _dense(h=h, u=u, delta=delta, A=A, B=B, C=C, D=D, delta_bias=delta_bias, z=z)
     Bt, Dd = u.shape
     desc = make_desc(Bt, 1, Dd, A.shape[1], _DTYPE[u.dtype], _DTYPE[out_dtype], _DISC[disc],
                      softplus)
@@ -422,6 +435,7 @@ def scan_step_complex(h, u, delta, A, B, C, D=None, delta_bias=None, z=None, dis
 def conv1d_fwd(x, w, bias=None, silu=True, out_dtype=None, stream=None):
     """Causal depthwise conv of width w.shape[1] (+ SiLU) over x (B, L, D);
     returns u (B, L, D) in out_dtype (default: x's dtype)."""
+    _dense(x=x, w=w, bias=bias)
     Bt, L, Dd = x.shape
     out_dtype = x.dtype if out_dtype is None else out_dtype
     desc = make_conv_desc(Bt, L, Dd, w.shape[1], _DTYPE[x.dtype], _DTYPE[out_dtype], silu)
@@ -432,6 +446,7 @@ def conv1d_fwd(x, w, bias=None, silu=True, out_dtype=None, stream=None):
 
 def conv1d_bwd(x, w, du, bias=None, silu=True, stream=None):
     """Backward of conv1d_fwd given du (fp32); returns dict dx, dw, dbias (fp32)."""
+    _dense(x=x, w=w, du=du, bias=bias)
     Bt, L, Dd = x.shape
     desc = make_conv_desc(Bt, L, Dd, w.shape[1], _DTYPE[x.dtype], SS_F32, silu)
     f32 = dict(dtype=torch.float32, device=x.device)
@@ -446,6 +461,7 @@ def conv1d_bwd(x, w, du, bias=None, silu=True, stream=None):
 
 def conv1d_step(state, x, w, bias=None, silu=True, out_dtype=torch.float32, stream=None):
     """One decode step: state (B, D, K-1) fp32 updated in place, x (B, D); returns u."""
+    _dense(state=state, x=x, w=w, bias=bias)
     Bt, Dd = x.shape
     desc = make_conv_desc(Bt, 1, Dd, w.shape[1], _DTYPE[x.dtype], _DTYPE[out_dtype], silu)
     u = torch.empty(x.shape, dtype=out_dtype, device=x.device)
@@ -459,6 +475,7 @@ def ssd_fwd(x, dt, A, B, C, D=None, dt_bias=None, softplus=True, out_dtype=torch
     (Bt, L, G, N) in bf16; A, D, dt_bias (H,) fp32; optional start state h0
     (Bt, H, N, P) fp32.  Returns y (Bt, L, H, P), and with return_last the
     state after the last step as well."""
+    _dense(x=x, dt=dt, A=A, B=B, C=C, D=D, dt_bias=dt_bias, h0=h0)
     Bt, L, H, P = x.shape
     G, N = B.shape[2], B.shape[3]
     desc = make_ssd_desc(Bt, L, H, P, N, G, _DTYPE[x.dtype], _DTYPE[out_dtype], softplus)
@@ -477,6 +494,7 @@ def ssd_step(h, x, dt, A, B, C, D=None, dt_bias=None, softplus=True, out_dtype=t
              stream=None):
     """One SSD decode step: h (Bt, H, N, P) fp32 updated in place; x (Bt, H, P),
     dt (Bt, H), B and C (Bt, G, N) bf16.  Returns y (Bt, H, P)."""
+    _dense(h=h, x=x, dt=dt, A=A, B=B, C=C, D=D, dt_bias=dt_bias)
     Bt, H, P = x.shape
     G, N = B.shape[1], B.shape[2]
     desc = make_ssd_desc(Bt, 1, H, P, N, G, _DTYPE[x.dtype], _DTYPE[out_dtype], softplus)

@@ -459,3 +459,27 @@ def test_binding_row_stride():
         B._bc_stride(x[:, :, 8:24], torch.zeros(2, 5, 16), 16)      # different strides
     with pytest.raises(ValueError):
         B._bc_stride(x[:, :, 0:40:2], x[:, :, 1:40:2], 20)          # last axis not unit
+
+
+def test_binding_refuses_strided_dense_args():
+    """The torch-level wrappers refuse non-contiguous views where the library reads
+    dense rows (everything but strided B, C), before any library call."""
+    import torch
+    u = torch.zeros(2, 8, 32)
+    A = torch.zeros(32, 16)
+    Bm = torch.zeros(2, 8, 16)
+    bad = torch.zeros(2, 32, 8).transpose(1, 2)          # (2, 8, 32), not contiguous
+    with pytest.raises(ValueError, match="u must be contiguous"):
+        B.scan_fwd(bad, u, A, Bm, Bm)
+    with pytest.raises(ValueError, match="delta must be contiguous"):
+        B.scan_fwd(u, bad, A, Bm, Bm)
+    with pytest.raises(ValueError, match="dy must be contiguous"):
+        B.scan_bwd(u, u, A, Bm, Bm, bad)
+    with pytest.raises(ValueError, match="B must be contiguous"):
+        B.scan_fwd_complex(u, u, torch.zeros(32, 16, 2), torch.zeros(2, 16, 8, 2).transpose(1, 2),
+                           torch.zeros(2, 8, 16, 2))
+    with pytest.raises(ValueError, match="x must be contiguous"):
+        B.conv1d_fwd(bad, torch.zeros(32, 4))
+    with pytest.raises(ValueError, match="x must be contiguous"):
+        B.ssd_fwd(torch.zeros(2, 8, 64, 3).transpose(2, 3), torch.zeros(2, 8, 3),
+                  torch.zeros(3), torch.zeros(2, 8, 1, 64), torch.zeros(2, 8, 1, 64))
