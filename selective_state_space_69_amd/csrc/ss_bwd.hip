@@ -851,11 +851,8 @@ int launch_bwd(const ss_desc_t& d, const BwdPlan& plan, const BwdArgs& a, void* 
     e = d.in_dtype == SS_BF16 ? dispatch_bwd<uint16_t>(d, p, true, cols * nc, st)
                               : dispatch_bwd<float>(d, p, true, cols * nc, st);
     if (e != hipSuccess) return int(e);
-    int ec = launch_chunk_carry(hend, dsum, a.A, a.h0, d.batch, d.dim, int(d.dstate), nc, false,
-                                stream);
-    if (ec != 0) return ec;
-    ec = launch_chunk_carry(lam, dsum, a.A, nullptr, d.batch, d.dim, int(d.dstate), nc, true,
-                            stream);
+    const int ec = launch_chunk_carry_pair(hend, lam, dsum, a.A, a.h0, d.batch, d.dim,
+                                           int(d.dstate), nc, stream);
     if (ec != 0) return ec;
   }
   e = d.in_dtype == SS_BF16 ? dispatch_bwd<uint16_t>(d, p, false, cols * nc, st)

@@ -165,14 +165,14 @@ __global__ __launch_bounds__(kWave * kWaves) void chunk_carry_kernel(float* __re
 // its chain runs, so a lane waits on memory once per group, not once per chunk.
 constexpr int kWalkG = 16;
 
+// One lane's walk over (b, n, d): REVERSE = false turns the zero-start end
+// states in `states` into start states, REVERSE = true the local adjoints into
+// the adjoints entering each chunk from its end.
 template <bool REVERSE>
-__global__ __launch_bounds__(256) void chunk_walk_kernel(float* __restrict__ states,
-                                                         const float* __restrict__ dsum,
-                                                         const float* __restrict__ A,
-                                                         const float* __restrict__ h0,
-                                                         int64_t B, int64_t D, int N, int nc) {
-  const int64_t gid = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (gid >= B * N * D) return;
+__device__ __forceinline__ void chunk_walk(float* __restrict__ states, const float* __restrict__ dsum,
+                                           const float* __restrict__ A,
+                                           const float* __restrict__ h0, int64_t gid, int64_t D,
+                                           int N, int nc) {
   const int64_t d = gid % D;
   const int n = int((gid / D) % N);
   const int64_t b = gid / (D * N);
@@ -223,6 +223,32 @@ __global__ __launch_bounds__(256) void chunk_walk_kernel(float* __restrict__ sta
   }
 }
 
+template <bool REVERSE>
+__global__ __launch_bounds__(256) void chunk_walk_kernel(float* __restrict__ states,
+                                                         const float* __restrict__ dsum,
+                                                         const float* __restrict__ A,
+                                                         const float* __restrict__ h0,
+                                                         int64_t B, int64_t D, int N, int nc) {
+  const int64_t gid = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (gid >= B * N * D) return;
+  chunk_walk<REVERSE>(states, dsum, A, h0, gid, D, N, nc);
+}
+
+// Both walks of the backward in one launch (they are independent): the first
+// B N D lanes walk the start states forward, the next B N D the adjoints
+// backward, so twice the lanes cover each other's memory waits.
+__global__ __launch_bounds__(256) void chunk_walk_pair_kernel(float* __restrict__ hstates,
+                                                              float* __restrict__ lstates,
+                                                              const float* __restrict__ dsum,
+                                                              const float* __restrict__ A,
+                                                              const float* __restrict__ h0,
+                                                              int64_t B, int64_t D, int N, int nc) {
+  const int64_t total = B * N * D;
+  const int64_t gid = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (gid < total) chunk_walk<false>(hstates, dsum, A, h0, gid, D, N, nc);
+  else if (gid < 2 * total) chunk_walk<true>(lstates, dsum, A, nullptr, gid - total, D, N, nc);
+}
+
 }  // namespace
 
 int launch_chunk_carry(float* states, const float* dsum, const float* A, const float* h0,
@@ -248,6 +274,22 @@ int launch_chunk_carry(float* states, const float* dsum, const float* A, const f
   else
     hipLaunchKernelGGL(chunk_carry_kernel<false>, grid, block, 0, st, states, dsum, A, h0, D, N,
                        nc, ndblk);
+  return int(hipGetLastError());
+}
+
+int launch_chunk_carry_pair(float* hstates, float* lstates, const float* dsum, const float* A,
+                            const float* h0, int64_t batch, int64_t D, int N, int nc,
+                            void* stream) {
+  if (nc < 2) return 0;
+  if (nc >= kScanMinChunks) {
+    const int e = launch_chunk_carry(hstates, dsum, A, h0, batch, D, N, nc, false, stream);
+    if (e != 0) return e;
+    return launch_chunk_carry(lstates, dsum, A, nullptr, batch, D, N, nc, true, stream);
+  }
+  const int64_t total = 2 * batch * N * D;
+  const dim3 grid(unsigned((total + 255) / 256)), block(256);
+  hipLaunchKernelGGL(chunk_walk_pair_kernel, grid, block, 0, static_cast<hipStream_t>(stream),
+                     hstates, lstates, dsum, A, h0, batch, D, N, nc);
   return int(hipGetLastError());
 }
 

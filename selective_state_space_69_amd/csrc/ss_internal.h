@@ -164,6 +164,11 @@ int launch_conv_step(const ss_conv_desc_t& d, float* state, const void* x, const
 // adjoints into the adjoints entering each chunk from its end.
 int launch_chunk_carry(float* states, const float* dsum, const float* A, const float* h0,
                        int64_t batch, int64_t D, int N, int nc, bool reverse, void* stream);
+// Both carries of the backward (forward on hstates, reverse on lstates), in
+// one launch when the chunks are walked in order.
+int launch_chunk_carry_pair(float* hstates, float* lstates, const float* dsum, const float* A,
+                            const float* h0, int64_t batch, int64_t D, int N, int nc,
+                            void* stream);
 int launch_step(const ss_desc_t& d, const StepArgs& a, void* stream);
 // Complex-A forward plan: 32 channels per workgroup, time cut into nchunks
 // chunks of chunk_len steps (one when nchunks == 1).  Workspace (256-byte
