@@ -704,12 +704,11 @@ __global__ __launch_bounds__(kWave * kNW, 5) void summary_kernel(BwdParams p) {
 }
 
 // ---------------------------------------------------------------- reductions
-__global__ __launch_bounds__(256) void reduce_rows_kernel(const float* __restrict__ pB,
-                                                          const float* __restrict__ pC,
-                                                          float* __restrict__ dB,
-                                                          float* __restrict__ dC, int64_t rows,
-                                                          int nblk, int N) {
-  const int64_t gid = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+// dB, dC (B, L, N): the per-(b, t) rows of partials summed over channel groups.
+__device__ __forceinline__ void reduce_rows(const float* __restrict__ pB,
+                                            const float* __restrict__ pC, float* __restrict__ dB,
+                                            float* __restrict__ dC, int64_t rows, int nblk, int N,
+                                            int64_t gid) {
   if (gid >= rows * N) return;
   const int64_t r = gid / N;
   const int n = int(gid % N);
@@ -731,13 +730,15 @@ __global__ __launch_bounds__(256) void reduce_rows_kernel(const float* __restric
 // groups, each with 8 interleaved running sums, so 128 loads per column are in
 // flight.  Every addition happens in a fixed order: the result is deterministic.
 constexpr int kRedCols = 64, kRedGroups = 16, kRedAcc = 8;
-__global__ __launch_bounds__(kRedCols * kRedGroups) void reduce_chan_kernel(
-    const float* __restrict__ pA, const float* __restrict__ pD, const float* __restrict__ pbias,
-    float* __restrict__ dA, float* __restrict__ dD, float* __restrict__ dbias, int64_t B,
-    int64_t D, int N, int nchunks) {
-  __shared__ float part[2][kRedGroups][kRedCols];
+constexpr int kRedThreads = kRedCols * kRedGroups;
+__device__ __forceinline__ void reduce_chan(const float* __restrict__ pA,
+                                            const float* __restrict__ pD,
+                                            const float* __restrict__ pbias, float* __restrict__ dA,
+                                            float* __restrict__ dD, float* __restrict__ dbias,
+                                            int64_t B, int64_t D, int N, int nchunks, int64_t blk,
+                                            float (&part)[2][kRedGroups][kRedCols]) {
   const int c = int(threadIdx.x) % kRedCols, g = int(threadIdx.x) / kRedCols;
-  const int64_t col = int64_t(blockIdx.x) * kRedCols + c;
+  const int64_t col = blk * kRedCols + c;
   const bool valid = col < D * (N + 1);
   const int64_t d = valid ? col % D : 0;
   const int n = valid ? int(col / D) : 0;
@@ -779,6 +780,22 @@ __global__ __launch_bounds__(kRedCols * kRedGroups) void reduce_chan_kernel(
   } else {
     if (dD) dD[d] = t0;
     if (dbias) dbias[d] = t1;
+  }
+}
+
+// Both reductions in one launch: workgroups [0, nchan) take the channel
+// columns, the rest kRedThreads (b, t, n) entries of dB and dC each (the two
+// are independent; every workgroup takes one branch as a whole).
+__global__ __launch_bounds__(kRedThreads) void reduce_kernel(BwdParams p, float* dA, float* dB,
+                                                            float* dC, float* dD, float* dbias,
+                                                            int64_t B, int64_t nchan) {
+  __shared__ float part[2][kRedGroups][kRedCols];
+  const int64_t blk = blockIdx.x;
+  if (blk < nchan) {
+    reduce_chan(p.pA, p.pD, p.pbias, dA, dD, dbias, B, p.D, p.N, p.nchunks, blk, part);
+  } else {
+    reduce_rows(p.pB, p.pC, dB, dC, B * p.L, p.ndblk, p.N,
+                (blk - nchan) * kRedThreads + threadIdx.x);
   }
 }
 
@@ -859,14 +876,10 @@ int launch_bwd(const ss_desc_t& d, const BwdPlan& plan, const BwdArgs& a, void* 
                             : dispatch_bwd<float>(d, p, false, cols * nc, st);
   if (e != hipSuccess) return int(e);
   const int64_t rows = d.batch * d.seqlen;
-  hipLaunchKernelGGL(reduce_rows_kernel, dim3(unsigned((rows * d.dstate + 255) / 256)), dim3(256),
-                     0, st, p.pB, p.pC, a.dB, a.dC, rows, ndblk, int(d.dstate));
-  e = hipGetLastError();
-  if (e != hipSuccess) return int(e);
-  hipLaunchKernelGGL(reduce_chan_kernel,
-                     dim3(unsigned((d.dim * (d.dstate + 1) + kRedCols - 1) / kRedCols)),
-                     dim3(kRedCols * kRedGroups), 0, st, p.pA, p.pD, p.pbias, a.dA, a.dDskip,
-                     a.dbias, d.batch, d.dim, int(d.dstate), nc);
+  const int64_t nchan = (d.dim * (d.dstate + 1) + kRedCols - 1) / kRedCols;
+  const int64_t nrow = (rows * d.dstate + kRedThreads - 1) / kRedThreads;
+  hipLaunchKernelGGL(reduce_kernel, dim3(unsigned(nchan + nrow)), dim3(kRedThreads), 0, st, p,
+                     a.dA, a.dB, a.dC, a.dDskip, a.dbias, d.batch, nchan);
   return int(hipGetLastError());
 }
 
