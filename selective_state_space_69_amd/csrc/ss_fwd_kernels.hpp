@@ -272,6 +272,13 @@ struct Scan {
             float coef;
             const float e = precise_decay<true>(d2, ch.A[n], ch.iA[n], coef);
             h[n] += __builtin_fmaf(e, h[n], coef * (Bv[n] * uk));
+          } else if (SUMMARY) {
+            // the chunk summary from a zero start keeps s = A h, as the
+            // 32-channel kernel's states: s <- a (s + B u) - B u, one operation
+            // fewer (every |A| >= kWeakA on this path; unscaled at the end)
+            const float a = hw_exp2(d2 * ch.A[n]);
+            const float bu = Bv[n] * uk;
+            h[n] = __builtin_fmaf(a, h[n] + bu, -bu);
           } else {
             const float a = hw_exp2(d2 * ch.A[n]);                // A_bar = exp(dt A)
             const float coef = __builtin_fmaf(a, ch.iA[n], -ch.iA[n]);   // (A_bar - 1) / A
@@ -441,6 +448,10 @@ __global__ __launch_bounds__(kWave * NSPLIT, kMinWaves<NSPLIT>) void fwd_kernel(
   } else {
     Scan<In, Out, DISC, HAS_Z, SOFTPLUS, SUMMARY, false, NSPLIT, REV> sc{p, ch, h};
     dsum = setup(sc);
+    if (SUMMARY && DISC == kZoh) {
+#pragma unroll
+      for (int j = 0; j < NS; ++j) h[j] *= ch.iA[j];       // s = A h -> h
+    }
   }
 
   if (!active) return;
