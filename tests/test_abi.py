@@ -1,6 +1,5 @@
 """CPU-side checks of the C ABI: the library loads, exports every function the
 header declares, and rejects invalid arguments before any HIP call."""
-import ctypes
 import os
 import re
 
