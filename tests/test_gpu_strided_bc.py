@@ -166,3 +166,35 @@ def test_noalloc_strided_bc():
     torch.cuda.synchronize()
     assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
     assert np.isfinite(outs[0][0].cpu().numpy()).all()
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_dense_rows_at_odd_address(oracle, dtype):
+    """Dense B, C rows starting one element into a buffer (not 16-byte aligned):
+    the binding passes bc_stride = N, the forward packs the rows and the step
+    reads them element by element; both equal the aligned dense call bit for bit."""
+    Bt, L, D, N = 2, 130, 96, 16
+    inp = synth.make_inputs(Bt, L, D, N, seed=5400, dtype=dtype, with_h0=True, a_mode="random")
+    d = upload(inp)
+
+    def odd(t):
+        buf = torch.zeros(t.numel() + 8, dtype=t.dtype, device=t.device)
+        v = buf[1:1 + t.numel()].view(t.shape)
+        v.copy_(t)
+        return v
+
+    Bv, Cv = odd(d["B"]), odd(d["C"])
+    assert B._bc_stride(Bv, Cv, N) == N
+    kw = dict(D=d["D"], delta_bias=d["delta_bias"], z=d["z"], h0=d["h0"], disc="zoh",
+              return_last_state=True)
+    y, hl = B.scan_fwd(d["u"], d["delta"], d["A"], Bv, Cv, **kw)
+    y0, hl0 = B.scan_fwd(d["u"], d["delta"], d["A"], d["B"], d["C"], **kw)
+    b1, c1 = odd(d["B"][:, 0].contiguous()), odd(d["C"][:, 0].contiguous())
+    args = (d["u"][:, 0].contiguous(), d["delta"][:, 0].contiguous(), d["A"])
+    skw = dict(D=d["D"], delta_bias=d["delta_bias"], z=d["z"][:, 0].contiguous(), disc="zoh")
+    h, h0 = d["h0"].clone(), d["h0"].clone()
+    ys = B.scan_step(h, *args, b1, c1, **skw)
+    ys0 = B.scan_step(h0, *args, d["B"][:, 0].contiguous(), d["C"][:, 0].contiguous(), **skw)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y0) and torch.equal(hl, hl0)
+    assert torch.equal(ys, ys0) and torch.equal(h, h0)
