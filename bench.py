@@ -423,6 +423,7 @@ def main():
                         "runs": 20}
         roof["stream_gbs"] = round(sgbs, 1)
         roof["frac_of_stream"] = round(hbm_gbs / sgbs, 4)
+        roof["graph"] = time_graph(step, torch)
     del d, y, ws
     torch.cuda.empty_cache()
 
@@ -431,6 +432,36 @@ def main():
     if not args.no_cpu:
         res["cpu_baseline"] = cpu_baseline(inp, w)
     print(json.dumps(res), flush=True)
+
+
+def time_graph(step, torch, calls=20, replays=5):
+    """The same call captured 20 times in one graph and replayed: the per-call
+    time without the host's launches between calls (informational; value is the
+    eagerly launched loop)."""
+    try:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.current_stream().wait_stream(side)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(calls):
+                step()
+        for _ in range(2):
+            g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(replays):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / (calls * replays)
+        del g
+        return {"ms_per_call": round(ms, 4), "calls_per_replay": calls, "replays": replays}
+    except Exception as exc:   # informational: never fail the benchmark over it
+        return {"error": str(exc)[:200]}
 
 
 def extras(torch, Bnd, synth, args):
