@@ -482,3 +482,38 @@ def test_binding_refuses_strided_dense_args():
     with pytest.raises(ValueError, match="x must be contiguous"):
         B.ssd_fwd(torch.zeros(2, 8, 64, 3).transpose(2, 3), torch.zeros(2, 8, 3),
                   torch.zeros(3), torch.zeros(2, 8, 1, 64), torch.zeros(2, 8, 1, 64))
+
+
+def test_binding_structs_match_headers(tmp_path):
+    """The ctypes descriptors have the C layout: a C program built against the
+    headers prints each struct's size and field offsets, which must equal the
+    binding's (a mismatch would hand the library shifted fields)."""
+    import ctypes
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    structs = {"ss_desc_t": B.ss_desc_t, "ss_conv_desc_t": B.ss_conv_desc_t,
+               "ss_ssd_desc_t": B.ss_ssd_desc_t}
+    lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "ss_scan.h"',
+             '#include "ss_conv.h"', '#include "ss_ssd.h"', "int main(void) {"]
+    for cname, py in structs.items():
+        lines.append('  printf("%s size %%zu\\n", sizeof(%s));' % (cname, cname))
+        for fname, _ in py._fields_:
+            lines.append('  printf("%s %s %%zu\\n", offsetof(%s, %s));' % (cname, fname, cname, fname))
+    lines += ["  return 0;", "}"]
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines) + "\n")
+    exe = tmp_path / "layout"
+    subprocess.check_call([cc, "-std=c99", "-I", INCLUDE, str(src), "-o", str(exe)])
+    out = subprocess.check_output([str(exe)]).decode().split("\n")
+    got = {}
+    for line in out:
+        if line.strip():
+            parts = line.split()
+            got[tuple(parts[:-1])] = int(parts[-1])
+    for cname, py in structs.items():
+        assert got[(cname, "size")] == ctypes.sizeof(py), cname
+        for fname, _ in py._fields_:
+            assert got[(cname, fname)] == getattr(py, fname).offset, (cname, fname)
