@@ -147,8 +147,9 @@ int ss_scan_fwd(const ss_desc_t* desc,
  *   Arguments, results and other status codes: exactly ss_scan_fwd (the same
  *   kernels and plan, so the output is bitwise that of ss_scan_fwd).
  *   Returns SS_ERR_SCRATCH_LIMIT, before any HIP call, when the plan needs
- *   more than SS_SCAN_STATIC_SCRATCH_BYTES (e.g. dstate < 16 with a very long
- *   batch * seqlen, whose padded rows scale with it); use ss_scan_fwd then.
+ *   more than SS_SCAN_STATIC_SCRATCH_BYTES (e.g. dstate < 16 or a nonzero
+ *   bc_stride with a very long batch * seqlen, whose padded rows scale with
+ *   it); use ss_scan_fwd then.
  * All calls on one GPU share its array, which keeps the last call's contents
  * (every value a call reads from it, that call has written first): calls that
  * overlap on one GPU (different streams, or threads without ordering) race.
