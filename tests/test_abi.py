@@ -517,3 +517,15 @@ def test_binding_structs_match_headers(tmp_path):
         assert got[(cname, "size")] == ctypes.sizeof(py), cname
         for fname, _ in py._fields_:
             assert got[(cname, fname)] == getattr(py, fname).offset, (cname, fname)
+
+
+def test_noalloc_scratch_limit_with_strided_rows(lib):
+    """Strided B/C rows are copied into the scratch: a long problem with a row
+    stride exceeds the static array where the dense one needs none."""
+    P = FAKE
+    args = [P, P + 256, P + 512, P + 1026, P + 1538, None, None, None, None, P + 4096, None]
+    dense = B.make_desc(1, 1 << 20, 5120, 16, B.SS_BF16, B.SS_F32)
+    strided = B.make_desc(1, 1 << 20, 5120, 16, B.SS_BF16, B.SS_F32, bc_stride=48)
+    assert B.ss_scan_workspace_bytes(dense, B.SS_OP_FWD) <= B.SS_SCAN_STATIC_SCRATCH_BYTES
+    assert B.ss_scan_workspace_bytes(strided, B.SS_OP_FWD) > B.SS_SCAN_STATIC_SCRATCH_BYTES
+    assert B.ss_scan_fwd_noalloc(strided, *args, stream=0) == B.SS_ERR_SCRATCH_LIMIT
